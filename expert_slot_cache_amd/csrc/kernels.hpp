@@ -1,0 +1,65 @@
+// Launchers of the gfx950 kernels (C++ linkage, used by the C-ABI runtime only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+enum WType { W_F32 = 0, W_BF16 = 1, W_INT4 = 2 };
+enum AType { A_F32 = 0, A_BF16 = 1 };
+
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 64;
+constexpr int kDecodeMaxTokens = 8;   // n_tokens above this use the grouped GEMM path
+constexpr int kMaxLdsFloats = 12288;  // 48 KiB of fp32 activations per workgroup
+
+// Shape and byte layout of one expert as stored in a slot.
+struct Geom {
+    int H, I, K;
+    int wtype, atype;
+    size_t slot_stride;             // bytes per slot (= bytes per expert)
+    size_t off_w13, off_w2, off_s13, off_s2;
+};
+
+// Distinct ids of ids[0..n): rb[0] = D, rb[1] = 1 if an id is outside [0,E),
+// rb[2..2+D) = ascending distinct ids; rank[e] = position of e in that list.
+hipError_t launch_distinct(const int32_t* ids, int n, int E, int32_t* rb, int32_t* rank,
+                           hipStream_t stream);
+
+// out[i] = table[ids[i]] (ids outside [0,E) give -1).
+hipError_t launch_remap(const int32_t* ids, int n, int E, const int32_t* table, int32_t* out,
+                        hipStream_t stream);
+
+// Optional event pairs around the two projection stages (any may be null).
+struct StageEvents {
+    hipEvent_t w13_start = nullptr, w13_stop = nullptr;
+    hipEvent_t w2_start = nullptr, w2_stop = nullptr;
+};
+
+struct ForwardArgs {
+    const char* wbase;      // slot 0 of the pool (or staging)
+    int nslots;             // valid slot ids are [0, nslots)
+    const int32_t* slot_ids;// [T][K]
+    const void* x;          // [T][H]
+    const float* topk_w;    // [T][K]
+    const void* resid;      // [T][H] or null
+    void* out;              // [T][H]
+    int T;
+    // scratch
+    float* act;             // [T*K][I] fp32 (decode path)
+    uint16_t* act_bf16;     // [T*K][I] bf16 (grouped path)
+    float* y;               // [T*K][H] fp32 (grouped path)
+    int32_t* grp;           // grouped-path index buffers (see launch_forward)
+    int n_slot_groups;      // number of distinct slot ids possible (nslots)
+};
+
+// The slot-indexed fused MoE for one layer.
+hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents* ev,
+                          hipStream_t stream);
+
+// Bytes of the grouped-path index buffer for max_tokens tokens and nslots slots.
+size_t grouped_index_bytes(int max_tokens, int K, int nslots);
+
+}  // namespace moe

@@ -1,0 +1,746 @@
+// C-ABI runtime of the expert slot cache: pinned host store, fixed-address HBM slot
+// pools, copy streams joined by events, the per-layer slot manager, prepare/forward.
+//
+// Step order per layer (llama.cpp "Persistent expert slot pool", section "Design"
+// item 3: read ids back, update the LRU, issue async H2D for misses and rewrite the
+// map table before the remap consumes it):
+//   1. k_distinct on the compute stream -> distinct ids in pinned host memory;
+//      wait for it (the one host sync of a step).
+//   2. host: range check, route rule, LRU update (SlotLRU) -> miss list.
+//   3. copy streams wait for the layer's last forward (its slot reads, WAR), then
+//      hipMemcpyAsync store -> slot for each miss, optionally in chunks, then an
+//      event per copy stream that the compute stream waits on (RAW).
+//   4. the changed map entries are written to a pinned copy of the table, which is
+//      uploaded on the compute stream; k_remap then reads the fresh table.
+//   5. forward kernels on the compute stream; record the layer's reads-done event.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "moe_pool.h"
+#include "kernels.hpp"
+#include "slot_lru.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+#define FAIL(code, ...)        \
+    do {                       \
+        set_err(__VA_ARGS__);  \
+        return (code);         \
+    } while (0)
+
+#define HIPCHK(call)                                                                     \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess) {                                                          \
+            set_err("%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, __LINE__); \
+            return MOE_EHIP;                                                             \
+        }                                                                                \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t off_w13 = 0, off_w2 = 0, off_s13 = 0, off_s2 = 0, total = 0;
+};
+
+bool make_layout(int32_t wtype, int32_t H, int32_t I, Layout* L) {
+    if (H <= 0 || I <= 0) return false;
+    size_t w13, w2, s13 = 0, s2 = 0;
+    if (wtype == MOE_W_F32) {
+        if (H % 4 || I % 4) return false;
+        w13 = (size_t)2 * I * H * 4;
+        w2 = (size_t)H * I * 4;
+    } else if (wtype == MOE_W_BF16) {
+        if (H % 8 || I % 8) return false;
+        w13 = (size_t)2 * I * H * 2;
+        w2 = (size_t)H * I * 2;
+    } else if (wtype == MOE_W_INT4_G128) {
+        if (H % 128 || I % 128) return false;
+        w13 = (size_t)I * H;           // 2I rows x H/2 bytes
+        w2 = (size_t)H * I / 2;
+        s13 = (size_t)2 * I * (H / 128) * 2;
+        s2 = (size_t)H * (I / 128) * 2;
+    } else {
+        return false;
+    }
+    L->off_w13 = 0;
+    L->off_w2 = round_up(w13);
+    size_t end = round_up(L->off_w2 + w2);
+    if (wtype == MOE_W_INT4_G128) {
+        L->off_s13 = end;
+        L->off_s2 = round_up(L->off_s13 + s13);
+        end = round_up(L->off_s2 + s2);
+    } else {
+        L->off_s13 = L->off_s2 = 0;
+    }
+    L->total = end;
+    return true;
+}
+
+struct Timing {
+    hipEvent_t a = nullptr, b = nullptr;   // start, stop
+    bool pending = false;
+};
+
+struct LayerState {
+    moe::SlotLRU lru;
+    char* store = nullptr;       // pinned host: E experts
+    char* slots = nullptr;       // HBM: nslot_alloc experts + zeroed tail
+    int32_t* map_dev = nullptr;  // HBM int32 [E]
+    int32_t* map_host = nullptr; // pinned int32 [E], source of the table upload
+    hipEvent_t reads_done = nullptr;
+    bool reads_recorded = false;
+    bool prepared = false;
+    int32_t prep_tokens = 0;
+    int32_t prep_path = MOE_PATH_POOL;
+    uint64_t bytes_h2d = 0;
+    uint64_t staged = 0;
+    std::vector<Timing> copy_t;  // one per copy stream
+    Timing w13_t, w2_t;
+};
+
+}  // namespace
+
+struct moe_pool {
+    moe_pool_config_t cfg{};
+    Layout lay;
+    moe::Geom geom{};
+    int32_t nslot_alloc = 0;
+    hipStream_t compute = nullptr;
+    std::vector<hipStream_t> copy;
+    std::vector<hipEvent_t> copy_done;
+    std::vector<LayerState> layers;
+    char* staging = nullptr;
+    int32_t staging_cap = 0;
+    int32_t staging_owner = -1;
+    hipEvent_t staging_reads_done = nullptr;
+    bool staging_recorded = false;
+    int32_t* rb_host = nullptr;   // pinned [2 + E], written by k_distinct
+    int32_t* rb_dev = nullptr;    // device view of rb_host
+    hipEvent_t rb_event = nullptr;
+    int32_t* rank_dev = nullptr;  // HBM [E]
+    int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
+    float* act = nullptr;         // HBM [max_tokens * K * I]
+    std::vector<moe::Miss> misses;
+    std::vector<char> used_copy;
+    int copy_rr = 0;
+    // timing totals
+    double copy_ms = 0, w13_ms = 0, w2_ms = 0, sync_ms = 0;
+    uint64_t copy_calls = 0, fwd_calls = 0;
+};
+
+struct moe_lru {
+    moe::SlotLRU lru;
+    std::vector<moe::Miss> misses;
+    std::vector<int32_t> u;
+};
+
+namespace {
+
+void destroy_pool(moe_pool* p) {
+    if (!p) return;
+    if (p->compute || !p->copy.empty()) (void)hipDeviceSynchronize();
+    for (auto& L : p->layers) {
+        if (L.store) (void)hipHostFree(L.store);
+        if (L.slots) (void)hipFree(L.slots);
+        if (L.map_dev) (void)hipFree(L.map_dev);
+        if (L.map_host) (void)hipHostFree(L.map_host);
+        if (L.reads_done) (void)hipEventDestroy(L.reads_done);
+        for (auto& t : L.copy_t) {
+            if (t.a) (void)hipEventDestroy(t.a);
+            if (t.b) (void)hipEventDestroy(t.b);
+        }
+        for (Timing* t : {&L.w13_t, &L.w2_t}) {
+            if (t->a) (void)hipEventDestroy(t->a);
+            if (t->b) (void)hipEventDestroy(t->b);
+        }
+    }
+    for (auto s : p->copy) (void)hipStreamDestroy(s);
+    for (auto e : p->copy_done) (void)hipEventDestroy(e);
+    if (p->staging) (void)hipFree(p->staging);
+    if (p->staging_reads_done) (void)hipEventDestroy(p->staging_reads_done);
+    if (p->rb_host) (void)hipHostFree(p->rb_host);
+    if (p->rb_event) (void)hipEventDestroy(p->rb_event);
+    if (p->rank_dev) (void)hipFree(p->rank_dev);
+    if (p->ident_dev) (void)hipFree(p->ident_dev);
+    if (p->act) (void)hipFree(p->act);
+    delete p;
+}
+
+moe_status_t check_layer(const moe_pool* p, int32_t layer) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    if (layer < 0 || layer >= p->cfg.n_layers) FAIL(MOE_EINVAL, "layer %d outside [0,%d)", layer, p->cfg.n_layers);
+    return MOE_OK;
+}
+
+// Harvest finished timing event pairs (all work before the last readback sync).
+void harvest(moe_pool* p, Timing& t, double* acc) {
+    if (!t.pending) return;
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) *acc += ms;
+    t.pending = false;
+}
+
+void harvest_layer(moe_pool* p, LayerState& L) {
+    if (!p->cfg.timing) return;
+    // the copy span of a step: earliest start to latest stop over the copy streams
+    bool any = false;
+    for (auto& t : L.copy_t) any = any || t.pending;
+    if (any) {
+        int ref = -1;
+        for (size_t i = 0; i < L.copy_t.size(); ++i)
+            if (L.copy_t[i].pending) {
+                ref = (int)i;
+                break;
+            }
+        float lo = 0, hi = 0;
+        for (auto& t : L.copy_t) {
+            if (!t.pending) continue;
+            float s = 0, e = 0;
+            (void)hipEventElapsedTime(&s, L.copy_t[ref].a, t.a);
+            (void)hipEventElapsedTime(&e, L.copy_t[ref].a, t.b);
+            lo = std::min(lo, s);
+            hi = std::max(hi, e);
+            t.pending = false;
+        }
+        p->copy_ms += hi - lo;
+        p->copy_calls++;
+    }
+    harvest(p, L.w13_t, &p->w13_ms);
+    harvest(p, L.w2_t, &p->w2_ms);
+}
+
+void harvest_all(moe_pool* p) {
+    for (auto& L : p->layers) harvest_layer(p, L);
+}
+
+// Enqueue host->HBM copies of `n` experts (src[i] -> dst[i]) on the copy streams,
+// after `war` (the last reads of the destination), and make the compute stream
+// wait for them.
+moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, const char*>>& jobs,
+                          hipEvent_t war, bool war_recorded) {
+    if (jobs.empty()) return MOE_OK;
+    const int ns = (int)p->copy.size();
+    const size_t eb = p->lay.total;
+    const size_t chunk = p->cfg.copy_chunk_bytes ? p->cfg.copy_chunk_bytes : eb;
+    std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
+    // every stream that may carry a piece first waits for the WAR event
+    const int streams_needed = std::min<size_t>(ns, jobs.size() * ((eb + chunk - 1) / chunk));
+    for (int i = 0; i < streams_needed; ++i) {
+        const int s = (p->copy_rr + i) % ns;
+        if (war_recorded) HIPCHK(hipStreamWaitEvent(p->copy[s], war, 0));
+        if (p->cfg.timing) {
+            HIPCHK(hipEventRecord(L.copy_t[s].a, p->copy[s]));
+        }
+        p->used_copy[s] = 1;
+    }
+    int rr = p->copy_rr;
+    for (const auto& j : jobs) {
+        for (size_t off = 0; off < eb; off += chunk) {
+            const size_t n = std::min(chunk, eb - off);
+            HIPCHK(hipMemcpyAsync(j.first + off, j.second + off, n, hipMemcpyHostToDevice, p->copy[rr]));
+            rr = (rr + 1) % ns;
+        }
+    }
+    p->copy_rr = rr;
+    for (int s = 0; s < ns; ++s) {
+        if (!p->used_copy[s]) continue;
+        if (p->cfg.timing) {
+            HIPCHK(hipEventRecord(L.copy_t[s].b, p->copy[s]));
+            L.copy_t[s].pending = true;
+        }
+        HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
+        HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+    }
+    L.bytes_h2d += (uint64_t)eb * jobs.size();
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ENOMEM: return "out of memory";
+        case MOE_EHIP: return "HIP runtime error";
+        case MOE_ERANGE: return "expert id out of range";
+        case MOE_ESTATE: return "forward without a matching prepare";
+    }
+    return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_expert_bytes(int32_t wtype, int32_t hidden, int32_t inter) {
+    Layout L;
+    return make_layout(wtype, hidden, inter, &L) ? L.total : 0;
+}
+
+moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_pool_t** out) {
+    if (!cfg || !out) FAIL(MOE_EINVAL, "null argument");
+    *out = nullptr;
+    const moe_pool_config_t& c = *cfg;
+    if (c.n_layers < 1) FAIL(MOE_EINVAL, "n_layers %d < 1", c.n_layers);
+    if (c.n_experts < 1 || c.n_experts > moe::kMaxExperts) FAIL(MOE_EINVAL, "n_experts %d outside [1,%d]", c.n_experts, moe::kMaxExperts);
+    if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > moe::kMaxTopK) FAIL(MOE_EINVAL, "top_k %d invalid", c.top_k);
+    if (c.n_slots < 0) FAIL(MOE_EINVAL, "n_slots %d < 0", c.n_slots);
+    if (c.atype != MOE_A_F32 && c.atype != MOE_A_BF16) FAIL(MOE_EINVAL, "atype %d invalid", c.atype);
+    if (c.rule != MOE_RULE_DISTINCT && c.rule != MOE_RULE_STATIC) FAIL(MOE_EINVAL, "rule %d invalid", c.rule);
+    if (c.max_tokens < 1) FAIL(MOE_EINVAL, "max_tokens %d < 1", c.max_tokens);
+    if (c.n_copy_streams < 1 || c.n_copy_streams > 8) FAIL(MOE_EINVAL, "n_copy_streams %d outside [1,8]", c.n_copy_streams);
+    if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
+    Layout lay;
+    if (!make_layout(c.wtype, c.hidden, c.inter, &lay)) FAIL(MOE_EINVAL, "unsupported shape/format (wtype %d, H %d, I %d)", c.wtype, c.hidden, c.inter);
+    if (c.hidden > moe::kMaxLdsFloats || (size_t)c.top_k * c.inter > (size_t)moe::kMaxLdsFloats)
+        FAIL(MOE_EINVAL, "hidden and top_k*inter must be <= %d", moe::kMaxLdsFloats);
+
+    moe_pool* p = new (std::nothrow) moe_pool();
+    if (!p) FAIL(MOE_ENOMEM, "host allocation failed");
+    p->cfg = c;
+    p->lay = lay;
+    p->compute = static_cast<hipStream_t>(stream);
+    p->geom.H = c.hidden;
+    p->geom.I = c.inter;
+    p->geom.K = c.top_k;
+    p->geom.wtype = c.wtype;
+    p->geom.atype = c.atype;
+    p->geom.slot_stride = lay.total;
+    p->geom.off_w13 = lay.off_w13;
+    p->geom.off_w2 = lay.off_w2;
+    p->geom.off_s13 = lay.off_s13;
+    p->geom.off_s2 = lay.off_s2;
+    const int32_t E = c.n_experts;
+    p->nslot_alloc = c.resident ? E : c.n_slots;
+    p->staging_cap = c.resident ? 0 : (int32_t)std::min<int64_t>(E, (int64_t)c.top_k * c.max_tokens);
+
+    const size_t eb = lay.total;
+    const size_t slot_bytes = (size_t)p->nslot_alloc * eb + kAlign;
+    const size_t act_bytes = (size_t)c.max_tokens * c.top_k * c.inter * sizeof(float);
+    const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4) + (size_t)p->staging_cap * eb + act_bytes +
+                       (size_t)E * 8;
+    if (c.hbm_budget_bytes && hbm > c.hbm_budget_bytes) {
+        delete p;
+        FAIL(MOE_ENOMEM, "pool needs %zu HBM bytes, budget is %zu", hbm, c.hbm_budget_bytes);
+    }
+
+#define CREATE_HIP(call)                                                                            \
+    do {                                                                                            \
+        hipError_t e_ = (call);                                                                     \
+        if (e_ != hipSuccess) {                                                                     \
+            set_err("%s failed: %s", #call, hipGetErrorString(e_));                                 \
+            destroy_pool(p);                                                                        \
+            return (e_ == hipErrorOutOfMemory || e_ == hipErrorMemoryAllocation) ? MOE_ENOMEM : MOE_EHIP; \
+        }                                                                                           \
+    } while (0)
+
+    p->copy.resize(c.n_copy_streams, nullptr);
+    p->copy_done.resize(c.n_copy_streams, nullptr);
+    p->used_copy.assign(c.n_copy_streams, 0);
+    for (int i = 0; i < c.n_copy_streams; ++i) {
+        CREATE_HIP(hipStreamCreateWithFlags(&p->copy[i], hipStreamNonBlocking));
+        CREATE_HIP(hipEventCreateWithFlags(&p->copy_done[i], hipEventDisableTiming));
+    }
+    const unsigned tflag = c.timing ? hipEventDefault : hipEventDisableTiming;
+    p->layers.resize(c.n_layers);
+    for (int32_t l = 0; l < c.n_layers; ++l) {
+        LayerState& L = p->layers[l];
+        L.lru.init(E, c.resident ? 0 : c.n_slots, c.rule);
+        CREATE_HIP(hipHostMalloc((void**)&L.store, (size_t)E * eb, hipHostMallocDefault));
+        CREATE_HIP(hipMalloc((void**)&L.slots, slot_bytes));
+        CREATE_HIP(hipMemset(L.slots + (size_t)p->nslot_alloc * eb, 0, kAlign));
+        CREATE_HIP(hipMalloc((void**)&L.map_dev, (size_t)E * 4));
+        CREATE_HIP(hipHostMalloc((void**)&L.map_host, (size_t)E * 4, hipHostMallocDefault));
+        for (int32_t e = 0; e < E; ++e) L.map_host[e] = -1;
+        CREATE_HIP(hipMemcpy(L.map_dev, L.map_host, (size_t)E * 4, hipMemcpyHostToDevice));
+        CREATE_HIP(hipEventCreateWithFlags(&L.reads_done, hipEventDisableTiming));
+        L.copy_t.resize(c.n_copy_streams);
+        if (c.timing) {
+            for (auto& t : L.copy_t) {
+                CREATE_HIP(hipEventCreateWithFlags(&t.a, tflag));
+                CREATE_HIP(hipEventCreateWithFlags(&t.b, tflag));
+            }
+            for (Timing* t : {&L.w13_t, &L.w2_t}) {
+                CREATE_HIP(hipEventCreateWithFlags(&t->a, tflag));
+                CREATE_HIP(hipEventCreateWithFlags(&t->b, tflag));
+            }
+        }
+    }
+    if (p->staging_cap > 0) CREATE_HIP(hipMalloc((void**)&p->staging, (size_t)p->staging_cap * eb));
+    CREATE_HIP(hipEventCreateWithFlags(&p->staging_reads_done, hipEventDisableTiming));
+    CREATE_HIP(hipHostMalloc((void**)&p->rb_host, (size_t)(E + 2) * 4, hipHostMallocCoherent | hipHostMallocMapped));
+    CREATE_HIP(hipHostGetDevicePointer((void**)&p->rb_dev, p->rb_host, 0));
+    CREATE_HIP(hipEventCreateWithFlags(&p->rb_event, hipEventDisableTiming));
+    CREATE_HIP(hipMalloc((void**)&p->rank_dev, (size_t)E * 4));
+    CREATE_HIP(hipMalloc((void**)&p->ident_dev, (size_t)E * 4));
+    {
+        std::vector<int32_t> id(E);
+        for (int32_t e = 0; e < E; ++e) id[e] = e;
+        CREATE_HIP(hipMemcpy(p->ident_dev, id.data(), (size_t)E * 4, hipMemcpyHostToDevice));
+    }
+    CREATE_HIP(hipMalloc((void**)&p->act, act_bytes));
+#undef CREATE_HIP
+    p->misses.reserve(E);
+    *out = p;
+    return MOE_OK;
+}
+
+void moe_pool_destroy(moe_pool_t* pool) { destroy_pool(pool); }
+
+moe_status_t moe_pool_load_expert(moe_pool_t* p, int32_t layer, int32_t expert, const void* host_src,
+                                  size_t nbytes) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (expert < 0 || expert >= p->cfg.n_experts) FAIL(MOE_EINVAL, "expert %d outside [0,%d)", expert, p->cfg.n_experts);
+    if (!host_src || nbytes != p->lay.total) FAIL(MOE_EINVAL, "need %zu bytes, got %zu", p->lay.total, nbytes);
+    LayerState& L = p->layers[layer];
+    // the store may be the source of a queued copy: let those finish first
+    for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
+    std::memcpy(L.store + (size_t)expert * p->lay.total, host_src, nbytes);
+    if (p->cfg.resident)
+        HIPCHK(hipMemcpy(L.slots + (size_t)expert * p->lay.total, L.store + (size_t)expert * p->lay.total, nbytes,
+                         hipMemcpyHostToDevice));
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_reset(moe_pool_t* p) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    HIPCHK(hipStreamSynchronize(p->compute));
+    for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
+    for (auto& L : p->layers) {
+        L.lru.reset();
+        for (int32_t e = 0; e < p->cfg.n_experts; ++e) L.map_host[e] = -1;
+        HIPCHK(hipMemcpy(L.map_dev, L.map_host, (size_t)p->cfg.n_experts * 4, hipMemcpyHostToDevice));
+        L.prepared = false;
+        L.bytes_h2d = 0;
+        L.staged = 0;
+    }
+    p->staging_owner = -1;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
+                              int32_t* slot_ids_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss,
+                              int32_t* path) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (n_tokens < 0 || n_tokens > p->cfg.max_tokens) FAIL(MOE_EINVAL, "n_tokens %d outside [0,%d]", n_tokens, p->cfg.max_tokens);
+    if (n_tokens > 0 && (!topk_ids_dev || !slot_ids_dev)) FAIL(MOE_EINVAL, "null ids");
+    if (miss_cap < 0) FAIL(MOE_EINVAL, "miss_cap < 0");
+    LayerState& L = p->layers[layer];
+    const int32_t E = p->cfg.n_experts;
+    const int n = n_tokens * p->cfg.top_k;
+    const size_t eb = p->lay.total;
+
+    if (n_tokens == 0) {
+        p->misses.clear();
+        if (p->cfg.resident) L.lru.count_resident(0); else L.lru.step(nullptr, 0, 0, p->misses);
+        L.prepared = true;
+        L.prep_tokens = 0;
+        L.prep_path = MOE_PATH_POOL;
+        if (n_miss) *n_miss = 0;
+        if (path) *path = MOE_PATH_POOL;
+        return MOE_OK;
+    }
+
+    // 1. distinct ids, read back: the step's one host sync
+    HIPCHK(moe::launch_distinct(topk_ids_dev, n, E, p->rb_dev, p->rank_dev, p->compute));
+    HIPCHK(hipEventRecord(p->rb_event, p->compute));
+    const auto t0 = std::chrono::steady_clock::now();
+    HIPCHK(hipEventSynchronize(p->rb_event));
+    if (p->cfg.timing) {
+        p->sync_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        harvest_all(p);
+    }
+    const int32_t D = p->rb_host[0];
+    if (p->rb_host[1] != 0) FAIL(MOE_ERANGE, "layer %d: an expert id is outside [0,%d)", layer, E);
+    if (D < 1 || D > E) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
+    const int32_t* u = p->rb_host + 2;
+
+    // 2. route + LRU
+    p->misses.clear();
+    int32_t the_path = MOE_PATH_POOL;
+    if (p->cfg.resident) {
+        L.lru.count_resident(D);
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, slot_ids_dev, p->compute));
+    } else if (L.lru.step(u, D, (int64_t)n, p->misses)) {
+        // 3. misses: store -> slot on the copy streams, after this layer's last reads
+        if (!p->misses.empty()) {
+            std::vector<std::pair<char*, const char*>> jobs;
+            jobs.reserve(p->misses.size());
+            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.store + (size_t)m.expert * eb);
+            st = issue_copies(p, L, jobs, L.reads_done, L.reads_recorded);
+            if (st) return st;
+            // 4. rewrite the changed map entries and upload the table before the remap
+            for (const auto& m : p->misses) {
+                if (m.evicted >= 0) L.map_host[m.evicted] = -1;
+                L.map_host[m.expert] = m.slot;
+            }
+            HIPCHK(hipMemcpyAsync(L.map_dev, L.map_host, (size_t)E * 4, hipMemcpyHostToDevice, p->compute));
+        }
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, slot_ids_dev, p->compute));
+    } else {
+        // selective-copy fallback: the step's experts go to staging in rank order;
+        // the pool is untouched
+        the_path = MOE_PATH_FALLBACK;
+        std::vector<std::pair<char*, const char*>> jobs;
+        jobs.reserve(D);
+        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.store + (size_t)u[r] * eb);
+        st = issue_copies(p, L, jobs, p->staging_reads_done, p->staging_recorded);
+        if (st) return st;
+        L.staged += (uint64_t)D;
+        p->staging_owner = layer;
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->rank_dev, slot_ids_dev, p->compute));
+    }
+    L.prepared = true;
+    L.prep_tokens = n_tokens;
+    L.prep_path = the_path;
+    const int32_t nm = (int32_t)p->misses.size();
+    if (miss_host) {
+        for (int32_t i = 0; i < std::min(nm, miss_cap); ++i)
+            miss_host[i] = moe_miss_t{p->misses[i].expert, p->misses[i].slot, p->misses[i].evicted};
+    }
+    if (n_miss) *n_miss = nm;
+    if (path) *path = the_path;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, const int32_t* slot_ids_dev,
+                              const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    LayerState& L = p->layers[layer];
+    if (!L.prepared || L.prep_tokens != n_tokens)
+        FAIL(MOE_ESTATE, "layer %d: forward(n_tokens=%d) without a matching prepare", layer, n_tokens);
+    const bool fb = L.prep_path == MOE_PATH_FALLBACK;
+    if (fb && p->staging_owner != layer)
+        FAIL(MOE_ESTATE, "layer %d: its staged experts were replaced by layer %d's fallback", layer, p->staging_owner);
+    if (n_tokens == 0) return MOE_OK;
+    if (!x_dev || !slot_ids_dev || !topk_w_dev || !out_dev) FAIL(MOE_EINVAL, "null buffer");
+    moe::ForwardArgs a{};
+    a.wbase = fb ? p->staging : L.slots;
+    a.nslots = fb ? p->staging_cap : p->nslot_alloc;
+    a.slot_ids = slot_ids_dev;
+    a.x = x_dev;
+    a.topk_w = topk_w_dev;
+    a.resid = resid_dev;
+    a.out = out_dev;
+    a.T = n_tokens;
+    a.act = p->act;
+    moe::StageEvents ev;
+    if (p->cfg.timing) {
+        ev.w13_start = L.w13_t.a;
+        ev.w13_stop = L.w13_t.b;
+        ev.w2_start = L.w2_t.a;
+        ev.w2_stop = L.w2_t.b;
+    }
+    HIPCHK(moe::launch_forward(p->geom, a, p->cfg.timing ? &ev : nullptr, p->compute));
+    if (p->cfg.timing) {
+        L.w13_t.pending = true;
+        L.w2_t.pending = true;
+        p->fwd_calls++;
+    }
+    if (fb) {
+        HIPCHK(hipEventRecord(p->staging_reads_done, p->compute));
+        p->staging_recorded = true;
+    } else {
+        HIPCHK(hipEventRecord(L.reads_done, p->compute));
+        L.reads_recorded = true;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_sync(moe_pool_t* p) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
+    HIPCHK(hipStreamSynchronize(p->compute));
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_get_stats(const moe_pool_t* p, int32_t layer, moe_pool_stats_t* out) {
+    if (!p || !out) FAIL(MOE_EINVAL, "null argument");
+    if (layer < -1 || layer >= p->cfg.n_layers) FAIL(MOE_EINVAL, "layer %d invalid", layer);
+    std::memset(out, 0, sizeof(*out));
+    for (int32_t l = 0; l < p->cfg.n_layers; ++l) {
+        if (layer >= 0 && l != layer) continue;
+        const LayerState& L = p->layers[l];
+        out->steps += L.lru.steps();
+        out->hits += L.lru.hits();
+        out->misses += L.lru.misses();
+        out->fallbacks += L.lru.fallbacks();
+        out->bytes_h2d += L.bytes_h2d;
+        out->staged += L.staged;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map_E, int32_t* owner_N,
+                                int32_t* lru_N) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    const moe::SlotLRU& s = p->layers[layer].lru;
+    if (map_E) std::copy(s.map().begin(), s.map().end(), map_E);
+    if (owner_N) std::copy(s.owner().begin(), s.owner().end(), owner_N);
+    if (lru_N) s.lru_order(lru_N, s.n_slots());
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_read_slot(moe_pool_t* p, int32_t layer, int32_t slot, void* host_dst, size_t n) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (!host_dst || n > p->lay.total) FAIL(MOE_EINVAL, "bad destination or size");
+    const char* src;
+    if (slot >= 0) {
+        if (slot >= p->nslot_alloc) FAIL(MOE_EINVAL, "slot %d outside [0,%d)", slot, p->nslot_alloc);
+        src = p->layers[layer].slots + (size_t)slot * p->lay.total;
+    } else {
+        const int32_t r = -slot - 1;
+        if (r >= p->staging_cap) FAIL(MOE_EINVAL, "staging entry %d outside [0,%d)", r, p->staging_cap);
+        src = p->staging + (size_t)r * p->lay.total;
+    }
+    st = moe_pool_sync(p);
+    if (st) return st;
+    HIPCHK(hipMemcpy(host_dst, src, n, hipMemcpyDeviceToHost));
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_slot_ptr(const moe_pool_t* p, int32_t layer, int32_t slot, void** dev_ptr) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (!dev_ptr || slot < 0 || slot >= p->nslot_alloc) FAIL(MOE_EINVAL, "bad slot %d", slot);
+    *dev_ptr = p->layers[layer].slots + (size_t)slot * p->lay.total;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_store_ptr(const moe_pool_t* p, int32_t layer, int32_t expert, void** host_ptr) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (!host_ptr || expert < 0 || expert >= p->cfg.n_experts) FAIL(MOE_EINVAL, "bad expert %d", expert);
+    *host_ptr = p->layers[layer].store + (size_t)expert * p->lay.total;
+    return MOE_OK;
+}
+
+moe_status_t moe_ptr_is_pinned_host(const void* ptr, int32_t* is_pinned) {
+    if (!ptr || !is_pinned) FAIL(MOE_EINVAL, "null argument");
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *is_pinned = 0;
+        return MOE_OK;
+    }
+    *is_pinned = attr.type == hipMemoryTypeHost ? 1 : 0;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_get_timing(moe_pool_t* p, moe_pool_timing_t* out) {
+    if (!p || !out) FAIL(MOE_EINVAL, "null argument");
+    moe_status_t st = moe_pool_sync(p);
+    if (st) return st;
+    harvest_all(p);
+    out->copy_ms = p->copy_ms;
+    out->copy_calls = p->copy_calls;
+    out->w13_ms = p->w13_ms;
+    out->w2_ms = p->w2_ms;
+    out->forward_calls = p->fwd_calls;
+    out->sync_wait_ms = p->sync_ms;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_reset_timing(moe_pool_t* p) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    moe_status_t st = moe_pool_sync(p);
+    if (st) return st;
+    harvest_all(p);
+    p->copy_ms = p->w13_ms = p->w2_ms = p->sync_ms = 0;
+    p->copy_calls = p->fwd_calls = 0;
+    return MOE_OK;
+}
+
+// ---- host-only slot manager ---------------------------------------------------
+moe_status_t moe_lru_create(int32_t n_experts, int32_t n_slots, int32_t rule, moe_lru_t** out) {
+    if (!out) FAIL(MOE_EINVAL, "null out");
+    *out = nullptr;
+    if (n_experts < 1 || n_experts > moe::kMaxExperts || n_slots < 0) FAIL(MOE_EINVAL, "bad sizes");
+    if (rule != MOE_RULE_DISTINCT && rule != MOE_RULE_STATIC) FAIL(MOE_EINVAL, "bad rule");
+    moe_lru* l = new (std::nothrow) moe_lru();
+    if (!l) FAIL(MOE_ENOMEM, "host allocation failed");
+    l->lru.init(n_experts, n_slots, rule);
+    l->u.reserve(n_experts);
+    *out = l;
+    return MOE_OK;
+}
+
+void moe_lru_destroy(moe_lru_t* l) { delete l; }
+
+moe_status_t moe_lru_step(moe_lru_t* l, const int32_t* ids, int32_t n_tokens, int32_t top_k, int32_t* slot_ids,
+                          moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
+    if (!l) FAIL(MOE_EINVAL, "null lru");
+    if (n_tokens < 0 || top_k < 1 || miss_cap < 0) FAIL(MOE_EINVAL, "bad sizes");
+    const int64_t n = (int64_t)n_tokens * top_k;
+    if (n > 0 && (!ids || !slot_ids)) FAIL(MOE_EINVAL, "null ids");
+    const int32_t E = l->lru.n_experts();
+    std::vector<char> seen(E, 0);
+    for (int64_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= E) FAIL(MOE_ERANGE, "expert id %d outside [0,%d)", ids[i], E);
+        seen[ids[i]] = 1;
+    }
+    l->u.clear();
+    std::vector<int32_t> rank(E, -1);
+    for (int32_t e = 0; e < E; ++e)
+        if (seen[e]) {
+            rank[e] = (int32_t)l->u.size();
+            l->u.push_back(e);
+        }
+    l->misses.clear();
+    const bool pooled = l->lru.step(l->u.data(), (int32_t)l->u.size(), n, l->misses);
+    for (int64_t i = 0; i < n; ++i) slot_ids[i] = pooled ? l->lru.map()[ids[i]] : rank[ids[i]];
+    const int32_t nm = (int32_t)l->misses.size();
+    if (miss_host)
+        for (int32_t i = 0; i < std::min(nm, miss_cap); ++i)
+            miss_host[i] = moe_miss_t{l->misses[i].expert, l->misses[i].slot, l->misses[i].evicted};
+    if (n_miss) *n_miss = nm;
+    if (path) *path = pooled ? MOE_PATH_POOL : MOE_PATH_FALLBACK;
+    return MOE_OK;
+}
+
+moe_status_t moe_lru_get_state(const moe_lru_t* l, int32_t* map_E, int32_t* owner_N, int32_t* lru_N) {
+    if (!l) FAIL(MOE_EINVAL, "null lru");
+    if (map_E) std::copy(l->lru.map().begin(), l->lru.map().end(), map_E);
+    if (owner_N) std::copy(l->lru.owner().begin(), l->lru.owner().end(), owner_N);
+    if (lru_N) l->lru.lru_order(lru_N, l->lru.n_slots());
+    return MOE_OK;
+}
+
+moe_status_t moe_lru_get_stats(const moe_lru_t* l, moe_pool_stats_t* out) {
+    if (!l || !out) FAIL(MOE_EINVAL, "null argument");
+    std::memset(out, 0, sizeof(*out));
+    out->steps = l->lru.steps();
+    out->hits = l->lru.hits();
+    out->misses = l->lru.misses();
+    out->fallbacks = l->lru.fallbacks();
+    return MOE_OK;
+}
+
+}  // extern "C"

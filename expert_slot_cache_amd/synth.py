@@ -159,7 +159,7 @@ def normal_bf16_bits(rng: np.random.Generator, n: int, std: float) -> np.ndarray
     Used for the large stores, where a Ziggurat draw per weight would take minutes.
     The quantile grid (2**-16 in probability) is finer than bf16's own grid."""
     table = f32_to_bf16_bits(_normal_table() * np.float32(std))
-    idx = rng.integers(0, 65536, size=n, dtype=np.uint16)
+    idx = np.frombuffer(rng.bytes(2 * n), dtype=np.uint16)
     return table[idx]
 
 
@@ -182,33 +182,33 @@ def quantize_int4_g128(w: np.ndarray):
 
 
 def _int4_nibble_table() -> np.ndarray:
-    """65536-entry map from uniform 16-bit draws to a code 0..15 whose distribution is
-    that of quantize_int4_g128 applied to groups of 128 normal draws (Monte Carlo,
-    fixed seed)."""
+    """256-entry map from a uniform byte to a code 0..15 whose distribution is that
+    of quantize_int4_g128 applied to groups of 128 normal draws (Monte Carlo, fixed
+    seed; resolution 1/256 in probability)."""
     rng = np.random.Generator(np.random.PCG64(7))
     g = rng.standard_normal((4096, 128)).astype(np.float32)
-    codes, _ = quantize_int4_g128(g.reshape(4096, 128))
+    codes, _ = quantize_int4_g128(g)
     q = ((codes[:, :, None] >> (np.arange(8, dtype=np.uint32) * 4)) & 15).ravel()
     pmf = np.bincount(q, minlength=16).astype(np.float64)
     cdf = np.cumsum(pmf) / pmf.sum()
-    u = (np.arange(65536) + 0.5) / 65536.0
+    u = (np.arange(256) + 0.5) / 256.0
     return np.searchsorted(cdf, u).clip(0, 15).astype(np.uint8)
 
 
-_NIBBLE_TABLE = None
+_BYTE_TABLES = None
 
 
 def random_int4_codes(rng: np.random.Generator, n_words: int) -> np.ndarray:
-    """n_words uint32 words of 8 codes each, distributed like quantised normal weights."""
-    global _NIBBLE_TABLE
-    if _NIBBLE_TABLE is None:
-        _NIBBLE_TABLE = _int4_nibble_table()
-    nib = _NIBBLE_TABLE[rng.integers(0, 65536, size=n_words * 8, dtype=np.uint16)]
-    nib = nib.astype(np.uint32).reshape(n_words, 8)
-    out = np.zeros(n_words, dtype=np.uint32)
-    for j in range(8):
-        out |= nib[:, j] << np.uint32(4 * j)
-    return out
+    """n_words uint32 words of 8 codes each, distributed like quantised normal weights
+    (each byte holds two codes, each drawn from 8 uniform bits)."""
+    global _BYTE_TABLES
+    if _BYTE_TABLES is None:
+        nib = _int4_nibble_table()
+        _BYTE_TABLES = (nib, (nib << 4).astype(np.uint8))
+    lo, hi = _BYTE_TABLES
+    u = np.frombuffer(rng.bytes(8 * n_words), dtype=np.uint8)
+    b = lo[u[0::2]] | hi[u[1::2]]
+    return b.view(np.uint32)
 
 
 # --------------------------------------------------------------------------
@@ -270,6 +270,51 @@ def draw_expert(rng: np.random.Generator, wtype: str, hidden: int, inter: int,
                                   rng.standard_normal(n // 2, dtype=np.float32))
         buf[off:off + n] = f32_to_bf16_bits(np.abs(amax) / np.float32(7.0)).view(np.uint8)
     return buf
+
+
+class WindowedExperts:
+    """Experts for stores too large to draw weight by weight (tens of GiB): every
+    region of expert (layer, e) is a window, at a seeded random offset, into one
+    seeded buffer of that region's format (N(0, std) fp32/bf16, quantised-normal
+    INT4 codes, bf16 scales near max|w|/7).  Each expert's bytes differ; the value
+    distribution is the same as draw_expert(fast=True)."""
+
+    def __init__(self, wl: Workload, base_mib: int = 96, std: float = 0.02):
+        rng = streams(wl)[1]
+        self.wl = wl
+        self.reg = expert_regions(wl.wtype, wl.hidden, wl.inter)
+        nbytes = base_mib << 20
+        names = ["w13", "w2"] + (["s13", "s2"] if wl.wtype == "int4" else [])
+        self.base = {}
+        if wl.wtype == "f32":
+            b = (rng.standard_normal(nbytes // 4, dtype=np.float32) * np.float32(std))
+            self.base["w"] = b.view(np.uint8)
+        elif wl.wtype == "bf16":
+            self.base["w"] = normal_bf16_bits(rng, nbytes // 2, std).view(np.uint8)
+        else:
+            self.base["w"] = random_int4_codes(rng, nbytes // 4).view(np.uint8)
+            n_s = max(1 << 20, (self.reg["s13"][1] + self.reg["s2"][1]) * 4)
+            amax = np.float32(std) * (np.float32(2.6) + np.float32(0.25) *
+                                      rng.standard_normal(n_s // 2, dtype=np.float32))
+            self.base["s"] = f32_to_bf16_bits(np.abs(amax) / np.float32(7.0)).view(np.uint8)
+        self.offsets = {}
+        for name in names:
+            src = self.base["s" if name.startswith("s") else "w"]
+            n = self.reg[name][1]
+            span = (src.size - n) // 16
+            if span <= 0:
+                raise ValueError("base buffer too small")
+            self.offsets[name] = rng.integers(0, span, size=(wl.layers, wl.experts)) * 16
+        self.names = names
+
+    def expert(self, layer: int, e: int, out: np.ndarray | None = None) -> np.ndarray:
+        buf = np.zeros(self.reg["total"], np.uint8) if out is None else out
+        for name in self.names:
+            src = self.base["s" if name.startswith("s") else "w"]
+            off, n = self.reg[name]
+            o = int(self.offsets[name][layer, e])
+            buf[off:off + n] = src[o:o + n]
+        return buf
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,252 @@
+/*
+ * moe_pool.h -- MoE expert offload with a fixed-size HBM expert-slot cache (C ABI).
+ *
+ * All experts of every layer live in one pinned host store.  Each layer owns a
+ * pool of N fixed-address HBM slots; each step the router's topk_ids are reduced
+ * to their distinct experts, hits and misses are counted, the least recently used
+ * slot is evicted for each miss, misses are copied host -> HBM on copy streams,
+ * and topk_ids are remapped to slot ids through the layer's map table.  A step
+ * that touches more distinct experts than there are slots bypasses the pool:
+ * its experts are copied into a staging area and the pool is left untouched.
+ * The experts then run as a slot-indexed fused MoE (w13 projection, SwiGLU, w2
+ * projection, top-k weighted sum).
+ *
+ * Sources (the pages this library implements):
+ *  [vLLM-cache]  vLLM PR "Run MoE models exceeding VRAM via expert CPU offloading
+ *                with GPU cache (--moe-expert-cache-size)": sections "Architecture",
+ *                "How it works", "torch.compile compatibility", the test list, and the
+ *                review thread (OrderedDict LRU, persistent int32 mapping, async H2D).
+ *  [llama-pool]  llama.cpp discussion "RFC: Persistent expert slot pool for MoE CPU
+ *                offload (--moe-expert-cache)": sections "Summary", "Design" (items
+ *                1-4), "Why not the other approaches on the table" (prefill rule),
+ *                "Validation" (stale map table).
+ *  [flash-2x32]  "Running 125B MoE on Two 32 GB Cards": section 1 (INT4 g128 expert
+ *                shape and bytes), section 3.4 (an id of -1 must never reach a kernel).
+ *  [prefetch]    article on vLLM PR #51710 (layer prefetch): copy stream joined back to
+ *                the compute stream with events; large copies split into chunks.
+ *
+ * Conventions for every entry point:
+ *  - Every call returns a moe_status_t; nothing throws or aborts across the ABI.
+ *    moe_last_error() gives a message for the calling thread's last failure.
+ *  - A failing call leaves the pool's cache state (map, owners, LRU order,
+ *    counters, slot bytes) unchanged.
+ *  - "dev" pointers are device (HBM) addresses owned by the caller; "host"
+ *    pointers are ordinary host memory owned by the caller.  The library owns the
+ *    pinned store, the slot pools, the staging area, its scratch buffers, its
+ *    copy streams and events.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    kernels of a pool run on that one compute stream.
+ *  - One host thread per pool at a time ([vLLM-cache] review thread: prepare()
+ *    assumes a single-threaded forward).  Different pools are independent.
+ */
+#ifndef MOE_POOL_H
+#define MOE_POOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+#define MOE_OK       0
+#define MOE_EINVAL  (-1)  /* bad argument or configuration */
+#define MOE_ENOMEM  (-2)  /* host or device allocation failed, or over hbm_budget_bytes */
+#define MOE_EHIP    (-3)  /* a HIP runtime call failed */
+#define MOE_ERANGE  (-4)  /* an expert id outside [0, n_experts) */
+#define MOE_ESTATE  (-5)  /* forward without a matching prepare, or staging reused */
+
+/* weight formats; the byte layout of one expert is given at moe_pool_load_expert */
+#define MOE_W_F32        0
+#define MOE_W_BF16       1
+#define MOE_W_INT4_G128  2
+/* activation / output formats */
+#define MOE_A_F32   0
+#define MOE_A_BF16  1
+/* route rule: when a step bypasses the pool ([llama-pool] prefill rule) */
+#define MOE_RULE_DISTINCT 0  /* distinct experts of the step > n_slots (default) */
+#define MOE_RULE_STATIC   1  /* top_k * n_tokens > n_slots ("can touch more") */
+/* path a step took */
+#define MOE_PATH_POOL     0
+#define MOE_PATH_FALLBACK 1
+
+typedef struct moe_pool moe_pool_t;
+typedef struct moe_lru moe_lru_t;
+
+typedef struct {
+    int32_t n_layers;
+    int32_t n_experts;      /* E per layer, 1..4096 */
+    int32_t top_k;          /* K, 1..min(E, 64) */
+    int32_t hidden;         /* H */
+    int32_t inter;          /* I (w13 has 2I rows: gate rows [0,I), up rows [I,2I)) */
+    int32_t n_slots;        /* N slots per layer; 0 = no pool, every step falls back */
+    int32_t wtype;          /* MOE_W_* */
+    int32_t atype;          /* MOE_A_* */
+    int32_t rule;           /* MOE_RULE_* */
+    int32_t resident;       /* 1 = every expert also lives in HBM at slot = expert id and
+                               the map is the identity: the all-resident reference mode
+                               ([vLLM-cache] "FullGPUProvider"); n_slots is ignored */
+    int32_t max_tokens;     /* largest n_tokens accepted by prepare/forward (>= 1) */
+    int32_t n_copy_streams; /* copy streams for host -> HBM copies, 1..8 */
+    size_t copy_chunk_bytes;/* split each copy into pieces of at most this size
+                               (0 = one hipMemcpyAsync per expert) */
+    size_t hbm_budget_bytes;/* 0 = no limit; else slots + staging + scratch must fit */
+    int32_t timing;         /* 1 = record HIP events around copies and kernels
+                               (moe_pool_get_timing) */
+} moe_pool_config_t;
+
+typedef struct {
+    int32_t expert;   /* the expert copied in */
+    int32_t slot;     /* the slot it now occupies */
+    int32_t evicted;  /* the expert evicted from that slot, or -1 if the slot was free */
+} moe_miss_t;
+
+typedef struct {
+    uint64_t steps;      /* accepted prepare calls (pooled or not) */
+    uint64_t hits;       /* distinct experts found resident, per step */
+    uint64_t misses;     /* distinct experts copied into a slot, per step */
+    uint64_t fallbacks;  /* steps that bypassed the pool */
+    uint64_t bytes_h2d;  /* bytes copied host -> HBM (misses and staging) */
+    uint64_t staged;     /* experts copied into staging by fallback steps */
+} moe_pool_stats_t;
+
+typedef struct {
+    double copy_ms;      /* sum over prepare calls of the copy-stream span of its copies */
+    uint64_t copy_calls; /* prepare calls that issued copies */
+    double w13_ms;       /* sum of durations of the w13 (+ SwiGLU) kernel */
+    double w2_ms;        /* sum of durations of the w2 (+ combine) kernel(s) */
+    uint64_t forward_calls;
+    double sync_wait_ms; /* host time blocked on the distinct-id readback */
+} moe_pool_timing_t;
+
+/* ---- errors -------------------------------------------------------------- */
+const char* moe_strerror(moe_status_t s);
+/* Message for the calling thread's most recent failing call (static storage). */
+const char* moe_last_error(void);
+
+/* ---- layout -------------------------------------------------------------- */
+/* Bytes of one expert in format `wtype` with hidden H and intermediate I, or 0 if
+ * the shape is not supported (f32: H, I multiples of 4; bf16: multiples of 8;
+ * int4: multiples of 128).  Layout: see moe_pool_load_expert. */
+size_t moe_expert_bytes(int32_t wtype, int32_t hidden, int32_t inter);
+
+/* ---- pool lifetime ---------------------------------------------------------- */
+/* Allocates the pinned store (n_layers * n_experts experts, zero-filled), one HBM
+ * pool per layer (n_slots experts plus a zeroed 256-byte tail, allocated once so
+ * slot addresses never change: [vLLM-cache] "fixed-address (allocated once at
+ * init)"; [llama-pool] Design item 1), a staging area of min(E, K*max_tokens)
+ * experts, the per-layer map tables (int32 [E], all -1) and scratch buffers.
+ * hbm_budget_bytes, when set, caps the HBM part ([llama-pool] Design item 4).
+ * Errors: EINVAL (bad config), ENOMEM, EHIP. */
+moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_pool_t** out);
+void moe_pool_destroy(moe_pool_t* pool);
+
+/* Copies one expert's bytes from `host_src` (moe_expert_bytes bytes) into the
+ * pinned store ([vLLM-cache] "CPUBackingStore -- pinned DRAM, all local experts").
+ * In resident mode the bytes are also copied to HBM slot `expert`.  If the expert
+ * is currently resident in a slot, that slot is not refreshed: load experts before
+ * the first prepare.  Byte layout (regions in order, each on a 256-byte boundary):
+ *   f32 : w13 [2I][H] fp32 row-major, w2 [H][I] fp32 row-major
+ *   bf16: w13 [2I][H] bf16, w2 [H][I] bf16
+ *   int4: w13 codes [2I][H/8] u32, w2 codes [H][I/8] u32, s13 [2I][H/128] bf16,
+ *         s2 [H][I/128] bf16; element j of a row is bits 4*(j%8) of word j/8 and
+ *         decodes to (q - 8) * s[row][j/128] ([flash-2x32] section 1: codes plus
+ *         bf16 scales, no zero point).
+ * Errors: EINVAL (bad layer/expert/size), EHIP. */
+moe_status_t moe_pool_load_expert(moe_pool_t* pool, int32_t layer, int32_t expert,
+                                  const void* host_src, size_t nbytes);
+
+/* Returns the pool to cold: every map entry -1, all slots free, LRU empty,
+ * counters zero (resident mode: counters only).  Slot bytes are not cleared. */
+moe_status_t moe_pool_reset(moe_pool_t* pool);
+
+/* ---- the step --------------------------------------------------------------- */
+/* prepare ([vLLM-cache] "How it works": unique ids, hit -> move to MRU, miss ->
+ * evict LRU + H2D copy + update mapping, remap through the persistent mapping;
+ * [llama-pool] Design items 2-3: route rule, then ids readback, LRU update, async
+ * H2D for misses and a map-table rewrite before the remap reads it).
+ *
+ *  topk_ids_dev  int32 [n_tokens][top_k], device.  0 <= n_tokens <= max_tokens.
+ *  slot_ids_dev  int32 [n_tokens][top_k], device, written: the slot of each id
+ *                (POOL) or the id's rank among the step's distinct ids, which is its
+ *                staging index (FALLBACK).
+ *  miss_host     optional host array of miss_cap entries; receives the misses in
+ *                processing order (ascending expert id).  *n_miss is the full count
+ *                even when it exceeds miss_cap.  A FALLBACK step has no misses.
+ *  path          MOE_PATH_POOL or MOE_PATH_FALLBACK.
+ *
+ * The distinct ids are found on the GPU and read back: prepare blocks until that
+ * kernel is done (one sync per layer per step, as in [llama-pool] "Limitations").
+ * It returns once the copies (on the copy streams), the map upload and the remap
+ * are enqueued; the compute stream waits for the copies through events.
+ * Distinct ids are processed in ascending order; free slots are taken from the
+ * highest index down; a non-resident expert maps to -1.
+ * Errors: EINVAL, ERANGE (an id outside [0,E): nothing changes), EHIP. */
+moe_status_t moe_pool_prepare(moe_pool_t* pool, int32_t layer, const int32_t* topk_ids_dev,
+                              int32_t n_tokens, int32_t* slot_ids_dev,
+                              moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss,
+                              int32_t* path);
+
+/* forward: the slot-indexed fused MoE on the layer's last prepare.
+ *  x_dev        [n_tokens][H] activations (MOE_A_F32: float, MOE_A_BF16: bf16).
+ *  slot_ids_dev int32 [n_tokens][top_k] from that prepare.  A slot id outside the
+ *               prepared range contributes nothing (never dereferenced;
+ *               [flash-2x32] section 3.4).
+ *  topk_w_dev   float [n_tokens][top_k] gate weights.
+ *  resid_dev    optional [n_tokens][H] in the activation format, added to the result.
+ *  out_dev      [n_tokens][H] in the activation format:
+ *               out[t] = resid[t] + sum_k w[t][k] * W2[s] (silu(W13g[s] x[t]) * W13u[s] x[t])
+ *               with fp32 accumulation and the k sum in k order.
+ * Batch-1 to small-batch decode uses two GEMV kernels; larger n_tokens use a
+ * grouped GEMM over slot-sorted tokens.  The kernel choice depends only on
+ * (n_tokens, top_k, H, I, formats), so the pooled and the all-resident pools give
+ * bit-identical outputs.
+ * Errors: EINVAL, ESTATE (no prepare of this layer with this n_tokens since the
+ * last reset, or its staging area was reused by another layer's fallback), EHIP. */
+moe_status_t moe_pool_forward(moe_pool_t* pool, int32_t layer, const void* x_dev,
+                              const int32_t* slot_ids_dev, const float* topk_w_dev,
+                              const void* resid_dev, int32_t n_tokens, void* out_dev);
+
+/* Waits until all of the pool's copies and kernels issued so far are complete. */
+moe_status_t moe_pool_sync(moe_pool_t* pool);
+
+/* ---- introspection (tests, benchmarks) ------------------------------------ */
+/* layer = -1 sums over layers. */
+moe_status_t moe_pool_get_stats(const moe_pool_t* pool, int32_t layer, moe_pool_stats_t* out);
+/* map_E: int32[E] expert -> slot or -1; owner_N: int32[N] slot -> expert or -1;
+ * lru_N: int32[N] resident experts least recently used first, -1 padded.
+ * Any pointer may be NULL. */
+moe_status_t moe_pool_get_state(const moe_pool_t* pool, int32_t layer, int32_t* map_E,
+                                int32_t* owner_N, int32_t* lru_N);
+/* Synchronously copies n bytes (<= one expert) of HBM slot `slot` of `layer`
+ * (slot < 0: staging entry -slot-1) into host_dst, after the pool's queued work. */
+moe_status_t moe_pool_read_slot(moe_pool_t* pool, int32_t layer, int32_t slot,
+                                void* host_dst, size_t n);
+/* Device address of slot `slot` of `layer` (constant for the pool's lifetime). */
+moe_status_t moe_pool_slot_ptr(const moe_pool_t* pool, int32_t layer, int32_t slot, void** dev_ptr);
+/* Host address of expert `expert` of `layer` in the pinned store. */
+moe_status_t moe_pool_store_ptr(const moe_pool_t* pool, int32_t layer, int32_t expert, void** host_ptr);
+/* *is_pinned = 1 if `p` lies in page-locked host memory known to HIP. */
+moe_status_t moe_ptr_is_pinned_host(const void* p, int32_t* is_pinned);
+/* Accumulated event timings (config.timing = 1); waits for queued work first. */
+moe_status_t moe_pool_get_timing(moe_pool_t* pool, moe_pool_timing_t* out);
+moe_status_t moe_pool_reset_timing(moe_pool_t* pool);
+
+/* ---- the slot manager alone (host only, no GPU) ----------------------------- */
+/* The same per-layer LRU state machine prepare() runs, driven from host ids, for
+ * pool-size planning and for checking the bookkeeping without a GPU.  Semantics
+ * as moe_pool_prepare (ids host int32 [n_tokens][top_k]; slot_ids host). */
+moe_status_t moe_lru_create(int32_t n_experts, int32_t n_slots, int32_t rule, moe_lru_t** out);
+void moe_lru_destroy(moe_lru_t* lru);
+moe_status_t moe_lru_step(moe_lru_t* lru, const int32_t* ids_host, int32_t n_tokens,
+                          int32_t top_k, int32_t* slot_ids_host, moe_miss_t* miss_host,
+                          int32_t miss_cap, int32_t* n_miss, int32_t* path);
+moe_status_t moe_lru_get_state(const moe_lru_t* lru, int32_t* map_E, int32_t* owner_N,
+                               int32_t* lru_N);
+moe_status_t moe_lru_get_stats(const moe_lru_t* lru, moe_pool_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_POOL_H */

@@ -1,0 +1,203 @@
+"""GPU parity of the slot-indexed fused MoE against the float64 oracle, and
+bit-identity of the pooled layer with the all-resident layer (the pooled GPU path
+must match the all-resident GPU path exactly; the page-1 FullGPUProvider is the
+all-resident path; the llama.cpp discussion's backend matrix compares pooled and
+host-copy paths bit for bit over dtype x ubatch {1, 3} x cold / full eviction /
+hit + reload / rebuild)."""
+import numpy as np
+import pytest
+import torch
+
+from _gpu_helpers import DEV, Rig, check_close, from_dev_act, to_dev_act
+from expert_slot_cache_amd import binding, synth
+from oracle.lru import LayerLRU
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(wl, steps, T):
+    _, _, rx, rw = synth.streams(wl)
+    xs = [synth.draw_activations(rx, (T, wl.hidden), wl.atype) for _ in range(steps)]
+    ws = [synth.draw_gate_weights(rw, (T, wl.top_k)) for _ in range(steps)]
+    return xs, ws
+
+
+def _run(rig, trace, xs, ws, layer_major=False, check_every=1, resid=None):
+    """Runs the trace through the rig; returns outputs [step][layer] (host fp32) and
+    checks a sample against the oracle."""
+    outs = []
+    S, L = trace.shape[:2]
+    for s in range(S):
+        row = []
+        xd = to_dev_act(xs[s], rig.wl.atype)
+        wd = torch.from_numpy(ws[s]).to(DEV)
+        rd = None if resid is None else to_dev_act(resid[s], rig.wl.atype)
+        for l in range(L):
+            path, misses, slots, out = rig.step(l, trace[s, l], xd, wd, rd)
+            got = from_dev_act(out)
+            row.append(got)
+            if s % check_every == 0:
+                ref = rig.reference(l, xs[s], trace[s, l], ws[s],
+                                    resid=None if resid is None else resid[s])
+                check_close(got, ref, rig.wl.atype, rig.wl.wtype, f"step {s} layer {l}")
+        outs.append(row)
+    return outs
+
+
+def _assert_bitwise(a, b, what):
+    for s, (ra, rb) in enumerate(zip(a, b)):
+        for l, (x, y) in enumerate(zip(ra, rb)):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{what}: step {s} layer {l}"
+
+
+def test_tiny_f32_full_trace_and_resident_identity():
+    wl = synth.WORKLOADS["tiny_f32_e8"]
+    trace = synth.make_trace(wl)
+    xs, ws = _inputs(wl, wl.steps, 1)
+    pooled = Rig(wl, slots=4, fast=False)
+    out_p = _run(pooled, trace, xs, ws)
+    st = pooled.pool.stats()
+    assert st["misses"] > 0 and st["hits"] > st["misses"]
+    resident = Rig(wl, slots=4, resident=True, experts=pooled.experts)
+    out_r = _run(resident, trace, xs, ws, check_every=64)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    pooled.close()
+    resident.close()
+
+
+def test_olmoe_bf16_and_resident_identity():
+    wl = synth.WORKLOADS["olmoe_bf16_e64"].with_(layers=2)
+    steps = 12
+    trace = synth.make_trace(wl, steps=steps)
+    xs, ws = _inputs(wl, steps, 1)
+    pooled = Rig(wl, slots=16)
+    out_p = _run(pooled, trace, xs, ws)
+    resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
+    out_r = _run(resident, trace, xs, ws, check_every=steps)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    pooled.close()
+    resident.close()
+
+
+def test_fanout_int4_and_resident_identity():
+    wl = synth.WORKLOADS["fanout_int4_e512"].with_(layers=1)
+    steps = 6
+    trace = synth.make_trace(wl, steps=steps)
+    xs, ws = _inputs(wl, steps, 1)
+    pooled = Rig(wl, slots=16)
+    out_p = _run(pooled, trace, xs, ws)
+    resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
+    out_r = _run(resident, trace, xs, ws, check_every=steps)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    pooled.close()
+    resident.close()
+
+
+@pytest.mark.parametrize("wtype,atype", [("f32", "f32"), ("bf16", "bf16"), ("int4", "bf16"),
+                                         ("bf16", "f32")])
+@pytest.mark.parametrize("T", [1, 3])
+def test_backend_matrix(wtype, atype, T):
+    """dtype x ubatch x {cold, full eviction, hit + reload, reset}: pooled equals
+    all-resident bit for bit, and both are within tolerance of the oracle."""
+    wl = synth.Workload("matrix", 1, 24, 3, 256, 128, 6, T, 0, wtype, atype, 1.0, 0.0, 0, 7)
+    rng = np.random.default_rng(17)
+    cold = [np.stack([rng.permutation(6)[:3] for _ in range(T)])]              # experts 0..5
+    evict = [np.stack([rng.permutation(6)[:3] + 6 for _ in range(T)]),         # 6..11: evicts
+             np.stack([rng.permutation(6)[:3] + 12 for _ in range(T)])]
+    hit_reload = [cold[0], np.stack([rng.permutation(24)[:3] for _ in range(T)]), cold[0]]
+    seq = cold + evict + hit_reload
+    trace = np.stack(seq)[:, None].astype(np.int32)                           # [S, 1, T, K]
+    xs, ws = _inputs(wl, len(seq), T)
+    pooled = Rig(wl, slots=6, fast=False, std=0.05)
+    resident = Rig(wl, slots=6, resident=True, experts=pooled.experts)
+    out_p = _run(pooled, trace, xs, ws)
+    out_r = _run(resident, trace, xs, ws)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    pooled.pool.reset()
+    out_p2 = _run(pooled, trace, xs, ws, check_every=100)
+    _assert_bitwise(out_p, out_p2, "after reset")
+    pooled.close()
+    resident.close()
+
+
+def test_fallback_bitwise_equal_to_no_pool():
+    """Bypass control: with a pool allocated, steps that overflow it take the
+    selective-copy path and produce exactly what a pool of size 0 produces."""
+    wl = synth.Workload("bypass", 1, 32, 4, 256, 128, 6, 2, 0, "bf16", "bf16", 1.0, 0.0, 0, 8)
+    trace = synth.make_trace(wl, steps=30)
+    xs, ws = _inputs(wl, 30, 2)
+    pooled = Rig(wl, slots=6)
+    nopool = Rig(wl, slots=0, experts=pooled.experts)
+    ref_lru = LayerLRU(32, 6)
+    out_p = _run(pooled, trace, xs, ws)
+    out_n = _run(nopool, trace, xs, ws, check_every=100)
+    fb = 0
+    for s in range(30):
+        r = ref_lru.step(trace[s, 0])
+        if r.path == 1:
+            fb += 1
+            assert np.array_equal(out_p[s][0].view(np.uint32), out_n[s][0].view(np.uint32)), s
+    assert fb > 0 and pooled.pool.stats()["fallbacks"] == fb
+    assert nopool.pool.stats()["fallbacks"] == 30
+    pooled.close()
+    nopool.close()
+
+
+def test_evict_and_use_in_same_step_reads_fresh_table():
+    """The llama.cpp stale-table failure: a miss evicts a slot and the same step
+    reads it; the output must use the new expert's weights."""
+    wl = synth.Workload("stale", 1, 8, 2, 256, 128, 2, 1, 0, "bf16", "bf16", 1.0, 0.0, 0, 9)
+    trace = np.array([[[[0, 1]]], [[[1, 5]]], [[[5, 0]]], [[[2, 3]]]], np.int32)
+    xs, ws = _inputs(wl, 4, 1)
+    rig = Rig(wl, slots=2, fast=False, std=0.05)
+    _run(rig, trace, xs, ws)
+    assert rig.pool.stats()["misses"] == 2 + 1 + 1 + 2
+    rig.close()
+
+
+def test_residual_and_multi_token():
+    wl = synth.Workload("resid", 2, 16, 4, 512, 256, 8, 3, 0, "bf16", "bf16", 1.0, 0.5, 0, 10)
+    trace = synth.make_trace(wl, steps=10)
+    xs, ws = _inputs(wl, 10, 3)
+    _, _, rx, _ = synth.streams(wl.with_(seed=11))
+    resid = [synth.draw_activations(rx, (3, wl.hidden), "bf16") for _ in range(10)]
+    rig = Rig(wl, slots=8)
+    _run(rig, trace, xs, ws, resid=resid)
+    rig.close()
+
+
+def test_prefill_ubatch_leaves_pool_untouched():
+    """Prefill ubatches on the OLMoE shapes: 512 tokens touch all 64 experts, so with
+    16 slots (distinct rule) and with 64 slots (static rule, 8 * 512 > 64) the step
+    takes the selective-copy path; the pool state is bit-identical afterwards and
+    decode resumes on it.  Outputs checked on sampled tokens."""
+    base = synth.WORKLOADS["prefill_bf16_e64"].with_(layers=1)
+    trace_dec = synth.make_trace(synth.WORKLOADS["olmoe_bf16_e64"].with_(layers=1), steps=6)
+    trace_pf = synth.make_trace(base, steps=1)
+    rng = synth.streams(base)[2]
+    x_pf = synth.draw_activations(rng, (512, base.hidden), "bf16")
+    w_pf = synth.draw_gate_weights(rng, (512, base.top_k))
+    xs, ws = _inputs(base.with_(tokens=1), 6, 1)
+    experts = None
+    for slots, rule in ((16, "distinct"), (64, "static")):
+        rig = Rig(base, slots=slots, rule=rule, max_tokens=512, experts=experts)
+        experts = rig.experts
+        for s in range(3):
+            rig.step(0, trace_dec[s, 0], to_dev_act(xs[s], "bf16"), torch.from_numpy(ws[s]).to(DEV))
+        snap = [a.copy() for a in rig.pool.state(0)], rig.pool.stats(0)
+        path, misses, slots_h, out = rig.step(0, trace_pf[0, 0], to_dev_act(x_pf, "bf16"),
+                                              torch.from_numpy(w_pf).to(DEV))
+        assert path == binding.PATH_FALLBACK and misses == []
+        now = rig.pool.state(0), rig.pool.stats(0)
+        assert all((a == b).all() for a, b in zip(snap[0], now[0]))
+        assert now[1]["hits"] == snap[1]["hits"] and now[1]["misses"] == snap[1]["misses"]
+        sample = [0, 1, 255, 511]
+        ref = rig.reference(0, x_pf, trace_pf[0, 0], w_pf, tokens=sample)
+        check_close(from_dev_act(out)[sample], ref[sample], "bf16", "bf16", f"prefill N={slots}")
+        for s in range(3, 6):     # decode resumes on the untouched pool
+            path, _, _, out = rig.step(0, trace_dec[s, 0], to_dev_act(xs[s], "bf16"),
+                                       torch.from_numpy(ws[s]).to(DEV))
+            assert path == binding.PATH_POOL
+            ref = rig.reference(0, xs[s], trace_dec[s, 0], ws[s])
+            check_close(from_dev_act(out), ref, "bf16", "bf16", "decode after prefill")
+        rig.close()

@@ -1,0 +1,198 @@
+"""GPU tests of prepare(): slot maps, miss lists, counters, LRU order and slot bytes,
+bit-exact against the oracle.  Re-creates the page-1 unit list (vLLM PR "Run MoE
+models exceeding VRAM via expert CPU offloading with GPU cache", test results) and
+the llama.cpp discussion's checks (bypass control, stale map table)."""
+import numpy as np
+import pytest
+import torch
+
+from _gpu_helpers import DEV, Rig
+from expert_slot_cache_amd import binding, synth
+from oracle.lru import FALLBACK, POOL, LayerLRU
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = synth.Workload("small_bf16_e32", 2, 32, 4, 256, 128, 8, 1, 64, "bf16", "bf16",
+                            1.0, 0.5, 0, 99)
+SMALL_INT4 = synth.Workload("small_int4_e32", 2, 32, 4, 256, 128, 8, 1, 64, "int4", "bf16",
+                            1.0, 0.5, 0, 98)
+
+
+def _run_trace_prepare(rig, trace, lrus):
+    for s in range(trace.shape[0]):
+        for l in range(trace.shape[1]):
+            ids = trace[s, l]
+            ids_d = torch.from_numpy(ids).to(DEV)
+            slot_d = torch.empty_like(ids_d)
+            path, misses = rig.pool.prepare(l, ids_d, ids.shape[0], slot_d)
+            r = lrus[l].step(ids)
+            assert path == r.path, (s, l)
+            assert misses == r.misses, (s, l)
+            assert (slot_d.cpu().numpy() == r.slot_ids).all(), (s, l)
+
+
+def _check_state(rig, lrus):
+    for l, ref in enumerate(lrus):
+        m, o, order = rig.pool.state(l)
+        assert m.tolist() == ref.map
+        assert o.tolist() == ref.owner
+        lo = ref.lru_order()
+        assert order.tolist() == lo + [-1] * (len(o) - len(lo))
+        st = rig.pool.stats(l)
+        assert (st["steps"], st["hits"], st["misses"], st["fallbacks"]) == \
+            (ref.steps, ref.hits, ref.misses, ref.fallbacks)
+
+
+@pytest.mark.parametrize("name,slots,steps,layers", [
+    ("tiny_f32_e8", 4, 256, 1),
+    ("tiny_f32_e8", 1, 64, 1),
+    ("olmoe_bf16_e64", 16, 96, 2),
+    ("fanout_int4_e512", 32, 48, 2),
+])
+def test_prepare_matches_oracle(name, slots, steps, layers):
+    wl = synth.WORKLOADS[name].with_(layers=layers)
+    trace = synth.make_trace(wl, steps=steps)
+    # prepare never reads slot bytes: a store of zeros keeps set-up cheap
+    eb = synth.expert_bytes(wl.wtype, wl.hidden, wl.inter)
+    zero = np.zeros(eb, np.uint8)
+    rig = Rig(wl, slots=slots, experts=[[zero] * wl.experts] * layers)
+    lrus = [LayerLRU(wl.experts, slots) for _ in range(layers)]
+    _run_trace_prepare(rig, trace, lrus)
+    _check_state(rig, lrus)
+    rig.close()
+
+
+def test_slot_bytes_equal_store_after_eviction():
+    """test_gpu_buffer_matches_source_weights / _correct_after_eviction and the
+    scale tests: every occupied slot holds exactly its owner's bytes (codes and
+    scales for INT4), after heavy churn."""
+    for wl in (SMALL_BF16, SMALL_INT4):
+        rig = Rig(wl, slots=5, fast=True, copy_chunk_bytes=4096, copy_streams=3)
+        trace = synth.make_trace(wl, steps=40)
+        lrus = [LayerLRU(wl.experts, 5) for _ in range(wl.layers)]
+        _run_trace_prepare(rig, trace, lrus)
+        assert sum(l.misses for l in lrus) > 40
+        for l in range(wl.layers):
+            _, owner, _ = rig.pool.state(l)
+            for s, e in enumerate(owner):
+                if e >= 0:
+                    got = rig.pool.read_slot(l, s)
+                    assert (got == rig.experts[l][e]).all(), (wl.name, l, s, e)
+                    assert (rig.pool.store_view(l, e) == rig.experts[l][e]).all()
+        st = rig.pool.stats()
+        assert st["bytes_h2d"] == st["misses"] * rig.pool.expert_nbytes
+        rig.close()
+
+
+def test_store_is_pinned_and_slots_fixed():
+    wl = SMALL_BF16
+    rig = Rig(wl, slots=4)
+    assert binding.is_pinned_host(rig.pool.store_ptr(0, 3))
+    assert not binding.is_pinned_host(np.zeros(16, np.uint8).ctypes.data)
+    before = [rig.pool.slot_ptr(l, s) for l in range(wl.layers) for s in range(4)]
+    trace = synth.make_trace(wl, steps=30)
+    _run_trace_prepare(rig, trace, [LayerLRU(wl.experts, 4) for _ in range(wl.layers)])
+    after = [rig.pool.slot_ptr(l, s) for l in range(wl.layers) for s in range(4)]
+    assert before == after
+    eb = rig.pool.expert_nbytes
+    assert after[1] - after[0] == eb
+    rig.close()
+
+
+def test_capacity_equal_experts_and_capacity_one():
+    wl = SMALL_BF16.with_(layers=1)
+    trace = synth.make_trace(wl, steps=60)
+    rig = Rig(wl, slots=wl.experts)
+    lrus = [LayerLRU(wl.experts, wl.experts)]
+    _run_trace_prepare(rig, trace, lrus)
+    seen = len(set(trace.ravel().tolist()))
+    assert rig.pool.stats()["misses"] == seen
+    _run_trace_prepare(rig, trace, lrus)          # warm: no new misses
+    assert rig.pool.stats()["misses"] == seen
+    rig.close()
+    wl1 = wl.with_(top_k=1)
+    trace = synth.make_trace(wl1, steps=80)
+    rig = Rig(wl1, slots=1)
+    _run_trace_prepare(rig, trace, [LayerLRU(wl.experts, 1)])
+    changes = 1 + int((trace[1:, 0, 0, 0] != trace[:-1, 0, 0, 0]).sum())
+    assert rig.pool.stats()["misses"] == changes
+    rig.close()
+
+
+def test_overflow_falls_back_exactly_above_capacity():
+    """test_overflow_raises / test_no_overflow_at_capacity, with the fallback in
+    place of the raise: D == N pools, D == N + 1 falls back and leaves the pool
+    untouched; staging holds the step's experts in ascending id order."""
+    wl = SMALL_BF16.with_(layers=1, top_k=4)
+    rig = Rig(wl, slots=8, max_tokens=4)
+    ids = np.array([[0, 1, 2, 3], [4, 5, 6, 7]], np.int32)          # D = 8 = N
+    ids_d = torch.from_numpy(ids).to(DEV)
+    slot_d = torch.empty_like(ids_d)
+    path, misses = rig.pool.prepare(0, ids_d, 2, slot_d)
+    assert path == binding.PATH_POOL and len(misses) == 8
+    snap = [a.copy() for a in rig.pool.state(0)], rig.pool.stats(0)
+    ids9 = np.array([[0, 1, 2, 3], [4, 5, 6, 7], [30, 1, 2, 3]], np.int32)   # D = 9 > N
+    ids_d = torch.from_numpy(ids9).to(DEV)
+    slot_d = torch.empty_like(ids_d)
+    path, misses = rig.pool.prepare(0, ids_d, 3, slot_d)
+    assert path == binding.PATH_FALLBACK and misses == []
+    assert slot_d.cpu().numpy().tolist() == [[0, 1, 2, 3], [4, 5, 6, 7], [8, 1, 2, 3]]
+    now = rig.pool.state(0), rig.pool.stats(0)
+    assert all((a == b).all() for a, b in zip(snap[0], now[0]))
+    assert {k: v for k, v in now[1].items() if k not in ("steps", "fallbacks", "bytes_h2d", "staged")} == \
+        {k: v for k, v in snap[1].items() if k not in ("steps", "fallbacks", "bytes_h2d", "staged")}
+    assert now[1]["fallbacks"] == 1 and now[1]["staged"] == 9
+    for r, e in enumerate(sorted(set(ids9.ravel().tolist()))):
+        assert (rig.pool.read_staging(r) == rig.experts[0][e]).all()
+    rig.close()
+
+
+def test_out_of_range_id_rejected_state_untouched():
+    wl = SMALL_BF16.with_(layers=1)
+    rig = Rig(wl, slots=4)
+    ok = torch.tensor([[1, 2, 3, 4]], dtype=torch.int32, device=DEV)
+    slot_d = torch.empty_like(ok)
+    rig.pool.prepare(0, ok, 1, slot_d)
+    snap = [a.copy() for a in rig.pool.state(0)], rig.pool.stats(0)
+    for bad in ([[1, 2, 3, 32]], [[-1, 2, 3, 4]]):
+        with pytest.raises(binding.ExpertRangeError):
+            rig.pool.prepare(0, torch.tensor(bad, dtype=torch.int32, device=DEV), 1, slot_d)
+    now = rig.pool.state(0), rig.pool.stats(0)
+    assert all((a == b).all() for a, b in zip(snap[0], now[0])) and snap[1] == now[1]
+    rig.close()
+
+
+def test_forward_without_prepare_is_state_error():
+    wl = SMALL_BF16.with_(layers=2)
+    rig = Rig(wl, slots=4)
+    x = torch.zeros((1, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((1, wl.top_k), dtype=torch.float32, device=DEV)
+    s = torch.zeros((1, wl.top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(x)
+    with pytest.raises(binding.StateError):
+        rig.pool.forward(0, x, s, w, out, 1)
+    rig.pool.prepare(0, torch.tensor([[0, 1, 2, 3]], dtype=torch.int32, device=DEV), 1, s)
+    with pytest.raises(binding.StateError):
+        rig.pool.forward(0, x, s, w, out, 2)         # n_tokens differs from prepare
+    with pytest.raises(binding.StateError):
+        rig.pool.forward(1, x, s, w, out, 1)         # other layer never prepared
+    rig.pool.forward(0, x, s, w, out, 1)
+    rig.pool.reset()
+    with pytest.raises(binding.StateError):
+        rig.pool.forward(0, x, s, w, out, 1)
+    assert rig.pool.stats()["steps"] == 0
+    rig.close()
+
+
+def test_zero_tokens_and_zero_slots():
+    wl = SMALL_BF16.with_(layers=1)
+    rig = Rig(wl, slots=0, max_tokens=2)
+    ids = torch.tensor([[3, 1, 2, 0]], dtype=torch.int32, device=DEV)
+    s = torch.empty_like(ids)
+    path, misses = rig.pool.prepare(0, ids, 1, s)
+    assert path == binding.PATH_FALLBACK and s.cpu().tolist() == [[3, 1, 2, 0]]
+    path, misses = rig.pool.prepare(0, ids, 0, s)
+    assert path == binding.PATH_POOL and misses == []
+    st = rig.pool.stats(0)
+    assert st["steps"] == 2 and st["fallbacks"] == 1 and st["hits"] == st["misses"] == 0
+    rig.close()

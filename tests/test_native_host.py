@@ -1,0 +1,114 @@
+"""CPU tests of the native library: it loads, exports every entry point the header
+declares, and its slot manager (the same code prepare() runs) matches the oracle
+bit for bit on the workload traces.  No GPU call is made."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from expert_slot_cache_amd import binding, synth
+from oracle.lru import LayerLRU
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_pool.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = binding.lib()
+    declared = _header_functions()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(binding.exported_symbols()) == declared
+
+
+def test_expert_bytes_match_generator_layout():
+    for wtype, H, I in [("f32", 64, 32), ("bf16", 2048, 1024), ("int4", 2560, 640),
+                        ("bf16", 4096, 1536), ("int4", 128, 256)]:
+        assert binding.expert_bytes(wtype, H, I) == synth.expert_bytes(wtype, H, I)
+    assert binding.expert_bytes("int4", 2560, 640) == 2534400
+    assert binding.expert_bytes("int4", 100, 128) == 0
+    assert binding.expert_bytes("bf16", 2044, 1024) == 0
+
+
+def _compare(E, N, trace, rule="distinct"):
+    ref = LayerLRU(E, N, rule)
+    lib = binding.SlotLRU(E, N, rule)
+    for ids in trace:
+        r = ref.step(ids)
+        slot_ids, path, misses = lib.step(ids)
+        assert path == r.path
+        assert (slot_ids == r.slot_ids).all()
+        assert misses == r.misses
+    m, o, l = lib.state()
+    assert m.tolist() == ref.map
+    assert o.tolist() == ref.owner
+    order = ref.lru_order()
+    assert l.tolist() == order + [-1] * (N - len(order))
+    st = lib.stats()
+    assert (st["steps"], st["hits"], st["misses"], st["fallbacks"]) == \
+        (ref.steps, ref.hits, ref.misses, ref.fallbacks)
+    return st
+
+
+@pytest.mark.parametrize("name,slots", [("tiny_f32_e8", 4), ("tiny_f32_e8", 1),
+                                        ("olmoe_bf16_e64", 16), ("olmoe_bf16_e64", 64),
+                                        ("fanout_int4_e512", 16), ("fanout_int4_e512", 64)])
+def test_native_lru_matches_oracle_on_traces(name, slots):
+    wl = synth.WORKLOADS[name]
+    steps = wl.steps if wl.experts <= 64 else 128
+    trace = synth.make_trace(wl.with_(layers=min(wl.layers, 3)), steps=steps)
+    for layer in range(trace.shape[1]):
+        _compare(wl.experts, slots, [trace[s, layer] for s in range(trace.shape[0])])
+
+
+@pytest.mark.parametrize("rule", ["distinct", "static"])
+def test_native_lru_multi_token_and_fallback(rule):
+    wl = synth.WORKLOADS["batched_bf16_e128"].with_(layers=1, tokens=4)
+    trace = synth.make_trace(wl, steps=300)
+    st = _compare(128, 32, [trace[s, 0] for s in range(300)], rule)
+    if rule == "static":
+        assert st["fallbacks"] == 0          # 4 tokens x top-8 = 32 <= 32
+    wl = wl.with_(tokens=8)
+    trace = synth.make_trace(wl, steps=100)
+    st = _compare(128, 32, [trace[s, 0] for s in range(100)], rule)
+    assert st["fallbacks"] > 0
+
+
+def test_native_lru_random_small():
+    rng = np.random.default_rng(4)
+    for _ in range(400):
+        E = int(rng.integers(1, 9))
+        K = int(rng.integers(1, E + 1))
+        N = int(rng.integers(0, E + 2))
+        trace = [np.stack([rng.permutation(E)[:K] for _ in range(int(rng.integers(1, 4)))])
+                 for _ in range(int(rng.integers(1, 12)))]
+        _compare(E, N, trace, "distinct" if rng.random() < 0.5 else "static")
+
+
+def test_native_lru_errors_leave_state():
+    lib = binding.SlotLRU(8, 2)
+    lib.step(np.array([[1, 2]]))
+    before = [a.copy() for a in lib.state()], lib.stats()
+    with pytest.raises(binding.ExpertRangeError):
+        lib.step(np.array([[1, 8]]))
+    with pytest.raises(binding.ExpertRangeError):
+        lib.step(np.array([[-3, 1]]))
+    after = lib.state(), lib.stats()
+    assert all((a == b).all() for a, b in zip(before[0], after[0])) and before[1] == after[1]
+    with pytest.raises(binding.MoeError):
+        binding.SlotLRU(0, 2)
+
+
+def test_native_lru_empty_step():
+    lib = binding.SlotLRU(8, 2)
+    out, path, misses = lib.step(np.zeros((0, 2), np.int32))
+    assert path == binding.PATH_POOL and misses == [] and out.shape == (0, 2)
+    assert lib.stats()["steps"] == 1
