@@ -60,8 +60,9 @@ class Stats(C.Structure):
 
 
 class Timing(C.Structure):
-    _fields_ = [("copy_ms", C.c_double), ("copy_calls", C.c_uint64), ("w13_ms", C.c_double),
-                ("w2_ms", C.c_double), ("forward_calls", C.c_uint64), ("sync_wait_ms", C.c_double)]
+    _fields_ = [("copy_ms", C.c_double), ("copy_calls", C.c_uint64), ("copy_bytes", C.c_uint64),
+                ("w13_ms", C.c_double), ("w2_ms", C.c_double), ("kernel_calls", C.c_uint64),
+                ("sync_wait_ms", C.c_double)]
 
 
 _P = C.c_void_p
@@ -78,6 +79,8 @@ _SIGS = {
     "moe_pool_reset": (_I32, [_P]),
     "moe_pool_prepare": (_I32, [_P, _I32, _P, _I32, _P, C.POINTER(Miss), _I32, _PI32, _PI32]),
     "moe_pool_forward": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _P]),
+    "moe_pool_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, C.POINTER(Miss), _I32, _PI32,
+                             _PI32]),
     "moe_pool_sync": (_I32, [_P]),
     "moe_pool_get_stats": (_I32, [_P, _I32, C.POINTER(Stats)]),
     "moe_pool_get_state": (_I32, [_P, _I32, _P, _P, _P]),
@@ -153,12 +156,12 @@ class MoePool:
     def __init__(self, *, layers: int, experts: int, top_k: int, hidden: int, inter: int,
                  slots: int, wtype: str = "bf16", atype: str = "bf16", rule: str = "distinct",
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
-                 copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: bool = False,
+                 copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
                  stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
-                     copy_chunk_bytes, hbm_budget_bytes, int(bool(timing)))
+                     copy_chunk_bytes, hbm_budget_bytes, int(timing))
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -220,6 +223,14 @@ class MoePool:
         _check(lib().moe_pool_forward(self._h, layer, _ptr(x), _ptr(slot_ids), _ptr(topk_w),
                                       _ptr(resid), n_tokens, _ptr(out)))
         return out
+
+    def step(self, layer: int, topk_ids, n_tokens: int, slot_ids, x, topk_w, out, resid=None):
+        """prepare + forward in one call; returns (path, misses)."""
+        nm, path = C.c_int32(0), C.c_int32(0)
+        _check(lib().moe_pool_step(self._h, layer, _ptr(topk_ids), n_tokens, _ptr(slot_ids), _ptr(x),
+                                   _ptr(topk_w), _ptr(resid), _ptr(out), self._miss_buf,
+                                   len(self._miss_buf), C.byref(nm), C.byref(path)))
+        return path.value, _misses(self._miss_buf, min(nm.value, len(self._miss_buf)))
 
     def sync(self):
         _check(lib().moe_pool_sync(self._h))

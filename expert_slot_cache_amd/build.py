@@ -31,26 +31,26 @@ def hipcc() -> str:
     return p
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(ROOT, "_build")
+def build(verbose: bool = False, out: str = LIB, defines=(), objdir: str | None = None) -> str:
+    objdir = objdir or os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+        cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC, *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

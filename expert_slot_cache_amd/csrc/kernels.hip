@@ -5,6 +5,7 @@
 // every reduction has a fixed order, so a result depends only on the values it
 // reads -- never on which slot an expert sits in.  That is what makes a pooled
 // layer bit-identical to the same layer with every expert resident.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,12 +42,17 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // K-distinct: presence bitmap in LDS, then ordered compaction with a wave64
 // ballot + mbcnt lane prefix and a per-wave offset.  One workgroup.
 //   [vLLM-cache "How it works": unique ids of topk_ids, ascending]
+//
+// The result goes straight to host memory, each 32-bit word carrying the step's
+// tag in its top bits: rb[0] = tag<<14 | bad<<13 | D, rb[1 + i] = tag<<14 | id_i.
+// The host zeroes the words before the launch and waits for each word it needs
+// to show the tag, so no store ordering or cache flush is needed.
 // ---------------------------------------------------------------------------
 constexpr int kDistinctThreads = 1024;
 
 __global__ __launch_bounds__(kDistinctThreads) void k_distinct(const int32_t* __restrict__ ids, int n,
-                                                               int E, int32_t* __restrict__ rb,
-                                                               int32_t* __restrict__ rank) {
+                                                               int E, uint32_t* __restrict__ rb,
+                                                               int32_t* __restrict__ rank, uint32_t tag) {
     __shared__ uint32_t bits[kMaxExperts / 32];
     __shared__ int32_t wave_cnt[kDistinctThreads / 64];
     __shared__ int32_t bad;
@@ -54,6 +60,7 @@ __global__ __launch_bounds__(kDistinctThreads) void k_distinct(const int32_t* __
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int nwords = (E + 31) >> 5;
+    const uint32_t hi = tag << 14;
     for (int i = tid; i < nwords; i += kDistinctThreads) bits[i] = 0u;
     if (tid == 0) bad = 0;
     __syncthreads();
@@ -83,63 +90,65 @@ __global__ __launch_bounds__(kDistinctThreads) void k_distinct(const int32_t* __
         }
         if (present) {
             const int pos = base + off + (int)below;
-            rb[2 + pos] = e;
+            rb[1 + pos] = hi | (uint32_t)e;
             rank[e] = pos;
         }
         base += total;
         __syncthreads();
     }
-    if (tid == 0) {
-        rb[0] = base;
-        rb[1] = bad;
-    }
+    if (tid == 0) rb[0] = hi | ((uint32_t)(bad != 0) << 13) | (uint32_t)base;
 }
 
-hipError_t launch_distinct(const int32_t* ids, int n, int E, int32_t* rb, int32_t* rank,
+hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32_t* rank, uint32_t tag,
                            hipStream_t stream) {
-    hipLaunchKernelGGL(k_distinct, dim3(1), dim3(kDistinctThreads), 0, stream, ids, n, E, rb, rank);
+    hipLaunchKernelGGL(k_distinct, dim3(1), dim3(kDistinctThreads), 0, stream, ids, n, E, rb, rank, tag);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // K-remap: slot_ids[i] = table[ids[i]]  [vLLM-cache: remap topk_ids through the
-// persistent mapping; llama-pool: get_rows(table, ids)].  Out-of-range ids give -1,
-// which the forward kernels never dereference.
+// persistent mapping, updated in place at each miss; llama-pool: get_rows(table,
+// ids) on a table rewritten before the remap reads it].
+//
+// The step's table changes (pairs (expert, entry after the step)) are applied
+// inside the kernel: every workgroup copies the table into LDS and applies the
+// list there, and workgroup 0 also writes the changes back to the persistent
+// table.  So the remap can only read the fresh table.  An entry may be listed
+// twice, always with the same value, so the order of the writes does not matter.  Ids outside [0,E) give -1, which the
+// forward kernels never dereference.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ ids, int n, int E,
-                                               const int32_t* __restrict__ table,
-                                               int32_t* __restrict__ out) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
+                                               int32_t* __restrict__ table, const int32_t* __restrict__ upd,
+                                               int n_upd, int32_t* __restrict__ out) {
+    __shared__ int32_t tab[kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) tab[e] = table[e];
+    __syncthreads();
+    for (int u = tid; u < n_upd; u += 256) tab[upd[2 * u]] = upd[2 * u + 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int u = tid; u < n_upd; u += 256) table[upd[2 * u]] = upd[2 * u + 1];
+    const int i = blockIdx.x * 256 + tid;
     if (i < n) {
         const int e = ids[i];
-        out[i] = ((unsigned)e < (unsigned)E) ? table[e] : -1;
+        out[i] = ((unsigned)e < (unsigned)E) ? tab[e] : -1;
     }
 }
 
-hipError_t launch_remap(const int32_t* ids, int n, int E, const int32_t* table, int32_t* out,
-                        hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_remap, dim3((n + 255) / 256), dim3(256), 0, stream, ids, n, E, table, out);
+hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* upd, int n_upd,
+                        int32_t* out, hipStream_t stream) {
+    if (n <= 0 && n_upd <= 0) return hipSuccess;
+    const int blocks = n > 0 ? (n + 255) / 256 : 1;
+    hipLaunchKernelGGL(k_remap, dim3(blocks), dim3(256), 0, stream, ids, n, E, table, upd, n_upd, out);
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Decode GEMV kernels.
-//
-// A weight row is read as 16-byte chunks; lane l takes chunks l, l+64, ... of
-// the row, so a wave's load instruction covers 1 KiB of contiguous row bytes.
-// The activation vector sits in LDS as fp32 in a chunk-transposed layout: the
-// q-th float4 of chunk c is at float4 index q * n_chunks + c, so the 64 lanes of
-// a wave read 64 consecutive float4s (no bank conflicts).
-//   f32  : 4 elements per chunk (1 float4)
-//   bf16 : 8 elements per chunk (2 float4s)
-//   int4 : 32 elements per chunk (8 float4s), one bf16 scale per 4 chunks
-// ---------------------------------------------------------------------------
+// Elements per 16-byte chunk of a weight row.
 template <int WT>
 struct WTraits;
 template <>
 struct WTraits<W_F32> {
-    static constexpr int EPC = 4;   // elements per 16-byte chunk
+    static constexpr int EPC = 4;
 };
 template <>
 struct WTraits<W_BF16> {
@@ -150,260 +159,401 @@ struct WTraits<W_INT4> {
     static constexpr int EPC = 32;
 };
 
-// Partial dot of one chunk with its activations (xs = float4 base of the vector,
-// c = chunk index, nc = chunks per row).
-template <int WT>
-__device__ __forceinline__ float chunk_dot(const uint4 w, const float4* __restrict__ xs, int c, int nc);
-
-template <>
-__device__ __forceinline__ float chunk_dot<W_F32>(const uint4 w, const float4* __restrict__ xs, int c,
-                                                  int nc) {
-    const float4 a = xs[c];
-    float acc = __uint_as_float(w.x) * a.x;
-    acc = fmaf(__uint_as_float(w.y), a.y, acc);
-    acc = fmaf(__uint_as_float(w.z), a.z, acc);
-    acc = fmaf(__uint_as_float(w.w), a.w, acc);
-    return acc;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot<W_BF16>(const uint4 w, const float4* __restrict__ xs, int c,
-                                                   int nc) {
-    const float4 a = xs[c];
-    const float4 b = xs[nc + c];
-    float acc = bf16_lo(w.x) * a.x;
-    acc = fmaf(bf16_hi(w.x), a.y, acc);
-    acc = fmaf(bf16_lo(w.y), a.z, acc);
-    acc = fmaf(bf16_hi(w.y), a.w, acc);
-    acc = fmaf(bf16_lo(w.z), b.x, acc);
-    acc = fmaf(bf16_hi(w.z), b.y, acc);
-    acc = fmaf(bf16_lo(w.w), b.z, acc);
-    acc = fmaf(bf16_hi(w.w), b.w, acc);
-    return acc;
-}
-
-// sum_{j<8} (q_j - 8) * x_j for the eight codes of one word
-__device__ __forceinline__ float word_dot(uint32_t u, const float4 a, const float4 b) {
-    float acc = ((float)(int)(u & 15u) - 8.0f) * a.x;
-    acc = fmaf((float)(int)((u >> 4) & 15u) - 8.0f, a.y, acc);
-    acc = fmaf((float)(int)((u >> 8) & 15u) - 8.0f, a.z, acc);
-    acc = fmaf((float)(int)((u >> 12) & 15u) - 8.0f, a.w, acc);
-    acc = fmaf((float)(int)((u >> 16) & 15u) - 8.0f, b.x, acc);
-    acc = fmaf((float)(int)((u >> 20) & 15u) - 8.0f, b.y, acc);
-    acc = fmaf((float)(int)((u >> 24) & 15u) - 8.0f, b.z, acc);
-    acc = fmaf((float)(int)((u >> 28) & 15u) - 8.0f, b.w, acc);
-    return acc;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot<W_INT4>(const uint4 w, const float4* __restrict__ xs, int c,
-                                                   int nc) {
-    float acc = word_dot(w.x, xs[0 * nc + c], xs[1 * nc + c]);
-    acc += word_dot(w.y, xs[2 * nc + c], xs[3 * nc + c]);
-    acc += word_dot(w.z, xs[4 * nc + c], xs[5 * nc + c]);
-    acc += word_dot(w.w, xs[6 * nc + c], xs[7 * nc + c]);
-    return acc;
-}
-
-// Load element `i` (of n) of an activation row as fp32.
+// Element i of an activation array as fp32.
 template <int AT>
-__device__ __forceinline__ float load_act(const void* __restrict__ p, size_t i);
-template <>
-__device__ __forceinline__ float load_act<A_F32>(const void* __restrict__ p, size_t i) {
-    return static_cast<const float*>(p)[i];
-}
-template <>
-__device__ __forceinline__ float load_act<A_BF16>(const void* __restrict__ p, size_t i) {
+__device__ __forceinline__ float load_act(const void* __restrict__ p, size_t i) {
+    if (AT == A_F32) return static_cast<const float*>(p)[i];
     return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 
-// Position (in floats) of element e of a vector of nc chunks in the
-// chunk-transposed LDS layout.
-template <int WT>
-__device__ __forceinline__ int lds_pos(int e, int nc) {
-    constexpr int EPC = WTraits<WT>::EPC;
-    const int c = e / EPC;
-    const int r = e - c * EPC;
-    return ((r >> 2) * nc + c) * 4 + (r & 3);
+// ---------------------------------------------------------------------------
+// Decode GEMV kernels.
+//
+// A weight row is a run of 16-byte chunks (f32: 4 elements, bf16: 8, int4: 32).
+// G lanes share a row (G = the largest power of two <= 64 dividing the chunk
+// count), each lane taking CPL = chunks / G chunks at stride G, so one load
+// instruction of a lane group covers G * 16 contiguous bytes of the row and a
+// wave reads 64 / G rows side by side.  The activation vector stays in registers
+// for the whole wave ("lane-stationary"): lane j of a group always owns the same
+// chunk columns, loads their activations once (from L2) and reuses them for
+// every row it streams.  All weight loads of a lane are issued before any math.
+//
+// Products:
+//   bf16 x bf16 : v_dot2c_f32_bf16 over packed pairs (fp32 accumulate)
+//   int4 x bf16 : code q becomes the bf16 value 128 + q by OR-ing it into the
+//                 mantissa of 0x4300 (exact); sum (128+q) x with dot2, minus
+//                 136 * sum(x) of the chunk, times the group's bf16 scale
+//   otherwise   : fp32 FMAs
+// Every reduction (in-lane chunk order, the butterfly over G lanes, the k order
+// of the combine) is fixed, so results depend only on the bytes read.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
 }
 
-// Stage n fp32-convertible values into the chunk-transposed LDS layout.
-template <int WT, int AT>
-__device__ __forceinline__ void stage_vector(float* __restrict__ dst, const void* __restrict__ src,
-                                             size_t src_off, int n, int nc) {
-    for (int e = threadIdx.x; e < n; e += blockDim.x) dst[lds_pos<WT>(e, nc)] = load_act<AT>(src, src_off + e);
+#ifdef MOE_NT_LOADS
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16(const char* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
-template <int WT>
-__device__ __forceinline__ void stage_vector_f32(float* __restrict__ dst, const float* __restrict__ src,
-                                                 int n, int nc) {
-    for (int e = threadIdx.x; e < n; e += blockDim.x) dst[lds_pos<WT>(e, nc)] = src[e];
-}
-
+#else
 __device__ __forceinline__ uint4 load16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+#endif
 
-// Scale of chunk c of a row (int4 only): one bf16 per 128 elements = 4 chunks.
+// Sum over the G lanes of a group (G a power of two); every lane of the group
+// ends with the same value.
+__device__ __forceinline__ float group_sum(float v, int G) {
+    for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---- activation chunks held in registers ------------------------------------
+// XT_F32: fp32 values; XT_BF16: the chunk's 8 bf16 as loaded; XT_I4: pairs for
+// the int4 dot (x_m, x_{m+4}) of each 8-element word, plus the chunk's sum.
+enum { XT_F32 = 0, XT_BF16 = 1, XT_I4 = 2 };
+
+template <int WT, int AT>
+struct XSel {
+    static constexpr int XT = (WT == W_INT4) ? XT_I4 : ((WT == W_BF16 && AT == A_BF16) ? XT_BF16 : XT_F32);
+};
+
+template <int WT, int XT>
+struct XChunk;
+
+template <int WT>
+struct XChunk<WT, XT_F32> {
+    static constexpr int N = WTraits<WT>::EPC;
+    float v[N];
+    // element e0 .. e0+N-1 of a vector of type AT
+    template <int AT>
+    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
+        if (AT == A_F32) {
+            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e0);
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const float4 f = p[q];
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
+            }
+        } else {
+            const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + e0);
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const uint2 u = p[q];
+                v[4 * q] = bf16_lo(u.x);
+                v[4 * q + 1] = bf16_hi(u.x);
+                v[4 * q + 2] = bf16_lo(u.y);
+                v[4 * q + 3] = bf16_hi(u.y);
+            }
+        }
+    }
+};
+
+template <>
+struct XChunk<W_BF16, XT_BF16> {
+    uint4 v;
+    template <int AT>
+    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+    }
+};
+
+template <>
+struct XChunk<W_INT4, XT_I4> {
+    uint32_t p[16];
+    float sx;
+    template <int AT>
+    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {        // word i: elements 8i .. 8i+7
+            const uint4 u = src[i];
+            p[4 * i + 0] = (u.x & 0xFFFFu) | (u.z << 16);          // (x0, x4)
+            p[4 * i + 1] = (u.x >> 16) | (u.z & 0xFFFF0000u);      // (x1, x5)
+            p[4 * i + 2] = (u.y & 0xFFFFu) | (u.w << 16);          // (x2, x6)
+            p[4 * i + 3] = (u.y >> 16) | (u.w & 0xFFFF0000u);      // (x3, x7)
+            s += ((bf16_lo(u.x) + bf16_hi(u.x)) + (bf16_lo(u.y) + bf16_hi(u.y))) +
+                 ((bf16_lo(u.z) + bf16_hi(u.z)) + (bf16_lo(u.w) + bf16_hi(u.w)));
+        }
+        sx = s;
+    }
+};
+
+// ---- chunk dot products -------------------------------------------------------
+__device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_F32, XT_F32>& x) {
+    float acc = __uint_as_float(w.x) * x.v[0];
+    acc = fmaf(__uint_as_float(w.y), x.v[1], acc);
+    acc = fmaf(__uint_as_float(w.z), x.v[2], acc);
+    acc = fmaf(__uint_as_float(w.w), x.v[3], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_BF16, XT_F32>& x) {
+    float acc = bf16_lo(w.x) * x.v[0];
+    acc = fmaf(bf16_hi(w.x), x.v[1], acc);
+    acc = fmaf(bf16_lo(w.y), x.v[2], acc);
+    acc = fmaf(bf16_hi(w.y), x.v[3], acc);
+    acc = fmaf(bf16_lo(w.z), x.v[4], acc);
+    acc = fmaf(bf16_hi(w.z), x.v[5], acc);
+    acc = fmaf(bf16_lo(w.w), x.v[6], acc);
+    acc = fmaf(bf16_hi(w.w), x.v[7], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_BF16, XT_BF16>& x) {
+    float acc = dot2_bf16(w.x, x.v.x, 0.0f);
+    acc = dot2_bf16(w.y, x.v.y, acc);
+    acc = dot2_bf16(w.z, x.v.z, acc);
+    acc = dot2_bf16(w.w, x.v.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_INT4, XT_I4>& x) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t q2 = ((ws[i] >> (4 * m)) & 0x000F000Fu) | 0x43004300u;   // (128+q_m, 128+q_{m+4})
+            acc = dot2_bf16(q2, x.p[4 * i + m], acc);
+        }
+    }
+    return acc - 136.0f * x.sx;
+}
+
+// bf16 scale of chunk c of an int4 row (one scale per 128 elements = 4 chunks)
 __device__ __forceinline__ float chunk_scale(const uint16_t* __restrict__ srow, int c) {
     return bf16_to_f32(srow[c >> 2]);
 }
 
-// ---- w13 + SwiGLU ------------------------------------------------------------
-// grid.x: blocks of 4 waves x PPW gate/up row pairs; grid.y: (t, k) pairs.
-// act[pair][i] = silu(W13[s][i] . x[t]) * (W13[s][I + i] . x[t]).
-template <int WT, int AT, int CPL, int PPW>
-__global__ __launch_bounds__(256) void k_w13_gemv(const char* __restrict__ wbase, size_t stride,
-                                                  int nslots, const int32_t* __restrict__ slot_ids,
-                                                  const void* __restrict__ x, int K, int H, int I,
-                                                  size_t off_w, size_t off_s, float* __restrict__ act) {
-    extern __shared__ float4 xs4[];
-    float* xs = reinterpret_cast<float*>(xs4);
-    constexpr int EPC = WTraits<WT>::EPC;
-    const int pair = blockIdx.y;
-    const int t = pair / K;
-    const int nc = H / EPC;                       // chunks per row
-    stage_vector<WT, AT>(xs, x, (size_t)t * H, H, nc);
-    __syncthreads();
+// act element type written by the w13 stage: bf16 for bf16 / int4 weights
+template <int WT>
+struct ActOf {
+    static constexpr int AT = (WT == W_F32) ? A_F32 : A_BF16;
+};
 
+template <int AT>
+__device__ __forceinline__ void store_act(void* __restrict__ p, size_t i, float v) {
+    if (AT == A_F32)
+        static_cast<float*>(p)[i] = v;
+    else
+        static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
+}
+
+// ---- w13 + SwiGLU --------------------------------------------------------------
+// A row's nc chunks are split over WPR waves ("parts") of G lanes (WPR > 1 only
+// when G == 64), CPL chunks per lane: part q takes chunks [(q*CPL + j)*G + gl].
+// A lane group covers RP gate/up row pairs.  With WPR > 1 the parts' sums meet in
+// LDS and are added in part order.
+// grid.x: row blocks; grid.y: (t, k) pairs.
+// act[pair][i] = silu(W13[s][i] . x[t]) * (W13[s][I + i] . x[t])
+template <int WT, int AT, int CPL, int RP, int WPR>
+__global__ __launch_bounds__(256) void k_w13_gemv(const char* __restrict__ wbase, size_t stride, int nslots,
+                                                  const int32_t* __restrict__ slot_ids,
+                                                  const void* __restrict__ x, int K, int H, int I, int G,
+                                                  size_t off_w, size_t off_s, void* __restrict__ act) {
+    using X = XChunk<WT, XSel<WT, AT>::XT>;
+    constexpr int EPC = WTraits<WT>::EPC;
+    constexpr int ACT = ActOf<WT>::AT;
+    __shared__ float red[4][2][RP];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int i0 = (blockIdx.x * 4 + wave) * PPW;
-    if (i0 >= I) return;
+    const int gl = lane & (G - 1);
+    const int groups = 64 / G;
+    const int grp = lane / G;
+    const int part = wave % WPR;
+    const int pair = blockIdx.y;
+    const int t = pair / K;
+    const int i0 = ((blockIdx.x * (4 / WPR) + wave / WPR) * groups + grp) * RP;
+    if (WPR == 1 && i0 >= I) return;           // whole lane groups retire together
     const int slot = slot_ids[pair];
-    float* arow = act + (size_t)pair * I;
-    if (slot < 0 || slot >= nslots) {
-        if (lane < PPW && i0 + lane < I) arow[i0 + lane] = 0.0f;
-        return;
-    }
-    const char* ex = wbase + (size_t)slot * stride;
+    const bool ok = slot >= 0 && slot < nslots;
+    const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
+    const char* ex = wbase + (size_t)(ok ? slot : 0) * stride;
     const char* wrows = ex + off_w;
-    const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
-    const int spr = H / 128;                      // scales per row (int4)
 
-    uint4 wg[PPW][CPL], wu[PPW][CPL];
+    float pg[RP], pu[RP];
+    if (ok) {
+        uint4 wg[RP][CPL], wu[RP][CPL];
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-        const int i = min(i0 + p, I - 1);
-        const char* g = wrows + (size_t)i * row_bytes;
-        const char* u = wrows + (size_t)(I + i) * row_bytes;
+        for (int p = 0; p < RP; ++p) {
+            const int i = min(i0 + p, I - 1);
+            const char* g = wrows + (size_t)i * row_bytes;
+            const char* u = wrows + (size_t)(I + i) * row_bytes;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = lane + 64 * j;
-            if (c < nc) {
+            for (int j = 0; j < CPL; ++j) {
+                const int c = (part * CPL + j) * G + gl;
                 wg[p][j] = load16(g + (size_t)c * 16);
                 wu[p][j] = load16(u + (size_t)c * 16);
             }
         }
-    }
+        float sg[RP][CPL], su[RP][CPL];
+        if (WT == W_INT4) {
+            const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
+            const int spr = H / 128;
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-        const int i = min(i0 + p, I - 1);
-        float pg = 0.0f, pu = 0.0f;
+            for (int p = 0; p < RP; ++p) {
+                const int i = min(i0 + p, I - 1);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = lane + 64 * j;
-            if (c < nc) {
-                float dg = chunk_dot<WT>(wg[p][j], xs4, c, nc);
-                float du = chunk_dot<WT>(wu[p][j], xs4, c, nc);
-                if (WT == W_INT4) {
-                    dg *= chunk_scale(srows + (size_t)i * spr, c);
-                    du *= chunk_scale(srows + (size_t)(I + i) * spr, c);
+                for (int j = 0; j < CPL; ++j) {
+                    const int c = (part * CPL + j) * G + gl;
+                    sg[p][j] = chunk_scale(srows + (size_t)i * spr, c);
+                    su[p][j] = chunk_scale(srows + (size_t)(I + i) * spr, c);
                 }
-                pg += dg;
-                pu += du;
             }
         }
-        pg = wave_sum(pg);
-        pu = wave_sum(pu);
-        if (lane == 0 && i0 + p < I) arow[i0 + p] = silu(pg) * pu;
+        X xv[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            xv[j].template load<AT>(x, (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                float dg = cdot(wg[p][j], xv[j]);
+                float du = cdot(wu[p][j], xv[j]);
+                if (WT == W_INT4) {
+                    dg *= sg[p][j];
+                    du *= su[p][j];
+                }
+                a += dg;
+                b += du;
+            }
+            pg[p] = group_sum(a, G);
+            pu[p] = group_sum(b, G);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
     }
+    if (WPR > 1) {
+        if (lane == 0)
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                red[wave][0][p] = pg[p];
+                red[wave][1][p] = pu[p];
+            }
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            float a = 0.0f, b = 0.0f;
+            for (int q = 0; q < WPR; ++q) {
+                a += red[wave + q][0][p];
+                b += red[wave + q][1][p];
+            }
+            pg[p] = a;
+            pu[p] = b;
+        }
+    }
+    if (gl == 0)
+#pragma unroll
+        for (int p = 0; p < RP; ++p)
+            if (i0 + p < I) store_act<ACT>(act, (size_t)pair * I + i0 + p, ok ? silu(pg[p]) * pu[p] : 0.0f);
 }
 
-// ---- w2 + ordered top-k combine ----------------------------------------------
-// grid.x: blocks of 4 waves x RPW output rows; grid.y: tokens.
-// out[t][r] = resid[t][r] + sum_k w[t][k] * (W2[s_k][r] . act[t*K+k]).
-// Each lane weights its partial dot by w[t][k] (k in order), then one wave sum.
-template <int WT, int AT, int CPL, int RPW>
-__global__ __launch_bounds__(256) void k_w2_combine(const char* __restrict__ wbase, size_t stride,
-                                                    int nslots, const int32_t* __restrict__ slot_ids,
-                                                    const float* __restrict__ topk_w,
-                                                    const float* __restrict__ act,
-                                                    const void* __restrict__ resid, void* __restrict__ out,
-                                                    int K, int H, int I, size_t off_w, size_t off_s) {
-    extern __shared__ float4 as4[];
-    float* as = reinterpret_cast<float*>(as4);
-    __shared__ int32_t s_slot[kMaxTopK];
-    __shared__ float s_w[kMaxTopK];
+// ---- w2 + ordered top-k combine ------------------------------------------------
+// grid.x: blocks of RB = RP * (64 / G) output rows; grid.y: tokens.  The block's
+// waves take the K * WPR (expert, part) tasks in turn: y_k[r] = W2[s_k][r] .
+// act[t*K + k] (part sums) goes to LDS, then
+// out[t][r] = resid[t][r] + sum_{k = 0..K-1} w[t][k] * y_k[r]   (k in order).
+template <int WT, int AT, int CPL, int RP, int WPR, int NWMAX>
+__global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(const char* __restrict__ wbase, size_t stride,
+                                                           int nslots, const int32_t* __restrict__ slot_ids,
+                                                           const float* __restrict__ topk_w,
+                                                           const void* __restrict__ act,
+                                                           const void* __restrict__ resid, void* __restrict__ out,
+                                                           int K, int H, int I, int G, size_t off_w, size_t off_s) {
+    extern __shared__ float ys[];               // [K][WPR][RB]
+    constexpr int ACT = ActOf<WT>::AT;
+    using X = XChunk<WT, XSel<WT, ACT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
-    const int t = blockIdx.y;
-    const int nc = I / EPC;
-    const int vec = nc * EPC;                     // = I
-    for (int k = 0; k < K; ++k) stage_vector_f32<WT>(as + (size_t)k * vec, act + ((size_t)t * K + k) * I, I, nc);
-    if (threadIdx.x < K) {
-        const int s = slot_ids[t * K + threadIdx.x];
-        s_slot[threadIdx.x] = (s >= 0 && s < nslots) ? s : -1;
-        s_w[threadIdx.x] = topk_w[t * K + threadIdx.x];
-    }
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6;
-    const int r0 = (blockIdx.x * 4 + wave) * RPW;
-    if (r0 >= H) return;
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (G - 1);
+    const int groups = 64 / G;
+    const int grp = lane / G;
+    const int RB = RP * groups;
+    const int t = blockIdx.y;
+    const int rb0 = blockIdx.x * RB;
+    const int r0 = rb0 + grp * RP;
+    const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
     const int spr = I / 128;
-
-    float accl[RPW];
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) accl[p] = 0.0f;
-
-    for (int k = 0; k < K; ++k) {
-        const int s = s_slot[k];
-        if (s < 0) continue;
-        const char* ex = wbase + (size_t)s * stride;
-        const char* wrows = ex + off_w;
-        const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
-        const float4* a4 = as4 + (size_t)k * (vec / 4);
-        const float wk = s_w[k];
-        uint4 wr[RPW][CPL];
-#pragma unroll
-        for (int p = 0; p < RPW; ++p) {
-            const int r = min(r0 + p, H - 1);
-            const char* row = wrows + (size_t)r * row_bytes;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = lane + 64 * j;
-                if (c < nc) wr[p][j] = load16(row + (size_t)c * 16);
-            }
+    for (int task = wave; task < K * WPR; task += nw) {
+        const int k = task / WPR;
+        const int part = task - k * WPR;
+        const int pair = t * K + k;
+        const int slot = slot_ids[pair];
+        float* yk = ys + (size_t)task * RB + grp * RP;
+        if (slot < 0 || slot >= nslots) {
+            if (gl == 0)
+                for (int p = 0; p < RP; ++p) yk[p] = 0.0f;
+            continue;
         }
+        const char* ex = wbase + (size_t)slot * stride;
+        const char* wrows = ex + off_w;
+        uint4 wr[RP][CPL];
 #pragma unroll
-        for (int p = 0; p < RPW; ++p) {
-            const int r = min(r0 + p, H - 1);
-            float part = 0.0f;
+        for (int p = 0; p < RP; ++p) {
+            const char* row = wrows + (size_t)min(r0 + p, H - 1) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) wr[p][j] = load16(row + (size_t)((part * CPL + j) * G + gl) * 16);
+        }
+        float sc[RP][CPL];
+        if (WT == W_INT4) {
+            const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
+#pragma unroll
+            for (int p = 0; p < RP; ++p)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j)
+                    sc[p][j] = chunk_scale(srows + (size_t)min(r0 + p, H - 1) * spr, (part * CPL + j) * G + gl);
+        }
+        X av[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            av[j].template load<ACT>(act, (size_t)pair * I + (size_t)((part * CPL + j) * G + gl) * EPC);
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            float acc = 0.0f;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int c = lane + 64 * j;
-                if (c < nc) {
-                    float d = chunk_dot<WT>(wr[p][j], a4, c, nc);
-                    if (WT == W_INT4) d *= chunk_scale(srows + (size_t)r * spr, c);
-                    part += d;
-                }
+                float d = cdot(wr[p][j], av[j]);
+                if (WT == W_INT4) d *= sc[p][j];
+                acc += d;
             }
-            accl[p] = fmaf(wk, part, accl[p]);
+            acc = group_sum(acc, G);
+            if (gl == 0) yk[p] = acc;
         }
     }
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        const float acc = wave_sum(accl[p]);
-        const int r = r0 + p;
-        if (lane == 0 && r < H) {
-            const size_t o = (size_t)t * H + r;
-            float v = acc;
-            if (resid) v += load_act<AT>(resid, o);
-            if (AT == A_F32)
-                static_cast<float*>(out)[o] = v;
-            else
-                static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
+    __syncthreads();
+    const float* wt = topk_w + (size_t)t * K;
+    for (int i = threadIdx.x; i < RB; i += blockDim.x) {
+        const int r = rb0 + i;
+        if (r >= H) continue;
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float y = 0.0f;
+            for (int q = 0; q < WPR; ++q) y += ys[(size_t)(k * WPR + q) * RB + i];
+            acc = fmaf(wt[k], y, acc);
         }
+        const size_t o = (size_t)t * H + r;
+        if (resid) acc += load_act<AT>(resid, o);
+        if (AT == A_F32)
+            static_cast<float*>(out)[o] = acc;
+        else
+            static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(acc);
     }
 }
 
@@ -412,76 +562,153 @@ __global__ __launch_bounds__(256) void k_w2_combine(const char* __restrict__ wba
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kPPW = 2;   // gate/up row pairs per wave in k_w13_gemv
-constexpr int kRPW = 2;   // output rows per wave in k_w2_combine
+// Launch shape when a whole wave shares a row (G == 64): waves per row (WPR) and
+// rows per lane group (RP); otherwise one wave part and one row (pair) per group.
+#ifndef MOE_W13_WPR
+#define MOE_W13_WPR 1
+#endif
+#ifndef MOE_W13_RP64
+#define MOE_W13_RP64 2
+#endif
+#ifndef MOE_W2_WPR
+#define MOE_W2_WPR 1
+#endif
+#ifndef MOE_W2_RP64
+#define MOE_W2_RP64 2
+#endif
 
-int elem_bytes_x2(int wtype) { return wtype == W_F32 ? 8 : (wtype == W_BF16 ? 4 : 1); }
-
-// chunks per row for a row of `n` elements
-int chunks(int wtype, int n) { return n * elem_bytes_x2(wtype) / 2 / 16; }
-
-template <int WT, int AT, int CPL13, int CPL2>
-hipError_t run_decode(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t stream) {
-    const int T = a.T, K = g.K;
-    const int rows13 = 4 * kPPW, rows2 = 4 * kRPW;
-    const size_t lds13 = (size_t)g.H * sizeof(float);
-    const size_t lds2 = (size_t)K * g.I * sizeof(float);
-    hipError_t e = hipSuccess;
-    if (ev && ev->w13_start && (e = hipEventRecord(ev->w13_start, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL13, kPPW>), dim3((g.I + rows13 - 1) / rows13, T * K), dim3(256),
-                       lds13, stream, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.x, K, g.H, g.I,
-                       g.off_w13, g.off_s13, a.act);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev && ev->w13_stop && (e = hipEventRecord(ev->w13_stop, stream)) != hipSuccess) return e;
-    if (ev && ev->w2_start && (e = hipEventRecord(ev->w2_start, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_w2_combine<WT, AT, CPL2, kRPW>), dim3((g.H + rows2 - 1) / rows2, T), dim3(256), lds2,
-                       stream, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.topk_w, a.act, a.resid, a.out, K,
-                       g.H, g.I, g.off_w2, g.off_s2);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev && ev->w2_stop && (e = hipEventRecord(ev->w2_stop, stream)) != hipSuccess) return e;
-    return hipSuccess;
+int chunks_of(int wtype, int n) {
+    const int epc = wtype == W_F32 ? 4 : (wtype == W_BF16 ? 8 : 32);
+    return n / epc;
 }
 
-int cpl_bucket(int nc) {
-    const int c = (nc + 63) / 64;
-    if (c <= 1) return 1;
-    if (c <= 2) return 2;
-    if (c <= 4) return 4;
-    if (c <= 8) return 8;
-    if (c <= 16) return 16;
-    return -1;
+int group_lanes(int nc) {
+    int g = 64;
+    while (g > 1 && nc % g) g >>= 1;
+    return g;
 }
 
-template <int WT, int AT, int CPL13>
-hipError_t pick_cpl2(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
-    switch (cpl_bucket(chunks(WT, g.I))) {
-        case 1: return run_decode<WT, AT, CPL13, 1>(g, a, ev, s);
-        case 2: return run_decode<WT, AT, CPL13, 2>(g, a, ev, s);
-        case 4: return run_decode<WT, AT, CPL13, 4>(g, a, ev, s);
-        case 8: return run_decode<WT, AT, CPL13, 8>(g, a, ev, s);
-        case 16: return run_decode<WT, AT, CPL13, 16>(g, a, ev, s);
+// waves per row for a row of nc chunks split over G lanes: the largest of
+// {want, want/2, ..., 1} that divides nc / G (only for G == 64)
+int waves_per_row(int nc, int G, int want) {
+    if (G != 64) return 1;
+    int w = want;
+    while (w > 1 && (nc / G) % w) w >>= 1;
+    return w;
+}
+
+bool cpl_ok(int cpl) {
+    switch (cpl) {
+        case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 12: case 16: return true;
     }
+    return false;
+}
+
+template <int WT, int AT, int CPL, int RP, int WPR>
+hipError_t launch_w13(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
+    const int rows_per_block = (4 / WPR) * (64 / G) * RP;
+    const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, a.T * g.K);
+    if (ev && ev->w13_start)
+        hipExtLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, ev->w13_start,
+                              ev->w13_stop, 0, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.x, g.K, g.H, g.I, G,
+                              g.off_w13, g.off_s13, a.act);
+    else
+        hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, a.wbase, g.slot_stride,
+                           a.nslots, a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13, g.off_s13, a.act);
+    return hipGetLastError();
+}
+
+template <int WT, int AT, int CPL, int RP, int WPR>
+hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
+    constexpr int NWMAX = (WT == W_INT4) ? 8 : 16;
+    const int RB = (64 / G) * RP;
+    const int tasks = g.K * WPR;
+    const int nw = tasks < NWMAX ? tasks : NWMAX;
+    const size_t lds = (size_t)tasks * RB * sizeof(float);
+    const dim3 grid((g.H + RB - 1) / RB, a.T);
+    if (ev && ev->w2_start)
+        hipExtLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), (uint32_t)lds, s,
+                              ev->w2_start, ev->w2_stop, 0, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.topk_w,
+                              a.act, a.resid, a.out, g.K, g.H, g.I, G, g.off_w2, g.off_s2);
+    else
+        hipLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), lds, s, a.wbase,
+                           g.slot_stride, a.nslots, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I, G,
+                           g.off_w2, g.off_s2);
+    return hipGetLastError();
+}
+
+#define MOE_CPL_SWITCH(cpl, CALL)                       \
+    switch (cpl) {                                      \
+        case 1: { constexpr int C = 1; return CALL; }   \
+        case 2: { constexpr int C = 2; return CALL; }   \
+        case 3: { constexpr int C = 3; return CALL; }   \
+        case 4: { constexpr int C = 4; return CALL; }   \
+        case 5: { constexpr int C = 5; return CALL; }   \
+        case 6: { constexpr int C = 6; return CALL; }   \
+        case 8: { constexpr int C = 8; return CALL; }   \
+        case 12: { constexpr int C = 12; return CALL; } \
+        case 16: { constexpr int C = 16; return CALL; } \
+    }                                                   \
     return hipErrorInvalidValue;
+
+template <int WT, int AT>
+hipError_t run_w13(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    const int nc = chunks_of(WT, g.H);
+    const int G = group_lanes(nc);
+    const int wpr = waves_per_row(nc, G, MOE_W13_WPR);
+    const int cpl = nc / (G * wpr);
+    if (G != 64) {
+        MOE_CPL_SWITCH(cpl, (launch_w13<WT, AT, C, 1, 1>(g, a, G, ev, s)))
+    }
+    if (wpr == 4) {
+        MOE_CPL_SWITCH(cpl, (launch_w13<WT, AT, C, MOE_W13_RP64, 4>(g, a, G, ev, s)))
+    }
+    if (wpr == 2) {
+        MOE_CPL_SWITCH(cpl, (launch_w13<WT, AT, C, MOE_W13_RP64, 2>(g, a, G, ev, s)))
+    }
+    MOE_CPL_SWITCH(cpl, (launch_w13<WT, AT, C, MOE_W13_RP64, 1>(g, a, G, ev, s)))
 }
 
 template <int WT, int AT>
-hipError_t pick_cpl13(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
-    switch (cpl_bucket(chunks(WT, g.H))) {
-        case 1: return pick_cpl2<WT, AT, 1>(g, a, ev, s);
-        case 2: return pick_cpl2<WT, AT, 2>(g, a, ev, s);
-        case 4: return pick_cpl2<WT, AT, 4>(g, a, ev, s);
-        case 8: return pick_cpl2<WT, AT, 8>(g, a, ev, s);
-        case 16: return pick_cpl2<WT, AT, 16>(g, a, ev, s);
+hipError_t run_w2(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    const int nc = chunks_of(WT, g.I);
+    const int G = group_lanes(nc);
+    const int wpr = waves_per_row(nc, G, MOE_W2_WPR);
+    const int cpl = nc / (G * wpr);
+    if (G != 64) {
+        MOE_CPL_SWITCH(cpl, (launch_w2<WT, AT, C, 1, 1>(g, a, G, ev, s)))
     }
-    return hipErrorInvalidValue;
+    if (wpr == 4) {
+        MOE_CPL_SWITCH(cpl, (launch_w2<WT, AT, C, MOE_W2_RP64, 4>(g, a, G, ev, s)))
+    }
+    if (wpr == 2) {
+        MOE_CPL_SWITCH(cpl, (launch_w2<WT, AT, C, MOE_W2_RP64, 2>(g, a, G, ev, s)))
+    }
+    MOE_CPL_SWITCH(cpl, (launch_w2<WT, AT, C, MOE_W2_RP64, 1>(g, a, G, ev, s)))
 }
 
-template <int WT>
-hipError_t pick_at(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
-    return g.atype == A_F32 ? pick_cpl13<WT, A_F32>(g, a, ev, s) : pick_cpl13<WT, A_BF16>(g, a, ev, s);
+template <int WT, int AT>
+hipError_t run_decode(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    hipError_t e = run_w13<WT, AT>(g, a, ev, s);
+    if (e != hipSuccess) return e;
+    return run_w2<WT, AT>(g, a, ev, s);
+}
+
+bool split_ok(int nc, int want) {
+    const int G = group_lanes(nc);
+    return cpl_ok(nc / (G * waves_per_row(nc, G, want)));
 }
 
 }  // namespace
+
+bool decode_shape_supported(int wtype, int atype, int H, int I) {
+    if (wtype == W_INT4 && atype != A_BF16) return false;
+    const int n13 = chunks_of(wtype, H), n2 = chunks_of(wtype, I);
+    if (n13 < 1 || n2 < 1) return false;
+    return split_ok(n13, MOE_W13_WPR) && split_ok(n2, MOE_W2_WPR);
+}
+
+size_t act_bytes_per_pair(int wtype, int I) { return (size_t)I * (wtype == W_F32 ? 4 : 2); }
 
 size_t grouped_index_bytes(int max_tokens, int K, int nslots) {
     (void)max_tokens;
@@ -493,10 +720,12 @@ size_t grouped_index_bytes(int max_tokens, int K, int nslots) {
 hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t stream) {
     if (a.T <= 0) return hipSuccess;
     if ((long)a.T * g.K > 65535) return hipErrorInvalidValue;   // grid.y of the w13 kernel
-    switch (g.wtype) {
-        case W_F32: return pick_at<W_F32>(g, a, ev, stream);
-        case W_BF16: return pick_at<W_BF16>(g, a, ev, stream);
-        case W_INT4: return pick_at<W_INT4>(g, a, ev, stream);
+    switch (g.wtype * 2 + g.atype) {
+        case W_F32 * 2 + A_F32: return run_decode<W_F32, A_F32>(g, a, ev, stream);
+        case W_F32 * 2 + A_BF16: return run_decode<W_F32, A_BF16>(g, a, ev, stream);
+        case W_BF16 * 2 + A_F32: return run_decode<W_BF16, A_F32>(g, a, ev, stream);
+        case W_BF16 * 2 + A_BF16: return run_decode<W_BF16, A_BF16>(g, a, ev, stream);
+        case W_INT4 * 2 + A_BF16: return run_decode<W_INT4, A_BF16>(g, a, ev, stream);
     }
     return hipErrorInvalidValue;
 }

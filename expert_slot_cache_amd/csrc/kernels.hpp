@@ -13,7 +13,6 @@ enum AType { A_F32 = 0, A_BF16 = 1 };
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopK = 64;
 constexpr int kDecodeMaxTokens = 8;   // n_tokens above this use the grouped GEMM path
-constexpr int kMaxLdsFloats = 12288;  // 48 KiB of fp32 activations per workgroup
 
 // Shape and byte layout of one expert as stored in a slot.
 struct Geom {
@@ -23,14 +22,17 @@ struct Geom {
     size_t off_w13, off_w2, off_s13, off_s2;
 };
 
-// Distinct ids of ids[0..n): rb[0] = D, rb[1] = 1 if an id is outside [0,E),
-// rb[2..2+D) = ascending distinct ids; rank[e] = position of e in that list.
-hipError_t launch_distinct(const int32_t* ids, int n, int E, int32_t* rb, int32_t* rank,
+// Distinct ids of ids[0..n), written to host-mapped rb with a tag (1..2^18-1) in
+// bits 14..31 of every word: rb[0] = tag<<14 | bad<<13 | D (bad: an id outside
+// [0,E)), rb[1+i] = tag<<14 | i-th ascending distinct id.  rank[e] (device) =
+// position of e in that list.
+hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32_t* rank, uint32_t tag,
                            hipStream_t stream);
 
-// out[i] = table[ids[i]] (ids outside [0,E) give -1).
-hipError_t launch_remap(const int32_t* ids, int n, int E, const int32_t* table, int32_t* out,
-                        hipStream_t stream);
+// Applies the n_upd changes upd[2u] -> upd[2u+1] to `table` (in place), then
+// out[i] = table[ids[i]] (ids outside [0,E) give -1).  upd may be host-mapped memory.
+hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* upd, int n_upd,
+                        int32_t* out, hipStream_t stream);
 
 // Optional event pairs around the two projection stages (any may be null).
 struct StageEvents {
@@ -48,16 +50,20 @@ struct ForwardArgs {
     void* out;              // [T][H]
     int T;
     // scratch
-    float* act;             // [T*K][I] fp32 (decode path)
-    uint16_t* act_bf16;     // [T*K][I] bf16 (grouped path)
-    float* y;               // [T*K][H] fp32 (grouped path)
+    void* act;              // [T*K][I]: SwiGLU output (fp32 for f32 weights, else bf16)
+    float* y;               // [T*K][H] fp32: per-(token, expert) w2 output
     int32_t* grp;           // grouped-path index buffers (see launch_forward)
-    int n_slot_groups;      // number of distinct slot ids possible (nslots)
 };
 
 // The slot-indexed fused MoE for one layer.
 hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents* ev,
                           hipStream_t stream);
+
+// Whether the decode kernels support this shape (row chunk counts they can split).
+bool decode_shape_supported(int wtype, int atype, int H, int I);
+
+// Bytes of one (token, expert) pair's SwiGLU output in the act scratch.
+size_t act_bytes_per_pair(int wtype, int I);
 
 // Bytes of the grouped-path index buffer for max_tokens tokens and nslots slots.
 size_t grouped_index_bytes(int max_tokens, int K, int nslots);

@@ -10,12 +10,13 @@
 //   3. copy streams wait for the layer's last forward (its slot reads, WAR), then
 //      hipMemcpyAsync store -> slot for each miss, optionally in chunks, then an
 //      event per copy stream that the compute stream waits on (RAW).
-//   4. the changed map entries are written to a pinned copy of the table, which is
-//      uploaded on the compute stream; k_remap then reads the fresh table.
+//   4. the step's map changes go to a small pinned list that k_remap reads: it
+//      applies them to the persistent HBM table and remaps through the fresh table.
 //   5. forward kernels on the compute stream; record the layer's reads-done event.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cstdarg>
 #include <cstdio>
@@ -98,14 +99,16 @@ bool make_layout(int32_t wtype, int32_t H, int32_t I, Layout* L) {
 struct Timing {
     hipEvent_t a = nullptr, b = nullptr;   // start, stop
     bool pending = false;
+    uint64_t bytes = 0;                    // copies: bytes between the two events
 };
 
 struct LayerState {
     moe::SlotLRU lru;
     char* store = nullptr;       // pinned host: E experts
     char* slots = nullptr;       // HBM: nslot_alloc experts + zeroed tail
-    int32_t* map_dev = nullptr;  // HBM int32 [E]
-    int32_t* map_host = nullptr; // pinned int32 [E], source of the table upload
+    int32_t* map_dev = nullptr;  // HBM int32 [E]: the persistent map table
+    int32_t* upd_host = nullptr; // pinned int32 [2E]: this step's (entry, value) changes
+    int32_t* upd_dev = nullptr;  // device view of upd_host
     hipEvent_t reads_done = nullptr;
     bool reads_recorded = false;
     bool prepared = false;
@@ -133,18 +136,22 @@ struct moe_pool {
     int32_t staging_owner = -1;
     hipEvent_t staging_reads_done = nullptr;
     bool staging_recorded = false;
-    int32_t* rb_host = nullptr;   // pinned [2 + E], written by k_distinct
-    int32_t* rb_dev = nullptr;    // device view of rb_host
-    hipEvent_t rb_event = nullptr;
+    uint32_t* rb_host = nullptr;  // pinned [1 + E] tagged words, written by k_distinct
+    uint32_t* rb_dev = nullptr;   // device view of rb_host
+    uint32_t rb_tag = 0;          // tag of the last readback (1 .. 2^18 - 1)
+    int32_t rb_used = 0;          // words of rb_host written by the last readback
+    std::vector<int32_t> ulist;   // the last readback's distinct ids
     int32_t* rank_dev = nullptr;  // HBM [E]
     int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
-    float* act = nullptr;         // HBM [max_tokens * K * I]
+    void* act = nullptr;          // HBM [max_tokens * K][I] SwiGLU output
+    float* y = nullptr;           // HBM [max_tokens * K][H] per-pair w2 output
     std::vector<moe::Miss> misses;
     std::vector<char> used_copy;
     int copy_rr = 0;
-    // timing totals
+    // timing totals (sampled calls)
     double copy_ms = 0, w13_ms = 0, w2_ms = 0, sync_ms = 0;
-    uint64_t copy_calls = 0, fwd_calls = 0;
+    uint64_t copy_calls = 0, copy_bytes = 0, kern_calls = 0;
+    uint64_t n_copy_batches = 0, n_forwards = 0;   // all calls, for the sampling period
 };
 
 struct moe_lru {
@@ -162,7 +169,7 @@ void destroy_pool(moe_pool* p) {
         if (L.store) (void)hipHostFree(L.store);
         if (L.slots) (void)hipFree(L.slots);
         if (L.map_dev) (void)hipFree(L.map_dev);
-        if (L.map_host) (void)hipHostFree(L.map_host);
+        if (L.upd_host) (void)hipHostFree(L.upd_host);
         if (L.reads_done) (void)hipEventDestroy(L.reads_done);
         for (auto& t : L.copy_t) {
             if (t.a) (void)hipEventDestroy(t.a);
@@ -178,10 +185,10 @@ void destroy_pool(moe_pool* p) {
     if (p->staging) (void)hipFree(p->staging);
     if (p->staging_reads_done) (void)hipEventDestroy(p->staging_reads_done);
     if (p->rb_host) (void)hipHostFree(p->rb_host);
-    if (p->rb_event) (void)hipEventDestroy(p->rb_event);
     if (p->rank_dev) (void)hipFree(p->rank_dev);
     if (p->ident_dev) (void)hipFree(p->ident_dev);
     if (p->act) (void)hipFree(p->act);
+    if (p->y) (void)hipFree(p->y);
     delete p;
 }
 
@@ -192,11 +199,13 @@ moe_status_t check_layer(const moe_pool* p, int32_t layer) {
 }
 
 // Harvest finished timing event pairs (all work before the last readback sync).
-void harvest(moe_pool* p, Timing& t, double* acc) {
-    if (!t.pending) return;
+bool harvest(moe_pool* p, Timing& t, double* acc) {
+    if (!t.pending) return false;
     float ms = 0;
-    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) *acc += ms;
+    const bool ok = hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess;
+    if (ok) *acc += ms;
     t.pending = false;
+    return ok;
 }
 
 void harvest_layer(moe_pool* p, LayerState& L) {
@@ -212,6 +221,7 @@ void harvest_layer(moe_pool* p, LayerState& L) {
                 break;
             }
         float lo = 0, hi = 0;
+        uint64_t bytes = 0;
         for (auto& t : L.copy_t) {
             if (!t.pending) continue;
             float s = 0, e = 0;
@@ -219,13 +229,16 @@ void harvest_layer(moe_pool* p, LayerState& L) {
             (void)hipEventElapsedTime(&e, L.copy_t[ref].a, t.b);
             lo = std::min(lo, s);
             hi = std::max(hi, e);
+            bytes += t.bytes;
             t.pending = false;
         }
         p->copy_ms += hi - lo;
         p->copy_calls++;
+        p->copy_bytes += bytes;
     }
-    harvest(p, L.w13_t, &p->w13_ms);
-    harvest(p, L.w2_t, &p->w2_ms);
+    const bool a = harvest(p, L.w13_t, &p->w13_ms);
+    const bool b = harvest(p, L.w2_t, &p->w2_ms);
+    if (a && b) p->kern_calls++;
 }
 
 void harvest_all(moe_pool* p) {
@@ -242,13 +255,16 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
     const size_t eb = p->lay.total;
     const size_t chunk = p->cfg.copy_chunk_bytes ? p->cfg.copy_chunk_bytes : eb;
     std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
+    bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0;
+    for (const auto& t : L.copy_t) timed = timed && !t.pending;
     // every stream that may carry a piece first waits for the WAR event
     const int streams_needed = std::min<size_t>(ns, jobs.size() * ((eb + chunk - 1) / chunk));
     for (int i = 0; i < streams_needed; ++i) {
         const int s = (p->copy_rr + i) % ns;
         if (war_recorded) HIPCHK(hipStreamWaitEvent(p->copy[s], war, 0));
-        if (p->cfg.timing) {
+        if (timed) {
             HIPCHK(hipEventRecord(L.copy_t[s].a, p->copy[s]));
+            L.copy_t[s].bytes = 0;
         }
         p->used_copy[s] = 1;
     }
@@ -257,13 +273,14 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
         for (size_t off = 0; off < eb; off += chunk) {
             const size_t n = std::min(chunk, eb - off);
             HIPCHK(hipMemcpyAsync(j.first + off, j.second + off, n, hipMemcpyHostToDevice, p->copy[rr]));
+            if (timed) L.copy_t[rr].bytes += n;
             rr = (rr + 1) % ns;
         }
     }
     p->copy_rr = rr;
     for (int s = 0; s < ns; ++s) {
         if (!p->used_copy[s]) continue;
-        if (p->cfg.timing) {
+        if (timed) {
             HIPCHK(hipEventRecord(L.copy_t[s].b, p->copy[s]));
             L.copy_t[s].pending = true;
         }
@@ -308,12 +325,14 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.atype != MOE_A_F32 && c.atype != MOE_A_BF16) FAIL(MOE_EINVAL, "atype %d invalid", c.atype);
     if (c.rule != MOE_RULE_DISTINCT && c.rule != MOE_RULE_STATIC) FAIL(MOE_EINVAL, "rule %d invalid", c.rule);
     if (c.max_tokens < 1) FAIL(MOE_EINVAL, "max_tokens %d < 1", c.max_tokens);
+    if (c.timing < 0) FAIL(MOE_EINVAL, "timing %d < 0", c.timing);
     if (c.n_copy_streams < 1 || c.n_copy_streams > 8) FAIL(MOE_EINVAL, "n_copy_streams %d outside [1,8]", c.n_copy_streams);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
     Layout lay;
     if (!make_layout(c.wtype, c.hidden, c.inter, &lay)) FAIL(MOE_EINVAL, "unsupported shape/format (wtype %d, H %d, I %d)", c.wtype, c.hidden, c.inter);
-    if (c.hidden > moe::kMaxLdsFloats || (size_t)c.top_k * c.inter > (size_t)moe::kMaxLdsFloats)
-        FAIL(MOE_EINVAL, "hidden and top_k*inter must be <= %d", moe::kMaxLdsFloats);
+    if (!moe::decode_shape_supported(c.wtype, c.atype, c.hidden, c.inter))
+        FAIL(MOE_EINVAL, "shape not supported by the kernels (wtype %d, atype %d, H %d, I %d)", c.wtype, c.atype,
+             c.hidden, c.inter);
 
     moe_pool* p = new (std::nothrow) moe_pool();
     if (!p) FAIL(MOE_ENOMEM, "host allocation failed");
@@ -336,9 +355,10 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
 
     const size_t eb = lay.total;
     const size_t slot_bytes = (size_t)p->nslot_alloc * eb + kAlign;
-    const size_t act_bytes = (size_t)c.max_tokens * c.top_k * c.inter * sizeof(float);
+    const size_t act_bytes = (size_t)c.max_tokens * c.top_k * moe::act_bytes_per_pair(c.wtype, c.inter);
+    const size_t y_bytes = (size_t)c.max_tokens * c.top_k * c.hidden * sizeof(float);
     const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4) + (size_t)p->staging_cap * eb + act_bytes +
-                       (size_t)E * 8;
+                       y_bytes + (size_t)E * 8;
     if (c.hbm_budget_bytes && hbm > c.hbm_budget_bytes) {
         delete p;
         FAIL(MOE_ENOMEM, "pool needs %zu HBM bytes, budget is %zu", hbm, c.hbm_budget_bytes);
@@ -370,9 +390,9 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         CREATE_HIP(hipMalloc((void**)&L.slots, slot_bytes));
         CREATE_HIP(hipMemset(L.slots + (size_t)p->nslot_alloc * eb, 0, kAlign));
         CREATE_HIP(hipMalloc((void**)&L.map_dev, (size_t)E * 4));
-        CREATE_HIP(hipHostMalloc((void**)&L.map_host, (size_t)E * 4, hipHostMallocDefault));
-        for (int32_t e = 0; e < E; ++e) L.map_host[e] = -1;
-        CREATE_HIP(hipMemcpy(L.map_dev, L.map_host, (size_t)E * 4, hipMemcpyHostToDevice));
+        CREATE_HIP(hipMemset(L.map_dev, 0xFF, (size_t)E * 4));   // all -1
+        CREATE_HIP(hipHostMalloc((void**)&L.upd_host, (size_t)E * 8, hipHostMallocCoherent | hipHostMallocMapped));
+        CREATE_HIP(hipHostGetDevicePointer((void**)&L.upd_dev, L.upd_host, 0));
         CREATE_HIP(hipEventCreateWithFlags(&L.reads_done, hipEventDisableTiming));
         L.copy_t.resize(c.n_copy_streams);
         if (c.timing) {
@@ -388,9 +408,10 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     }
     if (p->staging_cap > 0) CREATE_HIP(hipMalloc((void**)&p->staging, (size_t)p->staging_cap * eb));
     CREATE_HIP(hipEventCreateWithFlags(&p->staging_reads_done, hipEventDisableTiming));
-    CREATE_HIP(hipHostMalloc((void**)&p->rb_host, (size_t)(E + 2) * 4, hipHostMallocCoherent | hipHostMallocMapped));
+    CREATE_HIP(hipHostMalloc((void**)&p->rb_host, (size_t)(E + 1) * 4, hipHostMallocCoherent | hipHostMallocMapped));
+    std::memset(p->rb_host, 0, (size_t)(E + 1) * 4);
     CREATE_HIP(hipHostGetDevicePointer((void**)&p->rb_dev, p->rb_host, 0));
-    CREATE_HIP(hipEventCreateWithFlags(&p->rb_event, hipEventDisableTiming));
+    p->ulist.resize(E);
     CREATE_HIP(hipMalloc((void**)&p->rank_dev, (size_t)E * 4));
     CREATE_HIP(hipMalloc((void**)&p->ident_dev, (size_t)E * 4));
     {
@@ -399,6 +420,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         CREATE_HIP(hipMemcpy(p->ident_dev, id.data(), (size_t)E * 4, hipMemcpyHostToDevice));
     }
     CREATE_HIP(hipMalloc((void**)&p->act, act_bytes));
+    CREATE_HIP(hipMalloc((void**)&p->y, y_bytes));
 #undef CREATE_HIP
     p->misses.reserve(E);
     *out = p;
@@ -429,8 +451,7 @@ moe_status_t moe_pool_reset(moe_pool_t* p) {
     for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
     for (auto& L : p->layers) {
         L.lru.reset();
-        for (int32_t e = 0; e < p->cfg.n_experts; ++e) L.map_host[e] = -1;
-        HIPCHK(hipMemcpy(L.map_dev, L.map_host, (size_t)p->cfg.n_experts * 4, hipMemcpyHostToDevice));
+        HIPCHK(hipMemset(L.map_dev, 0xFF, (size_t)p->cfg.n_experts * 4));
         L.prepared = false;
         L.bytes_h2d = 0;
         L.staged = 0;
@@ -463,26 +484,59 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
         return MOE_OK;
     }
 
-    // 1. distinct ids, read back: the step's one host sync
-    HIPCHK(moe::launch_distinct(topk_ids_dev, n, E, p->rb_dev, p->rank_dev, p->compute));
-    HIPCHK(hipEventRecord(p->rb_event, p->compute));
+    // 1. distinct ids, read back: the step's one host sync.  The kernel writes
+    // tagged words into pinned host memory (zeroed here beforehand); the host spins
+    // until each word it needs carries this step's tag, checking the stream now and
+    // then so that a failed launch cannot leave it spinning.
+    std::memset(p->rb_host, 0, (size_t)p->rb_used * 4);
+    p->rb_tag = p->rb_tag % ((1u << 18) - 1) + 1;
+    const uint32_t tag = p->rb_tag;
+    HIPCHK(moe::launch_distinct(topk_ids_dev, n, E, p->rb_dev, p->rank_dev, tag, p->compute));
     const auto t0 = std::chrono::steady_clock::now();
-    HIPCHK(hipEventSynchronize(p->rb_event));
+    const volatile uint32_t* rbv = p->rb_host;
+    auto wait_word = [&](int i) -> moe_status_t {
+        for (uint64_t it = 1;; ++it) {
+            const uint32_t w = rbv[i];
+            if ((w >> 14) == tag) return MOE_OK;
+            if ((it & 255) == 0) {
+                const hipError_t q = hipStreamQuery(p->compute);
+                if (q == hipSuccess) {
+                    // everything queued has finished, the distinct kernel included
+                    if ((rbv[i] >> 14) == tag) return MOE_OK;
+                    FAIL(MOE_EHIP, "distinct-id readback word %d missing after the stream drained", i);
+                }
+                if (q != hipErrorNotReady) FAIL(MOE_EHIP, "hipStreamQuery failed: %s", hipGetErrorString(q));
+            }
+            __builtin_ia32_pause();
+        }
+    };
+    p->rb_used = 1;
+    st = wait_word(0);
+    if (st) return st;
+    const uint32_t w0 = rbv[0];
+    const int32_t D = (int32_t)(w0 & 0x1FFFu);
+    const bool bad = (w0 >> 13) & 1u;
+    if (D > E) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
+    p->rb_used = 1 + D;
+    for (int32_t i = 0; i < D; ++i) {
+        st = wait_word(1 + i);
+        if (st) return st;
+        p->ulist[i] = (int32_t)(rbv[1 + i] & 0x3FFFu);
+    }
     if (p->cfg.timing) {
         p->sync_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
         harvest_all(p);
     }
-    const int32_t D = p->rb_host[0];
-    if (p->rb_host[1] != 0) FAIL(MOE_ERANGE, "layer %d: an expert id is outside [0,%d)", layer, E);
-    if (D < 1 || D > E) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
-    const int32_t* u = p->rb_host + 2;
+    if (bad) FAIL(MOE_ERANGE, "layer %d: an expert id is outside [0,%d)", layer, E);
+    if (D < 1) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
+    const int32_t* u = p->ulist.data();
 
     // 2. route + LRU
     p->misses.clear();
     int32_t the_path = MOE_PATH_POOL;
     if (p->cfg.resident) {
         L.lru.count_resident(D);
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, slot_ids_dev, p->compute));
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, nullptr, 0, slot_ids_dev, p->compute));
     } else if (L.lru.step(u, D, (int64_t)n, p->misses)) {
         // 3. misses: store -> slot on the copy streams, after this layer's last reads
         if (!p->misses.empty()) {
@@ -491,14 +545,26 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
             for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.store + (size_t)m.expert * eb);
             st = issue_copies(p, L, jobs, L.reads_done, L.reads_recorded);
             if (st) return st;
-            // 4. rewrite the changed map entries and upload the table before the remap
-            for (const auto& m : p->misses) {
-                if (m.evicted >= 0) L.map_host[m.evicted] = -1;
-                L.map_host[m.expert] = m.slot;
-            }
-            HIPCHK(hipMemcpyAsync(L.map_dev, L.map_host, (size_t)E * 4, hipMemcpyHostToDevice, p->compute));
         }
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, slot_ids_dev, p->compute));
+        // 4. the map changes, applied by the remap kernel before it reads the table.
+        // Each touched entry carries its value after the whole step: an expert can be
+        // evicted by an earlier (lower-id) miss of the step and re-inserted by its own
+        // miss later in the same step, so an entry may appear twice -- with the same
+        // final value, which makes the kernel's unordered writes safe.
+        // (The previous step's list was consumed before this step's readback sync.)
+        const std::vector<int32_t>& fmap = L.lru.map();
+        int n_upd = 0;
+        for (const auto& m : p->misses) {
+            if (m.evicted >= 0) {
+                L.upd_host[2 * n_upd] = m.evicted;
+                L.upd_host[2 * n_upd + 1] = fmap[m.evicted];
+                ++n_upd;
+            }
+            L.upd_host[2 * n_upd] = m.expert;
+            L.upd_host[2 * n_upd + 1] = fmap[m.expert];
+            ++n_upd;
+        }
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, L.upd_dev, n_upd, slot_ids_dev, p->compute));
     } else {
         // selective-copy fallback: the step's experts go to staging in rank order;
         // the pool is untouched
@@ -510,7 +576,7 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
         if (st) return st;
         L.staged += (uint64_t)D;
         p->staging_owner = layer;
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->rank_dev, slot_ids_dev, p->compute));
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->rank_dev, nullptr, 0, slot_ids_dev, p->compute));
     }
     L.prepared = true;
     L.prep_tokens = n_tokens;
@@ -547,18 +613,20 @@ moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, c
     a.out = out_dev;
     a.T = n_tokens;
     a.act = p->act;
+    a.y = p->y;
     moe::StageEvents ev;
-    if (p->cfg.timing) {
+    const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
+                       !L.w13_t.pending && !L.w2_t.pending;
+    if (timed) {
         ev.w13_start = L.w13_t.a;
         ev.w13_stop = L.w13_t.b;
         ev.w2_start = L.w2_t.a;
         ev.w2_stop = L.w2_t.b;
     }
-    HIPCHK(moe::launch_forward(p->geom, a, p->cfg.timing ? &ev : nullptr, p->compute));
-    if (p->cfg.timing) {
+    HIPCHK(moe::launch_forward(p->geom, a, timed ? &ev : nullptr, p->compute));
+    if (timed) {
         L.w13_t.pending = true;
         L.w2_t.pending = true;
-        p->fwd_calls++;
     }
     if (fb) {
         HIPCHK(hipEventRecord(p->staging_reads_done, p->compute));
@@ -568,6 +636,16 @@ moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, c
         L.reads_recorded = true;
     }
     return MOE_OK;
+}
+
+moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
+                           int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev, const void* resid_dev,
+                           void* out_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
+    if (n_tokens > 0 && (!x_dev || !topk_w_dev || !out_dev)) FAIL(MOE_EINVAL, "null buffer");
+    moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap, n_miss,
+                                       path);
+    if (st) return st;
+    return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
 }
 
 moe_status_t moe_pool_sync(moe_pool_t* p) {
@@ -661,9 +739,10 @@ moe_status_t moe_pool_get_timing(moe_pool_t* p, moe_pool_timing_t* out) {
     harvest_all(p);
     out->copy_ms = p->copy_ms;
     out->copy_calls = p->copy_calls;
+    out->copy_bytes = p->copy_bytes;
     out->w13_ms = p->w13_ms;
     out->w2_ms = p->w2_ms;
-    out->forward_calls = p->fwd_calls;
+    out->kernel_calls = p->kern_calls;
     out->sync_wait_ms = p->sync_ms;
     return MOE_OK;
 }
@@ -674,7 +753,7 @@ moe_status_t moe_pool_reset_timing(moe_pool_t* p) {
     if (st) return st;
     harvest_all(p);
     p->copy_ms = p->w13_ms = p->w2_ms = p->sync_ms = 0;
-    p->copy_calls = p->fwd_calls = 0;
+    p->copy_calls = p->copy_bytes = p->kern_calls = 0;
     return MOE_OK;
 }
 

@@ -92,8 +92,10 @@ typedef struct {
     size_t copy_chunk_bytes;/* split each copy into pieces of at most this size
                                (0 = one hipMemcpyAsync per expert) */
     size_t hbm_budget_bytes;/* 0 = no limit; else slots + staging + scratch must fit */
-    int32_t timing;         /* 1 = record HIP events around copies and kernels
-                               (moe_pool_get_timing) */
+    int32_t timing;         /* 0 = off; N >= 1 = time every Nth forward's two kernels
+                               and every Nth prepare's copies with HIP events
+                               (moe_pool_get_timing).  The events cost a few us per
+                               timed call, so a period > 1 keeps them off most calls. */
 } moe_pool_config_t;
 
 typedef struct {
@@ -112,12 +114,13 @@ typedef struct {
 } moe_pool_stats_t;
 
 typedef struct {
-    double copy_ms;      /* sum over prepare calls of the copy-stream span of its copies */
-    uint64_t copy_calls; /* prepare calls that issued copies */
-    double w13_ms;       /* sum of durations of the w13 (+ SwiGLU) kernel */
-    double w2_ms;        /* sum of durations of the w2 (+ combine) kernel(s) */
-    uint64_t forward_calls;
-    double sync_wait_ms; /* host time blocked on the distinct-id readback */
+    double copy_ms;       /* sum, over timed prepare calls, of the span of their copies */
+    uint64_t copy_calls;  /* timed prepare calls that issued copies */
+    uint64_t copy_bytes;  /* bytes those timed copies moved */
+    double w13_ms;        /* sum of durations of the timed w13 (+ SwiGLU) kernels */
+    double w2_ms;         /* sum of durations of the timed w2 (+ combine) kernels */
+    uint64_t kernel_calls;/* timed forward calls (each times both kernels) */
+    double sync_wait_ms;  /* host time blocked on the distinct-id readbacks (all calls) */
 } moe_pool_timing_t;
 
 /* ---- errors -------------------------------------------------------------- */
@@ -132,7 +135,8 @@ const char* moe_last_error(void);
 size_t moe_expert_bytes(int32_t wtype, int32_t hidden, int32_t inter);
 
 /* ---- pool lifetime ---------------------------------------------------------- */
-/* Allocates the pinned store (n_layers * n_experts experts, zero-filled), one HBM
+/* Allocates the pinned store (n_layers * n_experts experts; contents undefined
+ * until moe_pool_load_expert writes them), one HBM
  * pool per layer (n_slots experts plus a zeroed 256-byte tail, allocated once so
  * slot addresses never change: [vLLM-cache] "fixed-address (allocated once at
  * init)"; [llama-pool] Design item 1), a staging area of min(E, K*max_tokens)
@@ -176,8 +180,9 @@ moe_status_t moe_pool_reset(moe_pool_t* pool);
  *                even when it exceeds miss_cap.  A FALLBACK step has no misses.
  *  path          MOE_PATH_POOL or MOE_PATH_FALLBACK.
  *
- * The distinct ids are found on the GPU and read back: prepare blocks until that
- * kernel is done (one sync per layer per step, as in [llama-pool] "Limitations").
+ * The distinct ids are found on the GPU and written straight into pinned host
+ * memory: prepare spins until that kernel has published them (one sync per layer
+ * per step, as in [llama-pool] "Limitations").
  * It returns once the copies (on the copy streams), the map upload and the remap
  * are enqueued; the compute stream waits for the copies through events.
  * Distinct ids are processed in ascending order; free slots are taken from the
@@ -207,6 +212,13 @@ moe_status_t moe_pool_prepare(moe_pool_t* pool, int32_t layer, const int32_t* to
 moe_status_t moe_pool_forward(moe_pool_t* pool, int32_t layer, const void* x_dev,
                               const int32_t* slot_ids_dev, const float* topk_w_dev,
                               const void* resid_dev, int32_t n_tokens, void* out_dev);
+
+/* prepare + forward of one layer in one call (same arguments, same semantics,
+ * same errors), for callers that run the two back to back. */
+moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
+                           int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev,
+                           const void* resid_dev, void* out_dev, moe_miss_t* miss_host, int32_t miss_cap,
+                           int32_t* n_miss, int32_t* path);
 
 /* Waits until all of the pool's copies and kernels issued so far are complete. */
 moe_status_t moe_pool_sync(moe_pool_t* pool);

@@ -201,3 +201,28 @@ def test_prefill_ubatch_leaves_pool_untouched():
             ref = rig.reference(0, xs[s], trace_dec[s, 0], ws[s])
             check_close(from_dev_act(out), ref, "bf16", "bf16", "decode after prefill")
         rig.close()
+
+
+def test_step_equals_prepare_then_forward():
+    """moe_pool_step is prepare + forward in one call: same misses, slot ids and
+    bit-identical outputs on the same trace."""
+    wl = synth.Workload("stepcall", 2, 32, 4, 512, 256, 6, 2, 0, "bf16", "bf16", 1.0, 0.3, 0, 12)
+    trace = synth.make_trace(wl, steps=20)
+    xs, ws = _inputs(wl, 20, 2)
+    a = Rig(wl, slots=6)
+    b = Rig(wl, slots=6, experts=a.experts)
+    for s in range(20):
+        xd = to_dev_act(xs[s], "bf16")
+        wd = torch.from_numpy(ws[s]).to(DEV)
+        for l in range(2):
+            pa, ma, sa, oa = a.step(l, trace[s, l], xd, wd, xd)
+            ids_d = torch.from_numpy(trace[s, l]).to(DEV)
+            sb = torch.empty_like(ids_d)
+            ob = torch.empty_like(oa)
+            pb, mb = b.pool.step(l, ids_d, 2, sb, xd, wd, ob, resid=xd)
+            assert (pa, ma) == (pb, mb)
+            assert (sb.cpu().numpy() == sa).all()
+            assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), (s, l)
+    assert a.pool.stats() == b.pool.stats()
+    a.close()
+    b.close()

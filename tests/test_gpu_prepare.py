@@ -62,6 +62,25 @@ def test_prepare_matches_oracle(name, slots, steps, layers):
     rig.close()
 
 
+def test_evict_then_reinsert_in_same_step():
+    """Ascending processing can evict an expert of the step before its own turn:
+    with LRU order [5, 7], step [1, 5] evicts 5 for 1's miss, then re-inserts 5 by
+    evicting 7.  The map table must end with the step's final entries (here the
+    update list holds expert 5 twice)."""
+    wl = SMALL_BF16.with_(layers=1, experts=8, top_k=2)
+    rig = Rig(wl, slots=2)
+    ref = LayerLRU(8, 2)
+    for ids in ([[5, 7]], [[1, 5]], [[5, 1]], [[7, 5]], [[1, 7]]):
+        ids = np.array(ids, np.int32)
+        ids_d = torch.from_numpy(ids).to(DEV)
+        slot_d = torch.empty_like(ids_d)
+        path, misses = rig.pool.prepare(0, ids_d, 1, slot_d)
+        r = ref.step(ids)
+        assert misses == r.misses and (slot_d.cpu().numpy() == r.slot_ids).all(), (ids, misses)
+    assert ref.misses == 2 + 2 + 0 + 1 + 1   # [7,5]: 5 hits, 7 evicts 1; [1,7]: 1 evicts 5
+    rig.close()
+
+
 def test_slot_bytes_equal_store_after_eviction():
     """test_gpu_buffer_matches_source_weights / _correct_after_eviction and the
     scale tests: every occupied slot holds exactly its owner's bytes (codes and
