@@ -558,6 +558,284 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(const char* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Grouped path (n_tokens above the decode limit, bf16 weights): the (token, k)
+// pairs are grouped by slot, and each slot's group runs as a dense bf16 GEMM on
+// the matrix cores against that slot's weights, read once per 32-row tile.
+// ---------------------------------------------------------------------------
+constexpr int kGroupThreads = 1024;
+constexpr int kGBM = 32;        // pairs per tile (rows of one 32x32 MFMA block)
+constexpr int kGBN = 128;       // output columns per workgroup: 4 waves x 32
+
+// a6: per-slot counts, exclusive offsets, slot-sorted pair list and the tile list.
+// grp layout (int32): [0] = n_tiles; [16 + t] = slot of tile t;
+// [16 + S + t] = first sorted row of tile t; [16 + 2S + t] = rows in tile t;
+// [16 + 3S + pos] = pair index at sorted position pos   (S = tile stride).
+// Pairs of one slot are contiguous; their order inside the group is unspecified
+// (each GEMM row depends only on its own inputs, so results do not depend on it).
+__global__ __launch_bounds__(kGroupThreads) void k_group_build(const int32_t* __restrict__ slot_ids, int n,
+                                                               int nslots, int tile_stride,
+                                                               int32_t* __restrict__ grp) {
+    __shared__ int32_t cnt[kMaxExperts];
+    __shared__ int32_t off[kMaxExperts];
+    __shared__ int32_t toff[kMaxExperts];
+    __shared__ int32_t wsum[2][kGroupThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    for (int i = tid; i < nslots; i += kGroupThreads) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < n; p += kGroupThreads) {
+        const int sl = slot_ids[p];
+        if (sl >= 0 && sl < nslots) atomicAdd(&cnt[sl], 1);
+    }
+    __syncthreads();
+    // exclusive scans of counts and tile counts; thread tid owns slots 4*tid .. 4*tid+3
+    int c[4], tc[4], sc = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * tid + i;
+        c[i] = sl < nslots ? cnt[sl] : 0;
+        tc[i] = (c[i] + kGBM - 1) / kGBM;
+        sc += c[i];
+        st += tc[i];
+    }
+    int ic = sc, it = st;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int vc = __shfl_up(ic, o, 64);
+        const int vt = __shfl_up(it, o, 64);
+        if (lane >= o) {
+            ic += vc;
+            it += vt;
+        }
+    }
+    if (lane == 63) {
+        wsum[0][wave] = ic;
+        wsum[1][wave] = it;
+    }
+    __syncthreads();
+    int pc = 0, pt = 0, total_t = 0;
+    for (int w = 0; w < kGroupThreads / 64; ++w) {
+        if (w < wave) {
+            pc += wsum[0][w];
+            pt += wsum[1][w];
+        }
+        total_t += wsum[1][w];
+    }
+    int ec = pc + ic - sc, et = pt + it - st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * tid + i;
+        if (sl < nslots) {
+            off[sl] = ec;
+            toff[sl] = et;
+        }
+        ec += c[i];
+        et += tc[i];
+    }
+    if (tid == 0) grp[0] = total_t;
+    __syncthreads();
+    int32_t* t_slot = grp + 16;
+    int32_t* t_row0 = grp + 16 + tile_stride;
+    int32_t* t_rows = grp + 16 + 2 * tile_stride;
+    int32_t* perm = grp + 16 + 3 * tile_stride;
+    for (int sl = tid; sl < nslots; sl += kGroupThreads) {
+        const int cs = cnt[sl];
+        for (int j = 0; j * kGBM < cs; ++j) {
+            const int t = toff[sl] + j;
+            t_slot[t] = sl;
+            t_row0[t] = off[sl] + j * kGBM;
+            t_rows[t] = min(kGBM, cs - j * kGBM);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < nslots; i += kGroupThreads) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < n; p += kGroupThreads) {
+        const int sl = slot_ids[p];
+        if (sl >= 0 && sl < nslots) perm[off[sl] + atomicAdd(&cnt[sl], 1)] = p;
+    }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4 a, const uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                    c, 0, 0, 0);
+}
+
+// 8 bf16 activations at element e0 of an fp32 or bf16 row, as MFMA operand bits
+template <int AT>
+__device__ __forceinline__ uint4 load_a8(const void* __restrict__ p, size_t e0) {
+    if (AT == A_BF16) return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + e0);
+    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(p) + e0);
+    const float4 a = f[0], b = f[1];
+    uint4 r;
+    r.x = (uint32_t)f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
+    r.y = (uint32_t)f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+    r.z = (uint32_t)f32_to_bf16_rne(b.x) | ((uint32_t)f32_to_bf16_rne(b.y) << 16);
+    r.w = (uint32_t)f32_to_bf16_rne(b.z) | ((uint32_t)f32_to_bf16_rne(b.w) << 16);
+    return r;
+}
+
+// One wave computes a 32 x 32 block C = A (32 rows x Kd) . B^T (32 weight rows x Kd)
+// with B rows streamed from HBM straight into operand registers.  The k range is
+// walked in spans of 64: lane half h (= lane / 32) supplies elements
+// [span + 32h + 8j, +8) of its row to MFMA j (j = 0..3), for A and B alike, so each
+// lane reads 64 contiguous bytes of its row per span and the four MFMAs together
+// cover the span once.
+// ---- grouped w13 + SwiGLU ------------------------------------------------------
+// grid.x: tiles (blocks past n_tiles exit); grid.y: blocks of 128 columns of I.
+// act_sorted[pos][j] = silu(x[t(pos)] . W13[s][j]) * (x[t(pos)] . W13[s][I + j])
+template <int AT>
+__global__ __launch_bounds__(256) void k_grouped_w13(const char* __restrict__ wbase, size_t stride,
+                                                     const int32_t* __restrict__ grp, int tile_stride,
+                                                     const void* __restrict__ x, int K, int H, int I,
+                                                     size_t off_w, uint16_t* __restrict__ act_sorted) {
+    const int tile = blockIdx.x;
+    if (tile >= grp[0]) return;
+    const int slot = grp[16 + tile];
+    const int row0 = grp[16 + tile_stride + tile];
+    const int rows = grp[16 + 2 * tile_stride + tile];
+    const int32_t* perm = grp + 16 + 3 * tile_stride;
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    const int j0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
+    if (j0 >= I) return;
+    const int pair = perm[row0 + min(l32, rows - 1)];
+    const size_t xrow = (size_t)(pair / K) * H + hl * 32;
+    const int n = min(j0 + l32, I - 1);
+    const size_t rb = (size_t)H * 2;
+    const char* ex = wbase + (size_t)slot * stride + off_w;
+    const char* gr = ex + (size_t)n * rb + hl * 64;
+    const char* ur = ex + (size_t)(I + n) * rb + hl * 64;
+    f32x16_t cg = {}, cu = {};
+    uint4 bg[4], bu[4], a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bg[j] = load16(gr + 16 * j);
+        bu[j] = load16(ur + 16 * j);
+        a[j] = load_a8<AT>(x, xrow + 8 * j);
+    }
+    for (int k0 = 64; k0 <= H; k0 += 64) {
+        uint4 nbg[4], nbu[4], na[4];
+        if (k0 < H) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                nbg[j] = load16(gr + (size_t)k0 * 2 + 16 * j);
+                nbu[j] = load16(ur + (size_t)k0 * 2 + 16 * j);
+                na[j] = load_a8<AT>(x, xrow + k0 + 8 * j);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            cg = mfma_32x32x16(a[j], bg[j], cg);
+            cu = mfma_32x32x16(a[j], bu[j], cu);
+        }
+        if (k0 < H) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bg[j] = nbg[j];
+                bu[j] = nbu[j];
+                a[j] = na[j];
+            }
+        }
+    }
+    const int col = j0 + l32;
+    if (col < I) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (r < rows) act_sorted[(size_t)(row0 + r) * I + col] = f32_to_bf16_rne(silu(cg[i]) * cu[i]);
+        }
+    }
+}
+
+// ---- grouped w2 ------------------------------------------------------------------
+// grid.x: tiles; grid.y: blocks of 128 output columns of H.
+// y[pair(pos)][h] = act_sorted[pos] . W2[s][h]
+__global__ __launch_bounds__(256) void k_grouped_w2(const char* __restrict__ wbase, size_t stride,
+                                                    const int32_t* __restrict__ grp, int tile_stride,
+                                                    const uint16_t* __restrict__ act_sorted, int H, int I,
+                                                    size_t off_w, float* __restrict__ y) {
+    const int tile = blockIdx.x;
+    if (tile >= grp[0]) return;
+    const int slot = grp[16 + tile];
+    const int row0 = grp[16 + tile_stride + tile];
+    const int rows = grp[16 + 2 * tile_stride + tile];
+    const int32_t* perm = grp + 16 + 3 * tile_stride;
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    const int h0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
+    if (h0 >= H) return;
+    const uint16_t* arow = act_sorted + (size_t)(row0 + min(l32, rows - 1)) * I + hl * 32;
+    const int n = min(h0 + l32, H - 1);
+    const char* br = wbase + (size_t)slot * stride + off_w + (size_t)n * I * 2 + hl * 64;
+    f32x16_t c = {};
+    uint4 b[4], a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        b[j] = load16(br + 16 * j);
+        a[j] = *reinterpret_cast<const uint4*>(arow + 8 * j);
+    }
+    for (int k0 = 64; k0 <= I; k0 += 64) {
+        uint4 nb[4], na[4];
+        if (k0 < I) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                nb[j] = load16(br + (size_t)k0 * 2 + 16 * j);
+                na[j] = *reinterpret_cast<const uint4*>(arow + k0 + 8 * j);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = mfma_32x32x16(a[j], b[j], c);
+        if (k0 < I) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = nb[j];
+                a[j] = na[j];
+            }
+        }
+    }
+    const int col = h0 + l32;
+    if (col < H) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (r < rows) y[(size_t)perm[row0 + r] * H + col] = c[i];
+        }
+    }
+}
+
+// ---- ordered top-k combine (grouped path) -------------------------------------------
+// out[t][h] = resid[t][h] + sum_{k = 0..K-1} w[t][k] * y[t*K + k][h]   (k in order;
+// pairs whose slot id is out of range contribute nothing)
+template <int AT>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const float* __restrict__ topk_w,
+                                                 const int32_t* __restrict__ slot_ids, int nslots,
+                                                 const void* __restrict__ resid, void* __restrict__ out, int T,
+                                                 int K, int H) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * H) return;
+    const int t = (int)(idx / H);
+    const int h = (int)(idx - (size_t)t * H);
+    float acc = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int sl = slot_ids[t * K + k];
+        const float v = (sl >= 0 && sl < nslots) ? y[((size_t)t * K + k) * H + h] : 0.0f;
+        acc = fmaf(topk_w[(size_t)t * K + k], v, acc);
+    }
+    if (resid) acc += load_act<AT>(resid, idx);
+    if (AT == A_F32)
+        static_cast<float*>(out)[idx] = acc;
+    else
+        static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(acc);
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 namespace {
@@ -710,15 +988,60 @@ bool decode_shape_supported(int wtype, int atype, int H, int I) {
 
 size_t act_bytes_per_pair(int wtype, int I) { return (size_t)I * (wtype == W_F32 ? 4 : 2); }
 
-size_t grouped_index_bytes(int max_tokens, int K, int nslots) {
-    (void)max_tokens;
-    (void)K;
-    (void)nslots;
-    return 0;
+int grouped_tile_stride(int max_pairs, int nslots) {
+    return max_pairs / kGBM + (nslots < max_pairs ? nslots : max_pairs) + 1;
 }
+
+size_t grouped_index_bytes(int max_tokens, int K, int nslots) {
+    const int mp = max_tokens * K;
+    return (size_t)(16 + 3 * grouped_tile_stride(mp, nslots) + mp) * sizeof(int32_t);
+}
+
+bool grouped_shape(int wtype, int H, int I) { return wtype == W_BF16 && H % 64 == 0 && I % 64 == 0; }
+
+namespace {
+
+template <int AT>
+hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    const int n = a.T * g.K;
+    const int stride_t = grouped_tile_stride(a.max_pairs, a.nslots_alloc);
+    const int tiles = n / kGBM + (a.nslots < n ? a.nslots : n) + 1;   // bound on this call's tiles
+    hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.slot_ids, n, a.nslots, stride_t, a.grp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    uint16_t* act = static_cast<uint16_t*>(a.act);
+    const dim3 g13(tiles, (g.I + kGBN - 1) / kGBN), g2(tiles, (g.H + kGBN - 1) / kGBN);
+    if (ev && ev->w13_start)
+        hipExtLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.wbase,
+                              g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act);
+    else
+        hipLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, a.wbase, g.slot_stride, a.grp, stride_t, a.x,
+                           g.K, g.H, g.I, g.off_w13, act);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && ev->w2_start)
+        hipExtLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.wbase, g.slot_stride,
+                              a.grp, stride_t, act, g.H, g.I, g.off_w2, a.y);
+    else
+        hipLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, a.wbase, g.slot_stride, a.grp, stride_t, act, g.H,
+                           g.I, g.off_w2, a.y);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t nt = (size_t)a.T * g.H;
+    const dim3 gc((unsigned)((nt + 255) / 256));
+    if (ev && ev->w2_stop)
+        hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.y, a.topk_w,
+                              a.slot_ids, a.nslots, a.resid, a.out, a.T, g.K, g.H);
+    else
+        hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.y, a.topk_w, a.slot_ids, a.nslots, a.resid,
+                           a.out, a.T, g.K, g.H);
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t stream) {
     if (a.T <= 0) return hipSuccess;
+    if (a.T > kDecodeMaxTokens && grouped_shape(g.wtype, g.H, g.I))
+        return g.atype == A_F32 ? run_grouped<A_F32>(g, a, ev, stream) : run_grouped<A_BF16>(g, a, ev, stream);
     if ((long)a.T * g.K > 65535) return hipErrorInvalidValue;   // grid.y of the w13 kernel
     switch (g.wtype * 2 + g.atype) {
         case W_F32 * 2 + A_F32: return run_decode<W_F32, A_F32>(g, a, ev, stream);

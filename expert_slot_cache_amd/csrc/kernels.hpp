@@ -52,7 +52,9 @@ struct ForwardArgs {
     // scratch
     void* act;              // [T*K][I]: SwiGLU output (fp32 for f32 weights, else bf16)
     float* y;               // [T*K][H] fp32: per-(token, expert) w2 output
-    int32_t* grp;           // grouped-path index buffers (see launch_forward)
+    int32_t* grp;           // grouped-path index buffer (grouped_index_bytes)
+    int nslots_alloc;       // slot count the grp buffer was sized for
+    int max_pairs;          // max_tokens * K the scratch was sized for
 };
 
 // The slot-indexed fused MoE for one layer.
@@ -67,5 +69,8 @@ size_t act_bytes_per_pair(int wtype, int I);
 
 // Bytes of the grouped-path index buffer for max_tokens tokens and nslots slots.
 size_t grouped_index_bytes(int max_tokens, int K, int nslots);
+
+// Whether n_tokens above kDecodeMaxTokens take the grouped MFMA path for this shape.
+bool grouped_shape(int wtype, int H, int I);
 
 }  // namespace moe

@@ -145,6 +145,8 @@ struct moe_pool {
     int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
     void* act = nullptr;          // HBM [max_tokens * K][I] SwiGLU output
     float* y = nullptr;           // HBM [max_tokens * K][H] per-pair w2 output
+    int32_t* grp = nullptr;       // HBM grouped-path index buffer
+    int32_t grp_slots = 0;        // largest slot count a forward can address
     std::vector<moe::Miss> misses;
     std::vector<char> used_copy;
     int copy_rr = 0;
@@ -189,6 +191,7 @@ void destroy_pool(moe_pool* p) {
     if (p->ident_dev) (void)hipFree(p->ident_dev);
     if (p->act) (void)hipFree(p->act);
     if (p->y) (void)hipFree(p->y);
+    if (p->grp) (void)hipFree(p->grp);
     delete p;
 }
 
@@ -321,7 +324,8 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.n_layers < 1) FAIL(MOE_EINVAL, "n_layers %d < 1", c.n_layers);
     if (c.n_experts < 1 || c.n_experts > moe::kMaxExperts) FAIL(MOE_EINVAL, "n_experts %d outside [1,%d]", c.n_experts, moe::kMaxExperts);
     if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > moe::kMaxTopK) FAIL(MOE_EINVAL, "top_k %d invalid", c.top_k);
-    if (c.n_slots < 0) FAIL(MOE_EINVAL, "n_slots %d < 0", c.n_slots);
+    if (c.n_slots < 0 || c.n_slots > moe::kMaxExperts)
+        FAIL(MOE_EINVAL, "n_slots %d outside [0,%d]", c.n_slots, moe::kMaxExperts);
     if (c.atype != MOE_A_F32 && c.atype != MOE_A_BF16) FAIL(MOE_EINVAL, "atype %d invalid", c.atype);
     if (c.rule != MOE_RULE_DISTINCT && c.rule != MOE_RULE_STATIC) FAIL(MOE_EINVAL, "rule %d invalid", c.rule);
     if (c.max_tokens < 1) FAIL(MOE_EINVAL, "max_tokens %d < 1", c.max_tokens);
@@ -357,8 +361,10 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     const size_t slot_bytes = (size_t)p->nslot_alloc * eb + kAlign;
     const size_t act_bytes = (size_t)c.max_tokens * c.top_k * moe::act_bytes_per_pair(c.wtype, c.inter);
     const size_t y_bytes = (size_t)c.max_tokens * c.top_k * c.hidden * sizeof(float);
+    p->grp_slots = std::max(p->nslot_alloc, p->staging_cap);
+    const size_t grp_bytes = moe::grouped_index_bytes(c.max_tokens, c.top_k, std::max(1, p->grp_slots));
     const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4) + (size_t)p->staging_cap * eb + act_bytes +
-                       y_bytes + (size_t)E * 8;
+                       y_bytes + grp_bytes + (size_t)E * 8;
     if (c.hbm_budget_bytes && hbm > c.hbm_budget_bytes) {
         delete p;
         FAIL(MOE_ENOMEM, "pool needs %zu HBM bytes, budget is %zu", hbm, c.hbm_budget_bytes);
@@ -421,6 +427,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     }
     CREATE_HIP(hipMalloc((void**)&p->act, act_bytes));
     CREATE_HIP(hipMalloc((void**)&p->y, y_bytes));
+    CREATE_HIP(hipMalloc((void**)&p->grp, grp_bytes));
 #undef CREATE_HIP
     p->misses.reserve(E);
     *out = p;
@@ -614,6 +621,9 @@ moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, c
     a.T = n_tokens;
     a.act = p->act;
     a.y = p->y;
+    a.grp = p->grp;
+    a.nslots_alloc = std::max(1, p->grp_slots);
+    a.max_pairs = p->cfg.max_tokens * p->cfg.top_k;
     moe::StageEvents ev;
     const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
                        !L.w13_t.pending && !L.w2_t.pending;
