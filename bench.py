@@ -1,13 +1,17 @@
 """Benchmark: MoE decode tokens/s of a pooled expert stack on one MI355X.
 
-A step is one batch-1 decode token through every layer of the stack: per layer,
-prepare (distinct ids, LRU, miss copies, map upload, remap) then forward (w13 +
-SwiGLU, w2 + top-k combine, residual added).  Inputs (routing trace, activations,
-gate weights) are resident in HBM before the timed region; the experts live in the
-library's pinned host store and stream into the slot pools on misses.
+A step is one ubatch (default: one batch-1 decode token) through every layer of
+the stack: per layer, prepare (distinct ids, LRU, miss copies, table update,
+remap) and forward (w13 + SwiGLU, w2 + top-k combine, residual added), issued as
+one moe_pool_step call.  Inputs (routing trace, activations, gate weights) are
+resident in HBM before the timed region; the experts live in the library's pinned
+host store and stream into the slot pools on misses.
 
 Prints one JSON line.  Default workload: OLMoE-1B-7B shapes in bf16, 16 layers x
 64 experts, top-8, hidden 2048, intermediate 1024, 16 slots per layer.
+--sweep 0,16,32 repeats the run per slot count (fresh pool and store each) and
+reports every point in the line's "sweep" field; "value" is the workload's own
+slot count (or the first point).
 """
 from __future__ import annotations
 
@@ -26,6 +30,8 @@ from expert_slot_cache_amd import synth  # noqa: E402
 
 METRIC = "MoE decode tokens/s vs pool size; HBM GB/s on hits, link GB/s on misses"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (bf16)
 
 
 def log(*a):
@@ -39,7 +45,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="olmoe_bf16_e64", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--slots", type=int, default=None, help="slots per layer (default: workload's)")
+    ap.add_argument("--sweep", default="", help="comma-separated slot counts")
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per ubatch (default: workload's)")
+    ap.add_argument("--rule", default="distinct", choices=["distinct", "static"])
+    ap.add_argument("--resident", action="store_true", help="all experts resident (no pool)")
     ap.add_argument("--copy-streams", type=int, default=1)
     ap.add_argument("--copy-chunk-mib", type=int, default=0)
     ap.add_argument("--no-timing", action="store_true", help="no HIP events around kernels")
@@ -52,36 +62,36 @@ def parse():
 
 def link_peak_gbps(torch, dev, nbytes: int) -> float:
     """Pinned host -> HBM hipMemcpyAsync rate for copies of `nbytes` (the expert size)."""
-    h = torch.empty(max(nbytes, 1 << 20) * 8, dtype=torch.uint8, pin_memory=True)
+    n = max(nbytes, 1 << 20)
+    h = torch.empty(n * 8, dtype=torch.uint8, pin_memory=True)
     h.fill_(3)
     d = torch.empty_like(h, device=dev)
-    n = max(nbytes, 1 << 20)
     best = 0.0
     for _ in range(3):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        reps = 0
-        while reps < 64:
+        for _ in range(8):
             for i in range(8):
                 d[i * n:(i + 1) * n].copy_(h[i * n:(i + 1) * n], non_blocking=True)
-            reps += 8
         torch.cuda.synchronize()
-        best = max(best, reps * n / (time.perf_counter() - t0) / 1e9)
+        best = max(best, 64 * n / (time.perf_counter() - t0) / 1e9)
     del h, d
     return best
 
 
 def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
-    """The oracle (LRU simulator + float64 MoE layer) on a bounded sample of steps."""
+    """The oracle (LRU simulator + float64 MoE layer) on a bounded sample of steps,
+    counted per layer so that slow configurations still give a rate."""
     from threadpoolctl import threadpool_info
 
     from oracle import lru as olru
     from oracle import moe as omoe
 
     L = trace.shape[1]
+    T = trace.shape[2]
     stack = olru.StackLRU(L, wl.experts, wl.slots)
     t0 = time.perf_counter()
-    done = 0
+    layers_done = 0
     for s in range(trace.shape[0]):
         x = xs[s]
         for l in range(L):
@@ -89,69 +99,50 @@ def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
             y = omoe.moe_layer(x, trace[s, l], ws[s, l], lambda e: experts_fn(l, e), wl.wtype,
                                wl.hidden, wl.inter, resid=x, atype=wl.atype)
             x = synth.f32_to_bf16_bits(y.astype(np.float32)) if wl.atype == "bf16" else y.astype(np.float32)
-        done += 1
+            layers_done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode tokens x {L} layers of the same workload (LRU simulator + "
-                      f"float64 MoE layer, numpy BLAS threads={threads}), {dt:.1f} s"}
+    tokens = layers_done / L * T
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{layers_done} layer-steps ({tokens:.2f} tokens of the {L}-layer stack) of the "
+                      f"same workload: LRU simulator + float64 MoE layer, numpy BLAS threads={threads}, "
+                      f"{dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the slot cache is a single-GPU path); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    from expert_slot_cache_amd import binding
-
+def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
+    """One pool, one timed run; returns the result dict and the expert size."""
     dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
-    if args.layers:
-        wl = wl.with_(layers=args.layers)
-    slots = wl.slots if args.slots is None else args.slots
-    wl = wl.with_(slots=slots)
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
-    S = args.warmup + args.steps
-    log(f"[bench] workload {wl.name}: L={L} E={E} K={K} H={H} I={I} slots={slots} T={T} steps={S}")
-
     t0 = time.perf_counter()
-    trace = synth.make_trace(wl, steps=S)
-    _, _, rx, rg = synth.streams(wl)
-    xs = synth.draw_activations(rx, (S, T, H), wl.atype)
-    ws = synth.draw_gate_weights(rg, (S, L, T, K))
-    gen = synth.WindowedExperts(wl)
     pool = binding.MoePool(layers=L, experts=E, top_k=K, hidden=H, inter=I, slots=slots,
-                           wtype=wl.wtype, atype=wl.atype, max_tokens=T,
-                           copy_streams=args.copy_streams,
+                           wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
+                           max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20,
                            timing=0 if args.no_timing else args.timing_every)
-    for l in range(L):
-        for e in range(E):
-            gen.expert(l, e, pool.store_view(l, e))
     eb = pool.expert_nbytes
-    log(f"[bench] store filled: {L * E * eb / 2**30:.2f} GiB pinned, {time.perf_counter() - t0:.1f} s")
-
-    ids_d = torch.from_numpy(trace).to(dev)                     # [S, L, T, K]
-    adt = torch.float32 if wl.atype == "f32" else torch.bfloat16
-    if wl.atype == "f32":
-        x_d = torch.from_numpy(xs).to(dev)
+    if resident:
+        buf = np.empty(eb, np.uint8)
+        for l in range(L):
+            for e in range(E):
+                pool.load_expert(l, e, gen.expert(l, e, buf))
     else:
-        x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
-    w_d = torch.from_numpy(ws).to(dev)                          # [S, L, T, K]
+        for l in range(L):
+            for e in range(E):
+                gen.expert(l, e, pool.store_view(l, e))
+    log(f"[bench] slots={slots}: store filled, {L * E * eb / 2**30:.2f} GiB pinned, "
+        f"{time.perf_counter() - t0:.1f} s")
+    adt = torch.float32 if wl.atype == "f32" else torch.bfloat16
     slot_d = torch.empty((L, T, K), dtype=torch.int32, device=dev)
     bufs = [torch.empty((T, H), dtype=adt, device=dev) for _ in range(2)]
-    ids_p = ids_d.data_ptr()
-    w_p = w_d.data_ptr()
-    x_p = x_d.data_ptr()
-    slot_p = slot_d.data_ptr()
+    ids_d = torch.from_numpy(trace).to(dev)
+    ids_p, w_p, x_p, slot_p = ids_d.data_ptr(), ws_d.data_ptr(), xs_d.data_ptr(), slot_d.data_ptr()
     buf_p = [b.data_ptr() for b in bufs]
     ids_stride = T * K * 4
-    x_stride = T * H * x_d.element_size()
+    x_stride = T * H * xs_d.element_size()
     L_ = binding.lib()
     h = pool._h
 
@@ -169,7 +160,6 @@ def main():
     torch.cuda.synchronize()
     run(0, args.warmup)
     pool.sync()
-    torch.cuda.synchronize()
     st0 = pool.stats()
     pool.reset_timing()
     torch.cuda.synchronize()
@@ -180,58 +170,125 @@ def main():
     elapsed = time.perf_counter() - t_start
     st1 = pool.stats()
     tm = pool.timing()
+    pool.close()
+    del ids_d, slot_d, bufs
     d = {k: st1[k] - st0[k] for k in st1}
     tokens = args.steps * T
     value = tokens / elapsed
-    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s: {value:.1f} tokens/s; stats {d}")
+    log(f"[bench] slots={slots}: {args.steps} steps in {elapsed:.3f} s: {value:.2f} tokens/s; {d}")
 
-    # per-launch algorithmic bytes of the dominant kernel (w13 + SwiGLU), batch 1:
-    # K distinct experts' w13 (2I x H weights) + x + the activations written
+    # algorithmic work of one w13 / w2 launch, averaged over the timed layer-steps
+    timed = trace[args.warmup:args.warmup + args.steps]
+    flat = timed.reshape(-1, T * K)
+    D_mean = float(np.mean([len(np.unique(r)) for r in flat]))
     wbytes = {"f32": 4.0, "bf16": 2.0, "int4": 0.5}[wl.wtype]
     sbytes = 2.0 / 128 if wl.wtype == "int4" else 0.0      # bf16 scale per 128 weights
-    w13_bytes = K * 2 * I * H * (wbytes + sbytes) + T * H * x_d.element_size() + T * K * I * 4
-    w2_bytes = (K * H * I * (wbytes + sbytes) + T * K * I * 4 + 2 * T * H * x_d.element_size()
-                + T * K * 8)
-    roof = None
-    hbm_hits = None
+    xb = xs_d.element_size()
+    actb = 4 if wl.wtype == "f32" else 2
+    w13_bytes = D_mean * 2 * I * H * (wbytes + sbytes) + T * H * xb + T * K * I * actb
+    w2_bytes = D_mean * H * I * (wbytes + sbytes) + T * K * I * actb + 2 * T * H * xb + T * K * 8
+    w13_flops = 2.0 * 2 * I * H * T * K
+    grouped = T > DECODE_MAX_TOKENS and wl.wtype == "bf16"
+    res = {"slots": slots, "value": round(value, 3), "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+           "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
+           "misses_per_token": round(d["misses"] / tokens, 4),
+           "fallback_steps": d["fallbacks"], "staged_experts": d["staged"],
+           "h2d_gb": round(d["bytes_h2d"] / 1e9, 3),
+           "readback_wait_ms_per_step": round(tm["sync_wait_ms"] / args.steps, 4)}
+    if tm["copy_ms"] > 0:
+        res["link_gbps_misses"] = round(tm["copy_bytes"] / (tm["copy_ms"] * 1e-3) / 1e9, 2)
     if not args.no_timing and tm["kernel_calls"] > 0:
-        n_fwd = tm["kernel_calls"]
-        w13_avg_ms = tm["w13_ms"] / n_fwd
-        w2_avg_ms = tm["w2_ms"] / n_fwd
-        ach = w13_bytes / (w13_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_w13_gemv (w13 + SwiGLU)", "achieved": round(ach, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "traffic": None, "avg_launch_us": round(w13_avg_ms * 1e3, 2),
-                "bytes_per_launch": int(w13_bytes), "timed_launches": n_fwd,
-                "w2_kernel_avg_us": round(w2_avg_ms * 1e3, 2),
-                "w2_achieved_gbps": round(w2_bytes / (w2_avg_ms * 1e-3) / 1e9, 1)}
-        hit_bytes = (w13_bytes + w2_bytes) * n_fwd
-        hbm_hits = hit_bytes / ((tm["w13_ms"] + tm["w2_ms"]) * 1e-3) / 1e9
+        n = tm["kernel_calls"]
+        w13_us = tm["w13_ms"] / n * 1e3
+        w2_us = tm["w2_ms"] / n * 1e3
+        ach = w13_bytes / (w13_us * 1e-6) / 1e9
+        tflops = w13_flops / (w13_us * 1e-6) / 1e12
+        name = "k_grouped_w13 (grouped MFMA w13 + SwiGLU)" if grouped else "k_w13_gemv (w13 + SwiGLU)"
+        intensity = w13_flops / w13_bytes
+        mfma_bound = grouped and intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        if mfma_bound:
+            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4)}
+        roof.update({"traffic": None, "kernel": name, "avg_launch_us": round(w13_us, 2),
+                     "bytes_per_launch": int(w13_bytes), "flops_per_launch": int(w13_flops),
+                     "timed_launches": n, "distinct_experts_per_launch": round(D_mean, 2),
+                     "w2_stage_avg_us": round(w2_us, 2),
+                     "w2_stage_achieved_gbps": round(w2_bytes / (w2_us * 1e-6) / 1e9, 1)})
+        if grouped:
+            roof["mfma_tflops"] = round(tflops, 2)
+            roof["mfma_util"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 5)
+            roof["hbm_gbps"] = round(ach, 1)
+        res["roofline"] = roof
+        res["hbm_gbps_hits"] = round((w13_bytes + w2_bytes) / ((w13_us + w2_us) * 1e-6) / 1e9, 1)
+    torch.cuda.empty_cache()
+    return res, eb
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the slot cache is a single-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from expert_slot_cache_amd import binding
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(layers=args.layers)
+    if args.tokens:
+        wl = wl.with_(tokens=args.tokens)
+    points = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
+    slots = wl.slots if args.slots is None else args.slots
+    if points and args.slots is None:
+        slots = wl.slots if wl.slots in points else points[0]
+    wl = wl.with_(slots=slots)
+    L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
+    S = args.warmup + args.steps
+    log(f"[bench] workload {wl.name}: L={L} E={E} K={K} H={H} I={I} slots={slots} T={T} "
+        f"steps={S} rule={args.rule} resident={args.resident}")
+
+    trace = synth.make_trace(wl, steps=S)
+    _, _, rx, rg = synth.streams(wl)
+    xs = synth.draw_activations(rx, (S, T, H), wl.atype)
+    ws = synth.draw_gate_weights(rg, (S, L, T, K))
+    gen = synth.WindowedExperts(wl)
+    if wl.atype == "f32":
+        xs_d = torch.from_numpy(xs).to(dev)
+    else:
+        xs_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws_d = torch.from_numpy(ws).to(dev)
+
+    results = {}
+    eb = 0
+    for n in (points or [slots]):
+        results[n], eb = run_point(args, torch, binding, wl, n, trace, xs_d, ws_d, gen, args.resident)
+    main_res = results[slots]
     peak_link = link_peak_gbps(torch, dev, eb)
-    link = None
-    if tm.get("copy_ms", 0) > 0:
-        link = tm["copy_bytes"] / (tm["copy_ms"] * 1e-3) / 1e9
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "metric": METRIC, "value": main_res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.wtype if wl.wtype != "int4" else "int4-g128/bf16", "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "experts": E, "top_k": K, "hidden": H,
                    "inter": I, "slots": slots, "tokens_per_step": T, "weights": wl.wtype,
-                   "activations": wl.atype, "expert_bytes": eb, "copy_streams": args.copy_streams},
-        "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
-        "misses_per_token": round(d["misses"] / tokens, 3),
-        "fallback_steps": d["fallbacks"],
-        "hbm_gbps_hits": None if hbm_hits is None else round(hbm_hits, 1),
-        "link_gbps_misses": None if link is None else round(link, 2),
-        "link_peak_gbps": round(peak_link, 2),
-        "link_frac": None if link is None else round(link / peak_link, 4),
-        "readback_wait_ms_per_step": round(tm["sync_wait_ms"] / args.steps, 4),
-        "roofline": roof,
+                   "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
+                   "resident": args.resident, "copy_streams": args.copy_streams},
     }
-    pool.close()
-    del ids_d, x_d, w_d
-    torch.cuda.empty_cache()
+    for k, v in main_res.items():
+        if k not in ("value", "ms_per_step", "slots", "roofline"):
+            line[k] = v
+    line["link_peak_gbps"] = round(peak_link, 2)
+    if "link_gbps_misses" in main_res:
+        line["link_frac"] = round(main_res["link_gbps_misses"] / peak_link, 4)
+    line["roofline"] = main_res.get("roofline")
+    if points:
+        line["sweep"] = [results[n] for n in points]
     if args.cpu_seconds > 0:
         n_cpu = min(S, 64)
         line["cpu_baseline"] = cpu_baseline(wl, lambda l, e: gen.expert(l, e), trace[:n_cpu],

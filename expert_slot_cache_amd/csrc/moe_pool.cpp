@@ -102,9 +102,13 @@ struct Timing {
     uint64_t bytes = 0;                    // copies: bytes between the two events
 };
 
+// Pinned allocations are made in pieces of at most this many bytes (whole experts).
+constexpr size_t kStorePiece = (size_t)1 << 30;
+
 struct LayerState {
     moe::SlotLRU lru;
-    char* store = nullptr;       // pinned host: E experts
+    std::vector<char*> store;    // pinned host pieces holding the E experts in order
+    int32_t per_piece = 1;       // experts per piece
     char* slots = nullptr;       // HBM: nslot_alloc experts + zeroed tail
     int32_t* map_dev = nullptr;  // HBM int32 [E]: the persistent map table
     int32_t* upd_host = nullptr; // pinned int32 [2E]: this step's (entry, value) changes
@@ -112,6 +116,7 @@ struct LayerState {
     hipEvent_t reads_done = nullptr;
     bool reads_recorded = false;
     bool prepared = false;
+    char* expert(int32_t e, size_t eb) const { return store[e / per_piece] + (size_t)(e % per_piece) * eb; }
     int32_t prep_tokens = 0;
     int32_t prep_path = MOE_PATH_POOL;
     uint64_t bytes_h2d = 0;
@@ -168,7 +173,8 @@ void destroy_pool(moe_pool* p) {
     if (!p) return;
     if (p->compute || !p->copy.empty()) (void)hipDeviceSynchronize();
     for (auto& L : p->layers) {
-        if (L.store) (void)hipHostFree(L.store);
+        for (char* piece : L.store)
+            if (piece) (void)hipHostFree(piece);
         if (L.slots) (void)hipFree(L.slots);
         if (L.map_dev) (void)hipFree(L.map_dev);
         if (L.upd_host) (void)hipHostFree(L.upd_host);
@@ -389,10 +395,26 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     }
     const unsigned tflag = c.timing ? hipEventDefault : hipEventDisableTiming;
     p->layers.resize(c.n_layers);
+    size_t pinned_total = 0;
     for (int32_t l = 0; l < c.n_layers; ++l) {
         LayerState& L = p->layers[l];
         L.lru.init(E, c.resident ? 0 : c.n_slots, c.rule);
-        CREATE_HIP(hipHostMalloc((void**)&L.store, (size_t)E * eb, hipHostMallocDefault));
+        // The all-resident mode keeps every expert in HBM and never copies from a
+        // store, so it has none.
+        L.per_piece = (int32_t)std::max<size_t>(1, std::min<size_t>(E, kStorePiece / eb));
+        for (int32_t e0 = 0; !c.resident && e0 < E; e0 += L.per_piece) {
+            const size_t bytes = (size_t)std::min(L.per_piece, E - e0) * eb;
+            char* piece = nullptr;
+            const hipError_t he = hipHostMalloc((void**)&piece, bytes, hipHostMallocDefault);
+            if (he != hipSuccess) {
+                set_err("hipHostMalloc of %zu bytes (layer %d, experts %d..) failed after %zu pinned bytes: %s", bytes, l,
+                        e0, pinned_total, hipGetErrorString(he));
+                destroy_pool(p);
+                return MOE_ENOMEM;
+            }
+            L.store.push_back(piece);
+            pinned_total += bytes;
+        }
         CREATE_HIP(hipMalloc((void**)&L.slots, slot_bytes));
         CREATE_HIP(hipMemset(L.slots + (size_t)p->nslot_alloc * eb, 0, kAlign));
         CREATE_HIP(hipMalloc((void**)&L.map_dev, (size_t)E * 4));
@@ -445,10 +467,10 @@ moe_status_t moe_pool_load_expert(moe_pool_t* p, int32_t layer, int32_t expert, 
     LayerState& L = p->layers[layer];
     // the store may be the source of a queued copy: let those finish first
     for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
-    std::memcpy(L.store + (size_t)expert * p->lay.total, host_src, nbytes);
     if (p->cfg.resident)
-        HIPCHK(hipMemcpy(L.slots + (size_t)expert * p->lay.total, L.store + (size_t)expert * p->lay.total, nbytes,
-                         hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.slots + (size_t)expert * p->lay.total, host_src, nbytes, hipMemcpyHostToDevice));
+    else
+        std::memcpy(L.expert(expert, p->lay.total), host_src, nbytes);
     return MOE_OK;
 }
 
@@ -549,7 +571,7 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
         if (!p->misses.empty()) {
             std::vector<std::pair<char*, const char*>> jobs;
             jobs.reserve(p->misses.size());
-            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.store + (size_t)m.expert * eb);
+            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.expert(m.expert, eb));
             st = issue_copies(p, L, jobs, L.reads_done, L.reads_recorded);
             if (st) return st;
         }
@@ -578,7 +600,7 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
         the_path = MOE_PATH_FALLBACK;
         std::vector<std::pair<char*, const char*>> jobs;
         jobs.reserve(D);
-        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.store + (size_t)u[r] * eb);
+        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.expert(u[r], eb));
         st = issue_copies(p, L, jobs, p->staging_reads_done, p->staging_recorded);
         if (st) return st;
         L.staged += (uint64_t)D;
@@ -724,7 +746,8 @@ moe_status_t moe_pool_store_ptr(const moe_pool_t* p, int32_t layer, int32_t expe
     moe_status_t st = check_layer(p, layer);
     if (st) return st;
     if (!host_ptr || expert < 0 || expert >= p->cfg.n_experts) FAIL(MOE_EINVAL, "bad expert %d", expert);
-    *host_ptr = p->layers[layer].store + (size_t)expert * p->lay.total;
+    if (p->cfg.resident) FAIL(MOE_EINVAL, "the all-resident mode has no host store");
+    *host_ptr = p->layers[layer].expert(expert, p->lay.total);
     return MOE_OK;
 }
 

@@ -84,9 +84,10 @@ typedef struct {
     int32_t wtype;          /* MOE_W_* */
     int32_t atype;          /* MOE_A_* */
     int32_t rule;           /* MOE_RULE_* */
-    int32_t resident;       /* 1 = every expert also lives in HBM at slot = expert id and
-                               the map is the identity: the all-resident reference mode
-                               ([vLLM-cache] "FullGPUProvider"); n_slots is ignored */
+    int32_t resident;       /* 1 = every expert lives in HBM at slot = expert id and the
+                               map is the identity: the all-resident reference mode
+                               ([vLLM-cache] "FullGPUProvider"); n_slots is ignored and
+                               there is no host store (nothing is ever copied in) */
     int32_t max_tokens;     /* largest n_tokens accepted by prepare/forward (>= 1) */
     int32_t n_copy_streams; /* copy streams for host -> HBM copies, 1..8 */
     size_t copy_chunk_bytes;/* split each copy into pieces of at most this size
@@ -148,7 +149,7 @@ void moe_pool_destroy(moe_pool_t* pool);
 
 /* Copies one expert's bytes from `host_src` (moe_expert_bytes bytes) into the
  * pinned store ([vLLM-cache] "CPUBackingStore -- pinned DRAM, all local experts").
- * In resident mode the bytes are also copied to HBM slot `expert`.  If the expert
+ * In resident mode the bytes go straight to HBM slot `expert` instead.  If the expert
  * is currently resident in a slot, that slot is not refreshed: load experts before
  * the first prepare.  Byte layout (regions in order, each on a 256-byte boundary):
  *   f32 : w13 [2I][H] fp32 row-major, w2 [H][I] fp32 row-major
@@ -237,7 +238,9 @@ moe_status_t moe_pool_read_slot(moe_pool_t* pool, int32_t layer, int32_t slot,
                                 void* host_dst, size_t n);
 /* Device address of slot `slot` of `layer` (constant for the pool's lifetime). */
 moe_status_t moe_pool_slot_ptr(const moe_pool_t* pool, int32_t layer, int32_t slot, void** dev_ptr);
-/* Host address of expert `expert` of `layer` in the pinned store. */
+/* Host address of expert `expert` of `layer` in the pinned store (EINVAL in the
+ * all-resident mode, which has no store).  The store is allocated in pieces of at
+ * most 1 GiB; one expert never straddles two pieces. */
 moe_status_t moe_pool_store_ptr(const moe_pool_t* pool, int32_t layer, int32_t expert, void** host_ptr);
 /* *is_pinned = 1 if `p` lies in page-locked host memory known to HIP. */
 moe_status_t moe_ptr_is_pinned_host(const void* p, int32_t* is_pinned);
