@@ -33,6 +33,21 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (bf16)
 
+# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
+# copy of known size; valid only for the kernel source these were taken on.
+PMC_TRAFFIC = {
+    ("olmoe_bf16_e64", "0527f8486d8c8232"): {"fetch_kib": 32805.6, "fetch_scale": 2.0,
+                                    "write_kib": 32.0, "write_scale": 1.0},
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "expert_slot_cache_amd", "csrc", "kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -212,7 +227,10 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
         else:
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBPS, 4)}
-        roof.update({"traffic": None, "kernel": name, "avg_launch_us": round(w13_us, 2),
+        pmc = PMC_TRAFFIC.get((wl.name, kernel_source_hash())) if T == 1 and not resident else None
+        traffic = None if pmc is None else int((pmc["fetch_kib"] * pmc["fetch_scale"] +
+                                                pmc["write_kib"] * pmc["write_scale"]) * 1024)
+        roof.update({"traffic": traffic, "kernel": name, "avg_launch_us": round(w13_us, 2),
                      "bytes_per_launch": int(w13_bytes), "flops_per_launch": int(w13_flops),
                      "timed_launches": n, "distinct_experts_per_launch": round(D_mean, 2),
                      "w2_stage_avg_us": round(w2_us, 2),
