@@ -118,28 +118,68 @@ hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32
 // forward kernels never dereference.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ ids, int n, int E,
-                                               int32_t* __restrict__ table, const int32_t* __restrict__ upd,
-                                               int n_upd, int32_t* __restrict__ out) {
+                                               int32_t* __restrict__ table, const int32_t* __restrict__ rank,
+                                               const int32_t* __restrict__ upd, int n_upd, int status,
+                                               Gate* __restrict__ gate, uint32_t seq, unsigned long long limit,
+                                               int32_t* __restrict__ out, int32_t* __restrict__ path) {
     __shared__ int32_t tab[kMaxExperts];
+    __shared__ int32_t s_status, s_nupd;
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 256) tab[e] = table[e];
-    __syncthreads();
-    for (int u = tid; u < n_upd; u += 256) tab[upd[2 * u]] = upd[2 * u + 1];
-    __syncthreads();
-    if (blockIdx.x == 0)
-        for (int u = tid; u < n_upd; u += 256) table[upd[2 * u]] = upd[2 * u + 1];
-    const int i = blockIdx.x * 256 + tid;
-    if (i < n) {
-        const int e = ids[i];
-        out[i] = ((unsigned)e < (unsigned)E) ? tab[e] : -1;
+    if (tid == 0) {
+        int st = status, nu = n_upd;
+        if (gate) {
+            const unsigned long long t0 = wall_clock64();
+            for (;;) {
+                if (__hip_atomic_load(&gate->seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == seq) {
+                    st = __hip_atomic_load(&gate->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    nu = __hip_atomic_load(&gate->n_upd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                if (wall_clock64() - t0 > limit) {
+                    st = PATH_NONE;
+                    nu = 0;
+                    __hip_atomic_store(&gate->timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        s_status = st;
+        s_nupd = (st == PATH_POOL) ? nu : 0;
     }
+    __syncthreads();
+    const int st = s_status;
+    const int nu = s_nupd;
+    const int i = blockIdx.x * 256 + tid;
+    if (st == PATH_POOL) {
+        for (int e = tid; e < E; e += 256) tab[e] = table[e];
+        __syncthreads();
+        // The list lives in host memory and may have been written after the launch:
+        // read it with system-scope loads, which no stale cache line can serve.
+        for (int u = tid; u < nu; u += 256) {
+            const int32_t e = __hip_atomic_load(upd + 2 * u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            const int32_t v = __hip_atomic_load(upd + 2 * u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            tab[e] = v;
+            if (blockIdx.x == 0) table[e] = v;
+        }
+        __syncthreads();
+        if (i < n) {
+            const int e = ids[i];
+            out[i] = ((unsigned)e < (unsigned)E) ? tab[e] : -1;
+        }
+    } else if (i < n) {
+        const int e = ids[i];
+        out[i] = (st == PATH_STAGE && (unsigned)e < (unsigned)E) ? rank[e] : -1;
+    }
+    if (blockIdx.x == 0 && tid == 0) *path = st;
 }
 
-hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* upd, int n_upd,
-                        int32_t* out, hipStream_t stream) {
-    if (n <= 0 && n_upd <= 0) return hipSuccess;
+hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* rank, const int32_t* upd,
+                        int n_upd, int status, Gate* gate, uint32_t seq, unsigned long long limit, int32_t* out,
+                        int32_t* path, hipStream_t stream) {
     const int blocks = n > 0 ? (n + 255) / 256 : 1;
-    hipLaunchKernelGGL(k_remap, dim3(blocks), dim3(256), 0, stream, ids, n, E, table, upd, n_upd, out);
+    hipLaunchKernelGGL(k_remap, dim3(blocks), dim3(256), 0, stream, ids, n, E, table, rank, upd, n_upd, status, gate,
+                       seq, limit, out, path);
     return hipGetLastError();
 }
 
@@ -194,15 +234,35 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
-#ifdef MOE_NT_LOADS
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16(const char* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-#else
 __device__ __forceinline__ uint4 load16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-#endif
+
+// Reads of one slot's bytes through a buffer resource, with system-coherent cache
+// policy (sc0 sc1): a slot refilled by a host -> HBM DMA is always read from
+// memory, never from a stale cache line, whatever the ordering between the copy
+// and the kernel's launch.  Offsets are bytes within the slot; the hardware
+// returns zeros past the slot's end.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 1 | 16;   // sc0 | sc1
+
+struct SlotReader {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ SlotReader(const char* base, size_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000)) {}
+    __device__ __forceinline__ uint4 load16(size_t off) const {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    __device__ __forceinline__ float scale(size_t off) const {
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kCoherent));
+    }
+};
+
+// The base and slot count of the step's path (see Slots).
+__device__ __forceinline__ void pick_slots(const Slots& sl, const char*& base, int& n) {
+    const int p = *sl.path;
+    base = p == PATH_STAGE ? sl.stage : sl.pool;
+    n = p == PATH_POOL ? sl.npool : (p == PATH_STAGE ? sl.nstage : 0);
+}
 
 // Sum over the G lanes of a group (G a power of two); every lane of the group
 // ends with the same value.
@@ -329,10 +389,6 @@ __device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_INT4, XT_I4>
     return acc - 136.0f * x.sx;
 }
 
-// bf16 scale of chunk c of an int4 row (one scale per 128 elements = 4 chunks)
-__device__ __forceinline__ float chunk_scale(const uint16_t* __restrict__ srow, int c) {
-    return bf16_to_f32(srow[c >> 2]);
-}
 
 // act element type written by the w13 stage: bf16 for bf16 / int4 weights
 template <int WT>
@@ -352,53 +408,52 @@ __device__ __forceinline__ void store_act(void* __restrict__ p, size_t i, float 
 // A row's nc chunks are split over WPR waves ("parts") of G lanes (WPR > 1 only
 // when G == 64), CPL chunks per lane: part q takes chunks [(q*CPL + j)*G + gl].
 // A lane group covers RP gate/up row pairs.  With WPR > 1 the parts' sums meet in
-// LDS and are added in part order.
-// grid.x: row blocks; grid.y: (t, k) pairs.
+// LDS (red) and are added in part order.  One call covers row block `rblk` of
+// pair `pair` with the workgroup's 4 waves:
 // act[pair][i] = silu(W13[s][i] . x[t]) * (W13[s][I + i] . x[t])
 template <int WT, int AT, int CPL, int RP, int WPR>
-__global__ __launch_bounds__(256) void k_w13_gemv(const char* __restrict__ wbase, size_t stride, int nslots,
-                                                  const int32_t* __restrict__ slot_ids,
-                                                  const void* __restrict__ x, int K, int H, int I, int G,
-                                                  size_t off_w, size_t off_s, void* __restrict__ act) {
+__device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const int32_t* __restrict__ slot_ids,
+                                         const void* __restrict__ x, int K, int H, int I, int G, size_t off_w,
+                                         size_t off_s, void* __restrict__ act, int pair, int rblk,
+                                         float (*red)[2][RP]) {
     using X = XChunk<WT, XSel<WT, AT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
-    __shared__ float red[4][2][RP];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int gl = lane & (G - 1);
     const int groups = 64 / G;
     const int grp = lane / G;
     const int part = wave % WPR;
-    const int pair = blockIdx.y;
     const int t = pair / K;
-    const int i0 = ((blockIdx.x * (4 / WPR) + wave / WPR) * groups + grp) * RP;
+    const int i0 = ((rblk * (4 / WPR) + wave / WPR) * groups + grp) * RP;
     if (WPR == 1 && i0 >= I) return;           // whole lane groups retire together
+    const char* wbase;
+    int nslots;
+    pick_slots(sl, wbase, nslots);
     const int slot = slot_ids[pair];
     const bool ok = slot >= 0 && slot < nslots;
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
-    const char* ex = wbase + (size_t)(ok ? slot : 0) * stride;
-    const char* wrows = ex + off_w;
 
     float pg[RP], pu[RP];
     if (ok) {
+        const SlotReader rd(wbase + (size_t)slot * stride, stride);
         uint4 wg[RP][CPL], wu[RP][CPL];
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
             const int i = min(i0 + p, I - 1);
-            const char* g = wrows + (size_t)i * row_bytes;
-            const char* u = wrows + (size_t)(I + i) * row_bytes;
+            const size_t g = off_w + (size_t)i * row_bytes;
+            const size_t u = off_w + (size_t)(I + i) * row_bytes;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = (part * CPL + j) * G + gl;
-                wg[p][j] = load16(g + (size_t)c * 16);
-                wu[p][j] = load16(u + (size_t)c * 16);
+                wg[p][j] = rd.load16(g + (size_t)c * 16);
+                wu[p][j] = rd.load16(u + (size_t)c * 16);
             }
         }
         float sg[RP][CPL], su[RP][CPL];
         if (WT == W_INT4) {
-            const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
             const int spr = H / 128;
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
@@ -406,8 +461,8 @@ __global__ __launch_bounds__(256) void k_w13_gemv(const char* __restrict__ wbase
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = (part * CPL + j) * G + gl;
-                    sg[p][j] = chunk_scale(srows + (size_t)i * spr, c);
-                    su[p][j] = chunk_scale(srows + (size_t)(I + i) * spr, c);
+                    sg[p][j] = rd.scale(off_s + ((size_t)i * spr + (c >> 2)) * 2);
+                    su[p][j] = rd.scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
                 }
             }
         }
@@ -462,14 +517,24 @@ __global__ __launch_bounds__(256) void k_w13_gemv(const char* __restrict__ wbase
             if (i0 + p < I) store_act<ACT>(act, (size_t)pair * I + i0 + p, ok ? silu(pg[p]) * pu[p] : 0.0f);
 }
 
+// grid.x: row blocks; grid.y: (t, k) pairs.
+template <int WT, int AT, int CPL, int RP, int WPR>
+__global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const int32_t* __restrict__ slot_ids,
+                                                  const void* __restrict__ x, int K, int H, int I, int G,
+                                                  size_t off_w, size_t off_s, void* __restrict__ act) {
+    __shared__ float red[4][2][RP];
+    w13_rows<WT, AT, CPL, RP, WPR>(sl, stride, slot_ids, x, K, H, I, G, off_w, off_s, act, blockIdx.y, blockIdx.x,
+                                   red);
+}
+
 // ---- w2 + ordered top-k combine ------------------------------------------------
 // grid.x: blocks of RB = RP * (64 / G) output rows; grid.y: tokens.  The block's
 // waves take the K * WPR (expert, part) tasks in turn: y_k[r] = W2[s_k][r] .
 // act[t*K + k] (part sums) goes to LDS, then
 // out[t][r] = resid[t][r] + sum_{k = 0..K-1} w[t][k] * y_k[r]   (k in order).
 template <int WT, int AT, int CPL, int RP, int WPR, int NWMAX>
-__global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(const char* __restrict__ wbase, size_t stride,
-                                                           int nslots, const int32_t* __restrict__ slot_ids,
+__global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stride,
+                                                           const int32_t* __restrict__ slot_ids,
                                                            const float* __restrict__ topk_w,
                                                            const void* __restrict__ act,
                                                            const void* __restrict__ resid, void* __restrict__ out,
@@ -491,6 +556,9 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(const char* __restric
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
     const int spr = I / 128;
+    const char* wbase;
+    int nslots;
+    pick_slots(sl, wbase, nslots);
     for (int task = wave; task < K * WPR; task += nw) {
         const int k = task / WPR;
         const int part = task - k * WPR;
@@ -502,23 +570,21 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(const char* __restric
                 for (int p = 0; p < RP; ++p) yk[p] = 0.0f;
             continue;
         }
-        const char* ex = wbase + (size_t)slot * stride;
-        const char* wrows = ex + off_w;
+        const SlotReader rd(wbase + (size_t)slot * stride, stride);
         uint4 wr[RP][CPL];
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
-            const char* row = wrows + (size_t)min(r0 + p, H - 1) * row_bytes;
+            const size_t row = off_w + (size_t)min(r0 + p, H - 1) * row_bytes;
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) wr[p][j] = load16(row + (size_t)((part * CPL + j) * G + gl) * 16);
+            for (int j = 0; j < CPL; ++j) wr[p][j] = rd.load16(row + (size_t)((part * CPL + j) * G + gl) * 16);
         }
         float sc[RP][CPL];
         if (WT == W_INT4) {
-            const uint16_t* srows = reinterpret_cast<const uint16_t*>(ex + off_s);
 #pragma unroll
             for (int p = 0; p < RP; ++p)
 #pragma unroll
                 for (int j = 0; j < CPL; ++j)
-                    sc[p][j] = chunk_scale(srows + (size_t)min(r0 + p, H - 1) * spr, (part * CPL + j) * G + gl);
+                    sc[p][j] = rd.scale(off_s + ((size_t)min(r0 + p, H - 1) * spr + (((part * CPL + j) * G + gl) >> 2)) * 2);
         }
         X av[CPL];
 #pragma unroll
@@ -572,9 +638,11 @@ constexpr int kGBN = 128;       // output columns per workgroup: 4 waves x 32
 // [16 + 3S + pos] = pair index at sorted position pos   (S = tile stride).
 // Pairs of one slot are contiguous; their order inside the group is unspecified
 // (each GEMM row depends only on its own inputs, so results do not depend on it).
-__global__ __launch_bounds__(kGroupThreads) void k_group_build(const int32_t* __restrict__ slot_ids, int n,
-                                                               int nslots, int tile_stride,
-                                                               int32_t* __restrict__ grp) {
+__global__ __launch_bounds__(kGroupThreads) void k_group_build(Slots sl, const int32_t* __restrict__ slot_ids,
+                                                               int n, int tile_stride, int32_t* __restrict__ grp) {
+    const char* unused_base;
+    int nslots;
+    pick_slots(sl, unused_base, nslots);
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts];
     __shared__ int32_t toff[kMaxExperts];
@@ -689,12 +757,15 @@ __device__ __forceinline__ uint4 load_a8(const void* __restrict__ p, size_t e0) 
 // grid.x: tiles (blocks past n_tiles exit); grid.y: blocks of 128 columns of I.
 // act_sorted[pos][j] = silu(x[t(pos)] . W13[s][j]) * (x[t(pos)] . W13[s][I + j])
 template <int AT>
-__global__ __launch_bounds__(256) void k_grouped_w13(const char* __restrict__ wbase, size_t stride,
+__global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
                                                      const int32_t* __restrict__ grp, int tile_stride,
                                                      const void* __restrict__ x, int K, int H, int I,
                                                      size_t off_w, uint16_t* __restrict__ act_sorted) {
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
+    const char* wbase;
+    int nslots;
+    pick_slots(sl, wbase, nslots);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
@@ -756,12 +827,15 @@ __global__ __launch_bounds__(256) void k_grouped_w13(const char* __restrict__ wb
 // ---- grouped w2 ------------------------------------------------------------------
 // grid.x: tiles; grid.y: blocks of 128 output columns of H.
 // y[pair(pos)][h] = act_sorted[pos] . W2[s][h]
-__global__ __launch_bounds__(256) void k_grouped_w2(const char* __restrict__ wbase, size_t stride,
+__global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
                                                     const int32_t* __restrict__ grp, int tile_stride,
                                                     const uint16_t* __restrict__ act_sorted, int H, int I,
                                                     size_t off_w, float* __restrict__ y) {
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
+    const char* wbase;
+    int nslots;
+    pick_slots(sl, wbase, nslots);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
@@ -814,12 +888,16 @@ __global__ __launch_bounds__(256) void k_grouped_w2(const char* __restrict__ wba
 // out[t][h] = resid[t][h] + sum_{k = 0..K-1} w[t][k] * y[t*K + k][h]   (k in order;
 // pairs whose slot id is out of range contribute nothing)
 template <int AT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const float* __restrict__ topk_w,
-                                                 const int32_t* __restrict__ slot_ids, int nslots,
+__global__ __launch_bounds__(256) void k_combine(Slots sl, const float* __restrict__ y,
+                                                 const float* __restrict__ topk_w,
+                                                 const int32_t* __restrict__ slot_ids,
                                                  const void* __restrict__ resid, void* __restrict__ out, int T,
                                                  int K, int H) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * H) return;
+    const char* unused_base;
+    int nslots;
+    pick_slots(sl, unused_base, nslots);
     const int t = (int)(idx / H);
     const int h = (int)(idx - (size_t)t * H);
     float acc = 0.0f;
@@ -888,11 +966,11 @@ hipError_t launch_w13(const Geom& g, const ForwardArgs& a, int G, const StageEve
     const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, a.T * g.K);
     if (ev && ev->w13_start)
         hipExtLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, ev->w13_start,
-                              ev->w13_stop, 0, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.x, g.K, g.H, g.I, G,
-                              g.off_w13, g.off_s13, a.act);
+                              ev->w13_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13,
+                              g.off_s13, a.act);
     else
-        hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, a.wbase, g.slot_stride,
-                           a.nslots, a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13, g.off_s13, a.act);
+        hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, a.sl, g.slot_stride,
+                           a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13, g.off_s13, a.act);
     return hipGetLastError();
 }
 
@@ -906,12 +984,12 @@ hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEven
     const dim3 grid((g.H + RB - 1) / RB, a.T);
     if (ev && ev->w2_start)
         hipExtLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), (uint32_t)lds, s,
-                              ev->w2_start, ev->w2_stop, 0, a.wbase, g.slot_stride, a.nslots, a.slot_ids, a.topk_w,
-                              a.act, a.resid, a.out, g.K, g.H, g.I, G, g.off_w2, g.off_s2);
+                              ev->w2_start, ev->w2_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.topk_w, a.act,
+                              a.resid, a.out, g.K, g.H, g.I, G, g.off_w2, g.off_s2);
     else
-        hipLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), lds, s, a.wbase,
-                           g.slot_stride, a.nslots, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I, G,
-                           g.off_w2, g.off_s2);
+        hipLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), lds, s, a.sl,
+                           g.slot_stride, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I, G, g.off_w2,
+                           g.off_s2);
     return hipGetLastError();
 }
 
@@ -1005,34 +1083,35 @@ template <int AT>
 hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     const int n = a.T * g.K;
     const int stride_t = grouped_tile_stride(a.max_pairs, a.nslots_alloc);
-    const int tiles = n / kGBM + (a.nslots < n ? a.nslots : n) + 1;   // bound on this call's tiles
-    hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.slot_ids, n, a.nslots, stride_t, a.grp);
+    const int nsl = a.sl.npool > a.sl.nstage ? a.sl.npool : a.sl.nstage;
+    const int tiles = n / kGBM + (nsl < n ? nsl : n) + 1;   // bound on this call's tiles
+    hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.sl, a.slot_ids, n, stride_t, a.grp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* act = static_cast<uint16_t*>(a.act);
     const dim3 g13(tiles, (g.I + kGBN - 1) / kGBN), g2(tiles, (g.H + kGBN - 1) / kGBN);
     if (ev && ev->w13_start)
-        hipExtLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.wbase,
+        hipExtLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
                               g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act);
     else
-        hipLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, a.wbase, g.slot_stride, a.grp, stride_t, a.x,
+        hipLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, a.x,
                            g.K, g.H, g.I, g.off_w13, act);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && ev->w2_start)
-        hipExtLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.wbase, g.slot_stride,
+        hipExtLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
                               a.grp, stride_t, act, g.H, g.I, g.off_w2, a.y);
     else
-        hipLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, a.wbase, g.slot_stride, a.grp, stride_t, act, g.H,
-                           g.I, g.off_w2, a.y);
+        hipLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H, g.I,
+                           g.off_w2, a.y);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t nt = (size_t)a.T * g.H;
     const dim3 gc((unsigned)((nt + 255) / 256));
     if (ev && ev->w2_stop)
-        hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.y, a.topk_w,
-                              a.slot_ids, a.nslots, a.resid, a.out, a.T, g.K, g.H);
+        hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.sl, a.y, a.topk_w,
+                              a.slot_ids, a.resid, a.out, a.T, g.K, g.H);
     else
-        hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.y, a.topk_w, a.slot_ids, a.nslots, a.resid,
-                           a.out, a.T, g.K, g.H);
+        hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.sl, a.y, a.topk_w, a.slot_ids, a.resid, a.out,
+                           a.T, g.K, g.H);
     return hipGetLastError();
 }
 

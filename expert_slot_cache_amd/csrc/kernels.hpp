@@ -29,10 +29,30 @@ struct Geom {
 hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32_t* rank, uint32_t tag,
                            hipStream_t stream);
 
-// Applies the n_upd changes upd[2u] -> upd[2u+1] to `table` (in place), then
-// out[i] = table[ids[i]] (ids outside [0,E) give -1).  upd may be host-mapped memory.
-hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* upd, int n_upd,
-                        int32_t* out, hipStream_t stream);
+// Per-layer publication of a step's decision, in host-mapped memory (64 bytes).
+// The host (or a copy stream, once the step's copies have landed) writes `seq`
+// last; status and n_upd are valid once seq matches.
+struct Gate {
+    uint32_t seq;
+    int32_t status;   // PATH_POOL, PATH_STAGE or PATH_NONE
+    int32_t n_upd;    // table changes in the layer's update list
+    uint32_t timeout; // set by the remap kernel when it gave up waiting
+    int32_t pad[12];
+};
+enum { PATH_POOL = 0, PATH_STAGE = 1, PATH_NONE = 2 };
+
+// The remap of one step.  If `gate` is null the decision is status/n_upd;
+// otherwise thread 0 of each workgroup waits (at most `limit` wall-clock ticks)
+// until gate->seq == seq and takes status/n_upd from the gate.
+//   PATH_POOL : apply upd[2u] -> upd[2u+1] (u < n_upd) to `table` in place, then
+//               out[i] = table[ids[i]]
+//   PATH_STAGE: out[i] = rank[ids[i]]
+//   PATH_NONE : out[i] = -1
+// ids outside [0,E) give -1.  The path is also written to *path (device), which
+// the forward kernels read to pick the slot base.  upd and gate may be host-mapped.
+hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* rank, const int32_t* upd,
+                        int n_upd, int status, Gate* gate, uint32_t seq, unsigned long long limit, int32_t* out,
+                        int32_t* path, hipStream_t stream);
 
 // Optional event pairs around the two projection stages (any may be null).
 struct StageEvents {
@@ -40,9 +60,18 @@ struct StageEvents {
     hipEvent_t w2_start = nullptr, w2_stop = nullptr;
 };
 
+// The two places a layer's experts can be read from; *path (written by the
+// step's remap) picks one: PATH_POOL -> pool, PATH_STAGE -> stage, PATH_NONE -> none.
+struct Slots {
+    const char* pool;
+    const char* stage;
+    int npool;              // valid slot ids in the pool: [0, npool)
+    int nstage;             // valid staging ranks: [0, nstage)
+    const int32_t* path;    // device word
+};
+
 struct ForwardArgs {
-    const char* wbase;      // slot 0 of the pool (or staging)
-    int nslots;             // valid slot ids are [0, nslots)
+    Slots sl;
     const int32_t* slot_ids;// [T][K]
     const void* x;          // [T][H]
     const float* topk_w;    // [T][K]

@@ -1,5 +1,5 @@
 // C-ABI runtime of the expert slot cache: pinned host store, fixed-address HBM slot
-// pools, copy streams joined by events, the per-layer slot manager, prepare/forward.
+// pools, copy streams, the per-layer slot manager, prepare/forward/step.
 //
 // Step order per layer (llama.cpp "Persistent expert slot pool", section "Design"
 // item 3: read ids back, update the LRU, issue async H2D for misses and rewrite the
@@ -7,12 +7,17 @@
 //   1. k_distinct on the compute stream -> distinct ids in pinned host memory;
 //      wait for it (the one host sync of a step).
 //   2. host: range check, route rule, LRU update (SlotLRU) -> miss list.
-//   3. copy streams wait for the layer's last forward (its slot reads, WAR), then
-//      hipMemcpyAsync store -> slot for each miss, optionally in chunks, then an
-//      event per copy stream that the compute stream waits on (RAW).
+//   3. hipMemcpyAsync store -> slot for each miss on the copy streams, optionally
+//      in chunks.  No write-after-read wait is needed: every kernel that reads a
+//      slot or the staging area runs on the compute stream, and the readback of
+//      step 1 has seen k_distinct finish -- so every kernel queued before it,
+//      the last reader of any destination included, has finished too.
 //   4. the step's map changes go to a small pinned list that k_remap reads: it
 //      applies them to the persistent HBM table and remaps through the fresh table.
-//   5. forward kernels on the compute stream; record the layer's reads-done event.
+//      The compute stream waits for the copies (an event per copy stream), or, in
+//      the gated one-call step, the remap waits until the copy stream publishes
+//      the step's sequence number.
+//   5. forward kernels on the compute stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -113,8 +118,10 @@ struct LayerState {
     int32_t* map_dev = nullptr;  // HBM int32 [E]: the persistent map table
     int32_t* upd_host = nullptr; // pinned int32 [2E]: this step's (entry, value) changes
     int32_t* upd_dev = nullptr;  // device view of upd_host
-    hipEvent_t reads_done = nullptr;
-    bool reads_recorded = false;
+    moe::Gate* gate = nullptr;   // pinned coherent: this layer's step publication
+    moe::Gate* gate_dev = nullptr;
+    uint32_t gate_seq = 0;       // last published sequence number
+    int32_t* path_dev = nullptr; // HBM int32: the path the last remap chose
     bool prepared = false;
     char* expert(int32_t e, size_t eb) const { return store[e / per_piece] + (size_t)(e % per_piece) * eb; }
     int32_t prep_tokens = 0;
@@ -139,8 +146,6 @@ struct moe_pool {
     char* staging = nullptr;
     int32_t staging_cap = 0;
     int32_t staging_owner = -1;
-    hipEvent_t staging_reads_done = nullptr;
-    bool staging_recorded = false;
     uint32_t* rb_host = nullptr;  // pinned [1 + E] tagged words, written by k_distinct
     uint32_t* rb_dev = nullptr;   // device view of rb_host
     uint32_t rb_tag = 0;          // tag of the last readback (1 .. 2^18 - 1)
@@ -148,6 +153,9 @@ struct moe_pool {
     std::vector<int32_t> ulist;   // the last readback's distinct ids
     int32_t* rank_dev = nullptr;  // HBM [E]
     int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
+    moe::Gate* gates = nullptr;   // pinned coherent [n_layers]
+    int32_t* paths_dev = nullptr; // HBM [n_layers]
+    unsigned long long gate_limit = 0;   // wall-clock ticks a gated remap waits at most
     void* act = nullptr;          // HBM [max_tokens * K][I] SwiGLU output
     float* y = nullptr;           // HBM [max_tokens * K][H] per-pair w2 output
     int32_t* grp = nullptr;       // HBM grouped-path index buffer
@@ -178,7 +186,6 @@ void destroy_pool(moe_pool* p) {
         if (L.slots) (void)hipFree(L.slots);
         if (L.map_dev) (void)hipFree(L.map_dev);
         if (L.upd_host) (void)hipHostFree(L.upd_host);
-        if (L.reads_done) (void)hipEventDestroy(L.reads_done);
         for (auto& t : L.copy_t) {
             if (t.a) (void)hipEventDestroy(t.a);
             if (t.b) (void)hipEventDestroy(t.b);
@@ -191,9 +198,10 @@ void destroy_pool(moe_pool* p) {
     for (auto s : p->copy) (void)hipStreamDestroy(s);
     for (auto e : p->copy_done) (void)hipEventDestroy(e);
     if (p->staging) (void)hipFree(p->staging);
-    if (p->staging_reads_done) (void)hipEventDestroy(p->staging_reads_done);
     if (p->rb_host) (void)hipHostFree(p->rb_host);
     if (p->rank_dev) (void)hipFree(p->rank_dev);
+    if (p->gates) (void)hipHostFree(p->gates);
+    if (p->paths_dev) (void)hipFree(p->paths_dev);
     if (p->ident_dev) (void)hipFree(p->ident_dev);
     if (p->act) (void)hipFree(p->act);
     if (p->y) (void)hipFree(p->y);
@@ -208,6 +216,8 @@ moe_status_t check_layer(const moe_pool* p, int32_t layer) {
 }
 
 // Harvest finished timing event pairs (all work before the last readback sync).
+bool done(const Timing& t) { return t.pending && hipEventQuery(t.b) == hipSuccess; }
+
 bool harvest(moe_pool* p, Timing& t, double* acc) {
     if (!t.pending) return false;
     float ms = 0;
@@ -220,9 +230,13 @@ bool harvest(moe_pool* p, Timing& t, double* acc) {
 void harvest_layer(moe_pool* p, LayerState& L) {
     if (!p->cfg.timing) return;
     // the copy span of a step: earliest start to latest stop over the copy streams
-    bool any = false;
-    for (auto& t : L.copy_t) any = any || t.pending;
-    if (any) {
+    bool any = false, ready = true;
+    for (auto& t : L.copy_t)
+        if (t.pending) {
+            any = true;
+            ready = ready && done(t);
+        }
+    if (any && ready) {
         int ref = -1;
         for (size_t i = 0; i < L.copy_t.size(); ++i)
             if (L.copy_t[i].pending) {
@@ -245,6 +259,7 @@ void harvest_layer(moe_pool* p, LayerState& L) {
         p->copy_calls++;
         p->copy_bytes += bytes;
     }
+    if (L.w13_t.pending && L.w2_t.pending && (!done(L.w13_t) || !done(L.w2_t))) return;
     const bool a = harvest(p, L.w13_t, &p->w13_ms);
     const bool b = harvest(p, L.w2_t, &p->w2_ms);
     if (a && b) p->kern_calls++;
@@ -254,11 +269,12 @@ void harvest_all(moe_pool* p) {
     for (auto& L : p->layers) harvest_layer(p, L);
 }
 
-// Enqueue host->HBM copies of `n` experts (src[i] -> dst[i]) on the copy streams,
-// after `war` (the last reads of the destination), and make the compute stream
-// wait for them.
+// Enqueue host->HBM copies of the experts (src -> dst pairs) on the copy streams and
+// make the compute stream wait for them (join) -- or, for a gated step, make the
+// first copy stream used wait for all of them and then publish `seq` to the
+// layer's gate (a stream-ordered 32-bit write into the host-mapped gate).
 moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, const char*>>& jobs,
-                          hipEvent_t war, bool war_recorded) {
+                          bool join, uint32_t seq) {
     if (jobs.empty()) return MOE_OK;
     const int ns = (int)p->copy.size();
     const size_t eb = p->lay.total;
@@ -266,17 +282,16 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
     std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
     bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0;
     for (const auto& t : L.copy_t) timed = timed && !t.pending;
-    // every stream that may carry a piece first waits for the WAR event
     const int streams_needed = std::min<size_t>(ns, jobs.size() * ((eb + chunk - 1) / chunk));
     for (int i = 0; i < streams_needed; ++i) {
         const int s = (p->copy_rr + i) % ns;
-        if (war_recorded) HIPCHK(hipStreamWaitEvent(p->copy[s], war, 0));
         if (timed) {
             HIPCHK(hipEventRecord(L.copy_t[s].a, p->copy[s]));
             L.copy_t[s].bytes = 0;
         }
         p->used_copy[s] = 1;
     }
+    const int first = p->copy_rr;
     int rr = p->copy_rr;
     for (const auto& j : jobs) {
         for (size_t off = 0; off < eb; off += chunk) {
@@ -294,9 +309,212 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
             L.copy_t[s].pending = true;
         }
         HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
-        HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+        if (join)
+            HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+        else if (s != first)
+            HIPCHK(hipStreamWaitEvent(p->copy[first], p->copy_done[s], 0));
     }
+    if (!join) HIPCHK(hipStreamWriteValue32(p->copy[first], &L.gate_dev->seq, seq, 0));
     L.bytes_h2d += (uint64_t)eb * jobs.size();
+    return MOE_OK;
+}
+
+// Host-side publication of a gated step's decision: status and n_upd first, the
+// sequence number last (x86 stores are seen in order; the remap kernel reads the
+// fields only after it has seen the sequence number).
+void publish_fields(LayerState& L, int status, int n_upd) {
+    volatile moe::Gate* g = L.gate;
+    g->status = status;
+    g->n_upd = n_upd;
+}
+
+void publish_seq(LayerState& L, uint32_t seq) {
+    std::atomic_thread_fence(std::memory_order_release);
+    volatile moe::Gate* g = L.gate;
+    g->seq = seq;
+}
+
+// ---- the steps of prepare, shared by the two-call and the gated flow -----------
+
+// A gated remap that gave up waiting leaves a flag in its gate; the next call on
+// the layer reports it.
+moe_status_t check_gate(LayerState& L, int32_t layer) {
+    volatile moe::Gate* g = L.gate;
+    if (g->timeout) {
+        g->timeout = 0;
+        FAIL(MOE_EHIP, "layer %d: a step's remap timed out waiting for its copies; that step's output is invalid", layer);
+    }
+    return MOE_OK;
+}
+
+// Distinct ids of the step, written by the kernel as tagged words into pinned host
+// memory (zeroed here beforehand) and rank[] on the device.
+moe_status_t launch_distinct_ids(moe_pool* p, const int32_t* ids_dev, int n) {
+    std::memset(p->rb_host, 0, (size_t)p->rb_used * 4);
+    p->rb_tag = p->rb_tag % ((1u << 18) - 1) + 1;
+    HIPCHK(moe::launch_distinct(ids_dev, n, p->cfg.n_experts, p->rb_dev, p->rank_dev, p->rb_tag, p->compute));
+    p->rb_used = 0;
+    return MOE_OK;
+}
+
+// The readback: the step's one host sync.  The host spins until each word it needs
+// carries this step's tag, checking the stream now and then so that a failed launch
+// cannot leave it spinning.  Fills p->ulist[0..D).
+moe_status_t read_distinct(moe_pool* p, int32_t layer, int32_t* D_out) {
+    const uint32_t tag = p->rb_tag;
+    const int32_t E = p->cfg.n_experts;
+    const auto t0 = std::chrono::steady_clock::now();
+    const volatile uint32_t* rbv = p->rb_host;
+    auto wait_word = [&](int i) -> moe_status_t {
+        for (uint64_t it = 1;; ++it) {
+            const uint32_t w = rbv[i];
+            if ((w >> 14) == tag) return MOE_OK;
+            if ((it & 255) == 0) {
+                const hipError_t q = hipStreamQuery(p->compute);
+                if (q == hipSuccess) {
+                    // everything queued has finished, the distinct kernel included
+                    if ((rbv[i] >> 14) == tag) return MOE_OK;
+                    FAIL(MOE_EHIP, "distinct-id readback word %d missing after the stream drained", i);
+                }
+                if (q != hipErrorNotReady) FAIL(MOE_EHIP, "hipStreamQuery failed: %s", hipGetErrorString(q));
+            }
+            __builtin_ia32_pause();
+        }
+    };
+    p->rb_used = 1;
+    moe_status_t st = wait_word(0);
+    if (st) return st;
+    const uint32_t w0 = rbv[0];
+    const int32_t D = (int32_t)(w0 & 0x1FFFu);
+    const bool bad = (w0 >> 13) & 1u;
+    if (D > E) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
+    p->rb_used = 1 + D;
+    for (int32_t i = 0; i < D; ++i) {
+        st = wait_word(1 + i);
+        if (st) return st;
+        p->ulist[i] = (int32_t)(rbv[1 + i] & 0x3FFFu);
+    }
+    if (p->cfg.timing) {
+        p->sync_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        harvest_all(p);
+    }
+    if (bad) FAIL(MOE_ERANGE, "layer %d: an expert id is outside [0,%d)", layer, E);
+    if (D < 1) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
+    *D_out = D;
+    return MOE_OK;
+}
+
+// The LRU step over p->ulist[0..D), the map-change list and the miss copies.
+// join: the compute stream waits for the copies (two-call flow); otherwise the
+// copies publish `seq` to the layer's gate when they land (gated flow; the caller
+// publishes when there are none).
+moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, bool join, uint32_t seq,
+                   int32_t* the_path, int32_t* n_upd_out, bool* published = nullptr) {
+    const size_t eb = p->lay.total;
+    const int32_t* u = p->ulist.data();
+    moe_status_t st;
+    p->misses.clear();
+    *the_path = MOE_PATH_POOL;
+    *n_upd_out = 0;
+    if (published) *published = false;
+    // The readback has seen this step's distinct kernel finish, and with it every
+    // earlier kernel of the compute stream: no reads of a destination are pending,
+    // so the copies wait for nothing.
+    if (p->cfg.resident) {
+        L.lru.count_resident(D);
+    } else if (L.lru.step(u, D, (int64_t)n, p->misses)) {
+        // The map changes, applied by the remap kernel before it reads the table.
+        // Each touched entry carries its value after the whole step: an expert can
+        // be evicted by an earlier (lower-id) miss of the step and re-inserted by
+        // its own miss later in the same step, so an entry may appear twice -- with
+        // the same final value, which makes the kernel's unordered writes safe.
+        // (The previous step's list was consumed before this step's readback.)
+        const std::vector<int32_t>& fmap = L.lru.map();
+        int n_upd = 0;
+        for (const auto& m : p->misses) {
+            if (m.evicted >= 0) {
+                L.upd_host[2 * n_upd] = m.evicted;
+                L.upd_host[2 * n_upd + 1] = fmap[m.evicted];
+                ++n_upd;
+            }
+            L.upd_host[2 * n_upd] = m.expert;
+            L.upd_host[2 * n_upd + 1] = fmap[m.expert];
+            ++n_upd;
+        }
+        *n_upd_out = n_upd;
+        if (!p->misses.empty()) {
+            std::vector<std::pair<char*, const char*>> jobs;
+            jobs.reserve(p->misses.size());
+            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.expert(m.expert, eb));
+            if (!join) publish_fields(L, moe::PATH_POOL, n_upd);
+            st = issue_copies(p, L, jobs, join, seq);
+            if (st) return st;
+            if (published) *published = !join;
+        }
+    } else {
+        // selective-copy fallback: the step's experts go to staging in rank order;
+        // the pool is untouched
+        *the_path = MOE_PATH_FALLBACK;
+        std::vector<std::pair<char*, const char*>> jobs;
+        jobs.reserve(D);
+        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.expert(u[r], eb));
+        if (!join) publish_fields(L, moe::PATH_STAGE, 0);
+        st = issue_copies(p, L, jobs, join, seq);
+        if (st) return st;
+        if (published) *published = !join;
+        L.staged += (uint64_t)D;
+        p->staging_owner = layer;
+    }
+    return MOE_OK;
+}
+
+void finish_prepare(moe_pool* p, LayerState& L, int32_t n_tokens, int32_t the_path, moe_miss_t* miss_host,
+                    int32_t miss_cap, int32_t* n_miss, int32_t* path) {
+    L.prepared = true;
+    L.prep_tokens = n_tokens;
+    L.prep_path = the_path;
+    const int32_t nm = (int32_t)p->misses.size();
+    if (miss_host) {
+        for (int32_t i = 0; i < std::min(nm, miss_cap); ++i)
+            miss_host[i] = moe_miss_t{p->misses[i].expert, p->misses[i].slot, p->misses[i].evicted};
+    }
+    if (n_miss) *n_miss = nm;
+    if (path) *path = the_path;
+}
+
+moe::Slots layer_slots(const moe_pool* p, const LayerState& L) {
+    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev};
+}
+
+moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
+                                  const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev) {
+    moe::ForwardArgs a{};
+    a.sl = layer_slots(p, L);
+    a.slot_ids = slot_ids_dev;
+    a.x = x_dev;
+    a.topk_w = topk_w_dev;
+    a.resid = resid_dev;
+    a.out = out_dev;
+    a.T = n_tokens;
+    a.act = p->act;
+    a.y = p->y;
+    a.grp = p->grp;
+    a.nslots_alloc = std::max(1, p->grp_slots);
+    a.max_pairs = p->cfg.max_tokens * p->cfg.top_k;
+    moe::StageEvents ev;
+    const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
+                       !L.w13_t.pending && !L.w2_t.pending;
+    if (timed) {
+        ev.w13_start = L.w13_t.a;
+        ev.w13_stop = L.w13_t.b;
+        ev.w2_start = L.w2_t.a;
+        ev.w2_stop = L.w2_t.b;
+    }
+    HIPCHK(moe::launch_forward(p->geom, a, timed ? &ev : nullptr, p->compute));
+    if (timed) {
+        L.w13_t.pending = true;
+        L.w2_t.pending = true;
+    }
     return MOE_OK;
 }
 
@@ -421,7 +639,6 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         CREATE_HIP(hipMemset(L.map_dev, 0xFF, (size_t)E * 4));   // all -1
         CREATE_HIP(hipHostMalloc((void**)&L.upd_host, (size_t)E * 8, hipHostMallocCoherent | hipHostMallocMapped));
         CREATE_HIP(hipHostGetDevicePointer((void**)&L.upd_dev, L.upd_host, 0));
-        CREATE_HIP(hipEventCreateWithFlags(&L.reads_done, hipEventDisableTiming));
         L.copy_t.resize(c.n_copy_streams);
         if (c.timing) {
             for (auto& t : L.copy_t) {
@@ -435,7 +652,6 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         }
     }
     if (p->staging_cap > 0) CREATE_HIP(hipMalloc((void**)&p->staging, (size_t)p->staging_cap * eb));
-    CREATE_HIP(hipEventCreateWithFlags(&p->staging_reads_done, hipEventDisableTiming));
     CREATE_HIP(hipHostMalloc((void**)&p->rb_host, (size_t)(E + 1) * 4, hipHostMallocCoherent | hipHostMallocMapped));
     std::memset(p->rb_host, 0, (size_t)(E + 1) * 4);
     CREATE_HIP(hipHostGetDevicePointer((void**)&p->rb_dev, p->rb_host, 0));
@@ -446,6 +662,27 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         std::vector<int32_t> id(E);
         for (int32_t e = 0; e < E; ++e) id[e] = e;
         CREATE_HIP(hipMemcpy(p->ident_dev, id.data(), (size_t)E * 4, hipMemcpyHostToDevice));
+    }
+    CREATE_HIP(hipHostMalloc((void**)&p->gates, sizeof(moe::Gate) * c.n_layers,
+                             hipHostMallocCoherent | hipHostMallocMapped));
+    std::memset(p->gates, 0, sizeof(moe::Gate) * c.n_layers);
+    moe::Gate* gates_dev = nullptr;
+    CREATE_HIP(hipHostGetDevicePointer((void**)&gates_dev, p->gates, 0));
+    CREATE_HIP(hipMalloc((void**)&p->paths_dev, sizeof(int32_t) * c.n_layers));
+    CREATE_HIP(hipMemset(p->paths_dev, 0, sizeof(int32_t) * c.n_layers));
+    for (int32_t l = 0; l < c.n_layers; ++l) {
+        p->layers[l].gate = p->gates + l;
+        p->layers[l].gate_dev = gates_dev + l;
+        p->layers[l].path_dev = p->paths_dev + l;
+    }
+    {
+        // A gated remap gives up (and reports it) after 10 s plus 1 s per GB the
+        // step can copy at most; the copies of a step run at ~50 GB/s.
+        int dev = 0, khz = 0;
+        CREATE_HIP(hipGetDevice(&dev));
+        CREATE_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+        const double max_copy = (double)std::max(p->nslot_alloc, p->staging_cap) * (double)eb;
+        p->gate_limit = (unsigned long long)((10.0 + max_copy * 1e-9) * (double)std::max(khz, 1) * 1e3);
     }
     CREATE_HIP(hipMalloc((void**)&p->act, act_bytes));
     CREATE_HIP(hipMalloc((void**)&p->y, y_bytes));
@@ -500,7 +737,8 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
     LayerState& L = p->layers[layer];
     const int32_t E = p->cfg.n_experts;
     const int n = n_tokens * p->cfg.top_k;
-    const size_t eb = p->lay.total;
+    st = check_gate(L, layer);
+    if (st) return st;
 
     if (n_tokens == 0) {
         p->misses.clear();
@@ -513,110 +751,22 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
         return MOE_OK;
     }
 
-    // 1. distinct ids, read back: the step's one host sync.  The kernel writes
-    // tagged words into pinned host memory (zeroed here beforehand); the host spins
-    // until each word it needs carries this step's tag, checking the stream now and
-    // then so that a failed launch cannot leave it spinning.
-    std::memset(p->rb_host, 0, (size_t)p->rb_used * 4);
-    p->rb_tag = p->rb_tag % ((1u << 18) - 1) + 1;
-    const uint32_t tag = p->rb_tag;
-    HIPCHK(moe::launch_distinct(topk_ids_dev, n, E, p->rb_dev, p->rank_dev, tag, p->compute));
-    const auto t0 = std::chrono::steady_clock::now();
-    const volatile uint32_t* rbv = p->rb_host;
-    auto wait_word = [&](int i) -> moe_status_t {
-        for (uint64_t it = 1;; ++it) {
-            const uint32_t w = rbv[i];
-            if ((w >> 14) == tag) return MOE_OK;
-            if ((it & 255) == 0) {
-                const hipError_t q = hipStreamQuery(p->compute);
-                if (q == hipSuccess) {
-                    // everything queued has finished, the distinct kernel included
-                    if ((rbv[i] >> 14) == tag) return MOE_OK;
-                    FAIL(MOE_EHIP, "distinct-id readback word %d missing after the stream drained", i);
-                }
-                if (q != hipErrorNotReady) FAIL(MOE_EHIP, "hipStreamQuery failed: %s", hipGetErrorString(q));
-            }
-            __builtin_ia32_pause();
-        }
-    };
-    p->rb_used = 1;
-    st = wait_word(0);
+    st = launch_distinct_ids(p, topk_ids_dev, n);
     if (st) return st;
-    const uint32_t w0 = rbv[0];
-    const int32_t D = (int32_t)(w0 & 0x1FFFu);
-    const bool bad = (w0 >> 13) & 1u;
-    if (D > E) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
-    p->rb_used = 1 + D;
-    for (int32_t i = 0; i < D; ++i) {
-        st = wait_word(1 + i);
-        if (st) return st;
-        p->ulist[i] = (int32_t)(rbv[1 + i] & 0x3FFFu);
-    }
-    if (p->cfg.timing) {
-        p->sync_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
-        harvest_all(p);
-    }
-    if (bad) FAIL(MOE_ERANGE, "layer %d: an expert id is outside [0,%d)", layer, E);
-    if (D < 1) FAIL(MOE_EHIP, "distinct-id readback returned D=%d", D);
-    const int32_t* u = p->ulist.data();
+    int32_t D = 0;
+    st = read_distinct(p, layer, &D);
+    if (st) return st;
 
-    // 2. route + LRU
-    p->misses.clear();
-    int32_t the_path = MOE_PATH_POOL;
-    if (p->cfg.resident) {
-        L.lru.count_resident(D);
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, nullptr, 0, slot_ids_dev, p->compute));
-    } else if (L.lru.step(u, D, (int64_t)n, p->misses)) {
-        // 3. misses: store -> slot on the copy streams, after this layer's last reads
-        if (!p->misses.empty()) {
-            std::vector<std::pair<char*, const char*>> jobs;
-            jobs.reserve(p->misses.size());
-            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.expert(m.expert, eb));
-            st = issue_copies(p, L, jobs, L.reads_done, L.reads_recorded);
-            if (st) return st;
-        }
-        // 4. the map changes, applied by the remap kernel before it reads the table.
-        // Each touched entry carries its value after the whole step: an expert can be
-        // evicted by an earlier (lower-id) miss of the step and re-inserted by its own
-        // miss later in the same step, so an entry may appear twice -- with the same
-        // final value, which makes the kernel's unordered writes safe.
-        // (The previous step's list was consumed before this step's readback sync.)
-        const std::vector<int32_t>& fmap = L.lru.map();
-        int n_upd = 0;
-        for (const auto& m : p->misses) {
-            if (m.evicted >= 0) {
-                L.upd_host[2 * n_upd] = m.evicted;
-                L.upd_host[2 * n_upd + 1] = fmap[m.evicted];
-                ++n_upd;
-            }
-            L.upd_host[2 * n_upd] = m.expert;
-            L.upd_host[2 * n_upd + 1] = fmap[m.expert];
-            ++n_upd;
-        }
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, L.upd_dev, n_upd, slot_ids_dev, p->compute));
-    } else {
-        // selective-copy fallback: the step's experts go to staging in rank order;
-        // the pool is untouched
-        the_path = MOE_PATH_FALLBACK;
-        std::vector<std::pair<char*, const char*>> jobs;
-        jobs.reserve(D);
-        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.expert(u[r], eb));
-        st = issue_copies(p, L, jobs, p->staging_reads_done, p->staging_recorded);
-        if (st) return st;
-        L.staged += (uint64_t)D;
-        p->staging_owner = layer;
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->rank_dev, nullptr, 0, slot_ids_dev, p->compute));
-    }
-    L.prepared = true;
-    L.prep_tokens = n_tokens;
-    L.prep_path = the_path;
-    const int32_t nm = (int32_t)p->misses.size();
-    if (miss_host) {
-        for (int32_t i = 0; i < std::min(nm, miss_cap); ++i)
-            miss_host[i] = moe_miss_t{p->misses[i].expert, p->misses[i].slot, p->misses[i].evicted};
-    }
-    if (n_miss) *n_miss = nm;
-    if (path) *path = the_path;
+    // 2. route + LRU; 3. misses: store -> slot on the copy streams, after this
+    // layer's last reads; 4. the remap (map changes applied first)
+    int32_t the_path = MOE_PATH_POOL, n_upd = 0;
+    st = route(p, L, layer, D, n, true, 0, &the_path, &n_upd);
+    if (st) return st;
+    int32_t* table = p->cfg.resident ? p->ident_dev : L.map_dev;
+    const int status = the_path == MOE_PATH_FALLBACK ? moe::PATH_STAGE : moe::PATH_POOL;
+    HIPCHK(moe::launch_remap(topk_ids_dev, n, E, table, p->rank_dev, L.upd_dev, n_upd, status, nullptr, 0, 0,
+                             slot_ids_dev, L.path_dev, p->compute));
+    finish_prepare(p, L, n_tokens, the_path, miss_host, miss_cap, n_miss, path);
     return MOE_OK;
 }
 
@@ -632,52 +782,76 @@ moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, c
         FAIL(MOE_ESTATE, "layer %d: its staged experts were replaced by layer %d's fallback", layer, p->staging_owner);
     if (n_tokens == 0) return MOE_OK;
     if (!x_dev || !slot_ids_dev || !topk_w_dev || !out_dev) FAIL(MOE_EINVAL, "null buffer");
-    moe::ForwardArgs a{};
-    a.wbase = fb ? p->staging : L.slots;
-    a.nslots = fb ? p->staging_cap : p->nslot_alloc;
-    a.slot_ids = slot_ids_dev;
-    a.x = x_dev;
-    a.topk_w = topk_w_dev;
-    a.resid = resid_dev;
-    a.out = out_dev;
-    a.T = n_tokens;
-    a.act = p->act;
-    a.y = p->y;
-    a.grp = p->grp;
-    a.nslots_alloc = std::max(1, p->grp_slots);
-    a.max_pairs = p->cfg.max_tokens * p->cfg.top_k;
-    moe::StageEvents ev;
-    const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
-                       !L.w13_t.pending && !L.w2_t.pending;
-    if (timed) {
-        ev.w13_start = L.w13_t.a;
-        ev.w13_stop = L.w13_t.b;
-        ev.w2_start = L.w2_t.a;
-        ev.w2_stop = L.w2_t.b;
-    }
-    HIPCHK(moe::launch_forward(p->geom, a, timed ? &ev : nullptr, p->compute));
-    if (timed) {
-        L.w13_t.pending = true;
-        L.w2_t.pending = true;
-    }
-    if (fb) {
-        HIPCHK(hipEventRecord(p->staging_reads_done, p->compute));
-        p->staging_recorded = true;
-    } else {
-        HIPCHK(hipEventRecord(L.reads_done, p->compute));
-        L.reads_recorded = true;
-    }
-    return MOE_OK;
+    return launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
 }
 
 moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev, const void* resid_dev,
                            void* out_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
     if (n_tokens > 0 && (!x_dev || !topk_w_dev || !out_dev)) FAIL(MOE_EINVAL, "null buffer");
-    moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap, n_miss,
-                                       path);
+    if (!p || n_tokens <= 0 || n_tokens > moe::kDecodeMaxTokens || n_tokens > p->cfg.max_tokens) {
+        moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap,
+                                           n_miss, path);
+        if (st) return st;
+        return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
+    }
+    // Decode-sized steps launch everything before the readback: distinct ids, a
+    // remap that waits on the layer's gate, and the forward kernels.  The host then
+    // reads the distinct ids back, runs the LRU, queues the miss copies and
+    // publishes the decision (from the copy stream once the copies have landed, or
+    // at once when there are none), so the kernels' launch latency overlaps the
+    // host's work and the copies.
+    moe_status_t st = check_layer(p, layer);
     if (st) return st;
-    return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
+    if (!topk_ids_dev || !slot_ids_dev) FAIL(MOE_EINVAL, "null ids");
+    if (miss_cap < 0) FAIL(MOE_EINVAL, "miss_cap < 0");
+    LayerState& L = p->layers[layer];
+    st = check_gate(L, layer);
+    if (st) return st;
+    L.prepared = false;
+    const int32_t E = p->cfg.n_experts;
+    const int n = n_tokens * p->cfg.top_k;
+    const bool gated = !p->cfg.resident;
+    st = launch_distinct_ids(p, topk_ids_dev, n);
+    if (st) return st;
+    uint32_t seq = 0;
+    if (gated) {
+        seq = ++L.gate_seq;
+        if (seq == 0) seq = ++L.gate_seq;   // 0 is the gate's initial value
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, p->rank_dev, L.upd_dev, 0, 0, L.gate_dev, seq,
+                                 p->gate_limit, slot_ids_dev, L.path_dev, p->compute));
+    } else {
+        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, p->rank_dev, L.upd_dev, 0, moe::PATH_POOL,
+                                 nullptr, 0, 0, slot_ids_dev, L.path_dev, p->compute));
+    }
+    // From here on a gated remap is queued: every exit publishes a decision, so
+    // that the kernel never waits out its limit.
+    bool published = !gated;
+    auto abort_gate = [&](moe_status_t e) {
+        if (!published) {
+            publish_fields(L, moe::PATH_NONE, 0);
+            publish_seq(L, seq);
+            published = true;
+        }
+        return e;
+    };
+    st = launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
+    if (st) return abort_gate(st);
+    int32_t D = 0;
+    st = read_distinct(p, layer, &D);
+    if (st) return abort_gate(st);
+    int32_t the_path = MOE_PATH_POOL, n_upd = 0;
+    bool by_copy = false;
+    st = route(p, L, layer, D, n, false, seq, &the_path, &n_upd, &by_copy);
+    published = published || by_copy;
+    if (st) return abort_gate(st);
+    if (!published) {
+        publish_fields(L, moe::PATH_POOL, n_upd);
+        publish_seq(L, seq);
+        published = true;
+    }
+    finish_prepare(p, L, n_tokens, the_path, miss_host, miss_cap, n_miss, path);
+    return MOE_OK;
 }
 
 moe_status_t moe_pool_sync(moe_pool_t* p) {

@@ -29,8 +29,9 @@ class Rig:
     def __init__(self, wl: synth.Workload, *, slots: int, layers: int | None = None,
                  resident: bool = False, rule: str = "distinct", max_tokens: int | None = None,
                  fast: bool = True, experts=None, std: float = 0.02, copy_streams: int = 1,
-                 copy_chunk_bytes: int = 0):
+                 copy_chunk_bytes: int = 0, one_call: bool = False):
         self.wl = wl
+        self.one_call = one_call   # one moe_pool_step call per layer instead of prepare + forward
         self.L = wl.layers if layers is None else layers
         self.E, self.K, self.H, self.I = wl.experts, wl.top_k, wl.hidden, wl.inter
         if experts is None:
@@ -48,14 +49,18 @@ class Rig:
                 self.pool.load_expert(l, e, experts[l][e])
 
     def step(self, layer: int, ids: np.ndarray, x_dev, w_dev, resid_dev=None):
-        """prepare + forward; returns (path, misses, slot_ids host, out device)."""
+        """prepare + forward (or one step call); returns (path, misses, slot_ids
+        host, out device)."""
         T = ids.shape[0]
         ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(DEV)
         slot_d = torch.empty_like(ids_d)
-        path, misses = self.pool.prepare(layer, ids_d, T, slot_d)
         dt = torch.float32 if self.wl.atype == "f32" else torch.bfloat16
         out = torch.empty((T, self.H), dtype=dt, device=DEV)
-        self.pool.forward(layer, x_dev, slot_d, w_dev, out, T, resid=resid_dev)
+        if self.one_call:
+            path, misses = self.pool.step(layer, ids_d, T, slot_d, x_dev, w_dev, out, resid=resid_dev)
+        else:
+            path, misses = self.pool.prepare(layer, ids_d, T, slot_d)
+            self.pool.forward(layer, x_dev, slot_d, w_dev, out, T, resid=resid_dev)
         return path, misses, slot_d.cpu().numpy(), out
 
     def reference(self, layer: int, x: np.ndarray, ids: np.ndarray, w: np.ndarray, resid=None,

@@ -50,11 +50,18 @@ def _assert_bitwise(a, b, what):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{what}: step {s} layer {l}"
 
 
-def test_tiny_f32_full_trace_and_resident_identity():
+# one_call: one moe_pool_step per layer (decode steps launch the forward before the
+# readback and gate it on the layer's published decision) instead of prepare +
+# forward
+ONE_CALL = pytest.mark.parametrize("one_call", [False, True], ids=["two_call", "step"])
+
+
+@ONE_CALL
+def test_tiny_f32_full_trace_and_resident_identity(one_call):
     wl = synth.WORKLOADS["tiny_f32_e8"]
     trace = synth.make_trace(wl)
     xs, ws = _inputs(wl, wl.steps, 1)
-    pooled = Rig(wl, slots=4, fast=False)
+    pooled = Rig(wl, slots=4, fast=False, one_call=one_call)
     out_p = _run(pooled, trace, xs, ws)
     st = pooled.pool.stats()
     assert st["misses"] > 0 and st["hits"] > st["misses"]
@@ -65,12 +72,13 @@ def test_tiny_f32_full_trace_and_resident_identity():
     resident.close()
 
 
-def test_olmoe_bf16_and_resident_identity():
+@ONE_CALL
+def test_olmoe_bf16_and_resident_identity(one_call):
     wl = synth.WORKLOADS["olmoe_bf16_e64"].with_(layers=2)
     steps = 12
     trace = synth.make_trace(wl, steps=steps)
     xs, ws = _inputs(wl, steps, 1)
-    pooled = Rig(wl, slots=16)
+    pooled = Rig(wl, slots=16, one_call=one_call)
     out_p = _run(pooled, trace, xs, ws)
     resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
     out_r = _run(resident, trace, xs, ws, check_every=steps)
@@ -79,12 +87,13 @@ def test_olmoe_bf16_and_resident_identity():
     resident.close()
 
 
-def test_fanout_int4_and_resident_identity():
+@ONE_CALL
+def test_fanout_int4_and_resident_identity(one_call):
     wl = synth.WORKLOADS["fanout_int4_e512"].with_(layers=1)
     steps = 6
     trace = synth.make_trace(wl, steps=steps)
     xs, ws = _inputs(wl, steps, 1)
-    pooled = Rig(wl, slots=16)
+    pooled = Rig(wl, slots=16, one_call=one_call)
     out_p = _run(pooled, trace, xs, ws)
     resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
     out_r = _run(resident, trace, xs, ws, check_every=steps)
@@ -96,7 +105,8 @@ def test_fanout_int4_and_resident_identity():
 @pytest.mark.parametrize("wtype,atype", [("f32", "f32"), ("bf16", "bf16"), ("int4", "bf16"),
                                          ("bf16", "f32")])
 @pytest.mark.parametrize("T", [1, 3])
-def test_backend_matrix(wtype, atype, T):
+@ONE_CALL
+def test_backend_matrix(wtype, atype, T, one_call):
     """dtype x ubatch x {cold, full eviction, hit + reload, reset}: pooled equals
     all-resident bit for bit, and both are within tolerance of the oracle."""
     wl = synth.Workload("matrix", 1, 24, 3, 256, 128, 6, T, 0, wtype, atype, 1.0, 0.0, 0, 7)
@@ -108,8 +118,8 @@ def test_backend_matrix(wtype, atype, T):
     seq = cold + evict + hit_reload
     trace = np.stack(seq)[:, None].astype(np.int32)                           # [S, 1, T, K]
     xs, ws = _inputs(wl, len(seq), T)
-    pooled = Rig(wl, slots=6, fast=False, std=0.05)
-    resident = Rig(wl, slots=6, resident=True, experts=pooled.experts)
+    pooled = Rig(wl, slots=6, fast=False, std=0.05, one_call=one_call)
+    resident = Rig(wl, slots=6, resident=True, experts=pooled.experts, one_call=one_call)
     out_p = _run(pooled, trace, xs, ws)
     out_r = _run(resident, trace, xs, ws)
     _assert_bitwise(out_p, out_r, "pooled vs resident")
@@ -120,14 +130,15 @@ def test_backend_matrix(wtype, atype, T):
     resident.close()
 
 
-def test_fallback_bitwise_equal_to_no_pool():
+@ONE_CALL
+def test_fallback_bitwise_equal_to_no_pool(one_call):
     """Bypass control: with a pool allocated, steps that overflow it take the
     selective-copy path and produce exactly what a pool of size 0 produces."""
     wl = synth.Workload("bypass", 1, 32, 4, 256, 128, 6, 2, 0, "bf16", "bf16", 1.0, 0.0, 0, 8)
     trace = synth.make_trace(wl, steps=30)
     xs, ws = _inputs(wl, 30, 2)
-    pooled = Rig(wl, slots=6)
-    nopool = Rig(wl, slots=0, experts=pooled.experts)
+    pooled = Rig(wl, slots=6, one_call=one_call)
+    nopool = Rig(wl, slots=0, experts=pooled.experts, one_call=one_call)
     ref_lru = LayerLRU(32, 6)
     out_p = _run(pooled, trace, xs, ws)
     out_n = _run(nopool, trace, xs, ws, check_every=100)
@@ -143,13 +154,14 @@ def test_fallback_bitwise_equal_to_no_pool():
     nopool.close()
 
 
-def test_evict_and_use_in_same_step_reads_fresh_table():
+@ONE_CALL
+def test_evict_and_use_in_same_step_reads_fresh_table(one_call):
     """The llama.cpp stale-table failure: a miss evicts a slot and the same step
     reads it; the output must use the new expert's weights."""
     wl = synth.Workload("stale", 1, 8, 2, 256, 128, 2, 1, 0, "bf16", "bf16", 1.0, 0.0, 0, 9)
     trace = np.array([[[[0, 1]]], [[[1, 5]]], [[[5, 0]]], [[[2, 3]]]], np.int32)
     xs, ws = _inputs(wl, 4, 1)
-    rig = Rig(wl, slots=2, fast=False, std=0.05)
+    rig = Rig(wl, slots=2, fast=False, std=0.05, one_call=one_call)
     _run(rig, trace, xs, ws)
     assert rig.pool.stats()["misses"] == 2 + 1 + 1 + 2
     rig.close()
@@ -161,7 +173,7 @@ def test_residual_and_multi_token():
     xs, ws = _inputs(wl, 10, 3)
     _, _, rx, _ = synth.streams(wl.with_(seed=11))
     resid = [synth.draw_activations(rx, (3, wl.hidden), "bf16") for _ in range(10)]
-    rig = Rig(wl, slots=8)
+    rig = Rig(wl, slots=8, one_call=True)
     _run(rig, trace, xs, ws, resid=resid)
     rig.close()
 

@@ -2,11 +2,13 @@
 bit-exact against the oracle.  Re-creates the page-1 unit list (vLLM PR "Run MoE
 models exceeding VRAM via expert CPU offloading with GPU cache", test results) and
 the llama.cpp discussion's checks (bypass control, stale map table)."""
+import time
+
 import numpy as np
 import pytest
 import torch
 
-from _gpu_helpers import DEV, Rig
+from _gpu_helpers import DEV, Rig, check_close, from_dev_act, to_dev_act
 from expert_slot_cache_amd import binding, synth
 from oracle.lru import FALLBACK, POOL, LayerLRU
 
@@ -179,6 +181,66 @@ def test_out_of_range_id_rejected_state_untouched():
     now = rig.pool.state(0), rig.pool.stats(0)
     assert all((a == b).all() for a, b in zip(snap[0], now[0])) and snap[1] == now[1]
     rig.close()
+
+
+def test_step_out_of_range_id_rejected_then_resumes():
+    """The one-call step launches its forward before the ids are checked: a bad id
+    must still be reported, leave the slot state untouched, and leave nothing
+    waiting on the device -- the next step runs at once and is correct."""
+    wl = SMALL_BF16.with_(layers=1)
+    rig = Rig(wl, slots=4, one_call=True)
+    rng = synth.streams(wl)[2]
+    x = synth.draw_activations(rng, (1, wl.hidden), "bf16")
+    w = synth.draw_gate_weights(rng, (1, wl.top_k))
+    xd, wd = to_dev_act(x, "bf16"), torch.from_numpy(w).to(DEV)
+    ok = np.array([[1, 2, 3, 4]], np.int32)
+    rig.step(0, ok, xd, wd)
+    snap = [a.copy() for a in rig.pool.state(0)], rig.pool.stats(0)
+    out = torch.empty((1, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    s = torch.empty((1, wl.top_k), dtype=torch.int32, device=DEV)
+    for bad in ([[1, 2, 3, 32]], [[-1, 2, 3, 4]]):
+        with pytest.raises(binding.ExpertRangeError):
+            rig.pool.step(0, torch.tensor(bad, dtype=torch.int32, device=DEV), 1, s, xd, wd, out)
+    now = rig.pool.state(0), rig.pool.stats(0)
+    assert all((a == b).all() for a, b in zip(snap[0], now[0])) and snap[1] == now[1]
+    with pytest.raises(binding.StateError):          # the failed step prepared nothing
+        rig.pool.forward(0, xd, s, wd, out, 1)
+    t0 = time.perf_counter()
+    ids = np.array([[4, 5, 6, 1]], np.int32)
+    _, misses, _, got = rig.step(0, ids, xd, wd)
+    torch.cuda.synchronize()
+    assert time.perf_counter() - t0 < 2.0
+    assert sorted(m[0] for m in misses) == [5, 6]
+    check_close(from_dev_act(got), rig.reference(0, x, ids, w), "bf16", "bf16", "after a rejected step")
+    rig.close()
+
+
+def test_mixed_call_styles_share_staging():
+    """Layers driven by one-call steps and by prepare + forward, interleaved, with
+    small pools so that several layers fall back into the shared staging area:
+    bit-identical to the all-resident layers, and the miss/fallback counts match
+    the oracle LRU."""
+    wl = synth.Workload("mixed", 3, 24, 4, 256, 128, 5, 2, 0, "bf16", "bf16", 1.1, 0.4, 0, 21)
+    trace = synth.make_trace(wl, steps=16)
+    rng = synth.streams(wl)[2]
+    xs = [synth.draw_activations(rng, (2, wl.hidden), "bf16") for _ in range(16)]
+    ws = [synth.draw_gate_weights(rng, (2, wl.top_k)) for _ in range(16)]
+    mixed = Rig(wl, slots=5)
+    res = Rig(wl, slots=5, resident=True, experts=mixed.experts)
+    refs = [LayerLRU(wl.experts, 5) for _ in range(wl.layers)]
+    for s_ in range(16):
+        xd, wd = to_dev_act(xs[s_], "bf16"), torch.from_numpy(ws[s_]).to(DEV)
+        for l in range(wl.layers):
+            mixed.one_call = (s_ + l) % 2 == 0
+            path, misses, _, got = mixed.step(l, trace[s_, l], xd, wd)
+            _, _, _, want = res.step(l, trace[s_, l], xd, wd)
+            r = refs[l].step(trace[s_, l])
+            assert path == r.path and misses == r.misses, (s_, l)
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (s_, l)
+    st = mixed.pool.stats()
+    assert st["fallbacks"] == sum(r.fallbacks for r in refs) > 0
+    mixed.close()
+    res.close()
 
 
 def test_forward_without_prepare_is_state_error():
