@@ -72,7 +72,24 @@ def parse():
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget for the oracle's CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 256 MiB 4 times (for scaling the HBM "
+                         "traffic counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(torch, dev):
+    """A plain elementwise device copy of exactly 256 MiB (read 256 MiB, write 256 MiB),
+    launched 4 times: the reference reading for FETCH_SIZE / WRITE_SIZE."""
+    n = (256 << 20) // 4
+    src = torch.full((n,), 7, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        torch.add(src, 0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise int32 copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 4}), flush=True)
 
 
 def link_peak_gbps(torch, dev, nbytes: int) -> float:
@@ -256,6 +273,9 @@ def main():
     from expert_slot_cache_amd import binding
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     if args.layers:
         wl = wl.with_(layers=args.layers)

@@ -30,8 +30,8 @@ hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32
                            hipStream_t stream);
 
 // Per-layer publication of a step's decision, in host-mapped memory (64 bytes).
-// The host (or a copy stream, once the step's copies have landed) writes `seq`
-// last; status and n_upd are valid once seq matches.
+// The host writes it once the step's copies have landed, `seq` last; status and
+// n_upd are valid once seq matches.
 struct Gate {
     uint32_t seq;
     int32_t status;   // PATH_POOL, PATH_STAGE or PATH_NONE
@@ -53,6 +53,13 @@ enum { PATH_POOL = 0, PATH_STAGE = 1, PATH_NONE = 2 };
 hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* rank, const int32_t* upd,
                         int n_upd, int status, Gate* gate, uint32_t seq, unsigned long long limit, int32_t* out,
                         int32_t* path, hipStream_t stream);
+
+// Distinct ids and remap of one decode-sized step in one launch (n <= 1024):
+// rb as launch_distinct writes it, then out/path as launch_remap writes them
+// (the ranks of PATH_STAGE come from this step's distinct list).
+hipError_t launch_route(const int32_t* ids, int n, int E, uint32_t* rb, uint32_t tag, int32_t* table,
+                        const int32_t* upd, int n_upd, int status, Gate* gate, uint32_t seq,
+                        unsigned long long limit, int32_t* out, int32_t* path, hipStream_t stream);
 
 // Optional event pairs around the two projection stages (any may be null).
 struct StageEvents {

@@ -15,8 +15,8 @@
 //   4. the step's map changes go to a small pinned list that k_remap reads: it
 //      applies them to the persistent HBM table and remaps through the fresh table.
 //      The compute stream waits for the copies (an event per copy stream), or, in
-//      the gated one-call step, the remap waits until the copy stream publishes
-//      the step's sequence number.
+//      the gated one-call step, the host waits for them and then publishes the
+//      step's decision and sequence number, which the pre-launched remap awaits.
 //   5. forward kernels on the compute stream.
 #include <hip/hip_runtime.h>
 
@@ -269,12 +269,11 @@ void harvest_all(moe_pool* p) {
     for (auto& L : p->layers) harvest_layer(p, L);
 }
 
-// Enqueue host->HBM copies of the experts (src -> dst pairs) on the copy streams and
-// make the compute stream wait for them (join) -- or, for a gated step, make the
-// first copy stream used wait for all of them and then publish `seq` to the
-// layer's gate (a stream-ordered 32-bit write into the host-mapped gate).
+// Enqueue host->HBM copies of the experts (src -> dst pairs) on the copy streams,
+// record each used stream's copy_done event, and, if `join`, make the compute
+// stream wait for those events.
 moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, const char*>>& jobs,
-                          bool join, uint32_t seq) {
+                          bool join) {
     if (jobs.empty()) return MOE_OK;
     const int ns = (int)p->copy.size();
     const size_t eb = p->lay.total;
@@ -291,7 +290,6 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
         }
         p->used_copy[s] = 1;
     }
-    const int first = p->copy_rr;
     int rr = p->copy_rr;
     for (const auto& j : jobs) {
         for (size_t off = 0; off < eb; off += chunk) {
@@ -309,12 +307,8 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
             L.copy_t[s].pending = true;
         }
         HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
-        if (join)
-            HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
-        else if (s != first)
-            HIPCHK(hipStreamWaitEvent(p->copy[first], p->copy_done[s], 0));
+        if (join) HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
     }
-    if (!join) HIPCHK(hipStreamWriteValue32(p->copy[first], &L.gate_dev->seq, seq, 0));
     L.bytes_h2d += (uint64_t)eb * jobs.size();
     return MOE_OK;
 }
@@ -347,13 +341,18 @@ moe_status_t check_gate(LayerState& L, int32_t layer) {
     return MOE_OK;
 }
 
+// The next readback: zero the words the last one used and take a new tag.
+void next_readback(moe_pool* p) {
+    std::memset(p->rb_host, 0, (size_t)p->rb_used * 4);
+    p->rb_tag = p->rb_tag % ((1u << 18) - 1) + 1;
+    p->rb_used = 0;
+}
+
 // Distinct ids of the step, written by the kernel as tagged words into pinned host
 // memory (zeroed here beforehand) and rank[] on the device.
 moe_status_t launch_distinct_ids(moe_pool* p, const int32_t* ids_dev, int n) {
-    std::memset(p->rb_host, 0, (size_t)p->rb_used * 4);
-    p->rb_tag = p->rb_tag % ((1u << 18) - 1) + 1;
+    next_readback(p);
     HIPCHK(moe::launch_distinct(ids_dev, n, p->cfg.n_experts, p->rb_dev, p->rank_dev, p->rb_tag, p->compute));
-    p->rb_used = 0;
     return MOE_OK;
 }
 
@@ -406,17 +405,16 @@ moe_status_t read_distinct(moe_pool* p, int32_t layer, int32_t* D_out) {
 
 // The LRU step over p->ulist[0..D), the map-change list and the miss copies.
 // join: the compute stream waits for the copies (two-call flow); otherwise the
-// copies publish `seq` to the layer's gate when they land (gated flow; the caller
-// publishes when there are none).
-moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, bool join, uint32_t seq,
-                   int32_t* the_path, int32_t* n_upd_out, bool* published = nullptr) {
+// caller waits for them (wait_copies) before it publishes the step (gated flow).
+moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, bool join, int32_t* the_path,
+                   int32_t* n_upd_out, bool* copied) {
     const size_t eb = p->lay.total;
     const int32_t* u = p->ulist.data();
     moe_status_t st;
     p->misses.clear();
     *the_path = MOE_PATH_POOL;
     *n_upd_out = 0;
-    if (published) *published = false;
+    *copied = false;
     // The readback has seen this step's distinct kernel finish, and with it every
     // earlier kernel of the compute stream: no reads of a destination are pending,
     // so the copies wait for nothing.
@@ -446,10 +444,9 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
             std::vector<std::pair<char*, const char*>> jobs;
             jobs.reserve(p->misses.size());
             for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.expert(m.expert, eb));
-            if (!join) publish_fields(L, moe::PATH_POOL, n_upd);
-            st = issue_copies(p, L, jobs, join, seq);
+            st = issue_copies(p, L, jobs, join);
             if (st) return st;
-            if (published) *published = !join;
+            *copied = true;
         }
     } else {
         // selective-copy fallback: the step's experts go to staging in rank order;
@@ -458,12 +455,27 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
         std::vector<std::pair<char*, const char*>> jobs;
         jobs.reserve(D);
         for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.expert(u[r], eb));
-        if (!join) publish_fields(L, moe::PATH_STAGE, 0);
-        st = issue_copies(p, L, jobs, join, seq);
+        st = issue_copies(p, L, jobs, join);
         if (st) return st;
-        if (published) *published = !join;
+        *copied = true;
         L.staged += (uint64_t)D;
         p->staging_owner = layer;
+    }
+    return MOE_OK;
+}
+
+// Host wait for the copies issue_copies just queued (their copy_done events).  The
+// gated step publishes only after this, so no kernel ever waits on work of another
+// stream: the step stays correct where dispatches are serialised (profilers).
+moe_status_t wait_copies(moe_pool* p) {
+    for (size_t s = 0; s < p->copy.size(); ++s) {
+        if (!p->used_copy[s]) continue;
+        for (;;) {
+            const hipError_t q = hipEventQuery(p->copy_done[s]);
+            if (q == hipSuccess) break;
+            if (q != hipErrorNotReady) FAIL(MOE_EHIP, "copy event query failed: %s", hipGetErrorString(q));
+            __builtin_ia32_pause();
+        }
     }
     return MOE_OK;
 }
@@ -760,7 +772,8 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
     // 2. route + LRU; 3. misses: store -> slot on the copy streams, after this
     // layer's last reads; 4. the remap (map changes applied first)
     int32_t the_path = MOE_PATH_POOL, n_upd = 0;
-    st = route(p, L, layer, D, n, true, 0, &the_path, &n_upd);
+    bool copied = false;
+    st = route(p, L, layer, D, n, true, &the_path, &n_upd, &copied);
     if (st) return st;
     int32_t* table = p->cfg.resident ? p->ident_dev : L.map_dev;
     const int status = the_path == MOE_PATH_FALLBACK ? moe::PATH_STAGE : moe::PATH_POOL;
@@ -795,12 +808,12 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
         if (st) return st;
         return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
     }
-    // Decode-sized steps launch everything before the readback: distinct ids, a
-    // remap that waits on the layer's gate, and the forward kernels.  The host then
-    // reads the distinct ids back, runs the LRU, queues the miss copies and
-    // publishes the decision (from the copy stream once the copies have landed, or
-    // at once when there are none), so the kernels' launch latency overlaps the
-    // host's work and the copies.
+    // Decode-sized steps launch everything before the readback: one kernel for the
+    // distinct ids and a remap that waits on the layer's gate, then the forward
+    // kernels.  The host then
+    // reads the distinct ids back, runs the LRU, queues the miss copies, waits for
+    // them to land, and publishes the decision to the gate, so the kernels' launch
+    // latency overlaps the host's work and the copies.
     moe_status_t st = check_layer(p, layer);
     if (st) return st;
     if (!topk_ids_dev || !slot_ids_dev) FAIL(MOE_EINVAL, "null ids");
@@ -812,17 +825,16 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
     const int32_t E = p->cfg.n_experts;
     const int n = n_tokens * p->cfg.top_k;
     const bool gated = !p->cfg.resident;
-    st = launch_distinct_ids(p, topk_ids_dev, n);
-    if (st) return st;
+    next_readback(p);
     uint32_t seq = 0;
     if (gated) {
         seq = ++L.gate_seq;
         if (seq == 0) seq = ++L.gate_seq;   // 0 is the gate's initial value
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, L.map_dev, p->rank_dev, L.upd_dev, 0, 0, L.gate_dev, seq,
-                                 p->gate_limit, slot_ids_dev, L.path_dev, p->compute));
+        HIPCHK(moe::launch_route(topk_ids_dev, n, E, p->rb_dev, p->rb_tag, L.map_dev, L.upd_dev, 0, 0, L.gate_dev,
+                                 seq, p->gate_limit, slot_ids_dev, L.path_dev, p->compute));
     } else {
-        HIPCHK(moe::launch_remap(topk_ids_dev, n, E, p->ident_dev, p->rank_dev, L.upd_dev, 0, moe::PATH_POOL,
-                                 nullptr, 0, 0, slot_ids_dev, L.path_dev, p->compute));
+        HIPCHK(moe::launch_route(topk_ids_dev, n, E, p->rb_dev, p->rb_tag, p->ident_dev, L.upd_dev, 0,
+                                 moe::PATH_POOL, nullptr, 0, 0, slot_ids_dev, L.path_dev, p->compute));
     }
     // From here on a gated remap is queued: every exit publishes a decision, so
     // that the kernel never waits out its limit.
@@ -841,12 +853,15 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
     st = read_distinct(p, layer, &D);
     if (st) return abort_gate(st);
     int32_t the_path = MOE_PATH_POOL, n_upd = 0;
-    bool by_copy = false;
-    st = route(p, L, layer, D, n, false, seq, &the_path, &n_upd, &by_copy);
-    published = published || by_copy;
+    bool copied = false;
+    st = route(p, L, layer, D, n, false, &the_path, &n_upd, &copied);
     if (st) return abort_gate(st);
+    if (copied) {
+        st = wait_copies(p);
+        if (st) return abort_gate(st);
+    }
     if (!published) {
-        publish_fields(L, moe::PATH_POOL, n_upd);
+        publish_fields(L, the_path == MOE_PATH_FALLBACK ? moe::PATH_STAGE : moe::PATH_POOL, n_upd);
         publish_seq(L, seq);
         published = true;
     }
