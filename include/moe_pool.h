@@ -215,7 +215,16 @@ moe_status_t moe_pool_forward(moe_pool_t* pool, int32_t layer, const void* x_dev
                               const void* resid_dev, int32_t n_tokens, void* out_dev);
 
 /* prepare + forward of one layer in one call (same arguments, same semantics,
- * same errors), for callers that run the two back to back. */
+ * same errors and the same bits), for callers that run the two back to back.
+ * For n_tokens <= 8 the call queues its kernels before it blocks: one kernel
+ * computes the distinct ids and then waits (on the GPU) for the host's decision,
+ * and the forward kernels follow it on the stream.  The host reads the ids back,
+ * runs the LRU, issues the miss copies, waits for them to land and publishes the
+ * decision ([llama-pool] Design item 3: the map table is rewritten before the
+ * remap reads it).  If the call fails after queueing, it publishes "no expert"
+ * so the queued kernels finish at once; out_dev is then undefined.  A kernel that
+ * waited past its limit (10 s + 1 s per GB the step can copy) makes the next
+ * call on the layer fail with EHIP. */
 moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev,
                            const void* resid_dev, void* out_dev, moe_miss_t* miss_host, int32_t miss_cap,
