@@ -346,6 +346,15 @@ struct SlotReader {
     }
 };
 
+// Activation-sized reads of a buffer, by byte offset (data written by an earlier
+// kernel).
+struct PlainMem {
+    const char* p;
+    __device__ __forceinline__ explicit PlainMem(const void* base) : p(static_cast<const char*>(base)) {}
+    __device__ __forceinline__ uint4 ld16(size_t off) const { return *reinterpret_cast<const uint4*>(p + off); }
+    __device__ __forceinline__ uint2 ld8(size_t off) const { return *reinterpret_cast<const uint2*>(p + off); }
+};
+
 // The base and slot count of the step's path (see Slots).
 __device__ __forceinline__ void pick_slots(const Slots& sl, const char*& base, int& n) {
     const int p = *sl.path;
@@ -353,11 +362,28 @@ __device__ __forceinline__ void pick_slots(const Slots& sl, const char*& base, i
     n = p == PATH_POOL ? sl.npool : (p == PATH_STAGE ? sl.nstage : 0);
 }
 
-// Sum over the G lanes of a group (G a power of two); every lane of the group
-// ends with the same value.
-__device__ __forceinline__ float group_sum(float v, int G) {
-    for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+// The wave's index in its workgroup, as a value the compiler knows is uniform
+// across the wave: addresses derived from it (slot ids, buffer resources) stay in
+// scalar registers instead of forcing a per-lane loop around every buffer load.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Sum over the G lanes of a group (G a power of two) of N values at once; every
+// lane of the group ends with the same values, in a fixed butterfly order (G/2,
+// G/4, ..., 1).  The offsets are constants and the N exchanges of a step are
+// independent, so the steps' cross-lane round trips overlap instead of running one
+// reduction after another (the guard on G is uniform across the wave).
+template <int N>
+__device__ __forceinline__ void group_sum_n(float (&v)[N], int G) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        if (off < G) {
+            float o[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) o[i] = __shfl_xor(v[i], off, 64);
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] += o[i];
+        }
+    }
 }
 
 // ---- activation chunks held in registers ------------------------------------
@@ -377,24 +403,22 @@ template <int WT>
 struct XChunk<WT, XT_F32> {
     static constexpr int N = WTraits<WT>::EPC;
     float v[N];
-    // element e0 .. e0+N-1 of a vector of type AT
-    template <int AT>
-    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
+    // element e0 .. e0+N-1 of a vector of type AT, read through m (byte offsets)
+    template <int AT, class M>
+    __device__ __forceinline__ void load(const M& m, size_t e0) {
         if (AT == A_F32) {
-            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e0);
 #pragma unroll
             for (int q = 0; q < N / 4; ++q) {
-                const float4 f = p[q];
-                v[4 * q] = f.x;
-                v[4 * q + 1] = f.y;
-                v[4 * q + 2] = f.z;
-                v[4 * q + 3] = f.w;
+                const uint4 f = m.ld16((e0 + 4 * q) * 4);
+                v[4 * q] = __uint_as_float(f.x);
+                v[4 * q + 1] = __uint_as_float(f.y);
+                v[4 * q + 2] = __uint_as_float(f.z);
+                v[4 * q + 3] = __uint_as_float(f.w);
             }
         } else {
-            const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + e0);
 #pragma unroll
             for (int q = 0; q < N / 4; ++q) {
-                const uint2 u = p[q];
+                const uint2 u = m.ld8((e0 + 4 * q) * 2);
                 v[4 * q] = bf16_lo(u.x);
                 v[4 * q + 1] = bf16_hi(u.x);
                 v[4 * q + 2] = bf16_lo(u.y);
@@ -407,9 +431,9 @@ struct XChunk<WT, XT_F32> {
 template <>
 struct XChunk<W_BF16, XT_BF16> {
     uint4 v;
-    template <int AT>
-    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
-        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+    template <int AT, class M>
+    __device__ __forceinline__ void load(const M& m, size_t e0) {
+        v = m.ld16(e0 * 2);
     }
 };
 
@@ -417,13 +441,12 @@ template <>
 struct XChunk<W_INT4, XT_I4> {
     uint32_t p[16];
     float sx;
-    template <int AT>
-    __device__ __forceinline__ void load(const void* __restrict__ base, size_t e0) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+    template <int AT, class M>
+    __device__ __forceinline__ void load(const M& m, size_t e0) {
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {        // word i: elements 8i .. 8i+7
-            const uint4 u = src[i];
+            const uint4 u = m.ld16((e0 + 8 * i) * 2);
             p[4 * i + 0] = (u.x & 0xFFFFu) | (u.z << 16);          // (x0, x4)
             p[4 * i + 1] = (u.x >> 16) | (u.z & 0xFFFF0000u);      // (x1, x5)
             p[4 * i + 2] = (u.y & 0xFFFFu) | (u.w << 16);          // (x2, x6)
@@ -478,7 +501,6 @@ __device__ __forceinline__ float cdot(const uint4 w, const XChunk<W_INT4, XT_I4>
     return acc - 136.0f * x.sx;
 }
 
-
 // act element type written by the w13 stage: bf16 for bf16 / int4 weights
 template <int WT>
 struct ActOf {
@@ -500,34 +522,41 @@ __device__ __forceinline__ void store_act(void* __restrict__ p, size_t i, float 
 // LDS (red) and are added in part order.  One call covers row block `rblk` of
 // pair `pair` with the workgroup's 4 waves:
 // act[pair][i] = silu(W13[s][i] . x[t]) * (W13[s][I + i] . x[t])
+// G = 1 << gs lanes share a row.  The slot id and the path word are read first, side by
+// side: they are the only loads the weight addresses depend on.
 template <int WT, int AT, int CPL, int RP, int WPR>
 __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const int32_t* __restrict__ slot_ids,
-                                         const void* __restrict__ x, int K, int H, int I, int G, size_t off_w,
-                                         size_t off_s, void* __restrict__ act, int pair, int rblk,
+                                         const void* __restrict__ x, int H, int I, int gs, size_t off_w,
+                                         size_t off_s, void* __restrict__ act, int t, int pair, int rblk,
                                          float (*red)[2][RP]) {
     using X = XChunk<WT, XSel<WT, AT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int gl = lane & (G - 1);
-    const int groups = 64 / G;
-    const int grp = lane / G;
-    const int part = wave % WPR;
-    const int t = pair / K;
-    const int i0 = ((rblk * (4 / WPR) + wave / WPR) * groups + grp) * RP;
-    if (WPR == 1 && i0 >= I) return;           // whole lane groups retire together
+    const int slot = slot_ids[pair];
     const char* wbase;
     int nslots;
     pick_slots(sl, wbase, nslots);
-    const int slot = slot_ids[pair];
-    const bool ok = slot >= 0 && slot < nslots;
+    const int G = 1 << gs;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int gl = lane & (G - 1);
+    const int groups = 64 >> gs;
+    const int grp = lane >> gs;
+    const int part = wave % WPR;
+    const int i0 = ((rblk * (4 / WPR) + wave / WPR) * groups + grp) * RP;
+    // lane groups past the last row skip their loads; no early return, which would
+    // let the compiler sink the slot and path loads below it
+    const bool ok = slot >= 0 && slot < nslots && i0 < I;
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
+    // the slot's address in scalar registers before the branch, so that the
+    // arguments it needs are loaded with the others (one round trip, not two)
+    const char* ebase = wbase + (size_t)slot * stride;
+    __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
 
     float pg[RP], pu[RP];
     if (ok) {
-        const SlotReader rd(wbase + (size_t)slot * stride, stride);
+        const SlotReader rd(ebase, stride);
         uint4 wg[RP][CPL], wu[RP][CPL];
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
@@ -558,7 +587,10 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
         X xv[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
-            xv[j].template load<AT>(x, (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+            xv[j].template load<AT>(PlainMem(x), (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+        // every load of the lane is in flight before the first use: the scheduler
+        // would otherwise hold some back to save registers (two round trips)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
             float a = 0.0f, b = 0.0f;
@@ -573,8 +605,20 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
                 a += dg;
                 b += du;
             }
-            pg[p] = group_sum(a, G);
-            pu[p] = group_sum(b, G);
+            pg[p] = a;
+            pu[p] = b;
+        }
+        float gu[2 * RP];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            gu[2 * p] = pg[p];
+            gu[2 * p + 1] = pu[p];
+        }
+        group_sum_n<2 * RP>(gu, G);
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            pg[p] = gu[2 * p];
+            pu[p] = gu[2 * p + 1];
         }
     } else {
 #pragma unroll
@@ -606,93 +650,123 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
             if (i0 + p < I) store_act<ACT>(act, (size_t)pair * I + i0 + p, ok ? silu(pg[p]) * pu[p] : 0.0f);
 }
 
-// grid.x: row blocks; grid.y: (t, k) pairs.
+// grid.x: row blocks; grid.y: k; grid.z: tokens.
 template <int WT, int AT, int CPL, int RP, int WPR>
 __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const int32_t* __restrict__ slot_ids,
-                                                  const void* __restrict__ x, int K, int H, int I, int G,
+                                                  const void* __restrict__ x, int H, int I, int gs,
                                                   size_t off_w, size_t off_s, void* __restrict__ act) {
     __shared__ float red[4][2][RP];
-    w13_rows<WT, AT, CPL, RP, WPR>(sl, stride, slot_ids, x, K, H, I, G, off_w, off_s, act, blockIdx.y, blockIdx.x,
-                                   red);
+    w13_rows<WT, AT, CPL, RP, WPR>(sl, stride, slot_ids, x, H, I, gs, off_w, off_s, act, blockIdx.z,
+                                   blockIdx.z * gridDim.y + blockIdx.y, blockIdx.x, red);
 }
 
 // ---- w2 + ordered top-k combine ------------------------------------------------
-// grid.x: blocks of RB = RP * (64 / G) output rows; grid.y: tokens.  The block's
-// waves take the K * WPR (expert, part) tasks in turn: y_k[r] = W2[s_k][r] .
-// act[t*K + k] (part sums) goes to LDS, then
+// A workgroup owns RB = RP * (64 / G) output rows of one token.  Its waves take the
+// K * WPR (expert, part) tasks in turn: y_k[r] = W2[s_k][r] . act[t*K + k] (part
+// sums) goes to LDS, then
 // out[t][r] = resid[t][r] + sum_{k = 0..K-1} w[t][k] * y_k[r]   (k in order).
-template <int WT, int AT, int CPL, int RP, int WPR, int NWMAX>
-__global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stride,
-                                                           const int32_t* __restrict__ slot_ids,
-                                                           const float* __restrict__ topk_w,
-                                                           const void* __restrict__ act,
-                                                           const void* __restrict__ resid, void* __restrict__ out,
-                                                           int K, int H, int I, int G, size_t off_w, size_t off_s) {
-    extern __shared__ float ys[];               // [K][WPR][RB]
+// A task is split into its weight fetch (which does not depend on act) and the
+// rest, so that the one-launch form can issue the fetch before its grid barrier.
+
+// Weight registers of one (expert, part) task of a lane: RP rows x CPL chunks.
+template <int WT, int CPL, int RP>
+struct W2Task {
+    uint4 w[RP][CPL];
+    float sc[RP][CPL];   // int4 group scales (unused otherwise)
+    int pair;            // t * K + k
+    int part;
+    bool ok;             // the pair's slot id is valid
+};
+
+// Lane geometry of a w2 workgroup.
+struct W2Lane {
+    int gl, grp, RB, r0;
+};
+
+__device__ __forceinline__ W2Lane w2_lane(int gs, int RP, int rb0) {
+    const int lane = threadIdx.x & 63;
+    W2Lane g;
+    g.gl = lane & ((1 << gs) - 1);
+    g.grp = lane >> gs;
+    g.RB = RP * (64 >> gs);
+    g.r0 = rb0 + g.grp * RP;
+    return g;
+}
+
+// `slot` is slot_ids[t * K + task / WPR], loaded by the caller (so that it can be
+// read together with the path word, before any branch).
+template <int WT, int CPL, int RP, int WPR>
+__device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wbase, int nslots, size_t stride,
+                                         int slot, int t, int K, int H, int I, int gs, const W2Lane& ln, int task,
+                                         size_t off_w, size_t off_s) {
+    const int G = 1 << gs;
+    const int k = task / WPR;
+    tk.part = task - k * WPR;
+    tk.pair = t * K + k;
+    tk.ok = slot >= 0 && slot < nslots;
+    const char* ebase = wbase + (size_t)slot * stride;
+    __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
+    if (!tk.ok) return;
+    const size_t row_bytes = (size_t)CPL * G * WPR * 16;
+    const int spr = I / 128;
+    const SlotReader rd(ebase, stride);
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+        const size_t row = off_w + (size_t)min(ln.r0 + p, H - 1) * row_bytes;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) tk.w[p][j] = rd.load16(row + (size_t)((tk.part * CPL + j) * G + ln.gl) * 16);
+    }
+    if (WT == W_INT4) {
+#pragma unroll
+        for (int p = 0; p < RP; ++p)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+                tk.sc[p][j] = rd.scale(off_s + ((size_t)min(ln.r0 + p, H - 1) * spr +
+                                                (((tk.part * CPL + j) * G + ln.gl) >> 2)) * 2);
+    }
+}
+
+// The dot products of a fetched task against its act row (read through m); the
+// RP results go to ys[task][grp * RP + p].
+template <int WT, int CPL, int RP, class M>
+__device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M& m, int I, int gs,
+                                          const W2Lane& ln, float* __restrict__ yk) {
+    const int G = 1 << gs;
     constexpr int ACT = ActOf<WT>::AT;
     using X = XChunk<WT, XSel<WT, ACT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
-    const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int gl = lane & (G - 1);
-    const int groups = 64 / G;
-    const int grp = lane / G;
-    const int RB = RP * groups;
-    const int t = blockIdx.y;
-    const int rb0 = blockIdx.x * RB;
-    const int r0 = rb0 + grp * RP;
-    const int nc = CPL * G * WPR;
-    const size_t row_bytes = (size_t)nc * 16;
-    const int spr = I / 128;
-    const char* wbase;
-    int nslots;
-    pick_slots(sl, wbase, nslots);
-    for (int task = wave; task < K * WPR; task += nw) {
-        const int k = task / WPR;
-        const int part = task - k * WPR;
-        const int pair = t * K + k;
-        const int slot = slot_ids[pair];
-        float* yk = ys + (size_t)task * RB + grp * RP;
-        if (slot < 0 || slot >= nslots) {
-            if (gl == 0)
-                for (int p = 0; p < RP; ++p) yk[p] = 0.0f;
-            continue;
-        }
-        const SlotReader rd(wbase + (size_t)slot * stride, stride);
-        uint4 wr[RP][CPL];
+    if (!tk.ok) {
+        if (ln.gl == 0)
+            for (int p = 0; p < RP; ++p) yk[p] = 0.0f;
+        return;
+    }
+    X av[CPL];
 #pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            const size_t row = off_w + (size_t)min(r0 + p, H - 1) * row_bytes;
+    for (int j = 0; j < CPL; ++j)
+        av[j].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[RP];
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) wr[p][j] = rd.load16(row + (size_t)((part * CPL + j) * G + gl) * 16);
-        }
-        float sc[RP][CPL];
-        if (WT == W_INT4) {
+    for (int p = 0; p < RP; ++p) {
+        acc[p] = 0.0f;
 #pragma unroll
-            for (int p = 0; p < RP; ++p)
-#pragma unroll
-                for (int j = 0; j < CPL; ++j)
-                    sc[p][j] = rd.scale(off_s + ((size_t)min(r0 + p, H - 1) * spr + (((part * CPL + j) * G + gl) >> 2)) * 2);
-        }
-        X av[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-            av[j].template load<ACT>(act, (size_t)pair * I + (size_t)((part * CPL + j) * G + gl) * EPC);
-#pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                float d = cdot(wr[p][j], av[j]);
-                if (WT == W_INT4) d *= sc[p][j];
-                acc += d;
-            }
-            acc = group_sum(acc, G);
-            if (gl == 0) yk[p] = acc;
+        for (int j = 0; j < CPL; ++j) {
+            float d = cdot(tk.w[p][j], av[j]);
+            if (WT == W_INT4) d *= tk.sc[p][j];
+            acc[p] += d;
         }
     }
-    __syncthreads();
+    group_sum_n<RP>(acc, G);
+    if (ln.gl == 0)
+#pragma unroll
+        for (int p = 0; p < RP; ++p) yk[p] = acc[p];
+}
+
+// The ordered top-k sum of the workgroup's RB rows (after a barrier on ys).
+template <int AT>
+__device__ __forceinline__ void w2_combine(const float* __restrict__ ys, int RB, int WPR, int rb0, int t, int K,
+                                           int H, const float* __restrict__ topk_w, const void* __restrict__ resid,
+                                           void* __restrict__ out) {
     const float* wt = topk_w + (size_t)t * K;
     for (int i = threadIdx.x; i < RB; i += blockDim.x) {
         const int r = rb0 + i;
@@ -710,6 +784,44 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
         else
             static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(acc);
     }
+}
+
+// grid.x: blocks of RB output rows; grid.y: tokens.  ONE: the block has one wave
+// per (expert, part) task (K * WPR <= NWMAX), so a wave's slot is known before any
+// branch.
+template <int WT, int AT, int CPL, int RP, int WPR, int NWMAX, bool ONE>
+__global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stride,
+                                                           const int32_t* __restrict__ slot_ids,
+                                                           const float* __restrict__ topk_w,
+                                                           const void* __restrict__ act,
+                                                           const void* __restrict__ resid, void* __restrict__ out,
+                                                           int K, int H, int I, int gs, size_t off_w, size_t off_s) {
+    extern __shared__ float ys[];               // [K][WPR][RB]
+    const int nw = blockDim.x >> 6;
+    const int wave = wave_id();
+    const int t = blockIdx.y;
+    const W2Lane ln = w2_lane(gs, RP, blockIdx.x * (RP * (64 >> gs)));
+    const int rb0 = blockIdx.x * ln.RB;
+    const char* wbase;
+    int nslots;
+    if (ONE) {
+        // the wave's slot and the path word, side by side, before any branch
+        const int slot = slot_ids[t * K + wave / WPR];
+        pick_slots(sl, wbase, nslots);
+        W2Task<WT, CPL, RP> tk;
+        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, t, K, H, I, gs, ln, wave, off_w, off_s);
+        w2_finish<WT, CPL, RP>(tk, PlainMem(act), I, gs, ln, ys + (size_t)wave * ln.RB + ln.grp * RP);
+    } else {
+        pick_slots(sl, wbase, nslots);
+        for (int task = wave; task < K * WPR; task += nw) {
+            W2Task<WT, CPL, RP> tk;
+            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR], t, K, H, I, gs, ln,
+                                       task, off_w, off_s);
+            w2_finish<WT, CPL, RP>(tk, PlainMem(act), I, gs, ln, ys + (size_t)task * ln.RB + ln.grp * RP);
+        }
+    }
+    __syncthreads();
+    w2_combine<AT>(ys, ln.RB, WPR, rb0, t, K, H, topk_w, resid, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1022,6 +1134,12 @@ namespace {
 #define MOE_W2_RP64 2
 #endif
 
+int log2_of(int g) {
+    int s = 0;
+    while ((1 << s) < g) ++s;
+    return s;
+}
+
 int chunks_of(int wtype, int n) {
     const int epc = wtype == W_F32 ? 4 : (wtype == W_BF16 ? 8 : 32);
     return n / epc;
@@ -1052,33 +1170,38 @@ bool cpl_ok(int cpl) {
 template <int WT, int AT, int CPL, int RP, int WPR>
 hipError_t launch_w13(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
     const int rows_per_block = (4 / WPR) * (64 / G) * RP;
-    const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, a.T * g.K);
+    const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, g.K, a.T);
     if (ev && ev->w13_start)
         hipExtLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, ev->w13_start,
-                              ev->w13_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13,
+                              ev->w13_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.x, g.H, g.I, log2_of(G), g.off_w13,
                               g.off_s13, a.act);
     else
         hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, a.sl, g.slot_stride,
-                           a.slot_ids, a.x, g.K, g.H, g.I, G, g.off_w13, g.off_s13, a.act);
+                           a.slot_ids, a.x, g.H, g.I, log2_of(G), g.off_w13, g.off_s13, a.act);
     return hipGetLastError();
 }
 
 template <int WT, int AT, int CPL, int RP, int WPR>
 hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
-    constexpr int NWMAX = (WT == W_INT4) ? 8 : 16;
+    constexpr int NWMAX = 16;
     const int RB = (64 / G) * RP;
     const int tasks = g.K * WPR;
     const int nw = tasks < NWMAX ? tasks : NWMAX;
     const size_t lds = (size_t)tasks * RB * sizeof(float);
     const dim3 grid((g.H + RB - 1) / RB, a.T);
-    if (ev && ev->w2_start)
-        hipExtLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), (uint32_t)lds, s,
-                              ev->w2_start, ev->w2_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.topk_w, a.act,
-                              a.resid, a.out, g.K, g.H, g.I, G, g.off_w2, g.off_s2);
+    auto go = [&](auto kern) {
+        if (ev && ev->w2_start)
+            hipExtLaunchKernelGGL(kern, grid, dim3(64 * nw), (uint32_t)lds, s, ev->w2_start, ev->w2_stop, 0, a.sl,
+                                  g.slot_stride, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I,
+                                  log2_of(G), g.off_w2, g.off_s2);
+        else
+            hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, s, a.sl, g.slot_stride, a.slot_ids, a.topk_w, a.act,
+                               a.resid, a.out, g.K, g.H, g.I, log2_of(G), g.off_w2, g.off_s2);
+    };
+    if (tasks <= NWMAX)
+        go(k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX, true>);
     else
-        hipLaunchKernelGGL((k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX>), grid, dim3(64 * nw), lds, s, a.sl,
-                           g.slot_stride, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I, G, g.off_w2,
-                           g.off_s2);
+        go(k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX, false>);
     return hipGetLastError();
 }
 
@@ -1210,7 +1333,7 @@ hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents
     if (a.T <= 0) return hipSuccess;
     if (a.T > kDecodeMaxTokens && grouped_shape(g.wtype, g.H, g.I))
         return g.atype == A_F32 ? run_grouped<A_F32>(g, a, ev, stream) : run_grouped<A_BF16>(g, a, ev, stream);
-    if ((long)a.T * g.K > 65535) return hipErrorInvalidValue;   // grid.y of the w13 kernel
+    if (a.T > 65535) return hipErrorInvalidValue;   // grid.z of the w13 kernel, grid.y of the w2 kernel
     switch (g.wtype * 2 + g.atype) {
         case W_F32 * 2 + A_F32: return run_decode<W_F32, A_F32>(g, a, ev, stream);
         case W_F32 * 2 + A_BF16: return run_decode<W_F32, A_BF16>(g, a, ev, stream);
