@@ -37,8 +37,8 @@ DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (b
 # WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
 # copy of known size; valid only for the kernel source these were taken on.
 PMC_TRAFFIC = {
-    ("olmoe_bf16_e64", "0527f8486d8c8232"): {"fetch_kib": 32805.6, "fetch_scale": 2.0,
-                                    "write_kib": 32.0, "write_scale": 1.0},
+    ("olmoe_bf16_e64", "bcfce94f23115e92"): {"fetch_kib": 32813.6, "fetch_scale": 1.9998,
+                                             "write_kib": 32.0, "write_scale": 1.0},
 }
 
 
@@ -90,6 +90,21 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "elementwise int32 copy", "bytes_read": n * 4, "bytes_written": n * 4,
                       "launches": 4}), flush=True)
+
+
+def read_ceiling(torch, dev, binding, nbytes: int, achieved_gbps: float) -> dict:
+    """What a plain streaming read of the dominant kernel's bytes per launch achieves
+    on this GPU in one launch, timed like the kernel (events around the dispatch),
+    rotating over 8 regions so no launch is served from the on-chip caches."""
+    nbytes = max(16, nbytes // 16 * 16)
+    buf = torch.empty(nbytes * 8, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    us = binding.read_calibration(buf, nbytes, reps=40)
+    del buf
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"gbps": round(gbps, 1), "bytes": nbytes, "avg_launch_us": round(us, 2),
+            "frac_of_read_ceiling": round(achieved_gbps / gbps, 4),
+            "method": "plain streaming read of the same bytes in one launch, event-timed, 8 rotating regions"}
 
 
 def link_peak_gbps(torch, dev, nbytes: int) -> float:
@@ -256,6 +271,8 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
             roof["mfma_tflops"] = round(tflops, 2)
             roof["mfma_util"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 5)
             roof["hbm_gbps"] = round(ach, 1)
+        if roof["bound"] == "hbm":
+            roof["read_ceiling"] = read_ceiling(torch, dev, binding, int(w13_bytes), ach)
         res["roofline"] = roof
         res["hbm_gbps_hits"] = round((w13_bytes + w2_bytes) / ((w13_us + w2_us) * 1e-6) / 1e9, 1)
     torch.cuda.empty_cache()

@@ -90,6 +90,7 @@ _SIGS = {
     "moe_ptr_is_pinned_host": (_I32, [_P, _PI32]),
     "moe_pool_get_timing": (_I32, [_P, C.POINTER(Timing)]),
     "moe_pool_reset_timing": (_I32, [_P]),
+    "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
     "moe_lru_destroy": (None, [_P]),
     "moe_lru_step": (_I32, [_P, _P, _I32, _I32, _P, C.POINTER(Miss), _I32, _PI32, _PI32]),
@@ -283,6 +284,18 @@ class MoePool:
 
     def reset_timing(self):
         _check(lib().moe_pool_reset_timing(self._h))
+
+
+def read_calibration(buf, bytes_per_launch: int, reps: int = 20, stream=None) -> float:
+    """Mean event-timed duration (us) of a plain streaming read of bytes_per_launch,
+    rotating over the device buffer `buf` (a torch tensor)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    us = C.c_double(0)
+    _check(lib().moe_read_calibration(_ptr(buf), buf.numel() * buf.element_size(), bytes_per_launch, reps,
+                                      C.c_void_p(stream), C.byref(us)))
+    return us.value
 
 
 def is_pinned_host(addr: int) -> bool:

@@ -106,6 +106,11 @@ size_t act_bytes_per_pair(int wtype, int I);
 // Bytes of the grouped-path index buffer for max_tokens tokens and nslots slots.
 size_t grouped_index_bytes(int max_tokens, int K, int nslots);
 
+// One launch of the streaming-read calibration kernel over [p, p + bytes) (bytes a
+// multiple of 16), timed by the event pair; sink: 1 KiB of device scratch.
+hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, hipEvent_t start, hipEvent_t stop,
+                             hipStream_t s);
+
 // Whether n_tokens above kDecodeMaxTokens take the grouped MFMA path for this shape.
 bool grouped_shape(int wtype, int H, int I);
 

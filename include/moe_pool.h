@@ -257,6 +257,18 @@ moe_status_t moe_ptr_is_pinned_host(const void* p, int32_t* is_pinned);
 moe_status_t moe_pool_get_timing(moe_pool_t* pool, moe_pool_timing_t* out);
 moe_status_t moe_pool_reset_timing(moe_pool_t* pool);
 
+/* ---- calibration (benchmarks) ----------------------------------------------- */
+/* What one kernel launch of `bytes` can read on this GPU: a plain streaming read
+ * (each wave 4 KiB contiguous), launched reps times (after two untimed launches)
+ * on `stream`, each launch over the next `bytes`-sized region of the caller's
+ * device buffer [buf_dev, buf_dev + buf_bytes) so that a repeat does not hit the
+ * on-chip caches, each timed with a HIP event pair around the dispatch (the way
+ * the forward kernels are timed).  *avg_us = mean duration.  bytes: a positive
+ * multiple of 16, at most buf_bytes.  The call synchronizes on each launch.
+ * Errors: EINVAL, EHIP. */
+moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t bytes, int32_t reps,
+                                  void* stream, double* avg_us);
+
 /* ---- the slot manager alone (host only, no GPU) ----------------------------- */
 /* The same per-layer LRU state machine prepare() runs, driven from host ids, for
  * pool-size planning and for checking the bookkeeping without a GPU.  Semantics

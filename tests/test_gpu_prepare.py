@@ -277,3 +277,13 @@ def test_zero_tokens_and_zero_slots():
     st = rig.pool.stats(0)
     assert st["steps"] == 2 and st["fallbacks"] == 1 and st["hits"] == st["misses"] == 0
     rig.close()
+
+
+def test_read_calibration_times_a_plain_read():
+    """The streaming-read calibration returns a positive duration, and a larger read
+    takes longer than a small one."""
+    buf = torch.empty(64 << 20, dtype=torch.uint8, device=DEV)
+    buf.fill_(3)
+    small = binding.read_calibration(buf, 1 << 20, reps=8)
+    big = binding.read_calibration(buf, 32 << 20, reps=8)
+    assert 0 < small < big

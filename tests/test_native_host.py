@@ -112,3 +112,14 @@ def test_native_lru_empty_step():
     out, path, misses = lib.step(np.zeros((0, 2), np.int32))
     assert path == binding.PATH_POOL and misses == [] and out.shape == (0, 2)
     assert lib.stats()["steps"] == 1
+
+
+def test_read_calibration_rejects_bad_arguments_without_a_gpu():
+    """The calibration entry point validates its arguments before touching the GPU."""
+    import ctypes as C
+    us = C.c_double(0)
+    L = binding.lib()
+    assert L.moe_read_calibration(None, 1 << 20, 1 << 16, 4, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 21, 4, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 100, 4, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 16, 0, None, C.byref(us)) == binding.EINVAL
