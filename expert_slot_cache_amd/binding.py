@@ -20,11 +20,13 @@ OK, EINVAL, ENOMEM, EHIP, ERANGE, ESTATE = 0, -1, -2, -3, -4, -5
 W_F32, W_BF16, W_INT4_G128 = 0, 1, 2
 A_F32, A_BF16 = 0, 1
 RULE_DISTINCT, RULE_STATIC = 0, 1
+COPY_KERNEL, COPY_DMA = 0, 1
 PATH_POOL, PATH_FALLBACK = 0, 1
 
 WTYPES = {"f32": W_F32, "bf16": W_BF16, "int4": W_INT4_G128}
 ATYPES = {"f32": A_F32, "bf16": A_BF16}
 RULES = {"distinct": RULE_DISTINCT, "static": RULE_STATIC}
+COPY_ENGINES = {"dma": COPY_DMA, "kernel": COPY_KERNEL}
 
 
 class MoeError(RuntimeError):
@@ -47,7 +49,7 @@ class Config(C.Structure):
                 ("wtype", C.c_int32), ("atype", C.c_int32), ("rule", C.c_int32),
                 ("resident", C.c_int32), ("max_tokens", C.c_int32), ("n_copy_streams", C.c_int32),
                 ("copy_chunk_bytes", C.c_size_t), ("hbm_budget_bytes", C.c_size_t),
-                ("timing", C.c_int32)]
+                ("timing", C.c_int32), ("copy_engine", C.c_int32)]
 
 
 class Miss(C.Structure):
@@ -91,6 +93,7 @@ _SIGS = {
     "moe_pool_get_timing": (_I32, [_P, C.POINTER(Timing)]),
     "moe_pool_reset_timing": (_I32, [_P]),
     "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
+    "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _P, C.POINTER(C.c_double)]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
     "moe_lru_destroy": (None, [_P]),
     "moe_lru_step": (_I32, [_P, _P, _I32, _I32, _P, C.POINTER(Miss), _I32, _PI32, _PI32]),
@@ -158,11 +161,11 @@ class MoePool:
                  slots: int, wtype: str = "bf16", atype: str = "bf16", rule: str = "distinct",
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
-                 stream=None):
+                 copy_engine: str = "kernel", stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
-                     copy_chunk_bytes, hbm_budget_bytes, int(timing))
+                     copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine])
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -295,6 +298,17 @@ def read_calibration(buf, bytes_per_launch: int, reps: int = 20, stream=None) ->
     us = C.c_double(0)
     _check(lib().moe_read_calibration(_ptr(buf), buf.numel() * buf.element_size(), bytes_per_launch, reps,
                                       C.c_void_p(stream), C.byref(us)))
+    return us.value
+
+
+def link_calibration(nbytes: int, engine: str = "kernel", reps: int = 8, stream=None) -> float:
+    """Mean event-timed duration (us) of one pinned host -> HBM copy of nbytes with
+    the given engine ("kernel" or "dma")."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    us = C.c_double(0)
+    _check(lib().moe_link_calibration(nbytes, reps, COPY_ENGINES[engine], C.c_void_p(stream), C.byref(us)))
     return us.value
 
 

@@ -106,6 +106,21 @@ size_t act_bytes_per_pair(int wtype, int I);
 // Bytes of the grouped-path index buffer for max_tokens tokens and nslots slots.
 size_t grouped_index_bytes(int max_tokens, int K, int nslots);
 
+// Whole-expert copies by a kernel (the miss path's copy engine when it is not the
+// DMA engine): job i copies `bytes` from src (a device-mapped pointer into pinned
+// host memory) to dst (HBM).  Jobs travel in the kernel arguments.
+constexpr int kFillMaxJobs = 16;
+struct FillJob {
+    const char* src;
+    char* dst;
+};
+struct FillBatch {
+    FillJob job[kFillMaxJobs];
+    int n;
+    size_t bytes;   // per job, a multiple of 16
+};
+hipError_t launch_fill(const FillBatch& b, hipStream_t s);
+
 // One launch of the streaming-read calibration kernel over [p, p + bytes) (bytes a
 // multiple of 16), timed by the event pair; sink: 1 KiB of device scratch.
 hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, hipEvent_t start, hipEvent_t stop,

@@ -113,6 +113,7 @@ constexpr size_t kStorePiece = (size_t)1 << 30;
 struct LayerState {
     moe::SlotLRU lru;
     std::vector<char*> store;    // pinned host pieces holding the E experts in order
+    std::vector<char*> store_dev;// the same pieces' device addresses (mapped)
     int32_t per_piece = 1;       // experts per piece
     char* slots = nullptr;       // HBM: nslot_alloc experts + zeroed tail
     int32_t* map_dev = nullptr;  // HBM int32 [E]: the persistent map table
@@ -124,6 +125,9 @@ struct LayerState {
     int32_t* path_dev = nullptr; // HBM int32: the path the last remap chose
     bool prepared = false;
     char* expert(int32_t e, size_t eb) const { return store[e / per_piece] + (size_t)(e % per_piece) * eb; }
+    const char* expert_dev(int32_t e, size_t eb) const {
+        return store_dev[e / per_piece] + (size_t)(e % per_piece) * eb;
+    }
     int32_t prep_tokens = 0;
     int32_t prep_path = MOE_PATH_POOL;
     uint64_t bytes_h2d = 0;
@@ -269,14 +273,60 @@ void harvest_all(moe_pool* p) {
     for (auto& L : p->layers) harvest_layer(p, L);
 }
 
+// The copy-kernel engine: the experts go in batches of up to kFillMaxJobs per launch,
+// batches round-robin over the copy streams; each used stream records its copy_done
+// event (joined into the compute stream if `join`), as with the DMA engine.
+moe_status_t issue_copy_kernels(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs,
+                                bool join) {
+    const int ns = (int)p->copy.size();
+    const size_t eb = p->lay.total;
+    std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
+    bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0;
+    for (const auto& t : L.copy_t) timed = timed && !t.pending;
+    const int nb = (int)((jobs.size() + moe::kFillMaxJobs - 1) / moe::kFillMaxJobs);
+    const int streams_needed = std::min(ns, nb);
+    for (int i = 0; i < streams_needed; ++i) {
+        const int s = (p->copy_rr + i) % ns;
+        if (timed) {
+            HIPCHK(hipEventRecord(L.copy_t[s].a, p->copy[s]));
+            L.copy_t[s].bytes = 0;
+        }
+        p->used_copy[s] = 1;
+    }
+    int rr = p->copy_rr;
+    for (size_t j0 = 0; j0 < jobs.size(); j0 += moe::kFillMaxJobs) {
+        moe::FillBatch b{};
+        b.bytes = eb;
+        b.n = (int)std::min<size_t>(moe::kFillMaxJobs, jobs.size() - j0);
+        for (int i = 0; i < b.n; ++i) b.job[i] = moe::FillJob{L.expert_dev(jobs[j0 + i].second, eb), jobs[j0 + i].first};
+        HIPCHK(moe::launch_fill(b, p->copy[rr]));
+        if (timed) L.copy_t[rr].bytes += (uint64_t)b.n * eb;
+        rr = (rr + 1) % ns;
+    }
+    p->copy_rr = rr;
+    for (int s = 0; s < ns; ++s) {
+        if (!p->used_copy[s]) continue;
+        if (timed) {
+            HIPCHK(hipEventRecord(L.copy_t[s].b, p->copy[s]));
+            L.copy_t[s].pending = true;
+        }
+        HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
+        if (join) HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+    }
+    L.bytes_h2d += (uint64_t)eb * jobs.size();
+    return MOE_OK;
+}
+
 // Enqueue host->HBM copies of the experts (src -> dst pairs) on the copy streams,
 // record each used stream's copy_done event, and, if `join`, make the compute
 // stream wait for those events.
-moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, const char*>>& jobs,
+// jobs: (destination in HBM, source expert index in the layer's store).
+moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs,
                           bool join) {
     if (jobs.empty()) return MOE_OK;
     const int ns = (int)p->copy.size();
     const size_t eb = p->lay.total;
+    if (p->cfg.copy_engine == MOE_COPY_KERNEL) return issue_copy_kernels(p, L, jobs, join);
     const size_t chunk = p->cfg.copy_chunk_bytes ? p->cfg.copy_chunk_bytes : eb;
     std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
     bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0;
@@ -292,9 +342,10 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
     }
     int rr = p->copy_rr;
     for (const auto& j : jobs) {
+        const char* src = L.expert(j.second, eb);
         for (size_t off = 0; off < eb; off += chunk) {
             const size_t n = std::min(chunk, eb - off);
-            HIPCHK(hipMemcpyAsync(j.first + off, j.second + off, n, hipMemcpyHostToDevice, p->copy[rr]));
+            HIPCHK(hipMemcpyAsync(j.first + off, src + off, n, hipMemcpyHostToDevice, p->copy[rr]));
             if (timed) L.copy_t[rr].bytes += n;
             rr = (rr + 1) % ns;
         }
@@ -439,9 +490,9 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
         }
         *n_upd_out = n_upd;
         if (!p->misses.empty()) {
-            std::vector<std::pair<char*, const char*>> jobs;
+            std::vector<std::pair<char*, int32_t>> jobs;
             jobs.reserve(p->misses.size());
-            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, L.expert(m.expert, eb));
+            for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, m.expert);
             st = issue_copies(p, L, jobs, join);
             if (st) return st;
             *copied = true;
@@ -450,9 +501,9 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
         // selective-copy fallback: the step's experts go to staging in rank order;
         // the pool is untouched
         *the_path = MOE_PATH_FALLBACK;
-        std::vector<std::pair<char*, const char*>> jobs;
+        std::vector<std::pair<char*, int32_t>> jobs;
         jobs.reserve(D);
-        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, L.expert(u[r], eb));
+        for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, u[r]);
         st = issue_copies(p, L, jobs, join);
         if (st) return st;
         *copied = true;
@@ -565,6 +616,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.max_tokens < 1) FAIL(MOE_EINVAL, "max_tokens %d < 1", c.max_tokens);
     if (c.timing < 0) FAIL(MOE_EINVAL, "timing %d < 0", c.timing);
     if (c.n_copy_streams < 1 || c.n_copy_streams > 8) FAIL(MOE_EINVAL, "n_copy_streams %d outside [1,8]", c.n_copy_streams);
+    if (c.copy_engine != MOE_COPY_DMA && c.copy_engine != MOE_COPY_KERNEL) FAIL(MOE_EINVAL, "copy_engine %d invalid", c.copy_engine);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
     Layout lay;
     if (!make_layout(c.wtype, c.hidden, c.inter, &lay)) FAIL(MOE_EINVAL, "unsupported shape/format (wtype %d, H %d, I %d)", c.wtype, c.hidden, c.inter);
@@ -633,7 +685,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         for (int32_t e0 = 0; !c.resident && e0 < E; e0 += L.per_piece) {
             const size_t bytes = (size_t)std::min(L.per_piece, E - e0) * eb;
             char* piece = nullptr;
-            const hipError_t he = hipHostMalloc((void**)&piece, bytes, hipHostMallocDefault);
+            const hipError_t he = hipHostMalloc((void**)&piece, bytes, hipHostMallocMapped);
             if (he != hipSuccess) {
                 set_err("hipHostMalloc of %zu bytes (layer %d, experts %d..) failed after %zu pinned bytes: %s", bytes, l,
                         e0, pinned_total, hipGetErrorString(he));
@@ -642,6 +694,9 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
             }
             L.store.push_back(piece);
             pinned_total += bytes;
+            char* piece_dev = nullptr;
+            CREATE_HIP(hipHostGetDevicePointer((void**)&piece_dev, piece, 0));
+            L.store_dev.push_back(piece_dev);
         }
         CREATE_HIP(hipMalloc((void**)&L.slots, slot_bytes));
         CREATE_HIP(hipMemset(L.slots + (size_t)p->nslot_alloc * eb, 0, kAlign));
@@ -1011,6 +1066,54 @@ moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t 
     if (a) (void)hipEventDestroy(a);
     if (b) (void)hipEventDestroy(b);
     if (sink) (void)hipFree(sink);
+    if (st) return st;
+    *avg_us = total / reps;
+    return MOE_OK;
+}
+
+moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, void* stream, double* avg_us) {
+    if (!avg_us || reps < 1 || bytes < 16 || bytes % 16 || (engine != MOE_COPY_KERNEL && engine != MOE_COPY_DMA))
+        FAIL(MOE_EINVAL, "bad calibration arguments");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* host = nullptr;
+    char* host_dev = nullptr;
+    char* dev = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    moe_status_t st = MOE_OK;
+    double total = 0;
+    auto fail = [&](hipError_t err, const char* what) {
+        set_err("%s failed: %s", what, hipGetErrorString(err));
+        st = (err == hipErrorOutOfMemory || err == hipErrorMemoryAllocation) ? MOE_ENOMEM : MOE_EHIP;
+    };
+    hipError_t e;
+    if ((e = hipHostMalloc((void**)&host, bytes, hipHostMallocMapped)) != hipSuccess) fail(e, "hipHostMalloc");
+    if (!st) std::memset(host, 0x5A, bytes);
+    if (!st && (e = hipHostGetDevicePointer((void**)&host_dev, host, 0)) != hipSuccess) fail(e, "hipHostGetDevicePointer");
+    if (!st && (e = hipMalloc((void**)&dev, bytes)) != hipSuccess) fail(e, "hipMalloc");
+    if (!st && (e = hipEventCreate(&a)) != hipSuccess) fail(e, "hipEventCreate");
+    if (!st && (e = hipEventCreate(&b)) != hipSuccess) fail(e, "hipEventCreate");
+    for (int32_t i = -1; !st && i < reps; ++i) {
+        if ((e = hipEventRecord(a, s)) != hipSuccess) { fail(e, "hipEventRecord"); break; }
+        if (engine == MOE_COPY_KERNEL) {
+            moe::FillBatch fb{};
+            fb.n = 1;
+            fb.bytes = bytes;
+            fb.job[0] = moe::FillJob{host_dev, dev};
+            e = moe::launch_fill(fb, s);
+        } else {
+            e = hipMemcpyAsync(dev, host, bytes, hipMemcpyHostToDevice, s);
+        }
+        if (e != hipSuccess) { fail(e, "copy"); break; }
+        if ((e = hipEventRecord(b, s)) != hipSuccess) { fail(e, "hipEventRecord"); break; }
+        if ((e = hipEventSynchronize(b)) != hipSuccess) { fail(e, "hipEventSynchronize"); break; }
+        float ms = 0;
+        if ((e = hipEventElapsedTime(&ms, a, b)) != hipSuccess) { fail(e, "hipEventElapsedTime"); break; }
+        if (i >= 0) total += ms * 1e3;
+    }
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    if (dev) (void)hipFree(dev);
+    if (host) (void)hipHostFree(host);
     if (st) return st;
     *avg_us = total / reps;
     return MOE_OK;

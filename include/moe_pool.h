@@ -67,6 +67,11 @@ typedef int32_t moe_status_t;
 /* route rule: when a step bypasses the pool ([llama-pool] prefill rule) */
 #define MOE_RULE_DISTINCT 0  /* distinct experts of the step > n_slots (default) */
 #define MOE_RULE_STATIC   1  /* top_k * n_tokens > n_slots ("can touch more") */
+/* copy engine of the miss path (host store -> HBM) */
+#define MOE_COPY_KERNEL 0  /* a copy kernel on the copy streams, reading the pinned store
+                              through its device mapping (default: on MI355X it moves a
+                              12 MiB expert ~3 % and a 2.4 MiB one ~15 % faster) */
+#define MOE_COPY_DMA    1  /* hipMemcpyAsync on the copy streams */
 /* path a step took */
 #define MOE_PATH_POOL     0
 #define MOE_PATH_FALLBACK 1
@@ -97,6 +102,9 @@ typedef struct {
                                and every Nth prepare's copies with HIP events
                                (moe_pool_get_timing).  The events cost a few us per
                                timed call, so a period > 1 keeps them off most calls. */
+    int32_t copy_engine;    /* MOE_COPY_KERNEL (0) or MOE_COPY_DMA (1); the same bytes land
+                               in the same places either way.  copy_chunk_bytes applies
+                               to the DMA engine only. */
 } moe_pool_config_t;
 
 typedef struct {
@@ -268,6 +276,13 @@ moe_status_t moe_pool_reset_timing(moe_pool_t* pool);
  * Errors: EINVAL, EHIP. */
 moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t bytes, int32_t reps,
                                   void* stream, double* avg_us);
+
+/* The host link's rate for whole-expert copies: `bytes` (a positive multiple of 16)
+ * from pinned, device-mapped host memory to HBM (both allocated by the call and
+ * freed before it returns), reps times after one untimed copy, with the given
+ * engine (MOE_COPY_KERNEL or MOE_COPY_DMA) on `stream`, each copy timed with
+ * events.  *avg_us = mean duration.  Errors: EINVAL, ENOMEM, EHIP. */
+moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, void* stream, double* avg_us);
 
 /* ---- the slot manager alone (host only, no GPU) ----------------------------- */
 /* The same per-layer LRU state machine prepare() runs, driven from host ids, for

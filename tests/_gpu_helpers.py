@@ -29,7 +29,8 @@ class Rig:
     def __init__(self, wl: synth.Workload, *, slots: int, layers: int | None = None,
                  resident: bool = False, rule: str = "distinct", max_tokens: int | None = None,
                  fast: bool = True, experts=None, std: float = 0.02, copy_streams: int = 1,
-                 copy_chunk_bytes: int = 0, one_call: bool = False, timing: int = 0):
+                 copy_chunk_bytes: int = 0, one_call: bool = False, timing: int = 0,
+                 copy_engine: str = "kernel"):
         self.wl = wl
         self.one_call = one_call   # one moe_pool_step call per layer instead of prepare + forward
         self.L = wl.layers if layers is None else layers
@@ -43,7 +44,8 @@ class Rig:
                                     inter=self.I, slots=slots, wtype=wl.wtype, atype=wl.atype,
                                     rule=rule, resident=resident,
                                     max_tokens=max_tokens or wl.tokens, copy_streams=copy_streams,
-                                    copy_chunk_bytes=copy_chunk_bytes, timing=timing)
+                                    copy_chunk_bytes=copy_chunk_bytes, timing=timing,
+                                    copy_engine=copy_engine)
         for l in range(self.L):
             for e in range(self.E):
                 self.pool.load_expert(l, e, experts[l][e])

@@ -73,12 +73,13 @@ def test_tiny_f32_full_trace_and_resident_identity(one_call):
 
 
 @ONE_CALL
-def test_olmoe_bf16_and_resident_identity(one_call):
+@pytest.mark.parametrize("engine", ["dma", "kernel"])
+def test_olmoe_bf16_and_resident_identity(one_call, engine):
     wl = synth.WORKLOADS["olmoe_bf16_e64"].with_(layers=2)
     steps = 12
     trace = synth.make_trace(wl, steps=steps)
     xs, ws = _inputs(wl, steps, 1)
-    pooled = Rig(wl, slots=16, one_call=one_call)
+    pooled = Rig(wl, slots=16, one_call=one_call, copy_engine=engine)
     out_p = _run(pooled, trace, xs, ws)
     resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
     out_r = _run(resident, trace, xs, ws, check_every=steps)
@@ -88,12 +89,13 @@ def test_olmoe_bf16_and_resident_identity(one_call):
 
 
 @ONE_CALL
-def test_fanout_int4_and_resident_identity(one_call):
+@pytest.mark.parametrize("engine", ["dma", "kernel"])
+def test_fanout_int4_and_resident_identity(one_call, engine):
     wl = synth.WORKLOADS["fanout_int4_e512"].with_(layers=1)
     steps = 6
     trace = synth.make_trace(wl, steps=steps)
     xs, ws = _inputs(wl, steps, 1)
-    pooled = Rig(wl, slots=16, one_call=one_call)
+    pooled = Rig(wl, slots=16, one_call=one_call, copy_engine=engine)
     out_p = _run(pooled, trace, xs, ws)
     resident = Rig(wl, slots=16, resident=True, experts=pooled.experts)
     out_r = _run(resident, trace, xs, ws, check_every=steps)

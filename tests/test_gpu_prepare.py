@@ -83,12 +83,13 @@ def test_evict_then_reinsert_in_same_step():
     rig.close()
 
 
-def test_slot_bytes_equal_store_after_eviction():
+@pytest.mark.parametrize("engine", ["dma", "kernel"])
+def test_slot_bytes_equal_store_after_eviction(engine):
     """test_gpu_buffer_matches_source_weights / _correct_after_eviction and the
     scale tests: every occupied slot holds exactly its owner's bytes (codes and
-    scales for INT4), after heavy churn."""
+    scales for INT4), after heavy churn, with either copy engine."""
     for wl in (SMALL_BF16, SMALL_INT4):
-        rig = Rig(wl, slots=5, fast=True, copy_chunk_bytes=4096, copy_streams=3)
+        rig = Rig(wl, slots=5, fast=True, copy_chunk_bytes=4096, copy_streams=3, copy_engine=engine)
         trace = synth.make_trace(wl, steps=40)
         lrus = [LayerLRU(wl.experts, 5) for _ in range(wl.layers)]
         _run_trace_prepare(rig, trace, lrus)
@@ -287,3 +288,50 @@ def test_read_calibration_times_a_plain_read():
     small = binding.read_calibration(buf, 1 << 20, reps=8)
     big = binding.read_calibration(buf, 32 << 20, reps=8)
     assert 0 < small < big
+
+
+@pytest.mark.parametrize("one_call", [False, True])
+def test_copy_kernel_many_misses_and_staging(one_call):
+    """More misses in one step than a copy-kernel launch carries (batches of 16),
+    and a fallback that stages every expert of the step: every slot and every
+    staging entry equals its expert's bytes, and the step's outputs equal those of
+    the DMA engine bit for bit."""
+    wl = synth.Workload("manymiss", 1, 48, 8, 256, 128, 24, 4, 0, "bf16", "bf16", 1.0, 0.0, 0, 31)
+    rng = np.random.default_rng(5)
+
+    def rows(lo, hi):        # 4 tokens x 8 distinct ids that together cover [lo, hi)
+        span = np.arange(lo, hi)
+        out = [np.resize(np.roll(span, -8 * t), 8) for t in range(4)]
+        return np.stack([rng.permutation(r) for r in out]).astype(np.int32)
+
+    steps = [rows(0, 20),      # 20 misses: two copy batches
+             rows(10, 40),     # 30 distinct > 24 slots: fallback, 30 experts staged
+             rows(20, 40)]     # 20 misses, 16 of them evicting
+    steps += [np.stack([rng.permutation(48)[:8] for _ in range(4)]).astype(np.int32) for _ in range(4)]
+    a = Rig(wl, slots=24, copy_engine="kernel", copy_streams=2, one_call=one_call, max_tokens=4)
+    b = Rig(wl, slots=24, copy_engine="dma", experts=a.experts, one_call=one_call, max_tokens=4)
+    _, _, rx, rw = synth.streams(wl)
+    for ids in steps:
+        x = to_dev_act(synth.draw_activations(rx, (4, wl.hidden), "bf16"), "bf16")
+        w = torch.from_numpy(synth.draw_gate_weights(rw, (4, wl.top_k))).to(DEV)
+        pa, ma, sa, oa = a.step(0, ids, x, w)
+        pb, mb, sb, ob = b.step(0, ids, x, w)
+        assert (pa, ma) == (pb, mb) and (sa == sb).all()
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+        if pa == binding.PATH_FALLBACK:
+            for r, e in enumerate(sorted(set(ids.ravel().tolist()))):
+                assert (a.pool.read_staging(r) == a.experts[0][e]).all(), (r, e)
+    assert a.pool.stats()["fallbacks"] > 0 and a.pool.stats()["misses"] > 16
+    _, owner, _ = a.pool.state(0)
+    for s_, e in enumerate(owner):
+        if e >= 0:
+            assert (a.pool.read_slot(0, s_) == a.experts[0][e]).all()
+    a.close()
+    b.close()
+
+
+def test_link_calibration_both_engines():
+    """Both copy engines move a 4 MiB expert-sized copy in a positive, finite time."""
+    for engine in ("kernel", "dma"):
+        us = binding.link_calibration(4 << 20, engine=engine, reps=4)
+        assert 0 < us < 1e6, (engine, us)

@@ -123,3 +123,6 @@ def test_read_calibration_rejects_bad_arguments_without_a_gpu():
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 21, 4, None, C.byref(us)) == binding.EINVAL
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 100, 4, None, C.byref(us)) == binding.EINVAL
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 16, 0, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(100, 4, binding.COPY_KERNEL, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 0, binding.COPY_DMA, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 4, 7, None, C.byref(us)) == binding.EINVAL
