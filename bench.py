@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--copy-engine", default="kernel", choices=["dma", "kernel"],
                     help="miss-path copies: DMA engine (hipMemcpyAsync) or a copy kernel reading the "
                          "mapped pinned store")
+    ap.add_argument("--policy", default="device", choices=["host", "device"],
+                    help="slot manager: LRU on the host (reads back the distinct ids) or in one GPU "
+                         "workgroup (no host round trip on the decode path)")
     ap.add_argument("--no-timing", action="store_true", help="no HIP events around kernels")
     ap.add_argument("--timing-every", type=int, default=7,
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
@@ -111,9 +114,10 @@ def read_ceiling(torch, dev, binding, nbytes: int, achieved_gbps: float) -> dict
 
 
 def link_peak_gbps(binding, nbytes: int) -> dict:
-    """Pinned host -> HBM rate for whole-expert copies of `nbytes` with each copy
-    engine (the library's calibration call, event-timed); the peak is the better of
-    the two."""
+    """Pinned host -> HBM rate for one transfer of `nbytes` (the mean bytes of one
+    timed miss batch of the run, so that the ceiling and the measured rate move the
+    same amount per event pair) with each copy engine (the library's calibration
+    call, event-timed); the peak is the better of the two."""
     r = {}
     for engine in ("dma", "kernel"):
         us = binding.link_calibration(nbytes, engine=engine, reps=8)
@@ -165,7 +169,7 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
                            wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
                            max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20, copy_engine=args.copy_engine,
-                           timing=0 if args.no_timing else args.timing_every)
+                           policy=args.policy, timing=0 if args.no_timing else args.timing_every)
     eb = pool.expert_nbytes
     if resident:
         buf = np.empty(eb, np.uint8)
@@ -240,6 +244,7 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
            "readback_wait_ms_per_step": round(tm["sync_wait_ms"] / args.steps, 4)}
     if tm["copy_ms"] > 0:
         res["link_gbps_misses"] = round(tm["copy_bytes"] / (tm["copy_ms"] * 1e-3) / 1e9, 2)
+        res["miss_batch_bytes"] = int(tm["copy_bytes"] // max(1, tm["copy_calls"]))
     if not args.no_timing and tm["kernel_calls"] > 0:
         n = tm["kernel_calls"]
         w13_us = tm["w13_ms"] / n * 1e3
@@ -320,7 +325,8 @@ def main():
     for n in (points or [slots]):
         results[n], eb = run_point(args, torch, binding, wl, n, trace, xs_d, ws_d, gen, args.resident)
     main_res = results[slots]
-    link = link_peak_gbps(binding, eb)
+    batch_bytes = main_res.get("miss_batch_bytes", eb)
+    link = link_peak_gbps(binding, max(eb, (batch_bytes + 4095) // 4096 * 4096))
     peak_link = link["peak"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "tokens/s", "n_gpus": 1,
@@ -331,13 +337,14 @@ def main():
                    "inter": I, "slots": slots, "tokens_per_step": T, "weights": wl.wtype,
                    "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
                    "resident": args.resident, "copy_streams": args.copy_streams,
-                   "copy_engine": args.copy_engine},
+                   "copy_engine": args.copy_engine, "policy": args.policy},
     }
     for k, v in main_res.items():
         if k not in ("value", "ms_per_step", "slots", "roofline"):
             line[k] = v
     line["link_peak_gbps"] = round(peak_link, 2)
-    line["link_calibration_gbps"] = {"dma": link["dma"], "kernel": link["kernel"], "bytes": eb}
+    line["link_calibration_gbps"] = {"dma": link["dma"], "kernel": link["kernel"],
+                                     "bytes": max(eb, (batch_bytes + 4095) // 4096 * 4096)}
     if "link_gbps_misses" in main_res:
         line["link_frac"] = round(main_res["link_gbps_misses"] / peak_link, 4)
     line["roofline"] = main_res.get("roofline")

@@ -27,6 +27,8 @@ WTYPES = {"f32": W_F32, "bf16": W_BF16, "int4": W_INT4_G128}
 ATYPES = {"f32": A_F32, "bf16": A_BF16}
 RULES = {"distinct": RULE_DISTINCT, "static": RULE_STATIC}
 COPY_ENGINES = {"dma": COPY_DMA, "kernel": COPY_KERNEL}
+POLICY_HOST, POLICY_DEVICE = 0, 1
+POLICIES = {"host": POLICY_HOST, "device": POLICY_DEVICE}
 
 
 class MoeError(RuntimeError):
@@ -49,7 +51,7 @@ class Config(C.Structure):
                 ("wtype", C.c_int32), ("atype", C.c_int32), ("rule", C.c_int32),
                 ("resident", C.c_int32), ("max_tokens", C.c_int32), ("n_copy_streams", C.c_int32),
                 ("copy_chunk_bytes", C.c_size_t), ("hbm_budget_bytes", C.c_size_t),
-                ("timing", C.c_int32), ("copy_engine", C.c_int32)]
+                ("timing", C.c_int32), ("copy_engine", C.c_int32), ("policy", C.c_int32)]
 
 
 class Miss(C.Structure):
@@ -84,6 +86,7 @@ _SIGS = {
     "moe_pool_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, C.POINTER(Miss), _I32, _PI32,
                              _PI32]),
     "moe_pool_sync": (_I32, [_P]),
+    "moe_pool_last_step": (_I32, [_P, _I32, _PI32, C.POINTER(Miss), _I32, _PI32]),
     "moe_pool_get_stats": (_I32, [_P, _I32, C.POINTER(Stats)]),
     "moe_pool_get_state": (_I32, [_P, _I32, _P, _P, _P]),
     "moe_pool_read_slot": (_I32, [_P, _I32, _I32, _P, C.c_size_t]),
@@ -161,11 +164,12 @@ class MoePool:
                  slots: int, wtype: str = "bf16", atype: str = "bf16", rule: str = "distinct",
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
-                 copy_engine: str = "kernel", stream=None):
+                 copy_engine: str = "kernel", policy: str = "host", stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
-                     copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine])
+                     copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine],
+                     POLICIES[policy])
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -176,6 +180,7 @@ class MoePool:
         self.layers, self.experts, self.top_k = layers, experts, top_k
         self.hidden, self.inter, self.slots = hidden, inter, slots
         self.wtype, self.atype, self.resident = wtype, atype, resident
+        self.policy = policy
         self.max_tokens = max_tokens
         self.expert_nbytes = expert_bytes(wtype, hidden, inter)
         self._miss_buf = (Miss * max(1, experts))()
@@ -238,6 +243,14 @@ class MoePool:
 
     def sync(self):
         _check(lib().moe_pool_sync(self._h))
+
+    def last_step(self, layer: int):
+        """(path, misses) of the layer's last prepare/step (waits for it under the
+        device policy)."""
+        nm, path = C.c_int32(0), C.c_int32(0)
+        _check(lib().moe_pool_last_step(self._h, layer, C.byref(path), self._miss_buf, len(self._miss_buf),
+                                        C.byref(nm)))
+        return path.value, _misses(self._miss_buf, min(nm.value, len(self._miss_buf)))
 
     # -- introspection ---------------------------------------------------------------
     def stats(self, layer: int = -1) -> dict:

@@ -134,6 +134,18 @@ struct LayerState {
     uint64_t staged = 0;
     std::vector<Timing> copy_t;  // one per copy stream
     Timing w13_t, w2_t;
+    // last step, as prepare returned it (MOE_POLICY_HOST) or as the host knows it
+    bool has_last = false;
+    int32_t last_path = MOE_PATH_POOL;
+    std::vector<moe::Miss> last_misses;
+    // MOE_POLICY_DEVICE: the slot manager's state in HBM, the store pieces' device
+    // addresses (device array), and the fill timing of this layer
+    char* dev_block = nullptr;
+    moe::DevState ds{};
+    const char** pieces_dev = nullptr;
+    bool last_empty = false;     // the last step had no tokens (not seen by the GPU)
+    uint64_t empty_steps = 0;    // steps with no tokens (counted on the host)
+    Timing fill_t;
 };
 
 }  // namespace
@@ -165,6 +177,12 @@ struct moe_pool {
     int32_t* grp = nullptr;       // HBM grouped-path index buffer
     int32_t grp_slots = 0;        // largest slot count a forward can address
     std::vector<moe::Miss> misses;
+    // MOE_POLICY_DEVICE
+    uint32_t* errs_host = nullptr;      // pinned coherent [n_layers]: set by the GPU on an id outside [0,E)
+    uint32_t* errs_dev = nullptr;
+    int32_t* timed_jobs_host = nullptr; // pinned coherent [n_layers]: jobs of the last timed fill
+    int32_t* timed_jobs_dev = nullptr;
+    int32_t last_prepared = -1;         // the layer of the latest prepare (device policy)
     std::vector<char> used_copy;
     int copy_rr = 0;
     // timing totals (sampled calls)
@@ -190,6 +208,10 @@ void destroy_pool(moe_pool* p) {
         if (L.slots) (void)hipFree(L.slots);
         if (L.map_dev) (void)hipFree(L.map_dev);
         if (L.upd_host) (void)hipHostFree(L.upd_host);
+        if (L.dev_block) (void)hipFree(L.dev_block);
+        if (L.pieces_dev) (void)hipFree(L.pieces_dev);
+        if (L.fill_t.a) (void)hipEventDestroy(L.fill_t.a);
+        if (L.fill_t.b) (void)hipEventDestroy(L.fill_t.b);
         for (auto& t : L.copy_t) {
             if (t.a) (void)hipEventDestroy(t.a);
             if (t.b) (void)hipEventDestroy(t.b);
@@ -210,6 +232,8 @@ void destroy_pool(moe_pool* p) {
     if (p->act) (void)hipFree(p->act);
     if (p->y) (void)hipFree(p->y);
     if (p->grp) (void)hipFree(p->grp);
+    if (p->errs_host) (void)hipHostFree(p->errs_host);
+    if (p->timed_jobs_host) (void)hipHostFree(p->timed_jobs_host);
     delete p;
 }
 
@@ -269,8 +293,27 @@ void harvest_layer(moe_pool* p, LayerState& L) {
     if (a && b) p->kern_calls++;
 }
 
+// A timed fill (device policy) counts only when it copied something; the kernel
+// leaves its job count in host memory for this.
+void harvest_fill(moe_pool* p, int32_t l) {
+    LayerState& L = p->layers[l];
+    if (!L.fill_t.pending || !done(L.fill_t)) return;
+    const int32_t jobs = ((volatile int32_t*)p->timed_jobs_host)[l];
+    if (jobs > 0) {
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, L.fill_t.a, L.fill_t.b) == hipSuccess) {
+            p->copy_ms += ms;
+            p->copy_calls++;
+            p->copy_bytes += (uint64_t)jobs * p->lay.total;
+        }
+    }
+    L.fill_t.pending = false;
+}
+
 void harvest_all(moe_pool* p) {
     for (auto& L : p->layers) harvest_layer(p, L);
+    if (p->cfg.policy == MOE_POLICY_DEVICE)
+        for (int32_t l = 0; l < p->cfg.n_layers; ++l) harvest_fill(p, l);
 }
 
 // The copy-kernel engine: the experts go in batches of up to kFillMaxJobs per launch,
@@ -541,6 +584,9 @@ void finish_prepare(moe_pool* p, LayerState& L, int32_t n_tokens, int32_t the_pa
     }
     if (n_miss) *n_miss = nm;
     if (path) *path = the_path;
+    L.has_last = true;
+    L.last_path = the_path;
+    L.last_misses = p->misses;
 }
 
 moe::Slots layer_slots(const moe_pool* p, const LayerState& L) {
@@ -576,6 +622,122 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
         L.w13_t.pending = true;
         L.w2_t.pending = true;
     }
+    return MOE_OK;
+}
+
+// ---- MOE_POLICY_DEVICE ------------------------------------------------------------
+// Byte layout of one layer's device state block (see moe::DevState).
+struct DevLayout {
+    size_t map, owner, free, prev, next, meta, ctr, rec, jobs, total;
+};
+
+DevLayout dev_layout(int32_t E, int32_t N, int32_t max_jobs) {
+    DevLayout d{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes);
+        return at;
+    };
+    d.map = take((size_t)E * 4);
+    d.owner = take((size_t)N * 4);
+    d.free = take((size_t)N * 4);
+    d.prev = take((size_t)E * 4);
+    d.next = take((size_t)E * 4);
+    d.meta = take(16 * 4);
+    d.ctr = take(8 * 8);
+    d.rec = take((size_t)(4 + 3 * N) * 4);
+    d.jobs = take((size_t)(1 + 2 * max_jobs) * 4);
+    d.total = o;
+    return d;
+}
+
+int32_t dev_max_jobs(const moe_pool* p) { return std::max(p->nslot_alloc, p->staging_cap); }
+
+// The cold state image: map -1, owners -1, free slots 0..N-1 (popped from the
+// end), empty LRU list, counters zero.
+std::vector<char> dev_cold_image(const moe_pool* p) {
+    const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
+    const DevLayout d = dev_layout(E, N, dev_max_jobs(p));
+    std::vector<char> img(d.total, 0);
+    auto w = [&](size_t off) { return reinterpret_cast<int32_t*>(img.data() + off); };
+    std::fill(w(d.map), w(d.map) + E, -1);
+    std::fill(w(d.owner), w(d.owner) + N, -1);
+    for (int32_t s2 = 0; s2 < N; ++s2) w(d.free)[s2] = s2;
+    std::fill(w(d.prev), w(d.prev) + E, -1);
+    std::fill(w(d.next), w(d.next) + E, -1);
+    w(d.meta)[0] = -1;
+    w(d.meta)[1] = -1;
+    w(d.meta)[2] = N;
+    return img;
+}
+
+moe_status_t dev_init_layers(moe_pool* p) {
+    const std::vector<char> img = dev_cold_image(p);
+    for (auto& L : p->layers) {
+        HIPCHK(hipMemcpy(L.dev_block, img.data(), img.size(), hipMemcpyHostToDevice));
+        L.has_last = false;
+        L.last_empty = false;
+        L.empty_steps = 0;
+    }
+    std::memset(p->errs_host, 0, sizeof(uint32_t) * p->cfg.n_layers);
+    return MOE_OK;
+}
+
+// An id outside [0,E) found by a layer's earlier device step.
+moe_status_t check_dev_err(moe_pool* p, int32_t layer) {
+    volatile uint32_t* e = p->errs_host + layer;
+    if (*e) {
+        *e = 0;
+        FAIL(MOE_ERANGE, "layer %d: an earlier step had an expert id outside [0,%d); it changed nothing and its"
+                         " output is undefined", layer, p->cfg.n_experts);
+    }
+    return MOE_OK;
+}
+
+// Queue the slot manager and the copy kernel for one step (n_tokens >= 1).
+moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
+                         int32_t* slot_ids_dev) {
+    const int n = n_tokens * p->cfg.top_k;
+    moe::PolicyArgs a{};
+    a.ids = ids_dev;
+    a.n = n;
+    a.E = p->cfg.n_experts;
+    a.N = p->cfg.resident ? 0 : p->cfg.n_slots;
+    a.rule = p->cfg.rule;
+    a.resident = p->cfg.resident;
+    a.eb = p->lay.total;
+    a.st = L.ds;
+    a.out = slot_ids_dev;
+    a.path = L.path_dev;
+    a.err = p->errs_dev + layer;
+    HIPCHK(moe::launch_policy(a, p->compute));
+    if (!p->cfg.resident) {
+        moe::FillDevArgs f{};
+        f.jobs = L.ds.jobs;
+        f.pieces = L.pieces_dev;
+        f.per_piece = L.per_piece;
+        f.eb = p->lay.total;
+        f.slots = L.slots;
+        f.staging = p->staging;
+        const bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 &&
+                           !L.fill_t.pending;
+        f.timed_jobs = timed ? p->timed_jobs_dev + layer : nullptr;
+        HIPCHK(moe::launch_fill_dev(f, 128, timed ? L.fill_t.a : nullptr, timed ? L.fill_t.b : nullptr, p->compute));
+        if (timed) L.fill_t.pending = true;
+    }
+    L.prepared = true;
+    L.prep_tokens = n_tokens;
+    L.prep_path = -1;            // known on the GPU only
+    L.has_last = true;
+    L.last_empty = false;
+    return MOE_OK;
+}
+
+template <class T>
+moe_status_t dev_read(const moe_pool* p, T* dst, const void* src, size_t n) {
+    HIPCHK(hipStreamSynchronize(p->compute));
+    HIPCHK(hipMemcpy(dst, src, n * sizeof(T), hipMemcpyDeviceToHost));
     return MOE_OK;
 }
 
@@ -617,6 +779,9 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.timing < 0) FAIL(MOE_EINVAL, "timing %d < 0", c.timing);
     if (c.n_copy_streams < 1 || c.n_copy_streams > 8) FAIL(MOE_EINVAL, "n_copy_streams %d outside [1,8]", c.n_copy_streams);
     if (c.copy_engine != MOE_COPY_DMA && c.copy_engine != MOE_COPY_KERNEL) FAIL(MOE_EINVAL, "copy_engine %d invalid", c.copy_engine);
+    if (c.policy != MOE_POLICY_HOST && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "policy %d invalid", c.policy);
+    if (c.policy == MOE_POLICY_DEVICE && c.n_experts > 2048)
+        FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS: n_experts %d > 2048", c.n_experts);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
     Layout lay;
     if (!make_layout(c.wtype, c.hidden, c.inter, &lay)) FAIL(MOE_EINVAL, "unsupported shape/format (wtype %d, H %d, I %d)", c.wtype, c.hidden, c.inter);
@@ -749,6 +914,36 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         const double max_copy = (double)std::max(p->nslot_alloc, p->staging_cap) * (double)eb;
         p->gate_limit = (unsigned long long)((10.0 + max_copy * 1e-9) * (double)std::max(khz, 1) * 1e3);
     }
+    if (c.policy == MOE_POLICY_DEVICE) {
+        const DevLayout d = dev_layout(E, c.resident ? 0 : c.n_slots, dev_max_jobs(p));
+        for (auto& L : p->layers) {
+            CREATE_HIP(hipMalloc((void**)&L.dev_block, d.total));
+            auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(L.dev_block + off); };
+            L.ds = moe::DevState{at(d.map), at(d.owner), at(d.free), at(d.prev), at(d.next), at(d.meta),
+                                 reinterpret_cast<unsigned long long*>(L.dev_block + d.ctr), at(d.rec), at(d.jobs)};
+            if (!L.store_dev.empty()) {
+                CREATE_HIP(hipMalloc((void**)&L.pieces_dev, sizeof(char*) * L.store_dev.size()));
+                CREATE_HIP(hipMemcpy(L.pieces_dev, L.store_dev.data(), sizeof(char*) * L.store_dev.size(),
+                                     hipMemcpyHostToDevice));
+            }
+            if (c.timing) {
+                CREATE_HIP(hipEventCreateWithFlags(&L.fill_t.a, tflag));
+                CREATE_HIP(hipEventCreateWithFlags(&L.fill_t.b, tflag));
+            }
+        }
+        CREATE_HIP(hipHostMalloc((void**)&p->errs_host, sizeof(uint32_t) * c.n_layers,
+                                 hipHostMallocCoherent | hipHostMallocMapped));
+        CREATE_HIP(hipHostGetDevicePointer((void**)&p->errs_dev, p->errs_host, 0));
+        CREATE_HIP(hipHostMalloc((void**)&p->timed_jobs_host, sizeof(int32_t) * c.n_layers,
+                                 hipHostMallocCoherent | hipHostMallocMapped));
+        std::memset(p->timed_jobs_host, 0, sizeof(int32_t) * c.n_layers);
+        CREATE_HIP(hipHostGetDevicePointer((void**)&p->timed_jobs_dev, p->timed_jobs_host, 0));
+        const moe_status_t ist = dev_init_layers(p);
+        if (ist) {
+            destroy_pool(p);
+            return ist;
+        }
+    }
     CREATE_HIP(hipMalloc((void**)&p->act, act_bytes));
     CREATE_HIP(hipMalloc((void**)&p->y, y_bytes));
     CREATE_HIP(hipMalloc((void**)&p->grp, grp_bytes));
@@ -786,8 +981,11 @@ moe_status_t moe_pool_reset(moe_pool_t* p) {
         L.prepared = false;
         L.bytes_h2d = 0;
         L.staged = 0;
+        L.has_last = false;
     }
     p->staging_owner = -1;
+    p->last_prepared = -1;
+    if (p->cfg.policy == MOE_POLICY_DEVICE) return dev_init_layers(p);
     return MOE_OK;
 }
 
@@ -805,14 +1003,31 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
     st = check_gate(L, layer);
     if (st) return st;
 
+    if (p->cfg.policy == MOE_POLICY_DEVICE) {
+        st = check_dev_err(p, layer);
+        if (st) return st;
+        if (n_miss) *n_miss = -1;
+        if (path) *path = -1;
+        if (n_tokens == 0) {
+            L.prepared = true;
+            L.prep_tokens = 0;
+            L.prep_path = MOE_PATH_POOL;
+            L.has_last = true;
+            L.last_empty = true;
+            L.empty_steps++;
+            return MOE_OK;
+        }
+        st = dev_prepare(p, L, layer, topk_ids_dev, n_tokens, slot_ids_dev);
+        if (st) return st;
+        p->last_prepared = layer;
+        if (p->cfg.timing) harvest_all(p);
+        return MOE_OK;
+    }
+
     if (n_tokens == 0) {
         p->misses.clear();
         if (p->cfg.resident) L.lru.count_resident(0); else L.lru.step(nullptr, 0, 0, p->misses);
-        L.prepared = true;
-        L.prep_tokens = 0;
-        L.prep_path = MOE_PATH_POOL;
-        if (n_miss) *n_miss = 0;
-        if (path) *path = MOE_PATH_POOL;
+        finish_prepare(p, L, 0, MOE_PATH_POOL, miss_host, miss_cap, n_miss, path);
         return MOE_OK;
     }
 
@@ -847,6 +1062,10 @@ moe_status_t moe_pool_forward(moe_pool_t* p, int32_t layer, const void* x_dev, c
     const bool fb = L.prep_path == MOE_PATH_FALLBACK;
     if (fb && p->staging_owner != layer)
         FAIL(MOE_ESTATE, "layer %d: its staged experts were replaced by layer %d's fallback", layer, p->staging_owner);
+    if (p->cfg.policy == MOE_POLICY_DEVICE && n_tokens > 0 && p->last_prepared != layer)
+        FAIL(MOE_ESTATE, "layer %d: layer %d was prepared after it (under the device policy a forward must follow its"
+                         " own prepare: staging is shared and the host does not know which steps fell back)",
+             layer, p->last_prepared);
     if (n_tokens == 0) return MOE_OK;
     if (!x_dev || !slot_ids_dev || !topk_w_dev || !out_dev) FAIL(MOE_EINVAL, "null buffer");
     return launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
@@ -856,7 +1075,8 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev, const void* resid_dev,
                            void* out_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
     if (n_tokens > 0 && (!x_dev || !topk_w_dev || !out_dev)) FAIL(MOE_EINVAL, "null buffer");
-    if (!p || n_tokens <= 0 || n_tokens > moe::kDecodeMaxTokens || n_tokens > p->cfg.max_tokens) {
+    if (!p || n_tokens <= 0 || n_tokens > moe::kDecodeMaxTokens || n_tokens > p->cfg.max_tokens ||
+        p->cfg.policy == MOE_POLICY_DEVICE) {
         moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap,
                                            n_miss, path);
         if (st) return st;
@@ -926,10 +1146,50 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
     return MOE_OK;
 }
 
+moe_status_t moe_pool_last_step(moe_pool_t* p, int32_t layer, int32_t* path, moe_miss_t* miss_host,
+                                int32_t miss_cap, int32_t* n_miss) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    if (miss_cap < 0) FAIL(MOE_EINVAL, "miss_cap < 0");
+    LayerState& L = p->layers[layer];
+    if (!L.has_last) FAIL(MOE_ESTATE, "layer %d: no step since create or reset", layer);
+    std::vector<moe::Miss> ms;
+    int32_t the_path = L.last_path;
+    if (p->cfg.policy == MOE_POLICY_DEVICE) {
+        if (L.last_empty) {
+            the_path = MOE_PATH_POOL;
+        } else {
+            const int32_t N = p->cfg.resident ? 0 : p->cfg.n_slots;
+            std::vector<int32_t> rec(4 + 3 * (size_t)N);
+            if ((st = dev_read(p, rec.data(), L.ds.rec, rec.size()))) return st;
+            if (rec[3]) {
+                p->errs_host[layer] = 0;
+                FAIL(MOE_ERANGE, "layer %d: the step had an expert id outside [0,%d); it changed nothing", layer,
+                     p->cfg.n_experts);
+            }
+            the_path = rec[0] == moe::PATH_STAGE ? MOE_PATH_FALLBACK : MOE_PATH_POOL;
+            for (int32_t i = 0; i < rec[2]; ++i) ms.push_back({rec[4 + 3 * i], rec[5 + 3 * i], rec[6 + 3 * i]});
+        }
+    } else {
+        ms = L.last_misses;
+    }
+    const int32_t nm = (int32_t)ms.size();
+    if (miss_host)
+        for (int32_t i = 0; i < std::min(nm, miss_cap); ++i) miss_host[i] = moe_miss_t{ms[i].expert, ms[i].slot, ms[i].evicted};
+    if (n_miss) *n_miss = nm;
+    if (path) *path = the_path;
+    return MOE_OK;
+}
+
 moe_status_t moe_pool_sync(moe_pool_t* p) {
     if (!p) FAIL(MOE_EINVAL, "null pool");
     for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
     HIPCHK(hipStreamSynchronize(p->compute));
+    if (p->cfg.policy == MOE_POLICY_DEVICE)
+        for (int32_t l = 0; l < p->cfg.n_layers; ++l) {
+            const moe_status_t st = check_dev_err(p, l);
+            if (st) return st;
+        }
     return MOE_OK;
 }
 
@@ -940,6 +1200,18 @@ moe_status_t moe_pool_get_stats(const moe_pool_t* p, int32_t layer, moe_pool_sta
     for (int32_t l = 0; l < p->cfg.n_layers; ++l) {
         if (layer >= 0 && l != layer) continue;
         const LayerState& L = p->layers[l];
+        if (p->cfg.policy == MOE_POLICY_DEVICE) {
+            unsigned long long c[8];
+            const moe_status_t st = dev_read(p, c, L.ds.ctr, 8);
+            if (st) return st;
+            out->steps += c[0] + L.empty_steps;
+            out->hits += c[1];
+            out->misses += c[2];
+            out->fallbacks += c[3];
+            out->bytes_h2d += c[4];
+            out->staged += c[5];
+            continue;
+        }
         out->steps += L.lru.steps();
         out->hits += L.lru.hits();
         out->misses += L.lru.misses();
@@ -954,6 +1226,23 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
                                 int32_t* lru_N) {
     moe_status_t st = check_layer(p, layer);
     if (st) return st;
+    if (p->cfg.policy == MOE_POLICY_DEVICE) {
+        const LayerState& L = p->layers[layer];
+        const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
+        std::vector<int32_t> map(E), owner(N), next(E), meta(16);
+        if ((st = dev_read(p, map.data(), L.ds.map, E))) return st;
+        if (N && (st = dev_read(p, owner.data(), L.ds.owner, N))) return st;
+        if ((st = dev_read(p, next.data(), L.ds.next, E))) return st;
+        if ((st = dev_read(p, meta.data(), L.ds.meta, 16))) return st;
+        if (map_E) std::copy(map.begin(), map.end(), map_E);
+        if (owner_N) std::copy(owner.begin(), owner.end(), owner_N);
+        if (lru_N) {
+            int32_t i = 0;
+            for (int32_t e = meta[0]; e >= 0 && i < N; e = next[e]) lru_N[i++] = e;
+            for (; i < N; ++i) lru_N[i] = -1;
+        }
+        return MOE_OK;
+    }
     const moe::SlotLRU& s = p->layers[layer].lru;
     if (map_E) std::copy(s.map().begin(), s.map().end(), map_E);
     if (owner_N) std::copy(s.owner().begin(), s.owner().end(), owner_N);

@@ -72,6 +72,13 @@ typedef int32_t moe_status_t;
                               through its device mapping (default: on MI355X it moves a
                               12 MiB expert ~3 % and a 2.4 MiB one ~15 % faster) */
 #define MOE_COPY_DMA    1  /* hipMemcpyAsync on the copy streams */
+/* where the slot manager runs */
+#define MOE_POLICY_HOST   0  /* on the host: prepare reads the step's distinct ids back
+                                (one sync per layer) and returns the path and misses */
+#define MOE_POLICY_DEVICE 1  /* on the GPU: prepare and step only queue work (a kernel runs
+                                the same LRU on device-resident state, a copy kernel pulls
+                                the misses); the path and misses of a step are read later
+                                with moe_pool_last_step */
 /* path a step took */
 #define MOE_PATH_POOL     0
 #define MOE_PATH_FALLBACK 1
@@ -105,6 +112,9 @@ typedef struct {
     int32_t copy_engine;    /* MOE_COPY_KERNEL (0) or MOE_COPY_DMA (1); the same bytes land
                                in the same places either way.  copy_chunk_bytes applies
                                to the DMA engine only. */
+    int32_t policy;         /* MOE_POLICY_HOST (0) or MOE_POLICY_DEVICE (1, n_experts <=
+                               2048, copies by the copy kernel on the compute stream).
+                               Both give the same slot ids, misses, counters and bits. */
 } moe_pool_config_t;
 
 typedef struct {
@@ -196,7 +206,16 @@ moe_status_t moe_pool_reset(moe_pool_t* pool);
  * are enqueued; the compute stream waits for the copies through events.
  * Distinct ids are processed in ascending order; free slots are taken from the
  * highest index down; a non-resident expert maps to -1.
- * Errors: EINVAL, ERANGE (an id outside [0,E): nothing changes), EHIP. */
+ * Errors: EINVAL, ERANGE (an id outside [0,E): nothing changes), EHIP.
+ *
+ * Under MOE_POLICY_DEVICE prepare only queues two kernels on the compute stream (the
+ * slot manager, then the copy kernel) and returns: *n_miss and *path are set to -1
+ * and miss_host is not written (moe_pool_last_step reads them later).  An id outside
+ * [0,E) is found on the GPU: that step changes nothing and writes -1 slot ids;
+ * moe_pool_last_step and moe_pool_sync report it as ERANGE, and so does any later
+ * prepare/step on the layer that runs after the GPU has flagged it.  A forward must
+ * follow its own prepare with no other layer's prepare in between (else ESTATE):
+ * staging is shared and the host does not know which steps fell back. */
 moe_status_t moe_pool_prepare(moe_pool_t* pool, int32_t layer, const int32_t* topk_ids_dev,
                               int32_t n_tokens, int32_t* slot_ids_dev,
                               moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss,
@@ -238,7 +257,17 @@ moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_
                            const void* resid_dev, void* out_dev, moe_miss_t* miss_host, int32_t miss_cap,
                            int32_t* n_miss, int32_t* path);
 
-/* Waits until all of the pool's copies and kernels issued so far are complete. */
+/* The path and misses of the layer's last prepare (or step), as that call would have
+ * returned them under MOE_POLICY_HOST; under MOE_POLICY_DEVICE the call first waits
+ * for the layer's queued work.  miss_host/n_miss/path as in moe_pool_prepare.
+ * Errors: EINVAL, ESTATE (no step yet since create or reset), ERANGE (that step had
+ * an id outside [0,E): it changed nothing), EHIP. */
+moe_status_t moe_pool_last_step(moe_pool_t* pool, int32_t layer, int32_t* path, moe_miss_t* miss_host,
+                                int32_t miss_cap, int32_t* n_miss);
+
+/* Waits until all of the pool's copies and kernels issued so far are complete.
+ * Under MOE_POLICY_DEVICE it then reports (and clears) an out-of-range id found by
+ * a queued step (ERANGE). */
 moe_status_t moe_pool_sync(moe_pool_t* pool);
 
 /* ---- introspection (tests, benchmarks) ------------------------------------ */
