@@ -122,22 +122,27 @@ struct FillBatch {
 hipError_t launch_fill(const FillBatch& b, hipStream_t s);
 
 // ---- the slot manager on the GPU -----------------------------------------------------
-// One layer's device-resident state (all HBM, int32 unless noted): map[E] (slot or
-// -1), owner[N] (expert or -1), free[N] (stack of free slots; meta[2] entries valid),
-// prev/next[E] (the LRU list over expert ids, -1 terminated), meta = {head, tail,
-// nfree}, ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d, staged}, rec = the
-// last step {path, D, n_miss, bad, then (expert, slot, evicted) per miss}, jobs = the
-// last step's copies {n, then (expert, slot or -(staging index)-1) per copy}.
-struct DevState {
+// One layer's LRU state (HBM, int32): map[E] (slot or -1), owner[N] (expert or -1),
+// free[N] (stack of free slots; meta[2] entries valid), prev/next[E] (the LRU list
+// over expert ids, -1 terminated), meta = {head, tail, nfree}.  Each layer keeps two
+// copies: a step reads one and writes the other, so that every workgroup of the step
+// can read the state it starts from while the first one writes the result.
+struct LruState {
     int32_t* map;
     int32_t* owner;
     int32_t* free;
     int32_t* prev;
     int32_t* next;
     int32_t* meta;
+};
+
+// The state copies plus ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d,
+// staged} and rec = the last step {path, D, n_miss, bad, then (expert, slot,
+// evicted) per miss}.
+struct DevState {
+    LruState s[2];
     unsigned long long* ctr;
     int32_t* rec;
-    int32_t* jobs;
 };
 
 struct PolicyArgs {
@@ -146,25 +151,23 @@ struct PolicyArgs {
     int E, N;
     int rule;                // 0: fallback iff D > N; 1: iff n > N (and D > 0)
     int resident;            // 1: every expert at slot = id (count hits only)
-    unsigned long long eb;   // bytes per expert (bytes_h2d counter)
-    DevState st;
+    unsigned long long eb;   // bytes per expert (bytes_h2d counter; a multiple of 16)
+    LruState src, dst;       // the state the step starts from / the one it leaves
+    unsigned long long* ctr;
+    int32_t* rec;
     int32_t* out;            // [n] slot ids (or staging ranks)
     int32_t* path;           // the layer's path word
     uint32_t* err;           // host-mapped: set to 1 when an id is outside [0, E)
-};
-size_t policy_lds_bytes(int E, int N);
-hipError_t launch_policy(const PolicyArgs& a, hipStream_t s);
-
-struct FillDevArgs {
-    const int32_t* jobs;     // DevState::jobs
+    // the copies (unused when resident)
     const char* const* pieces;  // device array: device-mapped base of each store piece
     int per_piece;           // experts per piece
-    size_t eb;               // bytes per expert (multiple of 16)
     char* slots;             // the layer's slot pool
     char* staging;           // the staging area
-    int32_t* timed_jobs;     // host-mapped, or null
+    int32_t* timed_jobs;     // host-mapped, or null: the step's copy count
 };
-hipError_t launch_fill_dev(const FillDevArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
+size_t policy_lds_bytes(int E, int N);
+// grid: workgroups of the launch (1 when resident; the copies spread over them).
+hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
 
 // One launch of the streaming-read calibration kernel over [p, p + bytes) (bytes a
 // multiple of 16), timed by the event pair; sink: 1 KiB of device scratch.

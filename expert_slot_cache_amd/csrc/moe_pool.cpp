@@ -109,6 +109,9 @@ struct Timing {
 
 // Pinned allocations are made in pieces of at most this many bytes (whole experts).
 constexpr size_t kStorePiece = (size_t)1 << 30;
+// Workgroups of one device-policy step: each runs the decision, then the copies
+// (64 KiB units) spread over all of them.
+constexpr int kPolicyGrid = 128;
 
 struct LayerState {
     moe::SlotLRU lru;
@@ -142,6 +145,7 @@ struct LayerState {
     // addresses (device array), and the fill timing of this layer
     char* dev_block = nullptr;
     moe::DevState ds{};
+    int par = 0;                 // the state copy the next step reads (ds.s[par])
     const char** pieces_dev = nullptr;
     bool last_empty = false;     // the last step had no tokens (not seen by the GPU)
     uint64_t empty_steps = 0;    // steps with no tokens (counted on the host)
@@ -628,10 +632,10 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
 // ---- MOE_POLICY_DEVICE ------------------------------------------------------------
 // Byte layout of one layer's device state block (see moe::DevState).
 struct DevLayout {
-    size_t map, owner, free, prev, next, meta, ctr, rec, jobs, total;
+    size_t map[2], owner[2], free[2], prev[2], next[2], meta[2], ctr, rec, total;
 };
 
-DevLayout dev_layout(int32_t E, int32_t N, int32_t max_jobs) {
+DevLayout dev_layout(int32_t E, int32_t N) {
     DevLayout d{};
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -639,36 +643,37 @@ DevLayout dev_layout(int32_t E, int32_t N, int32_t max_jobs) {
         o = round_up(o + bytes);
         return at;
     };
-    d.map = take((size_t)E * 4);
-    d.owner = take((size_t)N * 4);
-    d.free = take((size_t)N * 4);
-    d.prev = take((size_t)E * 4);
-    d.next = take((size_t)E * 4);
-    d.meta = take(16 * 4);
+    for (int c = 0; c < 2; ++c) {
+        d.map[c] = take((size_t)E * 4);
+        d.owner[c] = take((size_t)N * 4);
+        d.free[c] = take((size_t)N * 4);
+        d.prev[c] = take((size_t)E * 4);
+        d.next[c] = take((size_t)E * 4);
+        d.meta[c] = take(16 * 4);
+    }
     d.ctr = take(8 * 8);
     d.rec = take((size_t)(4 + 3 * N) * 4);
-    d.jobs = take((size_t)(1 + 2 * max_jobs) * 4);
     d.total = o;
     return d;
 }
 
-int32_t dev_max_jobs(const moe_pool* p) { return std::max(p->nslot_alloc, p->staging_cap); }
-
-// The cold state image: map -1, owners -1, free slots 0..N-1 (popped from the
-// end), empty LRU list, counters zero.
+// The cold state image (both copies): map -1, owners -1, free slots 0..N-1 (popped
+// from the end), empty LRU list, counters zero.
 std::vector<char> dev_cold_image(const moe_pool* p) {
     const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
-    const DevLayout d = dev_layout(E, N, dev_max_jobs(p));
+    const DevLayout d = dev_layout(E, N);
     std::vector<char> img(d.total, 0);
     auto w = [&](size_t off) { return reinterpret_cast<int32_t*>(img.data() + off); };
-    std::fill(w(d.map), w(d.map) + E, -1);
-    std::fill(w(d.owner), w(d.owner) + N, -1);
-    for (int32_t s2 = 0; s2 < N; ++s2) w(d.free)[s2] = s2;
-    std::fill(w(d.prev), w(d.prev) + E, -1);
-    std::fill(w(d.next), w(d.next) + E, -1);
-    w(d.meta)[0] = -1;
-    w(d.meta)[1] = -1;
-    w(d.meta)[2] = N;
+    for (int c = 0; c < 2; ++c) {
+        std::fill(w(d.map[c]), w(d.map[c]) + E, -1);
+        std::fill(w(d.owner[c]), w(d.owner[c]) + N, -1);
+        for (int32_t s2 = 0; s2 < N; ++s2) w(d.free[c])[s2] = s2;
+        std::fill(w(d.prev[c]), w(d.prev[c]) + E, -1);
+        std::fill(w(d.next[c]), w(d.next[c]) + E, -1);
+        w(d.meta[c])[0] = -1;
+        w(d.meta[c])[1] = -1;
+        w(d.meta[c])[2] = N;
+    }
     return img;
 }
 
@@ -676,6 +681,7 @@ moe_status_t dev_init_layers(moe_pool* p) {
     const std::vector<char> img = dev_cold_image(p);
     for (auto& L : p->layers) {
         HIPCHK(hipMemcpy(L.dev_block, img.data(), img.size(), hipMemcpyHostToDevice));
+        L.par = 0;
         L.has_last = false;
         L.last_empty = false;
         L.empty_steps = 0;
@@ -699,33 +705,34 @@ moe_status_t check_dev_err(moe_pool* p, int32_t layer) {
 moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
                          int32_t* slot_ids_dev) {
     const int n = n_tokens * p->cfg.top_k;
+    const bool resident = p->cfg.resident != 0;
     moe::PolicyArgs a{};
     a.ids = ids_dev;
     a.n = n;
     a.E = p->cfg.n_experts;
-    a.N = p->cfg.resident ? 0 : p->cfg.n_slots;
+    a.N = resident ? 0 : p->cfg.n_slots;
     a.rule = p->cfg.rule;
     a.resident = p->cfg.resident;
     a.eb = p->lay.total;
-    a.st = L.ds;
+    a.src = L.ds.s[L.par];
+    a.dst = L.ds.s[resident ? L.par : L.par ^ 1];
+    a.ctr = L.ds.ctr;
+    a.rec = L.ds.rec;
     a.out = slot_ids_dev;
     a.path = L.path_dev;
     a.err = p->errs_dev + layer;
-    HIPCHK(moe::launch_policy(a, p->compute));
-    if (!p->cfg.resident) {
-        moe::FillDevArgs f{};
-        f.jobs = L.ds.jobs;
-        f.pieces = L.pieces_dev;
-        f.per_piece = L.per_piece;
-        f.eb = p->lay.total;
-        f.slots = L.slots;
-        f.staging = p->staging;
-        const bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 &&
-                           !L.fill_t.pending;
-        f.timed_jobs = timed ? p->timed_jobs_dev + layer : nullptr;
-        HIPCHK(moe::launch_fill_dev(f, 128, timed ? L.fill_t.a : nullptr, timed ? L.fill_t.b : nullptr, p->compute));
-        if (timed) L.fill_t.pending = true;
-    }
+    a.pieces = L.pieces_dev;
+    a.per_piece = L.per_piece;
+    a.slots = L.slots;
+    a.staging = p->staging;
+    // the copy span of a timed step is the launch's (its decision takes a few us)
+    const bool timed = !resident && p->cfg.timing > 0 &&
+                       (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 && !L.fill_t.pending;
+    a.timed_jobs = timed ? p->timed_jobs_dev + layer : nullptr;
+    HIPCHK(moe::launch_policy(a, resident ? 1 : kPolicyGrid, timed ? L.fill_t.a : nullptr,
+                              timed ? L.fill_t.b : nullptr, p->compute));
+    if (timed) L.fill_t.pending = true;
+    if (!resident) L.par ^= 1;
     L.prepared = true;
     L.prep_tokens = n_tokens;
     L.prep_path = -1;            // known on the GPU only
@@ -915,12 +922,15 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         p->gate_limit = (unsigned long long)((10.0 + max_copy * 1e-9) * (double)std::max(khz, 1) * 1e3);
     }
     if (c.policy == MOE_POLICY_DEVICE) {
-        const DevLayout d = dev_layout(E, c.resident ? 0 : c.n_slots, dev_max_jobs(p));
+        const DevLayout d = dev_layout(E, c.resident ? 0 : c.n_slots);
         for (auto& L : p->layers) {
             CREATE_HIP(hipMalloc((void**)&L.dev_block, d.total));
             auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(L.dev_block + off); };
-            L.ds = moe::DevState{at(d.map), at(d.owner), at(d.free), at(d.prev), at(d.next), at(d.meta),
-                                 reinterpret_cast<unsigned long long*>(L.dev_block + d.ctr), at(d.rec), at(d.jobs)};
+            for (int k = 0; k < 2; ++k)
+                L.ds.s[k] = moe::LruState{at(d.map[k]), at(d.owner[k]), at(d.free[k]), at(d.prev[k]),
+                                          at(d.next[k]), at(d.meta[k])};
+            L.ds.ctr = reinterpret_cast<unsigned long long*>(L.dev_block + d.ctr);
+            L.ds.rec = at(d.rec);
             if (!L.store_dev.empty()) {
                 CREATE_HIP(hipMalloc((void**)&L.pieces_dev, sizeof(char*) * L.store_dev.size()));
                 CREATE_HIP(hipMemcpy(L.pieces_dev, L.store_dev.data(), sizeof(char*) * L.store_dev.size(),
@@ -1230,10 +1240,11 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
         const LayerState& L = p->layers[layer];
         const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
         std::vector<int32_t> map(E), owner(N), next(E), meta(16);
-        if ((st = dev_read(p, map.data(), L.ds.map, E))) return st;
-        if (N && (st = dev_read(p, owner.data(), L.ds.owner, N))) return st;
-        if ((st = dev_read(p, next.data(), L.ds.next, E))) return st;
-        if ((st = dev_read(p, meta.data(), L.ds.meta, 16))) return st;
+        const moe::LruState& cur = L.ds.s[L.par];
+        if ((st = dev_read(p, map.data(), cur.map, E))) return st;
+        if (N && (st = dev_read(p, owner.data(), cur.owner, N))) return st;
+        if ((st = dev_read(p, next.data(), cur.next, E))) return st;
+        if ((st = dev_read(p, meta.data(), cur.meta, 16))) return st;
         if (map_E) std::copy(map.begin(), map.end(), map_E);
         if (owner_N) std::copy(owner.begin(), owner.end(), owner_N);
         if (lru_N) {

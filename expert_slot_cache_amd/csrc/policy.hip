@@ -1,8 +1,8 @@
-// The slot manager on the GPU (policy = MOE_POLICY_DEVICE): one kernel per step
+// The slot manager on the GPU (policy = MOE_POLICY_DEVICE): one launch per step
 // computes the step's distinct expert ids, applies the route rule, runs the LRU on
-// the layer's state in HBM, remaps the ids, and writes the step's copy jobs; a copy
-// kernel then pulls the missed (or staged) experts from the pinned store.  Nothing
-// waits for the host, so a whole decode step can be queued at once.
+// the layer's state in HBM, remaps the ids, and pulls the missed (or staged)
+// experts from the pinned store.  Nothing waits for the host, so a whole decode
+// step can be queued at once.
 //
 // The LRU is the one of vLLM PR "Run MoE models exceeding VRAM via expert CPU
 // offloading with GPU cache" (section "How it works" and the review thread's
@@ -13,6 +13,12 @@
 // exceeds the slots takes the selective-copy path and leaves the state untouched).
 // It is the same state machine as the host slot manager, kept as the same arrays:
 // map[E], owner[N], a free stack, and a doubly linked LRU list over expert ids.
+//
+// Every workgroup of the launch runs the same decision on its own copy of the state
+// in LDS (a few microseconds of latency, the same in each), so that each knows the
+// step's copies without waiting for another workgroup; the first one also writes the
+// results.  The state is double-buffered (read one copy, write the other) so that
+// no workgroup can read a half-written state.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -22,10 +28,13 @@
 
 namespace moe {
 
-constexpr int kPolicyThreads = 1024;
+constexpr int kPolicyThreads = 256;
+constexpr int kPolicyWaves = kPolicyThreads / 64;
+constexpr size_t kFillUnit = (size_t)64 << 10;   // bytes of one copy work unit
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-// The step.  Dynamic LDS: map, prev, next, rank, list [E] and owner, free [N]
-// (int32), then the presence bits [E/32 + 1].
+// Dynamic LDS: map, prev, next, rank, list [E] and owner, free [N] (int32), then the
+// presence bits [E/32 + 1].
 __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     extern __shared__ int32_t sm[];
     const int E = a.E, N = a.N;
@@ -37,18 +46,36 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     int32_t* own = list + E;
     int32_t* fre = own + N;
     uint32_t* bits = reinterpret_cast<uint32_t*>(fre + N);
-    __shared__ int32_t wave_cnt[kPolicyThreads / 64];
-    __shared__ int32_t s_bad;
+    __shared__ int32_t wave_cnt[kPolicyWaves];
+    __shared__ int32_t s_bad, s_njobs;
+    __shared__ int32_t s_meta[3];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int nwords = (E + 31) >> 5;
-    DevState st = a.st;
+    const bool lead = blockIdx.x == 0;
+    unsigned long long* ctr = a.ctr;   // steps, hits, misses, fallbacks, bytes_h2d, staged
+    int32_t* rec = a.rec;
 
-    // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt)
+    // 0. the state the step starts from (loaded first: its latency overlaps the
+    // distinct-id pass), and an empty presence bitmap
+    if (!a.resident) {
+        for (int e = tid; e < E; e += kPolicyThreads) {
+            map[e] = a.src.map[e];
+            prv[e] = a.src.prev[e];
+            nxt[e] = a.src.next[e];
+        }
+        for (int s = tid; s < N; s += kPolicyThreads) {
+            own[s] = a.src.owner[s];
+            fre[s] = a.src.free[s];
+        }
+        if (tid < 3) s_meta[tid] = a.src.meta[tid];
+    }
     for (int i = tid; i < nwords; i += kPolicyThreads) bits[i] = 0u;
     if (tid == 0) s_bad = 0;
     __syncthreads();
+
+    // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt)
     for (int i = tid; i < a.n; i += kPolicyThreads) {
         const int e = a.ids[i];
         if ((unsigned)e < (unsigned)E)
@@ -66,7 +93,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         if (lane == 0) wave_cnt[wave] = __popcll(m);
         __syncthreads();
         int off = 0, total = 0;
-        for (int w = 0; w < kPolicyThreads / 64; ++w) {
+        for (int w = 0; w < kPolicyWaves; ++w) {
             const int cnt = wave_cnt[w];
             off += (w < wave) ? cnt : 0;
             total += cnt;
@@ -80,200 +107,193 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         __syncthreads();
     }
     const int D = base;
-    int32_t* rec = st.rec;
-    int32_t* jobs = st.jobs;
-    if (s_bad) {
-        // an id outside [0, E): nothing changes, the step produces no expert
-        for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = -1;
-        if (tid == 0) {
-            *a.path = PATH_NONE;
-            rec[0] = PATH_NONE;
-            rec[1] = D;
-            rec[2] = 0;
-            rec[3] = 1;
-            jobs[0] = 0;
-            __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-        return;
-    }
-    unsigned long long* ctr = st.ctr;   // steps, hits, misses, fallbacks, bytes_h2d, staged
+
     if (a.resident) {
         // every expert lives at slot = id: count the hits, the ids are the slots
-        for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = a.ids[i];
-        if (tid == 0) {
-            *a.path = PATH_POOL;
-            rec[0] = PATH_POOL;
-            rec[1] = D;
-            rec[2] = 0;
-            rec[3] = 0;
-            jobs[0] = 0;
-            ctr[0] += 1;
-            ctr[1] += (unsigned long long)D;
-        }
-        return;
-    }
-    // 2. route rule ([llama-pool] prefill rule): distinct ids above the slots, or
-    // (static rule) pairs above the slots
-    const bool fallback = a.rule == 1 ? (a.n > N && D > 0) : (D > N);
-    if (fallback) {
-        // selective copy: the step's experts go to staging in rank order; the pool
-        // state is untouched
-        for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = rank[a.ids[i]];
-        for (int r = tid; r < D; r += kPolicyThreads) {
-            jobs[1 + 2 * r] = list[r];
-            jobs[2 + 2 * r] = -(r + 1);
+        // (a single-workgroup launch; nothing to copy)
+        if (s_bad) {
+            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = -1;
+        } else {
+            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = a.ids[i];
         }
         if (tid == 0) {
-            *a.path = PATH_STAGE;
-            rec[0] = PATH_STAGE;
+            *a.path = s_bad ? PATH_NONE : PATH_POOL;
+            rec[0] = s_bad ? PATH_NONE : PATH_POOL;
             rec[1] = D;
             rec[2] = 0;
-            rec[3] = 0;
-            jobs[0] = D;
-            ctr[0] += 1;
-            ctr[3] += 1;
-            ctr[4] += (unsigned long long)D * a.eb;
-            ctr[5] += (unsigned long long)D;
-        }
-        return;
-    }
-    // 3. the LRU, in LDS
-    for (int e = tid; e < E; e += kPolicyThreads) {
-        map[e] = st.map[e];
-        prv[e] = st.prev[e];
-        nxt[e] = st.next[e];
-    }
-    for (int s = tid; s < N; s += kPolicyThreads) {
-        own[s] = st.owner[s];
-        fre[s] = st.free[s];
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int head = st.meta[0], tail = st.meta[1], nfree = st.meta[2];
-        int hits = 0, misses = 0;
-        auto unlink = [&](int e) {
-            const int p = prv[e], q = nxt[e];
-            if (p >= 0) nxt[p] = q; else head = q;
-            if (q >= 0) prv[q] = p; else tail = p;
-            prv[e] = nxt[e] = -1;
-        };
-        auto push_mru = [&](int e) {
-            prv[e] = tail;
-            nxt[e] = -1;
-            if (tail >= 0) nxt[tail] = e; else head = e;
-            tail = e;
-        };
-        for (int i = 0; i < D; ++i) {
-            const int e = list[i];
-            if (map[e] >= 0) {
-                unlink(e);
-                push_mru(e);
-                ++hits;
-                continue;
-            }
-            int slot, evicted;
-            if (nfree > 0) {
-                slot = fre[--nfree];
-                evicted = -1;
+            rec[3] = s_bad;
+            if (s_bad) {
+                __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             } else {
-                evicted = head;
-                unlink(evicted);
-                slot = map[evicted];
-                map[evicted] = -1;
+                ctr[0] += 1;
+                ctr[1] += (unsigned long long)D;
             }
-            map[e] = slot;
-            own[slot] = e;
-            push_mru(e);
-            rec[4 + 3 * misses] = e;
-            rec[5 + 3 * misses] = slot;
-            rec[6 + 3 * misses] = evicted;
-            jobs[1 + 2 * misses] = e;
-            jobs[2 + 2 * misses] = slot;
-            ++misses;
         }
-        st.meta[0] = head;
-        st.meta[1] = tail;
-        st.meta[2] = nfree;
-        *a.path = PATH_POOL;
-        rec[0] = PATH_POOL;
-        rec[1] = D;
-        rec[2] = misses;
-        rec[3] = 0;
-        jobs[0] = misses;
-        ctr[0] += 1;
-        ctr[1] += (unsigned long long)hits;
-        ctr[2] += (unsigned long long)misses;
-        ctr[4] += (unsigned long long)misses * a.eb;
+        return;
     }
-    __syncthreads();
-    // 4. write the state back and remap through the fresh table
-    for (int e = tid; e < E; e += kPolicyThreads) {
-        st.map[e] = map[e];
-        st.prev[e] = prv[e];
-        st.next[e] = nxt[e];
+
+    // 2. the step's outcome; every branch leaves the copies in list[0, njobs) with
+    // their destinations (pool: the expert's slot; staging: the list position)
+    int njobs = 0;
+    bool pool = true;
+    if (s_bad) {
+        // an id outside [0, E): nothing changes, the step produces no expert
+        if (lead) {
+            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = -1;
+            if (tid == 0) {
+                *a.path = PATH_NONE;
+                rec[0] = PATH_NONE;
+                rec[1] = D;
+                rec[2] = 0;
+                rec[3] = 1;
+                __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+    } else if (a.rule == 1 ? (a.n > N && D > 0) : (D > N)) {
+        // route rule ([llama-pool] prefill rule): selective copy -- the step's experts
+        // go to staging in rank order; the pool state is untouched
+        pool = false;
+        njobs = D;
+        if (lead) {
+            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = rank[a.ids[i]];
+            if (tid == 0) {
+                *a.path = PATH_STAGE;
+                rec[0] = PATH_STAGE;
+                rec[1] = D;
+                rec[2] = 0;
+                rec[3] = 0;
+                ctr[0] += 1;
+                ctr[3] += 1;
+                ctr[4] += (unsigned long long)D * a.eb;
+                ctr[5] += (unsigned long long)D;
+            }
+        }
+    } else {
+        // 3. the LRU, in LDS, one id at a time.  Miss j's expert is written to list[j]
+        // (j <= the id being processed, so nothing unread is overwritten).
+        if (tid == 0) {
+            int head = s_meta[0], tail = s_meta[1], nfree = s_meta[2];
+            int hits = 0, misses = 0;
+            auto unlink = [&](int e) {
+                const int p = prv[e], q = nxt[e];
+                if (p >= 0) nxt[p] = q; else head = q;
+                if (q >= 0) prv[q] = p; else tail = p;
+                prv[e] = nxt[e] = -1;
+            };
+            auto push_mru = [&](int e) {
+                prv[e] = tail;
+                nxt[e] = -1;
+                if (tail >= 0) nxt[tail] = e; else head = e;
+                tail = e;
+            };
+            for (int i = 0; i < D; ++i) {
+                const int e = list[i];
+                if (map[e] >= 0) {
+                    unlink(e);
+                    push_mru(e);
+                    ++hits;
+                    continue;
+                }
+                int slot, evicted;
+                if (nfree > 0) {
+                    slot = fre[--nfree];
+                    evicted = -1;
+                } else {
+                    evicted = head;
+                    unlink(evicted);
+                    slot = map[evicted];
+                    map[evicted] = -1;
+                }
+                map[e] = slot;
+                own[slot] = e;
+                push_mru(e);
+                if (lead) {
+                    rec[4 + 3 * misses] = e;
+                    rec[5 + 3 * misses] = slot;
+                    rec[6 + 3 * misses] = evicted;
+                }
+                list[misses] = e;
+                ++misses;
+            }
+            s_meta[0] = head;
+            s_meta[1] = tail;
+            s_meta[2] = nfree;
+            s_njobs = misses;
+            if (lead) {
+                *a.path = PATH_POOL;
+                rec[0] = PATH_POOL;
+                rec[1] = D;
+                rec[2] = misses;
+                rec[3] = 0;
+                ctr[0] += 1;
+                ctr[1] += (unsigned long long)hits;
+                ctr[2] += (unsigned long long)misses;
+                ctr[4] += (unsigned long long)misses * a.eb;
+            }
+        }
+        __syncthreads();
+        njobs = s_njobs;
+        // the remap, through the fresh table
+        if (lead)
+            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = map[a.ids[i]];
     }
-    for (int s = tid; s < N; s += kPolicyThreads) {
-        st.owner[s] = own[s];
-        st.free[s] = fre[s];
+
+    // 4. the state the step leaves (unchanged unless the LRU ran)
+    if (lead) {
+        for (int e = tid; e < E; e += kPolicyThreads) {
+            a.dst.map[e] = map[e];
+            a.dst.prev[e] = prv[e];
+            a.dst.next[e] = nxt[e];
+        }
+        for (int s = tid; s < N; s += kPolicyThreads) {
+            a.dst.owner[s] = own[s];
+            a.dst.free[s] = fre[s];
+        }
+        if (tid < 3) a.dst.meta[tid] = s_meta[tid];
+        if (tid == 0 && a.timed_jobs)
+            __hip_atomic_store(a.timed_jobs, njobs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = map[a.ids[i]];
-}
 
-size_t policy_lds_bytes(int E, int N) { return ((size_t)5 * E + 2 * N + E / 32 + 1) * sizeof(int32_t); }
-
-hipError_t launch_policy(const PolicyArgs& a, hipStream_t s) {
-    if (a.n < 1 || a.n > (1 << 24)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_policy, dim3(1), dim3(kPolicyThreads), policy_lds_bytes(a.E, a.N), s, a);
-    return hipGetLastError();
-}
-
-// The step's copy jobs (written by k_policy): job j copies expert jobs[1 + 2j]
-// from the pinned store to slot jobs[2 + 2j] (>= 0) or staging entry
-// -jobs[2 + 2j] - 1.  Work unit u: job u / units_per_job, 64 KiB of it.  When
-// `timed_jobs` is set, one thread records the launch's job count there (host-mapped)
-// so that event timings of launches without copies can be told apart.
-constexpr int kFillDevThreads = 256;
-constexpr size_t kFillDevUnit = (size_t)64 << 10;
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(kFillDevThreads) void k_fill_dev(FillDevArgs a) {
-    const int njobs = a.jobs[0];
-    if (blockIdx.x == 0 && threadIdx.x == 0 && a.timed_jobs)
-        __hip_atomic_store(a.timed_jobs, njobs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const size_t upj = (a.eb + kFillDevUnit - 1) / kFillDevUnit;
-    const size_t total = upj * (size_t)njobs;
-    for (size_t u = blockIdx.x; u < total; u += gridDim.x) {
+    // 5. the copies: 64 KiB work units over the launch, store -> slot / staging
+    const size_t eb = a.eb;
+    const size_t upj = (eb + kFillUnit - 1) / kFillUnit;
+    const size_t units = upj * (size_t)njobs;
+    for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
         const int j = (int)(u / upj);
-        const int e = a.jobs[1 + 2 * j];
-        const int d = a.jobs[2 + 2 * j];
-        const size_t off = (u - (size_t)j * upj) * kFillDevUnit;
-        const size_t nvec = (a.eb - off < kFillDevUnit ? a.eb - off : kFillDevUnit) / 16;
-        const char* src = a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * a.eb + off;
-        char* dst = (d >= 0 ? a.slots + (size_t)d * a.eb : a.staging + (size_t)(-d - 1) * a.eb) + off;
+        const int e = list[j];
+        const size_t off = (u - (size_t)j * upj) * kFillUnit;
+        const size_t nvec = (eb - off < kFillUnit ? eb - off : kFillUnit) / 16;
+        const char* src = a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * eb + off;
+        char* dst = (pool ? a.slots + (size_t)map[e] * eb : a.staging + (size_t)j * eb) + off;
         const u32x4v* __restrict__ s4 = reinterpret_cast<const u32x4v*>(src);
         u32x4v* __restrict__ d4 = reinterpret_cast<u32x4v*>(dst);
-        for (size_t i0 = threadIdx.x; i0 < nvec; i0 += 4 * kFillDevThreads) {
+        for (size_t i0 = tid; i0 < nvec; i0 += 4 * kPolicyThreads) {
             u32x4v v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const size_t i = i0 + (size_t)q * kFillDevThreads;
+                const size_t i = i0 + (size_t)q * kPolicyThreads;
                 if (i < nvec) v[q] = s4[i];
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const size_t i = i0 + (size_t)q * kFillDevThreads;
+                const size_t i = i0 + (size_t)q * kPolicyThreads;
                 if (i < nvec) __builtin_nontemporal_store(v[q], d4 + i);
             }
         }
     }
 }
 
-hipError_t launch_fill_dev(const FillDevArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s) {
-    if (grid < 1 || a.eb % 16) return hipErrorInvalidValue;
+size_t policy_lds_bytes(int E, int N) { return ((size_t)5 * E + 2 * N + E / 32 + 1) * sizeof(int32_t); }
+
+hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s) {
+    if (a.n < 1 || a.n > (1 << 24) || grid < 1 || (a.resident && grid != 1) || a.eb % 16 ||
+        (!a.resident && a.per_piece < 1))
+        return hipErrorInvalidValue;
+    const size_t lds = policy_lds_bytes(a.E, a.N);
     if (start)
-        hipExtLaunchKernelGGL(k_fill_dev, dim3(grid), dim3(kFillDevThreads), 0, s, start, stop, 0, a);
+        hipExtLaunchKernelGGL(k_policy, dim3(grid), dim3(kPolicyThreads), lds, s, start, stop, 0, a);
     else
-        hipLaunchKernelGGL(k_fill_dev, dim3(grid), dim3(kFillDevThreads), 0, s, a);
+        hipLaunchKernelGGL(k_policy, dim3(grid), dim3(kPolicyThreads), lds, s, a);
     return hipGetLastError();
 }
 
