@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--policy", default="device", choices=["host", "device"],
                     help="slot manager: LRU on the host (reads back the distinct ids) or in one GPU "
                          "workgroup (no host round trip on the decode path)")
+    ap.add_argument("--read-through", type=int, default=0, choices=[0, 1],
+                    help="device policy, one token per step: the forward's kernels read missed experts "
+                         "from the pinned store and write them through to their slots (no copy first)")
     ap.add_argument("--no-timing", action="store_true", help="no HIP events around kernels")
     ap.add_argument("--timing-every", type=int, default=7,
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
@@ -169,7 +172,8 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
                            wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
                            max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20, copy_engine=args.copy_engine,
-                           policy=args.policy, timing=0 if args.no_timing else args.timing_every)
+                           policy=args.policy, read_through=bool(args.read_through) and args.policy == "device"
+                           and not resident, timing=0 if args.no_timing else args.timing_every)
     eb = pool.expert_nbytes
     if resident:
         buf = np.empty(eb, np.uint8)
@@ -337,7 +341,8 @@ def main():
                    "inter": I, "slots": slots, "tokens_per_step": T, "weights": wl.wtype,
                    "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
                    "resident": args.resident, "copy_streams": args.copy_streams,
-                   "copy_engine": args.copy_engine, "policy": args.policy},
+                   "copy_engine": args.copy_engine, "policy": args.policy,
+                   "read_through": bool(args.read_through) and args.policy == "device" and not args.resident},
     }
     for k, v in main_res.items():
         if k not in ("value", "ms_per_step", "slots", "roofline"):

@@ -51,7 +51,8 @@ class Config(C.Structure):
                 ("wtype", C.c_int32), ("atype", C.c_int32), ("rule", C.c_int32),
                 ("resident", C.c_int32), ("max_tokens", C.c_int32), ("n_copy_streams", C.c_int32),
                 ("copy_chunk_bytes", C.c_size_t), ("hbm_budget_bytes", C.c_size_t),
-                ("timing", C.c_int32), ("copy_engine", C.c_int32), ("policy", C.c_int32)]
+                ("timing", C.c_int32), ("copy_engine", C.c_int32), ("policy", C.c_int32),
+                ("read_through", C.c_int32)]
 
 
 class Miss(C.Structure):
@@ -164,12 +165,13 @@ class MoePool:
                  slots: int, wtype: str = "bf16", atype: str = "bf16", rule: str = "distinct",
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
-                 copy_engine: str = "kernel", policy: str = "host", stream=None):
+                 copy_engine: str = "kernel", policy: str = "host", read_through: bool = False,
+                 stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
                      copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine],
-                     POLICIES[policy])
+                     POLICIES[policy], int(bool(read_through)))
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -181,6 +183,7 @@ class MoePool:
         self.hidden, self.inter, self.slots = hidden, inter, slots
         self.wtype, self.atype, self.resident = wtype, atype, resident
         self.policy = policy
+        self.read_through = bool(read_through)
         self.max_tokens = max_tokens
         self.expert_nbytes = expert_bytes(wtype, hidden, inter)
         self._miss_buf = (Miss * max(1, experts))()

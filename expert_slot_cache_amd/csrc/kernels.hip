@@ -346,6 +346,28 @@ struct SlotReader {
     }
 };
 
+// Vector stores into a slot: the write-through of an expert that a kernel reads from
+// the pinned store (the bytes land in the slot exactly as read; a scale goes back
+// to its bf16 bits, which the widening above keeps exactly).
+struct SlotWriter {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ SlotWriter(char* base, size_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000)) {}
+    __device__ __forceinline__ void store16(size_t off, uint4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ void store_scale(size_t off, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(__float_as_uint(v) >> 16), r, (int)off, 0, 0);
+    }
+};
+
+// The pair's source override (null pointers when the forward reads slots only).
+__device__ __forceinline__ PairSrc pair_src(const Slots& sl, int pair) {
+    PairSrc ps{nullptr, nullptr};
+    if (sl.src) ps = sl.src[pair];
+    return ps;
+}
+
 // Activation-sized reads of a buffer, by byte offset (data written by an earlier
 // kernel).
 struct PlainMem {
@@ -533,6 +555,7 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
     const int slot = slot_ids[pair];
+    const PairSrc ps = pair_src(sl, pair);
     const char* wbase;
     int nslots;
     pick_slots(sl, wbase, nslots);
@@ -549,9 +572,9 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     const bool ok = slot >= 0 && slot < nslots && i0 < I;
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
-    // the slot's address in scalar registers before the branch, so that the
+    // the expert's address in scalar registers before the branch, so that the
     // arguments it needs are loaded with the others (one round trip, not two)
-    const char* ebase = wbase + (size_t)slot * stride;
+    const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
 
     float pg[RP], pu[RP];
@@ -591,6 +614,37 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
         // every load of the lane is in flight before the first use: the scheduler
         // would otherwise hold some back to save registers (two round trips)
         __builtin_amdgcn_sched_barrier(0);
+        if (ps.to) {
+            // a miss read from the store: the lane writes what it read to the slot
+            const SlotWriter wr(ps.to, stride);
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                const int i = min(i0 + p, I - 1);
+                const size_t g = off_w + (size_t)i * row_bytes;
+                const size_t u = off_w + (size_t)(I + i) * row_bytes;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const int c = (part * CPL + j) * G + gl;
+                    wr.store16(g + (size_t)c * 16, wg[p][j]);
+                    wr.store16(u + (size_t)c * 16, wu[p][j]);
+                }
+            }
+            if (WT == W_INT4) {
+                const int spr = H / 128;
+#pragma unroll
+                for (int p = 0; p < RP; ++p) {
+                    const int i = min(i0 + p, I - 1);
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        const int c = (part * CPL + j) * G + gl;
+                        if ((c & 3) == 0) {
+                            wr.store_scale(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
+                            wr.store_scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
+                        }
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
             float a = 0.0f, b = 0.0f;
@@ -676,6 +730,7 @@ struct W2Task {
     int pair;            // t * K + k
     int part;
     bool ok;             // the pair's slot id is valid
+    char* to;            // write-through slot of an expert read from the store, or null
 };
 
 // Lane geometry of a w2 workgroup.
@@ -697,14 +752,15 @@ __device__ __forceinline__ W2Lane w2_lane(int gs, int RP, int rb0) {
 // read together with the path word, before any branch).
 template <int WT, int CPL, int RP, int WPR>
 __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wbase, int nslots, size_t stride,
-                                         int slot, int t, int K, int H, int I, int gs, const W2Lane& ln, int task,
-                                         size_t off_w, size_t off_s) {
+                                         int slot, const PairSrc& ps, int t, int K, int H, int I, int gs,
+                                         const W2Lane& ln, int task, size_t off_w, size_t off_s) {
     const int G = 1 << gs;
     const int k = task / WPR;
     tk.part = task - k * WPR;
     tk.pair = t * K + k;
     tk.ok = slot >= 0 && slot < nslots;
-    const char* ebase = wbase + (size_t)slot * stride;
+    tk.to = ps.to;
+    const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
     if (!tk.ok) return;
     const size_t row_bytes = (size_t)CPL * G * WPR * 16;
@@ -728,9 +784,10 @@ __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wb
 
 // The dot products of a fetched task against its act row (read through m); the
 // RP results go to ys[task][grp * RP + p].
-template <int WT, int CPL, int RP, class M>
-__device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M& m, int I, int gs,
-                                          const W2Lane& ln, float* __restrict__ yk) {
+template <int WT, int CPL, int RP, int WPR, class M>
+__device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M& m, int H, int I, int gs,
+                                          const W2Lane& ln, size_t stride, size_t off_w, size_t off_s,
+                                          float* __restrict__ yk) {
     const int G = 1 << gs;
     constexpr int ACT = ActOf<WT>::AT;
     using X = XChunk<WT, XSel<WT, ACT>::XT>;
@@ -745,6 +802,22 @@ __device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M
     for (int j = 0; j < CPL; ++j)
         av[j].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
     __builtin_amdgcn_sched_barrier(0);
+    if (tk.to) {
+        // a miss read from the store: the lane writes what it read to the slot
+        const SlotWriter wr(tk.to, stride);
+        const size_t row_bytes = (size_t)CPL * G * WPR * 16;
+        const int spr = I / 128;
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int r = min(ln.r0 + p, H - 1);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = (tk.part * CPL + j) * G + ln.gl;
+                wr.store16(off_w + (size_t)r * row_bytes + (size_t)c * 16, tk.w[p][j]);
+                if (WT == W_INT4 && (c & 3) == 0) wr.store_scale(off_s + ((size_t)r * spr + (c >> 2)) * 2, tk.sc[p][j]);
+            }
+        }
+    }
     float acc[RP];
 #pragma unroll
     for (int p = 0; p < RP; ++p) {
@@ -807,17 +880,20 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
     if (ONE) {
         // the wave's slot and the path word, side by side, before any branch
         const int slot = slot_ids[t * K + wave / WPR];
+        const PairSrc ps = pair_src(sl, t * K + wave / WPR);
         pick_slots(sl, wbase, nslots);
         W2Task<WT, CPL, RP> tk;
-        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, t, K, H, I, gs, ln, wave, off_w, off_s);
-        w2_finish<WT, CPL, RP>(tk, PlainMem(act), I, gs, ln, ys + (size_t)wave * ln.RB + ln.grp * RP);
+        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, ps, t, K, H, I, gs, ln, wave, off_w, off_s);
+        w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
+                                    ys + (size_t)wave * ln.RB + ln.grp * RP);
     } else {
         pick_slots(sl, wbase, nslots);
         for (int task = wave; task < K * WPR; task += nw) {
             W2Task<WT, CPL, RP> tk;
-            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR], t, K, H, I, gs, ln,
-                                       task, off_w, off_s);
-            w2_finish<WT, CPL, RP>(tk, PlainMem(act), I, gs, ln, ys + (size_t)task * ln.RB + ln.grp * RP);
+            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR],
+                                       pair_src(sl, t * K + task / WPR), t, K, H, I, gs, ln, task, off_w, off_s);
+            w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
+                                        ys + (size_t)task * ln.RB + ln.grp * RP);
         }
     }
     __syncthreads();

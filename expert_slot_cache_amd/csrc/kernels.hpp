@@ -69,12 +69,21 @@ struct StageEvents {
 
 // The two places a layer's experts can be read from; *path (written by the
 // step's remap) picks one: PATH_POOL -> pool, PATH_STAGE -> stage, PATH_NONE -> none.
+// Where a (token, expert) pair's expert is read from when it is not its slot: the
+// expert in the device-mapped pinned store (`from`), and the slot it is written
+// through to as it is read (`to`, or null).
+struct PairSrc {
+    const char* from;
+    char* to;
+};
+
 struct Slots {
     const char* pool;
     const char* stage;
     int npool;              // valid slot ids in the pool: [0, npool)
     int nstage;             // valid staging ranks: [0, nstage)
     const int32_t* path;    // device word
+    const PairSrc* src;     // null, or per pair: a non-null `from` replaces the slot (decode GEMVs)
 };
 
 struct ForwardArgs {
@@ -163,7 +172,9 @@ struct PolicyArgs {
     int per_piece;           // experts per piece
     char* slots;             // the layer's slot pool
     char* staging;           // the staging area
-    int32_t* timed_jobs;     // host-mapped, or null: the step's copy count
+    int32_t* timed_jobs;     // host-mapped, or null: experts the step moves over the link
+    PairSrc* tab;            // null: copy the step's experts; else [n]: the forward reads them
+                             // through (misses are written to their slots on the way)
 };
 size_t policy_lds_bytes(int E, int N);
 // grid: workgroups of the launch (1 when resident; the copies spread over them).

@@ -146,6 +146,8 @@ struct LayerState {
     char* dev_block = nullptr;
     moe::DevState ds{};
     int par = 0;                 // the state copy the next step reads (ds.s[par])
+    bool rt_prepared = false;    // the current prepare left a pair table (read-through forward)
+    bool rt_sample = false;      // the pending w13/w2 timing sample is a read-through step
     const char** pieces_dev = nullptr;
     bool last_empty = false;     // the last step had no tokens (not seen by the GPU)
     uint64_t empty_steps = 0;    // steps with no tokens (counted on the host)
@@ -186,6 +188,9 @@ struct moe_pool {
     uint32_t* errs_dev = nullptr;
     int32_t* timed_jobs_host = nullptr; // pinned coherent [n_layers]: jobs of the last timed fill
     int32_t* timed_jobs_dev = nullptr;
+    int32_t* rt_jobs_host = nullptr;    // pinned coherent [n_layers]: experts read through by the
+    int32_t* rt_jobs_dev = nullptr;     //   last timed read-through step
+    moe::PairSrc* tab_dev = nullptr;    // [top_k]: the read-through pair table (one-token steps)
     int32_t last_prepared = -1;         // the layer of the latest prepare (device policy)
     std::vector<char> used_copy;
     int copy_rr = 0;
@@ -238,6 +243,8 @@ void destroy_pool(moe_pool* p) {
     if (p->grp) (void)hipFree(p->grp);
     if (p->errs_host) (void)hipHostFree(p->errs_host);
     if (p->timed_jobs_host) (void)hipHostFree(p->timed_jobs_host);
+    if (p->rt_jobs_host) (void)hipHostFree(p->rt_jobs_host);
+    if (p->tab_dev) (void)hipFree(p->tab_dev);
     delete p;
 }
 
@@ -259,7 +266,7 @@ bool harvest(moe_pool* p, Timing& t, double* acc) {
     return ok;
 }
 
-void harvest_layer(moe_pool* p, LayerState& L) {
+void harvest_layer(moe_pool* p, LayerState& L, int32_t l) {
     if (!p->cfg.timing) return;
     // the copy span of a step: earliest start to latest stop over the copy streams
     bool any = false, ready = true;
@@ -292,6 +299,23 @@ void harvest_layer(moe_pool* p, LayerState& L) {
         p->copy_bytes += bytes;
     }
     if (L.w13_t.pending && L.w2_t.pending && (!done(L.w13_t) || !done(L.w2_t))) return;
+    if (L.rt_sample && L.w13_t.pending && L.w2_t.pending) {
+        // a read-through step: with experts read over the link its two launches are
+        // the step's transfer span; without, a forward like any other
+        L.rt_sample = false;
+        const int32_t jobs = ((volatile int32_t*)p->rt_jobs_host)[l];
+        if (jobs > 0) {
+            double ms = 0;
+            const bool a = harvest(p, L.w13_t, &ms);
+            const bool b = harvest(p, L.w2_t, &ms);
+            if (a && b) {
+                p->copy_ms += ms;
+                p->copy_calls++;
+                p->copy_bytes += (uint64_t)jobs * p->lay.total;
+            }
+            return;
+        }
+    }
     const bool a = harvest(p, L.w13_t, &p->w13_ms);
     const bool b = harvest(p, L.w2_t, &p->w2_ms);
     if (a && b) p->kern_calls++;
@@ -315,7 +339,7 @@ void harvest_fill(moe_pool* p, int32_t l) {
 }
 
 void harvest_all(moe_pool* p) {
-    for (auto& L : p->layers) harvest_layer(p, L);
+    for (int32_t l = 0; l < p->cfg.n_layers; ++l) harvest_layer(p, p->layers[l], l);
     if (p->cfg.policy == MOE_POLICY_DEVICE)
         for (int32_t l = 0; l < p->cfg.n_layers; ++l) harvest_fill(p, l);
 }
@@ -594,11 +618,14 @@ void finish_prepare(moe_pool* p, LayerState& L, int32_t n_tokens, int32_t the_pa
 }
 
 moe::Slots layer_slots(const moe_pool* p, const LayerState& L) {
-    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev};
+    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev,
+                      L.rt_prepared ? p->tab_dev : nullptr};
 }
 
+// timed: -1 = sample by the timing period, else as given (already counted).
 moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
-                                  const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev) {
+                                  const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev,
+                                  int timed_as = -1) {
     moe::ForwardArgs a{};
     a.sl = layer_slots(p, L);
     a.slot_ids = slot_ids_dev;
@@ -613,8 +640,9 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
     a.nslots_alloc = std::max(1, p->grp_slots);
     a.max_pairs = p->cfg.max_tokens * p->cfg.top_k;
     moe::StageEvents ev;
-    const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
-                       !L.w13_t.pending && !L.w2_t.pending;
+    const bool timed = timed_as >= 0 ? timed_as > 0
+                                     : p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
+                                           !L.w13_t.pending && !L.w2_t.pending;
     if (timed) {
         ev.w13_start = L.w13_t.a;
         ev.w13_stop = L.w13_t.b;
@@ -682,6 +710,8 @@ moe_status_t dev_init_layers(moe_pool* p) {
     for (auto& L : p->layers) {
         HIPCHK(hipMemcpy(L.dev_block, img.data(), img.size(), hipMemcpyHostToDevice));
         L.par = 0;
+        L.rt_prepared = false;
+        L.rt_sample = false;
         L.has_last = false;
         L.last_empty = false;
         L.empty_steps = 0;
@@ -702,8 +732,10 @@ moe_status_t check_dev_err(moe_pool* p, int32_t layer) {
 }
 
 // Queue the slot manager and the copy kernel for one step (n_tokens >= 1).
+// rt: leave the pair table for a read-through forward (one-token steps); rt_timed:
+// that forward is timed, so the launch records how many experts it reads through.
 moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
-                         int32_t* slot_ids_dev) {
+                         int32_t* slot_ids_dev, bool rt = false, bool rt_timed = false) {
     const int n = n_tokens * p->cfg.top_k;
     const bool resident = p->cfg.resident != 0;
     moe::PolicyArgs a{};
@@ -726,13 +758,15 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
     a.slots = L.slots;
     a.staging = p->staging;
     // the copy span of a timed step is the launch's (its decision takes a few us)
-    const bool timed = !resident && p->cfg.timing > 0 &&
+    const bool timed = !resident && !rt && p->cfg.timing > 0 &&
                        (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 && !L.fill_t.pending;
-    a.timed_jobs = timed ? p->timed_jobs_dev + layer : nullptr;
+    a.timed_jobs = timed ? p->timed_jobs_dev + layer : (rt && rt_timed ? p->rt_jobs_dev + layer : nullptr);
+    a.tab = rt ? p->tab_dev : nullptr;
     HIPCHK(moe::launch_policy(a, resident ? 1 : kPolicyGrid, timed ? L.fill_t.a : nullptr,
                               timed ? L.fill_t.b : nullptr, p->compute));
     if (timed) L.fill_t.pending = true;
     if (!resident) L.par ^= 1;
+    L.rt_prepared = rt;
     L.prepared = true;
     L.prep_tokens = n_tokens;
     L.prep_path = -1;            // known on the GPU only
@@ -787,6 +821,8 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.n_copy_streams < 1 || c.n_copy_streams > 8) FAIL(MOE_EINVAL, "n_copy_streams %d outside [1,8]", c.n_copy_streams);
     if (c.copy_engine != MOE_COPY_DMA && c.copy_engine != MOE_COPY_KERNEL) FAIL(MOE_EINVAL, "copy_engine %d invalid", c.copy_engine);
     if (c.policy != MOE_POLICY_HOST && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "policy %d invalid", c.policy);
+    if (c.read_through != 0 && c.read_through != 1) FAIL(MOE_EINVAL, "read_through %d invalid", c.read_through);
+    if (c.read_through && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "read_through needs the device policy");
     if (c.policy == MOE_POLICY_DEVICE && c.n_experts > 2048)
         FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS: n_experts %d > 2048", c.n_experts);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
@@ -948,6 +984,13 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
                                  hipHostMallocCoherent | hipHostMallocMapped));
         std::memset(p->timed_jobs_host, 0, sizeof(int32_t) * c.n_layers);
         CREATE_HIP(hipHostGetDevicePointer((void**)&p->timed_jobs_dev, p->timed_jobs_host, 0));
+        if (c.read_through && !c.resident) {
+            CREATE_HIP(hipHostMalloc((void**)&p->rt_jobs_host, sizeof(int32_t) * c.n_layers,
+                                     hipHostMallocCoherent | hipHostMallocMapped));
+            std::memset(p->rt_jobs_host, 0, sizeof(int32_t) * c.n_layers);
+            CREATE_HIP(hipHostGetDevicePointer((void**)&p->rt_jobs_dev, p->rt_jobs_host, 0));
+            CREATE_HIP(hipMalloc((void**)&p->tab_dev, sizeof(moe::PairSrc) * c.top_k));
+        }
         const moe_status_t ist = dev_init_layers(p);
         if (ist) {
             destroy_pool(p);
@@ -1022,6 +1065,7 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
             L.prepared = true;
             L.prep_tokens = 0;
             L.prep_path = MOE_PATH_POOL;
+            L.rt_prepared = false;
             L.has_last = true;
             L.last_empty = true;
             L.empty_steps++;
@@ -1085,6 +1129,36 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev, const void* resid_dev,
                            void* out_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
     if (n_tokens > 0 && (!x_dev || !topk_w_dev || !out_dev)) FAIL(MOE_EINVAL, "null buffer");
+    if (p && p->tab_dev && n_tokens == 1) {
+        // Read-through (device policy, one token): the decision leaves a pair table
+        // and copies nothing; the forward's kernels read each missed or staged expert
+        // from the store and write a missed one through to its slot.  Everything the
+        // forward needs is checked before the decision is queued, so a queued
+        // decision always has its forward (a miss's slot is filled by the forward).
+        moe_status_t st = check_layer(p, layer);
+        if (st) return st;
+        if (!topk_ids_dev || !slot_ids_dev) FAIL(MOE_EINVAL, "null ids");
+        if (miss_cap < 0) FAIL(MOE_EINVAL, "miss_cap < 0");
+        LayerState& L = p->layers[layer];
+        st = check_dev_err(p, layer);
+        if (st) return st;
+        if (n_miss) *n_miss = -1;
+        if (path) *path = -1;
+        const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
+                           !L.w13_t.pending && !L.w2_t.pending;
+        st = dev_prepare(p, L, layer, topk_ids_dev, 1, slot_ids_dev, true, timed);
+        if (st) return st;
+        p->last_prepared = layer;
+        st = launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, 1, out_dev, timed ? 1 : 0);
+        // the step's pair table belongs to this forward alone (staged experts were
+        // never written to staging): another forward needs another prepare
+        L.prepared = false;
+        L.rt_prepared = false;
+        if (st) return st;
+        if (timed) L.rt_sample = true;
+        if (p->cfg.timing) harvest_all(p);
+        return MOE_OK;
+    }
     if (!p || n_tokens <= 0 || n_tokens > moe::kDecodeMaxTokens || n_tokens > p->cfg.max_tokens ||
         p->cfg.policy == MOE_POLICY_DEVICE) {
         moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap,

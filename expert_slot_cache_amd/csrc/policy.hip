@@ -133,13 +133,22 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     }
 
     // 2. the step's outcome; every branch leaves the copies in list[0, njobs) with
-    // their destinations (pool: the expert's slot; staging: the list position)
+    // their destinations (pool: the expert's slot; staging: the list position).
+    // With a pair table (read-through) nothing is copied here: the table tells the
+    // forward which pairs read their expert from the store, and for a miss, which
+    // slot it writes the expert to on the way.
     int njobs = 0;
+    int nlink = 0;   // experts the step moves over the host link
     bool pool = true;
+    const size_t eb = a.eb;
+    auto store_at = [&](int e) { return a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * eb; };
     if (s_bad) {
         // an id outside [0, E): nothing changes, the step produces no expert
         if (lead) {
-            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = -1;
+            for (int i = tid; i < a.n; i += kPolicyThreads) {
+                a.out[i] = -1;
+                if (a.tab) a.tab[i] = PairSrc{nullptr, nullptr};
+            }
             if (tid == 0) {
                 *a.path = PATH_NONE;
                 rec[0] = PATH_NONE;
@@ -153,9 +162,14 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         // route rule ([llama-pool] prefill rule): selective copy -- the step's experts
         // go to staging in rank order; the pool state is untouched
         pool = false;
-        njobs = D;
+        nlink = D;
+        njobs = a.tab ? 0 : D;
         if (lead) {
-            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = rank[a.ids[i]];
+            for (int i = tid; i < a.n; i += kPolicyThreads) {
+                const int e = a.ids[i];
+                a.out[i] = rank[e];
+                if (a.tab) a.tab[i] = PairSrc{store_at(e), nullptr};
+            }
             if (tid == 0) {
                 *a.path = PATH_STAGE;
                 rec[0] = PATH_STAGE;
@@ -170,7 +184,8 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         }
     } else {
         // 3. the LRU, in LDS, one id at a time.  Miss j's expert is written to list[j]
-        // (j <= the id being processed, so nothing unread is overwritten).
+        // (j <= the id being processed, so nothing unread is overwritten), and a
+        // missed expert's rank entry becomes -1 (rank is not needed on this path).
         if (tid == 0) {
             int head = s_meta[0], tail = s_meta[1], nfree = s_meta[2];
             int hits = 0, misses = 0;
@@ -213,6 +228,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
                     rec[6 + 3 * misses] = evicted;
                 }
                 list[misses] = e;
+                rank[e] = -1;
                 ++misses;
             }
             s_meta[0] = head;
@@ -232,10 +248,18 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
             }
         }
         __syncthreads();
-        njobs = s_njobs;
+        nlink = s_njobs;
+        njobs = a.tab ? 0 : nlink;
         // the remap, through the fresh table
         if (lead)
-            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = map[a.ids[i]];
+            for (int i = tid; i < a.n; i += kPolicyThreads) {
+                const int e = a.ids[i];
+                const int slot = map[e];
+                a.out[i] = slot;
+                if (a.tab)
+                    a.tab[i] = rank[e] < 0 ? PairSrc{store_at(e), a.slots + (size_t)slot * eb}
+                                           : PairSrc{nullptr, nullptr};
+            }
     }
 
     // 4. the state the step leaves (unchanged unless the LRU ran)
@@ -251,11 +275,10 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         }
         if (tid < 3) a.dst.meta[tid] = s_meta[tid];
         if (tid == 0 && a.timed_jobs)
-            __hip_atomic_store(a.timed_jobs, njobs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(a.timed_jobs, nlink, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 
     // 5. the copies: 64 KiB work units over the launch, store -> slot / staging
-    const size_t eb = a.eb;
     const size_t upj = (eb + kFillUnit - 1) / kFillUnit;
     const size_t units = upj * (size_t)njobs;
     for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
@@ -263,7 +286,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         const int e = list[j];
         const size_t off = (u - (size_t)j * upj) * kFillUnit;
         const size_t nvec = (eb - off < kFillUnit ? eb - off : kFillUnit) / 16;
-        const char* src = a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * eb + off;
+        const char* src = store_at(e) + off;
         char* dst = (pool ? a.slots + (size_t)map[e] * eb : a.staging + (size_t)j * eb) + off;
         const u32x4v* __restrict__ s4 = reinterpret_cast<const u32x4v*>(src);
         u32x4v* __restrict__ d4 = reinterpret_cast<u32x4v*>(dst);

@@ -115,6 +115,14 @@ typedef struct {
     int32_t policy;         /* MOE_POLICY_HOST (0) or MOE_POLICY_DEVICE (1, n_experts <=
                                2048, copies by the copy kernel on the compute stream).
                                Both give the same slot ids, misses, counters and bits. */
+    int32_t read_through;   /* 1 (device policy, not resident): a one-token moe_pool_step
+                               copies nothing before its forward; the forward's kernels
+                               read each missed or staged expert from the pinned store and
+                               write a missed one through to its slot as they read it, so
+                               the step's compute overlaps its transfers.  Slot bytes,
+                               counters and outputs are those of the copying step.  0: the
+                               step's experts are copied first (prepare + forward always
+                               copy). */
 } moe_pool_config_t;
 
 typedef struct {

@@ -126,3 +126,14 @@ def test_read_calibration_rejects_bad_arguments_without_a_gpu():
     assert L.moe_link_calibration(100, 4, binding.COPY_KERNEL, None, C.byref(us)) == binding.EINVAL
     assert L.moe_link_calibration(1 << 20, 0, binding.COPY_DMA, None, C.byref(us)) == binding.EINVAL
     assert L.moe_link_calibration(1 << 20, 4, 7, None, C.byref(us)) == binding.EINVAL
+
+
+def test_create_rejects_read_through_without_the_device_policy():
+    """Config validation happens before any GPU call."""
+    import ctypes as C
+    for policy, rt in ((binding.POLICY_HOST, 1), (binding.POLICY_DEVICE, 2)):
+        cfg = binding.Config(1, 8, 2, 64, 32, 4, binding.WTYPES["f32"], binding.ATYPES["f32"],
+                             binding.RULES["distinct"], 0, 1, 1, 0, 0, 0, binding.COPY_KERNEL, policy, rt)
+        h = C.c_void_p()
+        assert binding.lib().moe_pool_create(C.byref(cfg), None, C.byref(h)) == binding.EINVAL
+        assert not h.value
