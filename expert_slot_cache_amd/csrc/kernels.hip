@@ -50,11 +50,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // ---------------------------------------------------------------------------
 constexpr int kDistinctThreads = 1024;
 
-// The body shared by k_distinct and k_route.  Writes rb (host) and, for each
-// present id e, rank_out[e] = its position (global memory or LDS).  Returns D.
-// The rb words are system-scope stores, which no cache holds back: the host sees
-// them while the workgroup is still running (k_route goes on to wait for the
-// host's answer).
+// The body of k_distinct.  Writes rb (host) and, for each present id e,
+// rank_out[e] = its position.  Returns D.  The rb words are system-scope stores,
+// which no cache holds back: the host reads them while the kernel runs.
 __device__ __forceinline__ int distinct_block(const int32_t* __restrict__ ids, int n, int E,
                                               uint32_t* __restrict__ rb, int32_t* __restrict__ rank_out,
                                               uint32_t tag, uint32_t* bits, int32_t* wave_cnt, int32_t& bad) {
@@ -128,51 +126,22 @@ hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32
 // inside the kernel: every workgroup copies the table into LDS and applies the
 // list there, and workgroup 0 also writes the changes back to the persistent
 // table.  So the remap can only read the fresh table.  An entry may be listed
-// twice, always with the same value, so the order of the writes does not matter.  Ids outside [0,E) give -1, which the
-// forward kernels never dereference.
+// twice, always with the same value, so the order of the writes does not matter.
+// Ids outside [0,E) give -1, which the forward kernels never dereference.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ ids, int n, int E,
                                                int32_t* __restrict__ table, const int32_t* __restrict__ rank,
                                                const int32_t* __restrict__ upd, int n_upd, int status,
-                                               Gate* __restrict__ gate, uint32_t seq, unsigned long long limit,
                                                int32_t* __restrict__ out, int32_t* __restrict__ path) {
     __shared__ int32_t tab[kMaxExperts];
-    __shared__ int32_t s_status, s_nupd;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        int st = status, nu = n_upd;
-        if (gate) {
-            const unsigned long long t0 = wall_clock64();
-            for (;;) {
-                if (__hip_atomic_load(&gate->seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == seq) {
-                    st = __hip_atomic_load(&gate->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    nu = __hip_atomic_load(&gate->n_upd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    break;
-                }
-                if (wall_clock64() - t0 > limit) {
-                    st = PATH_NONE;
-                    nu = 0;
-                    __hip_atomic_store(&gate->timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        s_status = st;
-        s_nupd = (st == PATH_POOL) ? nu : 0;
-    }
-    __syncthreads();
-    const int st = s_status;
-    const int nu = s_nupd;
     const int i = blockIdx.x * 256 + tid;
-    if (st == PATH_POOL) {
+    if (status == PATH_POOL) {
         for (int e = tid; e < E; e += 256) tab[e] = table[e];
         __syncthreads();
-        // The list lives in host memory and may have been written after the launch:
-        // read it with system-scope loads, which no stale cache line can serve.
-        for (int u = tid; u < nu; u += 256) {
-            const int32_t e = __hip_atomic_load(upd + 2 * u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            const int32_t v = __hip_atomic_load(upd + 2 * u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int u = tid; u < n_upd; u += 256) {
+            const int32_t e = upd[2 * u];
+            const int32_t v = upd[2 * u + 1];
             tab[e] = v;
             if (blockIdx.x == 0) table[e] = v;
         }
@@ -183,92 +152,16 @@ __global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ ids, 
         }
     } else if (i < n) {
         const int e = ids[i];
-        out[i] = (st == PATH_STAGE && (unsigned)e < (unsigned)E) ? rank[e] : -1;
+        out[i] = (status == PATH_STAGE && (unsigned)e < (unsigned)E) ? rank[e] : -1;
     }
-    if (blockIdx.x == 0 && tid == 0) *path = st;
+    if (blockIdx.x == 0 && tid == 0) *path = status;
 }
 
 hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* rank, const int32_t* upd,
-                        int n_upd, int status, Gate* gate, uint32_t seq, unsigned long long limit, int32_t* out,
-                        int32_t* path, hipStream_t stream) {
+                        int n_upd, int status, int32_t* out, int32_t* path, hipStream_t stream) {
     const int blocks = n > 0 ? (n + 255) / 256 : 1;
-    hipLaunchKernelGGL(k_remap, dim3(blocks), dim3(256), 0, stream, ids, n, E, table, rank, upd, n_upd, status, gate,
-                       seq, limit, out, path);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// K-route: the distinct ids and the remap of a decode-sized step in one
-// workgroup (n <= kDistinctThreads ids).  The distinct part is k_distinct's,
-// with the ranks kept in LDS; then, as in k_remap, thread 0 waits on the gate (if
-// any) for the step's decision and the ids are remapped through the fresh table
-// (PATH_POOL: the table with the update list applied, also written back), their
-// ranks (PATH_STAGE) or to -1 (PATH_NONE).  The host reads the distinct ids back
-// while the kernel waits.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDistinctThreads) void k_route(const int32_t* __restrict__ ids, int n, int E,
-                                                            uint32_t* __restrict__ rb, uint32_t tag,
-                                                            int32_t* __restrict__ table,
-                                                            const int32_t* __restrict__ upd, int n_upd, int status,
-                                                            Gate* __restrict__ gate, uint32_t seq,
-                                                            unsigned long long limit, int32_t* __restrict__ out,
-                                                            int32_t* __restrict__ path) {
-    __shared__ uint32_t bits[kMaxExperts / 32];
-    __shared__ int32_t wave_cnt[kDistinctThreads / 64];
-    __shared__ int32_t bad;
-    __shared__ int32_t arr[kMaxExperts];          // ranks, then (PATH_POOL) the table
-    __shared__ int32_t s_status, s_nupd;
-    const int tid = threadIdx.x;
-    distinct_block(ids, n, E, rb, arr, tag, bits, wave_cnt, bad);
-    if (tid == 0) {
-        int st = status, nu = n_upd;
-        if (gate) {
-            const unsigned long long t0 = wall_clock64();
-            for (;;) {
-                if (__hip_atomic_load(&gate->seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == seq) {
-                    st = __hip_atomic_load(&gate->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    nu = __hip_atomic_load(&gate->n_upd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    break;
-                }
-                if (wall_clock64() - t0 > limit) {
-                    st = PATH_NONE;
-                    nu = 0;
-                    __hip_atomic_store(&gate->timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        s_status = st;
-        s_nupd = (st == PATH_POOL) ? nu : 0;
-    }
-    __syncthreads();
-    const int st = s_status;
-    const int nu = s_nupd;
-    if (st == PATH_POOL) {
-        for (int e = tid; e < E; e += kDistinctThreads) arr[e] = table[e];
-        __syncthreads();
-        for (int u = tid; u < nu; u += kDistinctThreads) {
-            const int32_t e = __hip_atomic_load(upd + 2 * u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            const int32_t v = __hip_atomic_load(upd + 2 * u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            arr[e] = v;
-            table[e] = v;
-        }
-        __syncthreads();
-    }
-    for (int i = tid; i < n; i += kDistinctThreads) {
-        const int e = ids[i];
-        out[i] = (st != PATH_NONE && (unsigned)e < (unsigned)E) ? arr[e] : -1;
-    }
-    if (tid == 0) *path = st;
-}
-
-hipError_t launch_route(const int32_t* ids, int n, int E, uint32_t* rb, uint32_t tag, int32_t* table,
-                        const int32_t* upd, int n_upd, int status, Gate* gate, uint32_t seq,
-                        unsigned long long limit, int32_t* out, int32_t* path, hipStream_t stream) {
-    if (n > kDistinctThreads) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(kDistinctThreads), 0, stream, ids, n, E, rb, tag, table, upd, n_upd,
-                       status, gate, seq, limit, out, path);
+    hipLaunchKernelGGL(k_remap, dim3(blocks), dim3(256), 0, stream, ids, n, E, table, rank, upd, n_upd, status, out,
+                       path);
     return hipGetLastError();
 }
 

@@ -29,37 +29,17 @@ struct Geom {
 hipError_t launch_distinct(const int32_t* ids, int n, int E, uint32_t* rb, int32_t* rank, uint32_t tag,
                            hipStream_t stream);
 
-// Per-layer publication of a step's decision, in host-mapped memory (64 bytes).
-// The host writes it once the step's copies have landed, `seq` last; status and
-// n_upd are valid once seq matches.
-struct Gate {
-    uint32_t seq;
-    int32_t status;   // PATH_POOL, PATH_STAGE or PATH_NONE
-    int32_t n_upd;    // table changes in the layer's update list
-    uint32_t timeout; // set by the remap kernel when it gave up waiting
-    int32_t pad[12];
-};
 enum { PATH_POOL = 0, PATH_STAGE = 1, PATH_NONE = 2 };
 
-// The remap of one step.  If `gate` is null the decision is status/n_upd;
-// otherwise thread 0 of each workgroup waits (at most `limit` wall-clock ticks)
-// until gate->seq == seq and takes status/n_upd from the gate.
+// The remap of one step, with the decision status/n_upd:
 //   PATH_POOL : apply upd[2u] -> upd[2u+1] (u < n_upd) to `table` in place, then
 //               out[i] = table[ids[i]]
 //   PATH_STAGE: out[i] = rank[ids[i]]
 //   PATH_NONE : out[i] = -1
 // ids outside [0,E) give -1.  The path is also written to *path (device), which
-// the forward kernels read to pick the slot base.  upd and gate may be host-mapped.
+// the forward kernels read to pick the slot base.  upd may be host-mapped.
 hipError_t launch_remap(const int32_t* ids, int n, int E, int32_t* table, const int32_t* rank, const int32_t* upd,
-                        int n_upd, int status, Gate* gate, uint32_t seq, unsigned long long limit, int32_t* out,
-                        int32_t* path, hipStream_t stream);
-
-// Distinct ids and remap of one decode-sized step in one launch (n <= 1024):
-// rb as launch_distinct writes it, then out/path as launch_remap writes them
-// (the ranks of PATH_STAGE come from this step's distinct list).
-hipError_t launch_route(const int32_t* ids, int n, int E, uint32_t* rb, uint32_t tag, int32_t* table,
-                        const int32_t* upd, int n_upd, int status, Gate* gate, uint32_t seq,
-                        unsigned long long limit, int32_t* out, int32_t* path, hipStream_t stream);
+                        int n_upd, int status, int32_t* out, int32_t* path, hipStream_t stream);
 
 // Optional event pairs around the two projection stages (any may be null).
 struct StageEvents {
@@ -133,9 +113,7 @@ hipError_t launch_fill(const FillBatch& b, hipStream_t s);
 // ---- the slot manager on the GPU -----------------------------------------------------
 // One layer's LRU state (HBM, int32): map[E] (slot or -1), owner[N] (expert or -1),
 // free[N] (stack of free slots; meta[2] entries valid), prev/next[E] (the LRU list
-// over expert ids, -1 terminated), meta = {head, tail, nfree}.  Each layer keeps two
-// copies: a step reads one and writes the other, so that every workgroup of the step
-// can read the state it starts from while the first one writes the result.
+// over expert ids, -1 terminated), meta = {head, tail, nfree}.
 struct LruState {
     int32_t* map;
     int32_t* owner;
@@ -145,13 +123,15 @@ struct LruState {
     int32_t* meta;
 };
 
-// The state copies plus ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d,
-// staged} and rec = the last step {path, D, n_miss, bad, then (expert, slot,
-// evicted) per miss}.
+// The state plus ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d, staged},
+// rec = the last step {path, D, n_miss, bad, then (expert, slot, evicted) per miss}
+// and arrive = the step's count of workgroups holding their copy of the state (0
+// between steps).
 struct DevState {
-    LruState s[2];
+    LruState s;
     unsigned long long* ctr;
     int32_t* rec;
+    int32_t* arrive;
 };
 
 struct PolicyArgs {
@@ -161,12 +141,15 @@ struct PolicyArgs {
     int rule;                // 0: fallback iff D > N; 1: iff n > N (and D > 0)
     int resident;            // 1: every expert at slot = id (count hits only)
     unsigned long long eb;   // bytes per expert (bytes_h2d counter; a multiple of 16)
-    LruState src, dst;       // the state the step starts from / the one it leaves
+    LruState st;             // the layer's state, updated in place
     unsigned long long* ctr;
     int32_t* rec;
+    int32_t* arrive;         // 0 at launch; left 0
     int32_t* out;            // [n] slot ids (or staging ranks)
     int32_t* path;           // the layer's path word
-    uint32_t* err;           // host-mapped: set to 1 when an id is outside [0, E)
+    uint32_t* err;           // host-mapped: 1 = an id outside [0, E); 2 = the write-back's
+                             // wait for the other workgroups timed out
+    unsigned long long spin_limit;  // bound on that wait (polls)
     // the copies (unused when resident)
     const char* const* pieces;  // device array: device-mapped base of each store piece
     int per_piece;           // experts per piece

@@ -14,14 +14,14 @@
 //      the last reader of any destination included, has finished too.
 //   4. the step's map changes go to a small pinned list that k_remap reads: it
 //      applies them to the persistent HBM table and remaps through the fresh table.
-//      The compute stream waits for the copies (an event per copy stream), or, in
-//      the gated one-call step, the host waits for them and then publishes the
-//      step's decision and sequence number, which the pre-launched remap awaits.
+//      The compute stream waits for the copies (an event per copy stream).  No
+//      kernel ever waits for the host or for another stream: streams can share a
+//      hardware queue, and a kernel spinning on work queued behind it would only
+//      end at its time limit.
 //   5. forward kernels on the compute stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <chrono>
 #include <cstdarg>
 #include <cstdio>
@@ -122,9 +122,6 @@ struct LayerState {
     int32_t* map_dev = nullptr;  // HBM int32 [E]: the persistent map table
     int32_t* upd_host = nullptr; // pinned int32 [2E]: this step's (entry, value) changes
     int32_t* upd_dev = nullptr;  // device view of upd_host
-    moe::Gate* gate = nullptr;   // pinned coherent: this layer's step publication
-    moe::Gate* gate_dev = nullptr;
-    uint32_t gate_seq = 0;       // last published sequence number
     int32_t* path_dev = nullptr; // HBM int32: the path the last remap chose
     bool prepared = false;
     char* expert(int32_t e, size_t eb) const { return store[e / per_piece] + (size_t)(e % per_piece) * eb; }
@@ -145,7 +142,6 @@ struct LayerState {
     // addresses (device array), and the fill timing of this layer
     char* dev_block = nullptr;
     moe::DevState ds{};
-    int par = 0;                 // the state copy the next step reads (ds.s[par])
     bool rt_prepared = false;    // the current prepare left a pair table (read-through forward)
     bool rt_sample = false;      // the pending w13/w2 timing sample is a read-through step
     const char** pieces_dev = nullptr;
@@ -175,9 +171,11 @@ struct moe_pool {
     std::vector<int32_t> ulist;   // the last readback's distinct ids
     int32_t* rank_dev = nullptr;  // HBM [E]
     int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
-    moe::Gate* gates = nullptr;   // pinned coherent [n_layers]
     int32_t* paths_dev = nullptr; // HBM [n_layers]
-    unsigned long long gate_limit = 0;   // wall-clock ticks a gated remap waits at most
+    // polls a device step's write-back waits at most for the step's other workgroups
+    // to hold their copy of the state (each poll is a load and a short sleep; the
+    // wait normally ends within a few microseconds)
+    unsigned long long spin_limit = 1ull << 22;
     void* act = nullptr;          // HBM [max_tokens * K][I] SwiGLU output
     float* y = nullptr;           // HBM [max_tokens * K][H] per-pair w2 output
     int32_t* grp = nullptr;       // HBM grouped-path index buffer
@@ -235,7 +233,6 @@ void destroy_pool(moe_pool* p) {
     if (p->staging) (void)hipFree(p->staging);
     if (p->rb_host) (void)hipHostFree(p->rb_host);
     if (p->rank_dev) (void)hipFree(p->rank_dev);
-    if (p->gates) (void)hipHostFree(p->gates);
     if (p->paths_dev) (void)hipFree(p->paths_dev);
     if (p->ident_dev) (void)hipFree(p->ident_dev);
     if (p->act) (void)hipFree(p->act);
@@ -346,9 +343,8 @@ void harvest_all(moe_pool* p) {
 
 // The copy-kernel engine: the experts go in batches of up to kFillMaxJobs per launch,
 // batches round-robin over the copy streams; each used stream records its copy_done
-// event (joined into the compute stream if `join`), as with the DMA engine.
-moe_status_t issue_copy_kernels(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs,
-                                bool join) {
+// event (joined into the compute stream), as with the DMA engine.
+moe_status_t issue_copy_kernels(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs) {
     const int ns = (int)p->copy.size();
     const size_t eb = p->lay.total;
     std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
@@ -382,22 +378,21 @@ moe_status_t issue_copy_kernels(moe_pool* p, LayerState& L, const std::vector<st
             L.copy_t[s].pending = true;
         }
         HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
-        if (join) HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+        HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
     }
     L.bytes_h2d += (uint64_t)eb * jobs.size();
     return MOE_OK;
 }
 
 // Enqueue host->HBM copies of the experts (src -> dst pairs) on the copy streams,
-// record each used stream's copy_done event, and, if `join`, make the compute
-// stream wait for those events.
+// record each used stream's copy_done event, and make the compute stream wait
+// for those events.
 // jobs: (destination in HBM, source expert index in the layer's store).
-moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs,
-                          bool join) {
+moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pair<char*, int32_t>>& jobs) {
     if (jobs.empty()) return MOE_OK;
     const int ns = (int)p->copy.size();
     const size_t eb = p->lay.total;
-    if (p->cfg.copy_engine == MOE_COPY_KERNEL) return issue_copy_kernels(p, L, jobs, join);
+    if (p->cfg.copy_engine == MOE_COPY_KERNEL) return issue_copy_kernels(p, L, jobs);
     const size_t chunk = p->cfg.copy_chunk_bytes ? p->cfg.copy_chunk_bytes : eb;
     std::fill(p->used_copy.begin(), p->used_copy.end(), 0);
     bool timed = p->cfg.timing > 0 && (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0;
@@ -429,39 +424,13 @@ moe_status_t issue_copies(moe_pool* p, LayerState& L, const std::vector<std::pai
             L.copy_t[s].pending = true;
         }
         HIPCHK(hipEventRecord(p->copy_done[s], p->copy[s]));
-        if (join) HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
+        HIPCHK(hipStreamWaitEvent(p->compute, p->copy_done[s], 0));
     }
     L.bytes_h2d += (uint64_t)eb * jobs.size();
     return MOE_OK;
 }
 
-// Host-side publication of a gated step's decision: status and n_upd first, the
-// sequence number last (x86 stores are seen in order; the remap kernel reads the
-// fields only after it has seen the sequence number).
-void publish_fields(LayerState& L, int status, int n_upd) {
-    volatile moe::Gate* g = L.gate;
-    g->status = status;
-    g->n_upd = n_upd;
-}
-
-void publish_seq(LayerState& L, uint32_t seq) {
-    std::atomic_thread_fence(std::memory_order_release);
-    volatile moe::Gate* g = L.gate;
-    g->seq = seq;
-}
-
-// ---- the steps of prepare, shared by the two-call and the gated flow -----------
-
-// A gated remap that gave up waiting leaves a flag in its gate; the next call on
-// the layer reports it.
-moe_status_t check_gate(LayerState& L, int32_t layer) {
-    volatile moe::Gate* g = L.gate;
-    if (g->timeout) {
-        g->timeout = 0;
-        FAIL(MOE_EHIP, "layer %d: a step's remap timed out waiting for its copies; that step's output is invalid", layer);
-    }
-    return MOE_OK;
-}
+// ---- the steps of prepare -----------------------------------------------------------
 
 // The next readback: zero the words the last one used and take a new tag.
 void next_readback(moe_pool* p) {
@@ -523,18 +492,16 @@ moe_status_t read_distinct(moe_pool* p, int32_t layer, int32_t* D_out) {
     return MOE_OK;
 }
 
-// The LRU step over p->ulist[0..D), the map-change list and the miss copies.
-// join: the compute stream waits for the copies (two-call flow); otherwise the
-// caller waits for them (wait_copies) before it publishes the step (gated flow).
-moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, bool join, int32_t* the_path,
-                   int32_t* n_upd_out, bool* copied) {
+// The LRU step over p->ulist[0..D), the map-change list and the miss copies (the
+// compute stream waits for them).
+moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, int32_t* the_path,
+                   int32_t* n_upd_out) {
     const size_t eb = p->lay.total;
     const int32_t* u = p->ulist.data();
     moe_status_t st;
     p->misses.clear();
     *the_path = MOE_PATH_POOL;
     *n_upd_out = 0;
-    *copied = false;
     // The readback has seen this step's distinct kernel finish, and with it every
     // earlier kernel of the compute stream: no reads of a destination are pending,
     // so the copies wait for nothing.
@@ -564,9 +531,8 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
             std::vector<std::pair<char*, int32_t>> jobs;
             jobs.reserve(p->misses.size());
             for (const auto& m : p->misses) jobs.emplace_back(L.slots + (size_t)m.slot * eb, m.expert);
-            st = issue_copies(p, L, jobs, join);
+            st = issue_copies(p, L, jobs);
             if (st) return st;
-            *copied = true;
         }
     } else {
         // selective-copy fallback: the step's experts go to staging in rank order;
@@ -575,27 +541,10 @@ moe_status_t route(moe_pool* p, LayerState& L, int32_t layer, int32_t D, int n, 
         std::vector<std::pair<char*, int32_t>> jobs;
         jobs.reserve(D);
         for (int32_t r = 0; r < D; ++r) jobs.emplace_back(p->staging + (size_t)r * eb, u[r]);
-        st = issue_copies(p, L, jobs, join);
+        st = issue_copies(p, L, jobs);
         if (st) return st;
-        *copied = true;
         L.staged += (uint64_t)D;
         p->staging_owner = layer;
-    }
-    return MOE_OK;
-}
-
-// Host wait for the copies issue_copies just queued (their copy_done events).  The
-// gated step publishes only after this, so no kernel ever waits on work of another
-// stream: the step stays correct where dispatches are serialised (profilers).
-moe_status_t wait_copies(moe_pool* p) {
-    for (size_t s = 0; s < p->copy.size(); ++s) {
-        if (!p->used_copy[s]) continue;
-        for (;;) {
-            const hipError_t q = hipEventQuery(p->copy_done[s]);
-            if (q == hipSuccess) break;
-            if (q != hipErrorNotReady) FAIL(MOE_EHIP, "copy event query failed: %s", hipGetErrorString(q));
-            __builtin_ia32_pause();
-        }
     }
     return MOE_OK;
 }
@@ -660,7 +609,7 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
 // ---- MOE_POLICY_DEVICE ------------------------------------------------------------
 // Byte layout of one layer's device state block (see moe::DevState).
 struct DevLayout {
-    size_t map[2], owner[2], free[2], prev[2], next[2], meta[2], ctr, rec, total;
+    size_t map, owner, free, prev, next, meta, ctr, rec, arrive, total;
 };
 
 DevLayout dev_layout(int32_t E, int32_t N) {
@@ -671,37 +620,34 @@ DevLayout dev_layout(int32_t E, int32_t N) {
         o = round_up(o + bytes);
         return at;
     };
-    for (int c = 0; c < 2; ++c) {
-        d.map[c] = take((size_t)E * 4);
-        d.owner[c] = take((size_t)N * 4);
-        d.free[c] = take((size_t)N * 4);
-        d.prev[c] = take((size_t)E * 4);
-        d.next[c] = take((size_t)E * 4);
-        d.meta[c] = take(16 * 4);
-    }
+    d.map = take((size_t)E * 4);
+    d.owner = take((size_t)N * 4);
+    d.free = take((size_t)N * 4);
+    d.prev = take((size_t)E * 4);
+    d.next = take((size_t)E * 4);
+    d.meta = take(16 * 4);
     d.ctr = take(8 * 8);
     d.rec = take((size_t)(4 + 3 * N) * 4);
+    d.arrive = take(4);
     d.total = o;
     return d;
 }
 
-// The cold state image (both copies): map -1, owners -1, free slots 0..N-1 (popped
-// from the end), empty LRU list, counters zero.
+// The cold state image: map -1, owners -1, free slots 0..N-1 (popped from the end),
+// empty LRU list, counters and the arrival word zero.
 std::vector<char> dev_cold_image(const moe_pool* p) {
     const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
     const DevLayout d = dev_layout(E, N);
     std::vector<char> img(d.total, 0);
     auto w = [&](size_t off) { return reinterpret_cast<int32_t*>(img.data() + off); };
-    for (int c = 0; c < 2; ++c) {
-        std::fill(w(d.map[c]), w(d.map[c]) + E, -1);
-        std::fill(w(d.owner[c]), w(d.owner[c]) + N, -1);
-        for (int32_t s2 = 0; s2 < N; ++s2) w(d.free[c])[s2] = s2;
-        std::fill(w(d.prev[c]), w(d.prev[c]) + E, -1);
-        std::fill(w(d.next[c]), w(d.next[c]) + E, -1);
-        w(d.meta[c])[0] = -1;
-        w(d.meta[c])[1] = -1;
-        w(d.meta[c])[2] = N;
-    }
+    std::fill(w(d.map), w(d.map) + E, -1);
+    std::fill(w(d.owner), w(d.owner) + N, -1);
+    for (int32_t s2 = 0; s2 < N; ++s2) w(d.free)[s2] = s2;
+    std::fill(w(d.prev), w(d.prev) + E, -1);
+    std::fill(w(d.next), w(d.next) + E, -1);
+    w(d.meta)[0] = -1;
+    w(d.meta)[1] = -1;
+    w(d.meta)[2] = N;
     return img;
 }
 
@@ -709,7 +655,6 @@ moe_status_t dev_init_layers(moe_pool* p) {
     const std::vector<char> img = dev_cold_image(p);
     for (auto& L : p->layers) {
         HIPCHK(hipMemcpy(L.dev_block, img.data(), img.size(), hipMemcpyHostToDevice));
-        L.par = 0;
         L.rt_prepared = false;
         L.rt_sample = false;
         L.has_last = false;
@@ -723,8 +668,12 @@ moe_status_t dev_init_layers(moe_pool* p) {
 // An id outside [0,E) found by a layer's earlier device step.
 moe_status_t check_dev_err(moe_pool* p, int32_t layer) {
     volatile uint32_t* e = p->errs_host + layer;
-    if (*e) {
+    const uint32_t v = *e;
+    if (v) {
         *e = 0;
+        if (v == 2)
+            FAIL(MOE_EHIP, "layer %d: a device step's write-back gave up waiting for its workgroups (the GPU did"
+                           " not run them); the layer's state may be inconsistent: reset the pool", layer);
         FAIL(MOE_ERANGE, "layer %d: an earlier step had an expert id outside [0,%d); it changed nothing and its"
                          " output is undefined", layer, p->cfg.n_experts);
     }
@@ -746,10 +695,11 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
     a.rule = p->cfg.rule;
     a.resident = p->cfg.resident;
     a.eb = p->lay.total;
-    a.src = L.ds.s[L.par];
-    a.dst = L.ds.s[resident ? L.par : L.par ^ 1];
+    a.st = L.ds.s;
     a.ctr = L.ds.ctr;
     a.rec = L.ds.rec;
+    a.arrive = L.ds.arrive;
+    a.spin_limit = p->spin_limit;
     a.out = slot_ids_dev;
     a.path = L.path_dev;
     a.err = p->errs_dev + layer;
@@ -765,7 +715,6 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
     HIPCHK(moe::launch_policy(a, resident ? 1 : kPolicyGrid, timed ? L.fill_t.a : nullptr,
                               timed ? L.fill_t.b : nullptr, p->compute));
     if (timed) L.fill_t.pending = true;
-    if (!resident) L.par ^= 1;
     L.rt_prepared = rt;
     L.prepared = true;
     L.prep_tokens = n_tokens;
@@ -893,7 +842,10 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         for (int32_t e0 = 0; !c.resident && e0 < E; e0 += L.per_piece) {
             const size_t bytes = (size_t)std::min(L.per_piece, E - e0) * eb;
             char* piece = nullptr;
-            const hipError_t he = hipHostMalloc((void**)&piece, bytes, hipHostMallocMapped);
+            // coherent: the copy kernels read the store through its device mapping,
+            // and a GPU-cached line of host memory can outlive the allocation (a
+            // later pinned allocation at the same place then reads stale on the GPU)
+            const hipError_t he = hipHostMalloc((void**)&piece, bytes, hipHostMallocMapped | hipHostMallocCoherent);
             if (he != hipSuccess) {
                 set_err("hipHostMalloc of %zu bytes (layer %d, experts %d..) failed after %zu pinned bytes: %s", bytes, l,
                         e0, pinned_total, hipGetErrorString(he));
@@ -936,37 +888,18 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         for (int32_t e = 0; e < E; ++e) id[e] = e;
         CREATE_HIP(hipMemcpy(p->ident_dev, id.data(), (size_t)E * 4, hipMemcpyHostToDevice));
     }
-    CREATE_HIP(hipHostMalloc((void**)&p->gates, sizeof(moe::Gate) * c.n_layers,
-                             hipHostMallocCoherent | hipHostMallocMapped));
-    std::memset(p->gates, 0, sizeof(moe::Gate) * c.n_layers);
-    moe::Gate* gates_dev = nullptr;
-    CREATE_HIP(hipHostGetDevicePointer((void**)&gates_dev, p->gates, 0));
     CREATE_HIP(hipMalloc((void**)&p->paths_dev, sizeof(int32_t) * c.n_layers));
     CREATE_HIP(hipMemset(p->paths_dev, 0, sizeof(int32_t) * c.n_layers));
-    for (int32_t l = 0; l < c.n_layers; ++l) {
-        p->layers[l].gate = p->gates + l;
-        p->layers[l].gate_dev = gates_dev + l;
-        p->layers[l].path_dev = p->paths_dev + l;
-    }
-    {
-        // A gated remap gives up (and reports it) after 10 s plus 1 s per GB the
-        // step can copy at most; the copies of a step run at ~50 GB/s.
-        int dev = 0, khz = 0;
-        CREATE_HIP(hipGetDevice(&dev));
-        CREATE_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
-        const double max_copy = (double)std::max(p->nslot_alloc, p->staging_cap) * (double)eb;
-        p->gate_limit = (unsigned long long)((10.0 + max_copy * 1e-9) * (double)std::max(khz, 1) * 1e3);
-    }
+    for (int32_t l = 0; l < c.n_layers; ++l) p->layers[l].path_dev = p->paths_dev + l;
     if (c.policy == MOE_POLICY_DEVICE) {
         const DevLayout d = dev_layout(E, c.resident ? 0 : c.n_slots);
         for (auto& L : p->layers) {
             CREATE_HIP(hipMalloc((void**)&L.dev_block, d.total));
             auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(L.dev_block + off); };
-            for (int k = 0; k < 2; ++k)
-                L.ds.s[k] = moe::LruState{at(d.map[k]), at(d.owner[k]), at(d.free[k]), at(d.prev[k]),
-                                          at(d.next[k]), at(d.meta[k])};
+            L.ds.s = moe::LruState{at(d.map), at(d.owner), at(d.free), at(d.prev), at(d.next), at(d.meta)};
             L.ds.ctr = reinterpret_cast<unsigned long long*>(L.dev_block + d.ctr);
             L.ds.rec = at(d.rec);
+            L.ds.arrive = at(d.arrive);
             if (!L.store_dev.empty()) {
                 CREATE_HIP(hipMalloc((void**)&L.pieces_dev, sizeof(char*) * L.store_dev.size()));
                 CREATE_HIP(hipMemcpy(L.pieces_dev, L.store_dev.data(), sizeof(char*) * L.store_dev.size(),
@@ -1053,9 +986,9 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
     LayerState& L = p->layers[layer];
     const int32_t E = p->cfg.n_experts;
     const int n = n_tokens * p->cfg.top_k;
-    st = check_gate(L, layer);
-    if (st) return st;
-
+    // from here on a failure leaves no prepared step (a forward then needs a new
+    // prepare); the cache state is unchanged
+    L.prepared = false;
     if (p->cfg.policy == MOE_POLICY_DEVICE) {
         st = check_dev_err(p, layer);
         if (st) return st;
@@ -1094,12 +1027,11 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
     // 2. route + LRU; 3. misses: store -> slot on the copy streams, after this
     // layer's last reads; 4. the remap (map changes applied first)
     int32_t the_path = MOE_PATH_POOL, n_upd = 0;
-    bool copied = false;
-    st = route(p, L, layer, D, n, true, &the_path, &n_upd, &copied);
+    st = route(p, L, layer, D, n, &the_path, &n_upd);
     if (st) return st;
     int32_t* table = p->cfg.resident ? p->ident_dev : L.map_dev;
     const int status = the_path == MOE_PATH_FALLBACK ? moe::PATH_STAGE : moe::PATH_POOL;
-    HIPCHK(moe::launch_remap(topk_ids_dev, n, E, table, p->rank_dev, L.upd_dev, n_upd, status, nullptr, 0, 0,
+    HIPCHK(moe::launch_remap(topk_ids_dev, n, E, table, p->rank_dev, L.upd_dev, n_upd, status,
                              slot_ids_dev, L.path_dev, p->compute));
     finish_prepare(p, L, n_tokens, the_path, miss_host, miss_cap, n_miss, path);
     if (p->cfg.timing) harvest_all(p);   // event queries stay off the path to the remap
@@ -1159,75 +1091,10 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
         if (p->cfg.timing) harvest_all(p);
         return MOE_OK;
     }
-    if (!p || n_tokens <= 0 || n_tokens > moe::kDecodeMaxTokens || n_tokens > p->cfg.max_tokens ||
-        p->cfg.policy == MOE_POLICY_DEVICE) {
-        moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap,
-                                           n_miss, path);
-        if (st) return st;
-        return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
-    }
-    // Decode-sized steps launch everything before the readback: one kernel for the
-    // distinct ids and a remap that waits on the layer's gate, then the forward
-    // kernels.  The host then
-    // reads the distinct ids back, runs the LRU, queues the miss copies, waits for
-    // them to land, and publishes the decision to the gate, so the kernels' launch
-    // latency overlaps the host's work and the copies.
-    moe_status_t st = check_layer(p, layer);
+    moe_status_t st = moe_pool_prepare(p, layer, topk_ids_dev, n_tokens, slot_ids_dev, miss_host, miss_cap, n_miss,
+                                       path);
     if (st) return st;
-    if (!topk_ids_dev || !slot_ids_dev) FAIL(MOE_EINVAL, "null ids");
-    if (miss_cap < 0) FAIL(MOE_EINVAL, "miss_cap < 0");
-    LayerState& L = p->layers[layer];
-    st = check_gate(L, layer);
-    if (st) return st;
-    L.prepared = false;
-    const int32_t E = p->cfg.n_experts;
-    const int n = n_tokens * p->cfg.top_k;
-    const bool gated = !p->cfg.resident;
-    next_readback(p);
-    uint32_t seq = 0;
-    if (gated) {
-        seq = ++L.gate_seq;
-        if (seq == 0) seq = ++L.gate_seq;   // 0 is the gate's initial value
-        HIPCHK(moe::launch_route(topk_ids_dev, n, E, p->rb_dev, p->rb_tag, L.map_dev, L.upd_dev, 0, 0, L.gate_dev,
-                                 seq, p->gate_limit, slot_ids_dev, L.path_dev, p->compute));
-    } else {
-        HIPCHK(moe::launch_route(topk_ids_dev, n, E, p->rb_dev, p->rb_tag, p->ident_dev, L.upd_dev, 0,
-                                 moe::PATH_POOL, nullptr, 0, 0, slot_ids_dev, L.path_dev, p->compute));
-    }
-    // From here on a gated remap is queued: every exit publishes a decision, so
-    // that the kernel never waits out its limit.
-    bool published = !gated;
-    auto abort_gate = [&](moe_status_t e) {
-        if (!published) {
-            publish_fields(L, moe::PATH_NONE, 0);
-            publish_seq(L, seq);
-            published = true;
-        }
-        return e;
-    };
-    st = launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
-    if (st) return abort_gate(st);
-    int32_t D = 0;
-    st = read_distinct(p, layer, &D);
-    if (st) return abort_gate(st);
-    int32_t the_path = MOE_PATH_POOL, n_upd = 0;
-    bool copied = false;
-    st = route(p, L, layer, D, n, false, &the_path, &n_upd, &copied);
-    if (st) return abort_gate(st);
-    if (copied) {
-        st = wait_copies(p);
-        if (st) return abort_gate(st);
-    }
-    if (!published) {
-        publish_fields(L, the_path == MOE_PATH_FALLBACK ? moe::PATH_STAGE : moe::PATH_POOL, n_upd);
-        publish_seq(L, seq);
-        published = true;
-    }
-    finish_prepare(p, L, n_tokens, the_path, miss_host, miss_cap, n_miss, path);
-    // finished timing events are collected only now, while the kernels run: the
-    // queued remap waits for the publication above, not for this bookkeeping
-    if (p->cfg.timing) harvest_all(p);
-    return MOE_OK;
+    return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
 }
 
 moe_status_t moe_pool_last_step(moe_pool_t* p, int32_t layer, int32_t* path, moe_miss_t* miss_host,
@@ -1314,7 +1181,7 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
         const LayerState& L = p->layers[layer];
         const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
         std::vector<int32_t> map(E), owner(N), next(E), meta(16);
-        const moe::LruState& cur = L.ds.s[L.par];
+        const moe::LruState& cur = L.ds.s;
         if ((st = dev_read(p, map.data(), cur.map, E))) return st;
         if (N && (st = dev_read(p, owner.data(), cur.owner, N))) return st;
         if ((st = dev_read(p, next.data(), cur.next, E))) return st;
@@ -1460,7 +1327,9 @@ moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, vo
         st = (err == hipErrorOutOfMemory || err == hipErrorMemoryAllocation) ? MOE_ENOMEM : MOE_EHIP;
     };
     hipError_t e;
-    if ((e = hipHostMalloc((void**)&host, bytes, hipHostMallocMapped)) != hipSuccess) fail(e, "hipHostMalloc");
+    // the same kind of memory as the store (coherent, device-mapped)
+    if ((e = hipHostMalloc((void**)&host, bytes, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
+        fail(e, "hipHostMalloc");
     if (!st) std::memset(host, 0x5A, bytes);
     if (!st && (e = hipHostGetDevicePointer((void**)&host_dev, host, 0)) != hipSuccess) fail(e, "hipHostGetDevicePointer");
     if (!st && (e = hipMalloc((void**)&dev, bytes)) != hipSuccess) fail(e, "hipMalloc");

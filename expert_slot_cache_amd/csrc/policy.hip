@@ -17,8 +17,10 @@
 // Every workgroup of the launch runs the same decision on its own copy of the state
 // in LDS (a few microseconds of latency, the same in each), so that each knows the
 // step's copies without waiting for another workgroup; the first one also writes the
-// results.  The state is double-buffered (read one copy, write the other) so that
-// no workgroup can read a half-written state.
+// results.  It writes the state back in place once every other workgroup has its
+// copy: those count themselves in an arrival word and never wait for anything, so
+// the first workgroup's (bounded) wait always ends.  Nothing in a step depends on
+// the host, so a decode step can be captured in a graph and replayed.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -61,19 +63,21 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     // distinct-id pass), and an empty presence bitmap
     if (!a.resident) {
         for (int e = tid; e < E; e += kPolicyThreads) {
-            map[e] = a.src.map[e];
-            prv[e] = a.src.prev[e];
-            nxt[e] = a.src.next[e];
+            map[e] = a.st.map[e];
+            prv[e] = a.st.prev[e];
+            nxt[e] = a.st.next[e];
         }
         for (int s = tid; s < N; s += kPolicyThreads) {
-            own[s] = a.src.owner[s];
-            fre[s] = a.src.free[s];
+            own[s] = a.st.owner[s];
+            fre[s] = a.st.free[s];
         }
-        if (tid < 3) s_meta[tid] = a.src.meta[tid];
+        if (tid < 3) s_meta[tid] = a.st.meta[tid];
     }
     for (int i = tid; i < nwords; i += kPolicyThreads) bits[i] = 0u;
     if (tid == 0) s_bad = 0;
     __syncthreads();
+    // the copy is in LDS: this workgroup no longer reads the state in HBM
+    if (!lead && tid == 0) __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt)
     for (int i = tid; i < a.n; i += kPolicyThreads) {
@@ -262,18 +266,32 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
             }
     }
 
-    // 4. the state the step leaves (unchanged unless the LRU ran)
+    // 4. the state the step leaves (unchanged unless the LRU ran), written in place
+    // once every other workgroup has its copy; the arrival word goes back to 0
     if (lead) {
+        if (tid == 0) {
+            const int others = (int)gridDim.x - 1;
+            unsigned long long polls = 0;
+            while (__hip_atomic_load(a.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < others) {
+                if (++polls > a.spin_limit) {
+                    __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __hip_atomic_store(a.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
         for (int e = tid; e < E; e += kPolicyThreads) {
-            a.dst.map[e] = map[e];
-            a.dst.prev[e] = prv[e];
-            a.dst.next[e] = nxt[e];
+            a.st.map[e] = map[e];
+            a.st.prev[e] = prv[e];
+            a.st.next[e] = nxt[e];
         }
         for (int s = tid; s < N; s += kPolicyThreads) {
-            a.dst.owner[s] = own[s];
-            a.dst.free[s] = fre[s];
+            a.st.owner[s] = own[s];
+            a.st.free[s] = fre[s];
         }
-        if (tid < 3) a.dst.meta[tid] = s_meta[tid];
+        if (tid < 3) a.st.meta[tid] = s_meta[tid];
         if (tid == 0 && a.timed_jobs)
             __hip_atomic_store(a.timed_jobs, nlink, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }

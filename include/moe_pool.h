@@ -251,15 +251,12 @@ moe_status_t moe_pool_forward(moe_pool_t* pool, int32_t layer, const void* x_dev
 
 /* prepare + forward of one layer in one call (same arguments, same semantics,
  * same errors and the same bits), for callers that run the two back to back.
- * For n_tokens <= 8 the call queues its kernels before it blocks: one kernel
- * computes the distinct ids and then waits (on the GPU) for the host's decision,
- * and the forward kernels follow it on the stream.  The host reads the ids back,
- * runs the LRU, issues the miss copies, waits for them to land and publishes the
- * decision ([llama-pool] Design item 3: the map table is rewritten before the
- * remap reads it).  If the call fails after queueing, it publishes "no expert"
- * so the queued kernels finish at once; out_dev is then undefined.  A kernel that
- * waited past its limit (10 s + 1 s per GB the step can copy) makes the next
- * call on the layer fail with EHIP. */
+ * No kernel of the step waits for the host or for another stream: streams can
+ * share a hardware queue, so such a wait could sit behind the very work it waits
+ * for.  With the host policy the host reads the distinct ids back, runs the LRU,
+ * queues the copies (the compute stream waits for them) and then the remap and
+ * the forward; with the device policy nothing is read back.  See `read_through`
+ * for the one-token variant that copies nothing before the forward. */
 moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_ids_dev, int32_t n_tokens,
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev,
                            const void* resid_dev, void* out_dev, moe_miss_t* miss_host, int32_t miss_cap,

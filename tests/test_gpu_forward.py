@@ -50,9 +50,7 @@ def _assert_bitwise(a, b, what):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{what}: step {s} layer {l}"
 
 
-# one_call: one moe_pool_step per layer (decode steps launch the forward before the
-# readback and gate it on the layer's published decision) instead of prepare +
-# forward
+# one_call: one moe_pool_step per layer instead of prepare + forward
 ONE_CALL = pytest.mark.parametrize("one_call", [False, True], ids=["two_call", "step"])
 
 

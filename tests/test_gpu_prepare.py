@@ -185,9 +185,8 @@ def test_out_of_range_id_rejected_state_untouched():
 
 
 def test_step_out_of_range_id_rejected_then_resumes():
-    """The one-call step launches its forward before the ids are checked: a bad id
-    must still be reported, leave the slot state untouched, and leave nothing
-    waiting on the device -- the next step runs at once and is correct."""
+    """A bad id in a one-call step is reported, leaves the slot state untouched and
+    prepares nothing; the next step runs at once and is correct."""
     wl = SMALL_BF16.with_(layers=1)
     rig = Rig(wl, slots=4, one_call=True)
     rng = synth.streams(wl)[2]
