@@ -799,17 +799,20 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
 // the matrix cores against that slot's weights, read once per 32-row tile.
 // ---------------------------------------------------------------------------
 constexpr int kGroupThreads = 1024;
-constexpr int kGBM = 32;        // pairs per tile (rows of one 32x32 MFMA block)
+constexpr int kGBM = 32;        // rows of one 32x32 MFMA block; a tile has kGBM * MT rows
 constexpr int kGBN = 128;       // output columns per workgroup: 4 waves x 32
 
 // a6: per-slot counts, exclusive offsets, slot-sorted pair list and the tile list.
 // grp layout (int32): [0] = n_tiles; [16 + t] = slot of tile t;
 // [16 + S + t] = first sorted row of tile t; [16 + 2S + t] = rows in tile t;
 // [16 + 3S + pos] = pair index at sorted position pos   (S = tile stride).
+// A tile has at most `tile_rows` rows (a multiple of 32: the grouped GEMMs give each
+// wave tile_rows / 32 blocks of 32 rows against the same weight loads).
 // Pairs of one slot are contiguous; their order inside the group is unspecified
 // (each GEMM row depends only on its own inputs, so results do not depend on it).
 __global__ __launch_bounds__(kGroupThreads) void k_group_build(Slots sl, const int32_t* __restrict__ slot_ids,
-                                                               int n, int tile_stride, int32_t* __restrict__ grp) {
+                                                               int n, int tile_stride, int tile_rows,
+                                                               int32_t* __restrict__ grp) {
     const char* unused_base;
     int nslots;
     pick_slots(sl, unused_base, nslots);
@@ -833,7 +836,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_build(Slots sl, const i
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * tid + i;
         c[i] = sl < nslots ? cnt[sl] : 0;
-        tc[i] = (c[i] + kGBM - 1) / kGBM;
+        tc[i] = (c[i] + tile_rows - 1) / tile_rows;
         sc += c[i];
         st += tc[i];
     }
@@ -879,11 +882,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_build(Slots sl, const i
     int32_t* perm = grp + 16 + 3 * tile_stride;
     for (int sl = tid; sl < nslots; sl += kGroupThreads) {
         const int cs = cnt[sl];
-        for (int j = 0; j * kGBM < cs; ++j) {
+        for (int j = 0; j * tile_rows < cs; ++j) {
             const int t = toff[sl] + j;
             t_slot[t] = sl;
-            t_row0[t] = off[sl] + j * kGBM;
-            t_rows[t] = min(kGBM, cs - j * kGBM);
+            t_row0[t] = off[sl] + j * tile_rows;
+            t_rows[t] = min(tile_rows, cs - j * tile_rows);
         }
     }
     __syncthreads();
@@ -926,7 +929,10 @@ __device__ __forceinline__ uint4 load_a8(const void* __restrict__ p, size_t e0) 
 // ---- grouped w13 + SwiGLU ------------------------------------------------------
 // grid.x: tiles (blocks past n_tiles exit); grid.y: blocks of 128 columns of I.
 // act_sorted[pos][j] = silu(x[t(pos)] . W13[s][j]) * (x[t(pos)] . W13[s][I + j])
-template <int AT>
+// A wave owns 32 columns of the gate and of the up half for the tile's MT blocks of
+// 32 rows: every weight chunk it loads feeds MT MFMAs (blocks past the tile's rows
+// are skipped; the last valid row is loaded in place of rows past the end).
+template <int AT, int MT>
 __global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
                                                      const int32_t* __restrict__ grp, int tile_stride,
                                                      const void* __restrict__ x, int K, int H, int I,
@@ -945,58 +951,84 @@ __global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
     const int l32 = lane & 31;
     const int j0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
     if (j0 >= I) return;
-    const int pair = perm[row0 + min(l32, rows - 1)];
-    const size_t xrow = (size_t)(pair / K) * H + hl * 32;
+    const int nb = (rows + kGBM - 1) / kGBM;     // row blocks present (uniform)
+    size_t xrow[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int pair = perm[row0 + min(m * kGBM + l32, rows - 1)];
+        xrow[m] = (size_t)(pair / K) * H + hl * 32;
+    }
     const int n = min(j0 + l32, I - 1);
     const size_t rb = (size_t)H * 2;
     const char* ex = wbase + (size_t)slot * stride + off_w;
     const char* gr = ex + (size_t)n * rb + hl * 64;
     const char* ur = ex + (size_t)(I + n) * rb + hl * 64;
-    f32x16_t cg = {}, cu = {};
-    uint4 bg[4], bu[4], a[4];
+    f32x16_t cg[MT], cu[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) cg[m] = cu[m] = f32x16_t{};
+    uint4 bg[4], bu[4], a[MT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         bg[j] = load16(gr + 16 * j);
         bu[j] = load16(ur + 16 * j);
-        a[j] = load_a8<AT>(x, xrow + 8 * j);
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        if (m < nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[m][j] = load_a8<AT>(x, xrow[m] + 8 * j);
     for (int k0 = 64; k0 <= H; k0 += 64) {
-        uint4 nbg[4], nbu[4], na[4];
+        uint4 nbg[4], nbu[4], na[MT][4];
         if (k0 < H) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 nbg[j] = load16(gr + (size_t)k0 * 2 + 16 * j);
                 nbu[j] = load16(ur + (size_t)k0 * 2 + 16 * j);
-                na[j] = load_a8<AT>(x, xrow + k0 + 8 * j);
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) na[m][j] = load_a8<AT>(x, xrow[m] + k0 + 8 * j);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            cg = mfma_32x32x16(a[j], bg[j], cg);
-            cu = mfma_32x32x16(a[j], bu[j], cu);
-        }
+        for (int m = 0; m < MT; ++m)
+            if (m < nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    cg[m] = mfma_32x32x16(a[m][j], bg[j], cg[m]);
+                    cu[m] = mfma_32x32x16(a[m][j], bu[j], cu[m]);
+                }
         if (k0 < H) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 bg[j] = nbg[j];
                 bu[j] = nbu[j];
-                a[j] = na[j];
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[m][j] = na[m][j];
         }
     }
     const int col = j0 + l32;
     if (col < I) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (r < rows) act_sorted[(size_t)(row0 + r) * I + col] = f32_to_bf16_rne(silu(cg[i]) * cu[i]);
+        for (int m = 0; m < MT; ++m) {
+            if (m >= nb) break;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
+                if (r < rows) act_sorted[(size_t)(row0 + r) * I + col] = f32_to_bf16_rne(silu(cg[m][i]) * cu[m][i]);
+            }
         }
     }
 }
 
 // ---- grouped w2 ------------------------------------------------------------------
 // grid.x: tiles; grid.y: blocks of 128 output columns of H.
-// y[pair(pos)][h] = act_sorted[pos] . W2[s][h]
+// y[pair(pos)][h] = act_sorted[pos] . W2[s][h]   (MT blocks of 32 rows per wave, as above)
+template <int MT>
 __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
                                                     const int32_t* __restrict__ grp, int tile_stride,
                                                     const uint16_t* __restrict__ act_sorted, int H, int I,
@@ -1015,41 +1047,58 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     const int l32 = lane & 31;
     const int h0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
     if (h0 >= H) return;
-    const uint16_t* arow = act_sorted + (size_t)(row0 + min(l32, rows - 1)) * I + hl * 32;
+    const int nb = (rows + kGBM - 1) / kGBM;
+    const uint16_t* arow[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) arow[m] = act_sorted + (size_t)(row0 + min(m * kGBM + l32, rows - 1)) * I + hl * 32;
     const int n = min(h0 + l32, H - 1);
     const char* br = wbase + (size_t)slot * stride + off_w + (size_t)n * I * 2 + hl * 64;
-    f32x16_t c = {};
-    uint4 b[4], a[4];
+    f32x16_t c[MT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        b[j] = load16(br + 16 * j);
-        a[j] = *reinterpret_cast<const uint4*>(arow + 8 * j);
-    }
+    for (int m = 0; m < MT; ++m) c[m] = f32x16_t{};
+    uint4 b[4], a[MT][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = load16(br + 16 * j);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        if (m < nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[m][j] = *reinterpret_cast<const uint4*>(arow[m] + 8 * j);
     for (int k0 = 64; k0 <= I; k0 += 64) {
-        uint4 nb[4], na[4];
+        uint4 nb4[4], na[MT][4];
         if (k0 < I) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                nb[j] = load16(br + (size_t)k0 * 2 + 16 * j);
-                na[j] = *reinterpret_cast<const uint4*>(arow + k0 + 8 * j);
-            }
+            for (int j = 0; j < 4; ++j) nb4[j] = load16(br + (size_t)k0 * 2 + 16 * j);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) na[m][j] = *reinterpret_cast<const uint4*>(arow[m] + k0 + 8 * j);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c = mfma_32x32x16(a[j], b[j], c);
+        for (int m = 0; m < MT; ++m)
+            if (m < nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c[m] = mfma_32x32x16(a[m][j], b[j], c[m]);
         if (k0 < I) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = nb[j];
-                a[j] = na[j];
-            }
+            for (int j = 0; j < 4; ++j) b[j] = nb4[j];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[m][j] = na[m][j];
         }
     }
     const int col = h0 + l32;
     if (col < H) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (r < rows) y[(size_t)perm[row0 + r] * H + col] = c[i];
+        for (int m = 0; m < MT; ++m) {
+            if (m >= nb) break;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
+                if (r < rows) y[(size_t)perm[row0 + r] * H + col] = c[m][i];
+            }
         }
     }
 }
@@ -1260,30 +1309,44 @@ bool grouped_shape(int wtype, int H, int I) { return wtype == W_BF16 && H % 64 =
 
 namespace {
 
-template <int AT>
-hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+// Row blocks per wave of the grouped GEMMs, from the average pairs per expert
+// (the weights of a slot are read once per tile; small groups keep one block).
+// Measured on OLMoE shapes (64 and 256 pairs per expert): 4 blocks run w13 1.6x
+// faster than 1 (occupancy 1, but four MFMAs per weight load); 2 sit in between.
+#ifndef MOE_GROUPED_MT
+#define MOE_GROUPED_MT 0
+#endif
+int grouped_mt(int n_pairs, int n_experts) {
+    if (MOE_GROUPED_MT > 0) return MOE_GROUPED_MT;
+    const int per = n_pairs / (n_pairs < n_experts ? n_pairs : n_experts);
+    return per >= 40 ? 4 : per >= 20 ? 2 : 1;
+}
+
+template <int AT, int MT>
+hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     const int n = a.T * g.K;
     const int stride_t = grouped_tile_stride(a.max_pairs, a.nslots_alloc);
     const int nsl = a.sl.npool > a.sl.nstage ? a.sl.npool : a.sl.nstage;
-    const int tiles = n / kGBM + (nsl < n ? nsl : n) + 1;   // bound on this call's tiles
-    hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.sl, a.slot_ids, n, stride_t, a.grp);
+    const int tiles = n / (kGBM * MT) + (nsl < n ? nsl : n) + 1;   // bound on this call's tiles
+    hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.sl, a.slot_ids, n, stride_t, kGBM * MT,
+                       a.grp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* act = static_cast<uint16_t*>(a.act);
     const dim3 g13(tiles, (g.I + kGBN - 1) / kGBN), g2(tiles, (g.H + kGBN - 1) / kGBN);
     if (ev && ev->w13_start)
-        hipExtLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
+        hipExtLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
                               g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act);
     else
-        hipLaunchKernelGGL((k_grouped_w13<AT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, a.x,
+        hipLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, a.x,
                            g.K, g.H, g.I, g.off_w13, act);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && ev->w2_start)
-        hipExtLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
+        hipExtLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
                               a.grp, stride_t, act, g.H, g.I, g.off_w2, a.y);
     else
-        hipLaunchKernelGGL(k_grouped_w2, g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H, g.I,
-                           g.off_w2, a.y);
+        hipLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H,
+                           g.I, g.off_w2, a.y);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t nt = (size_t)a.T * g.H;
     const dim3 gc((unsigned)((nt + 255) / 256));
@@ -1294,6 +1357,15 @@ hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* e
         hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.sl, a.y, a.topk_w, a.slot_ids, a.resid, a.out,
                            a.T, g.K, g.H);
     return hipGetLastError();
+}
+
+template <int AT>
+hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    switch (grouped_mt(a.T * g.K, g.E)) {
+        case 4: return run_grouped_mt<AT, 4>(g, a, ev, s);
+        case 2: return run_grouped_mt<AT, 2>(g, a, ev, s);
+        default: return run_grouped_mt<AT, 1>(g, a, ev, s);
+    }
 }
 
 }  // namespace

@@ -17,6 +17,7 @@ constexpr int kDecodeMaxTokens = 8;   // n_tokens above this use the grouped GEM
 // Shape and byte layout of one expert as stored in a slot.
 struct Geom {
     int H, I, K;
+    int E;                          // experts per layer
     int wtype, atype;
     size_t slot_stride;             // bytes per slot (= bytes per expert)
     size_t off_w13, off_w2, off_s13, off_s2;

@@ -789,6 +789,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     p->geom.H = c.hidden;
     p->geom.I = c.inter;
     p->geom.K = c.top_k;
+    p->geom.E = c.n_experts;
     p->geom.wtype = c.wtype;
     p->geom.atype = c.atype;
     p->geom.slot_stride = lay.total;

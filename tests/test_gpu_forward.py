@@ -240,13 +240,15 @@ def test_step_equals_prepare_then_forward():
     b.close()
 
 
-@pytest.mark.parametrize("T", [9, 33, 64])
+@pytest.mark.parametrize("T", [9, 33, 64, 128, 256])
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
 def test_grouped_path_oracle_and_bitwise_across_paths(T, atype):
     """n_tokens above the decode limit run the slot-grouped MFMA GEMMs.  With skewed
-    routing some slot groups span several 32-row tiles.  All experts resident, a
-    pool large enough for every step, and a pool small enough that every step falls
-    back to staging must give the same bits; all within tolerance of the oracle."""
+    routing some slot groups span several tiles (T = 128 and 256 give ~21 and ~43
+    pairs per expert: tiles of 64 and 128 rows, i.e. 2 and 4 row blocks per wave,
+    with ragged last blocks).  All experts resident, a pool large enough for every
+    step, and a pool small enough that every step falls back to staging must give the
+    same bits; all within tolerance of the oracle."""
     wl = synth.Workload("grouped", 1, 24, 4, 256, 128, 24, T, 0, "bf16", atype, 1.3, 0.0, 0, 13)
     trace = synth.make_trace(wl, steps=4)
     xs, ws = _inputs(wl, 4, T)
@@ -262,8 +264,31 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype):
     assert small.pool.stats()["fallbacks"] == 4
     if T == 64:
         assert counts.max() > 32          # a group spans two tiles
+    if T == 256:
+        assert counts.max() > 128 and counts.max() % 32  # several 128-row tiles, ragged last block
     for r in (big, small, res):
         r.close()
+
+
+@pytest.mark.parametrize("atype", ["bf16", "f32"])
+def test_grouped_rows_do_not_depend_on_the_batch(atype):
+    """A token's output depends only on its own inputs: computed in a 256-token step
+    (4 row blocks per wave, 128-row tiles) and again in a 12-token step (1 block per
+    wave) it has the same bits."""
+    wl = synth.Workload("grouped", 1, 24, 4, 256, 128, 24, 256, 0, "bf16", atype, 1.3, 0.0, 0, 14)
+    trace = synth.make_trace(wl, steps=1)
+    xs, ws = _inputs(wl, 1, 256)
+    rig = Rig(wl, slots=24, resident=True, std=0.05)
+    _, _, _, out_all = rig.step(0, trace[0, 0], to_dev_act(xs[0], atype), torch.from_numpy(ws[0]).to(DEV))
+    got_all = from_dev_act(out_all)
+    pick = np.array([0, 3, 17, 64, 100, 129, 130, 200, 201, 240, 254, 255])
+    _, _, _, out_few = rig.step(0, np.ascontiguousarray(trace[0, 0][pick]), to_dev_act(xs[0][pick], atype),
+                                torch.from_numpy(np.ascontiguousarray(ws[0][pick])).to(DEV))
+    got_few = from_dev_act(out_few)
+    assert np.array_equal(got_all[pick].view(np.uint32), got_few.view(np.uint32))
+    ref = rig.reference(0, xs[0], trace[0, 0], ws[0], tokens=list(pick[:4]))
+    check_close(got_all[pick[:4]], ref[pick[:4]], atype, "bf16", "256-token step")
+    rig.close()
 
 
 def test_grouped_full_batched_shape_sampled():
