@@ -161,7 +161,7 @@ struct PolicyArgs {
                              // through (misses are written to their slots on the way)
 };
 size_t policy_lds_bytes(int E, int N);
-// grid: workgroups of the launch (1 when resident; the copies spread over them).
+// grid: workgroups of the launch (the per-id outputs and the copies spread over them).
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
 
 // One launch of the streaming-read calibration kernel over [p, p + bytes) (bytes a

@@ -712,7 +712,9 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
                        (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 && !L.fill_t.pending;
     a.timed_jobs = timed ? p->timed_jobs_dev + layer : (rt && rt_timed ? p->rt_jobs_dev + layer : nullptr);
     a.tab = rt ? p->tab_dev : nullptr;
-    HIPCHK(moe::launch_policy(a, resident ? 1 : kPolicyGrid, timed ? L.fill_t.a : nullptr,
+    // resident: no copies, so only as many workgroups as the ids need (256 per)
+    const int grid = resident ? std::max(1, std::min(kPolicyGrid, n / 256)) : kPolicyGrid;
+    HIPCHK(moe::launch_policy(a, grid, timed ? L.fill_t.a : nullptr,
                               timed ? L.fill_t.b : nullptr, p->compute));
     if (timed) L.fill_t.pending = true;
     L.rt_prepared = rt;

@@ -77,15 +77,61 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     if (tid == 0) s_bad = 0;
     __syncthreads();
     // the copy is in LDS: this workgroup no longer reads the state in HBM
-    if (!lead && tid == 0) __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!a.resident && !lead && tid == 0) __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt)
-    for (int i = tid; i < a.n; i += kPolicyThreads) {
-        const int e = a.ids[i];
-        if ((unsigned)e < (unsigned)E)
-            atomicOr(&bits[e >> 5], 1u << (e & 31));
-        else
-            s_bad = 1;
+    // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt).  A
+    // thread reads eight ids before it marks any, so that their loads are in flight
+    // together (a prefill step has thousands of ids per workgroup).  With at most 64
+    // experts the marks go into a 64-bit mask per lane, OR-ed across the wave, and
+    // one lane sets the (two) bitmap words: thousands of LDS atomics on two words
+    // would serialise.
+    if (E <= 64) {
+        uint64_t m = 0;
+        bool bad = false;
+        for (int i0 = tid; i0 < a.n; i0 += 8 * kPolicyThreads) {
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * kPolicyThreads;
+                e[q] = i < a.n ? a.ids[i] : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (i0 + q * kPolicyThreads >= a.n) break;
+                if ((unsigned)e[q] < (unsigned)E)
+                    m |= 1ull << e[q];
+                else
+                    bad = true;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+            m |= (uint64_t)(uint32_t)__shfl_xor((int)lo, off, 64) |
+                 ((uint64_t)(uint32_t)__shfl_xor((int)hi, off, 64) << 32);
+        }
+        if (bad) s_bad = 1;
+        if (lane == 0) {
+            if ((uint32_t)m) atomicOr(&bits[0], (uint32_t)m);
+            if (E > 32 && (uint32_t)(m >> 32)) atomicOr(&bits[1], (uint32_t)(m >> 32));
+        }
+    } else {
+        for (int i0 = tid; i0 < a.n; i0 += 8 * kPolicyThreads) {
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * kPolicyThreads;
+                e[q] = i < a.n ? a.ids[i] : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (i0 + q * kPolicyThreads >= a.n) break;
+                if ((unsigned)e[q] < (unsigned)E)
+                    atomicOr(&bits[e[q] >> 5], 1u << (e[q] & 31));
+                else
+                    s_bad = 1;
+            }
+        }
     }
     __syncthreads();
     int base = 0;
@@ -114,13 +160,11 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
 
     if (a.resident) {
         // every expert lives at slot = id: count the hits, the ids are the slots
-        // (a single-workgroup launch; nothing to copy)
-        if (s_bad) {
-            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = -1;
-        } else {
-            for (int i = tid; i < a.n; i += kPolicyThreads) a.out[i] = a.ids[i];
-        }
-        if (tid == 0) {
+        // (nothing to copy; the ids are spread over the launch's workgroups)
+        const int gtid = blockIdx.x * kPolicyThreads + tid;
+        const int gthreads = gridDim.x * kPolicyThreads;
+        for (int i = gtid; i < a.n; i += gthreads) a.out[i] = s_bad ? -1 : a.ids[i];
+        if (lead && tid == 0) {
             *a.path = s_bad ? PATH_NONE : PATH_POOL;
             rec[0] = s_bad ? PATH_NONE : PATH_POOL;
             rec[1] = D;
@@ -146,13 +190,17 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     bool pool = true;
     const size_t eb = a.eb;
     auto store_at = [&](int e) { return a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * eb; };
+    // every workgroup holds the decision, so the per-id outputs are spread over all
+    // of them (each id is written by exactly one thread of the launch)
+    const int gtid = blockIdx.x * kPolicyThreads + tid;
+    const int gthreads = gridDim.x * kPolicyThreads;
     if (s_bad) {
         // an id outside [0, E): nothing changes, the step produces no expert
+        for (int i = gtid; i < a.n; i += gthreads) {
+            a.out[i] = -1;
+            if (a.tab) a.tab[i] = PairSrc{nullptr, nullptr};
+        }
         if (lead) {
-            for (int i = tid; i < a.n; i += kPolicyThreads) {
-                a.out[i] = -1;
-                if (a.tab) a.tab[i] = PairSrc{nullptr, nullptr};
-            }
             if (tid == 0) {
                 *a.path = PATH_NONE;
                 rec[0] = PATH_NONE;
@@ -168,12 +216,12 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         pool = false;
         nlink = D;
         njobs = a.tab ? 0 : D;
+        for (int i = gtid; i < a.n; i += gthreads) {
+            const int e = a.ids[i];
+            a.out[i] = rank[e];
+            if (a.tab) a.tab[i] = PairSrc{store_at(e), nullptr};
+        }
         if (lead) {
-            for (int i = tid; i < a.n; i += kPolicyThreads) {
-                const int e = a.ids[i];
-                a.out[i] = rank[e];
-                if (a.tab) a.tab[i] = PairSrc{store_at(e), nullptr};
-            }
             if (tid == 0) {
                 *a.path = PATH_STAGE;
                 rec[0] = PATH_STAGE;
@@ -255,15 +303,14 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         nlink = s_njobs;
         njobs = a.tab ? 0 : nlink;
         // the remap, through the fresh table
-        if (lead)
-            for (int i = tid; i < a.n; i += kPolicyThreads) {
-                const int e = a.ids[i];
-                const int slot = map[e];
-                a.out[i] = slot;
-                if (a.tab)
-                    a.tab[i] = rank[e] < 0 ? PairSrc{store_at(e), a.slots + (size_t)slot * eb}
-                                           : PairSrc{nullptr, nullptr};
-            }
+        for (int i = gtid; i < a.n; i += gthreads) {
+            const int e = a.ids[i];
+            const int slot = map[e];
+            a.out[i] = slot;
+            if (a.tab)
+                a.tab[i] = rank[e] < 0 ? PairSrc{store_at(e), a.slots + (size_t)slot * eb}
+                                       : PairSrc{nullptr, nullptr};
+        }
     }
 
     // 4. the state the step leaves (unchanged unless the LRU ran), written in place
@@ -327,7 +374,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
 size_t policy_lds_bytes(int E, int N) { return ((size_t)5 * E + 2 * N + E / 32 + 1) * sizeof(int32_t); }
 
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s) {
-    if (a.n < 1 || a.n > (1 << 24) || grid < 1 || (a.resident && grid != 1) || a.eb % 16 ||
+    if (a.n < 1 || a.n > (1 << 24) || grid < 1 || a.eb % 16 ||
         (!a.resident && a.per_piece < 1))
         return hipErrorInvalidValue;
     const size_t lds = policy_lds_bytes(a.E, a.N);
