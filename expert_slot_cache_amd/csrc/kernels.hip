@@ -926,17 +926,50 @@ __device__ __forceinline__ uint4 load_a8(const void* __restrict__ p, size_t e0) 
 // [span + 32h + 8j, +8) of its row to MFMA j (j = 0..3), for A and B alike, so each
 // lane reads 64 contiguous bytes of its row per span and the four MFMAs together
 // cover the span once.
+// ---- staged activation tiles ---------------------------------------------------------
+// The grouped GEMMs stage the tile's rows of activations in LDS, 64 elements (one k
+// span) at a time, double-buffered: all 256 threads load the next span (two threads
+// per row, 32 elements each) while the MFMAs read the current one, and the four waves
+// of a workgroup share it instead of each loading its own copy.  Rows are padded to
+// 144 bytes so that the 32 rows read by one MFMA operand load spread over the banks.
+constexpr int kARowBytes = 144;
+
+// A thread's share of a staged row: 32 bf16 (64 bytes), kept as four named
+// registers (as an array the compiler left it in scratch memory).
+struct Row32 {
+    uint4 q0, q1, q2, q3;
+};
+template <int AT>
+__device__ __forceinline__ Row32 load_row32(const void* __restrict__ p, size_t e0) {
+    return Row32{load_a8<AT>(p, e0), load_a8<AT>(p, e0 + 8), load_a8<AT>(p, e0 + 16), load_a8<AT>(p, e0 + 24)};
+}
+__device__ __forceinline__ void store_row32(char* d, const Row32& r) {
+    uint4* q = reinterpret_cast<uint4*>(d);
+    q[0] = r.q0;
+    q[1] = r.q1;
+    q[2] = r.q2;
+    q[3] = r.q3;
+}
+
+// One MFMA operand (8 bf16) of row `row`, elements [hl * 32 + 8 j, +8) of the span.
+__device__ __forceinline__ uint4 lds_a8(const char* buf, int row, int hl, int j) {
+    return *reinterpret_cast<const uint4*>(buf + row * kARowBytes + hl * 64 + 16 * j);
+}
+
 // ---- grouped w13 + SwiGLU ------------------------------------------------------
 // grid.x: tiles (blocks past n_tiles exit); grid.y: blocks of 128 columns of I.
 // act_sorted[pos][j] = silu(x[t(pos)] . W13[s][j]) * (x[t(pos)] . W13[s][I + j])
 // A wave owns 32 columns of the gate and of the up half for the tile's MT blocks of
 // 32 rows: every weight chunk it loads feeds MT MFMAs (blocks past the tile's rows
-// are skipped; the last valid row is loaded in place of rows past the end).
+// are skipped; rows past the end repeat the last row and are never stored).
+// (256, 2): two waves per SIMD; the accumulators then stay in VGPRs (no AGPRs)
+// and the MT = 4 kernel fits without spilling.
 template <int AT, int MT>
-__global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
+__global__ __launch_bounds__(256, 2) void k_grouped_w13(Slots sl, size_t stride,
                                                      const int32_t* __restrict__ grp, int tile_stride,
                                                      const void* __restrict__ x, int K, int H, int I,
                                                      size_t off_w, uint16_t* __restrict__ act_sorted) {
+    __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
     const char* wbase;
@@ -946,18 +979,17 @@ __global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
     const int32_t* perm = grp + 16 + 3 * tile_stride;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int j0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
-    if (j0 >= I) return;
+    const int j0 = blockIdx.y * kGBN + (tid >> 6) * 32;
+    const bool cols = j0 < I;                    // the wave has columns (uniform per wave)
     const int nb = (rows + kGBM - 1) / kGBM;     // row blocks present (uniform)
-    size_t xrow[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int pair = perm[row0 + min(m * kGBM + l32, rows - 1)];
-        xrow[m] = (size_t)(pair / K) * H + hl * 32;
-    }
+    // staging: thread tid covers half `sh` of row `sr`
+    const int sr = tid >> 1, sh = tid & 1;
+    const bool srow = sr < nb * kGBM;
+    const size_t sx = srow ? (size_t)(perm[row0 + min(sr, rows - 1)] / K) * H + sh * 32 : 0;
     const int n = min(j0 + l32, I - 1);
     const size_t rb = (size_t)H * 2;
     const char* ex = wbase + (size_t)slot * stride + off_w;
@@ -966,53 +998,55 @@ __global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
     f32x16_t cg[MT], cu[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) cg[m] = cu[m] = f32x16_t{};
-    uint4 bg[4], bu[4], a[MT][4];
+    uint4 bg[4], bu[4];
+    Row32 sa{};
+    if (cols)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        bg[j] = load16(gr + 16 * j);
-        bu[j] = load16(ur + 16 * j);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        if (m < nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a[m][j] = load_a8<AT>(x, xrow[m] + 8 * j);
+        for (int j = 0; j < 4; ++j) {
+            bg[j] = load16(gr + 16 * j);
+            bu[j] = load16(ur + 16 * j);
+        }
+    if (srow) store_row32(As[0] + sr * kARowBytes + sh * 64, load_row32<AT>(x, sx));
+    __syncthreads();
+    int cur = 0;
     for (int k0 = 64; k0 <= H; k0 += 64) {
-        uint4 nbg[4], nbu[4], na[MT][4];
-        if (k0 < H) {
+        const bool more = k0 < H;
+        uint4 nbg[4], nbu[4];
+        if (more) {
+            if (cols)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                nbg[j] = load16(gr + (size_t)k0 * 2 + 16 * j);
-                nbu[j] = load16(ur + (size_t)k0 * 2 + 16 * j);
-            }
+                for (int j = 0; j < 4; ++j) {
+                    nbg[j] = load16(gr + (size_t)k0 * 2 + 16 * j);
+                    nbu[j] = load16(ur + (size_t)k0 * 2 + 16 * j);
+                }
+            if (srow) sa = load_row32<AT>(x, sx + k0);
+        }
+        if (cols) {
+            const char* buf = As[cur];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 if (m < nb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) na[m][j] = load_a8<AT>(x, xrow[m] + k0 + 8 * j);
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 a = lds_a8(buf, m * kGBM + l32, hl, j);
+                        cg[m] = mfma_32x32x16(a, bg[j], cg[m]);
+                        cu[m] = mfma_32x32x16(a, bu[j], cu[m]);
+                    }
         }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < nb)
+        if (more) {
+            if (srow) store_row32(As[cur ^ 1] + sr * kARowBytes + sh * 64, sa);
+            if (cols)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    cg[m] = mfma_32x32x16(a[m][j], bg[j], cg[m]);
-                    cu[m] = mfma_32x32x16(a[m][j], bu[j], cu[m]);
+                    bg[j] = nbg[j];
+                    bu[j] = nbu[j];
                 }
-        if (k0 < H) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bg[j] = nbg[j];
-                bu[j] = nbu[j];
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a[m][j] = na[m][j];
+            __syncthreads();
+            cur ^= 1;
         }
     }
     const int col = j0 + l32;
-    if (col < I) {
+    if (cols && col < I) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m >= nb) break;
@@ -1027,12 +1061,14 @@ __global__ __launch_bounds__(256) void k_grouped_w13(Slots sl, size_t stride,
 
 // ---- grouped w2 ------------------------------------------------------------------
 // grid.x: tiles; grid.y: blocks of 128 output columns of H.
-// y[pair(pos)][h] = act_sorted[pos] . W2[s][h]   (MT blocks of 32 rows per wave, as above)
+// y[pair(pos)][h] = act_sorted[pos] . W2[s][h]   (MT blocks of 32 rows per wave, the
+// act rows staged in LDS as above)
 template <int MT>
 __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
                                                     const int32_t* __restrict__ grp, int tile_stride,
                                                     const uint16_t* __restrict__ act_sorted, int H, int I,
                                                     size_t off_w, float* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
     const char* wbase;
@@ -1042,55 +1078,62 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
     const int32_t* perm = grp + 16 + 3 * tile_stride;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int h0 = blockIdx.y * kGBN + (threadIdx.x >> 6) * 32;
-    if (h0 >= H) return;
+    const int h0 = blockIdx.y * kGBN + (tid >> 6) * 32;
+    const bool cols = h0 < H;
     const int nb = (rows + kGBM - 1) / kGBM;
-    const uint16_t* arow[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) arow[m] = act_sorted + (size_t)(row0 + min(m * kGBM + l32, rows - 1)) * I + hl * 32;
+    const int sr = tid >> 1, sh = tid & 1;
+    const bool srow = sr < nb * kGBM;
+    const uint16_t* sp = act_sorted + (size_t)(row0 + min(sr, rows - 1)) * I + sh * 32;
     const int n = min(h0 + l32, H - 1);
     const char* br = wbase + (size_t)slot * stride + off_w + (size_t)n * I * 2 + hl * 64;
     f32x16_t c[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) c[m] = f32x16_t{};
-    uint4 b[4], a[MT][4];
+    uint4 b[4];
+    Row32 sa{};
+    if (cols)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = load16(br + 16 * j);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        if (m < nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a[m][j] = *reinterpret_cast<const uint4*>(arow[m] + 8 * j);
+        for (int j = 0; j < 4; ++j) b[j] = load16(br + 16 * j);
+    if (srow) store_row32(As[0] + sr * kARowBytes + sh * 64, load_row32<A_BF16>(sp, 0));
+    __syncthreads();
+    int cur = 0;
     for (int k0 = 64; k0 <= I; k0 += 64) {
-        uint4 nb4[4], na[MT][4];
-        if (k0 < I) {
+        const bool more = k0 < I;
+        uint4 nb4[4];
+        if (more) {
+            if (cols)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) nb4[j] = load16(br + (size_t)k0 * 2 + 16 * j);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                if (m < nb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) na[m][j] = *reinterpret_cast<const uint4*>(arow[m] + k0 + 8 * j);
+                for (int j = 0; j < 4; ++j) nb4[j] = load16(br + (size_t)k0 * 2 + 16 * j);
+            if (srow) sa = load_row32<A_BF16>(sp, k0);
         }
+        if (cols) {
+            const char* buf = As[cur];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < nb)
+            for (int j = 0; j < 4; ++j) {
+                const uint4 bj = b[j];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) c[m] = mfma_32x32x16(a[m][j], b[j], c[m]);
-        if (k0 < I) {
+                for (int m = 0; m < MT; ++m)
+                    if (m < nb) {
+                        const uint4 a = lds_a8(buf, m * kGBM + l32, hl, j);
+                        c[m] = mfma_32x32x16(a, bj, c[m]);
+                    }
+            }
+        }
+        if (more) {
+            if (srow) store_row32(As[cur ^ 1] + sr * kARowBytes + sh * 64, sa);
+            if (cols)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = nb4[j];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a[m][j] = na[m][j];
+                for (int j = 0; j < 4; ++j) b[j] = nb4[j];
+            __syncthreads();
+            cur ^= 1;
         }
     }
     const int col = h0 + l32;
-    if (col < H) {
+    if (cols && col < H) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m >= nb) break;
@@ -1105,31 +1148,59 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
 
 // ---- ordered top-k combine (grouped path) -------------------------------------------
 // out[t][h] = resid[t][h] + sum_{k = 0..K-1} w[t][k] * y[t*K + k][h]   (k in order;
-// pairs whose slot id is out of range contribute nothing)
+// pairs whose slot id is out of range contribute nothing).  grid.y walks the tokens
+// (a token's weights and slot ids are read once, into scalar registers); a thread
+// owns 4 consecutive h (H is a multiple of 64 on this path) and issues the loads of
+// y for eight k at a time before it adds them in order.
 template <int AT>
 __global__ __launch_bounds__(256) void k_combine(Slots sl, const float* __restrict__ y,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ slot_ids,
                                                  const void* __restrict__ resid, void* __restrict__ out, int T,
                                                  int K, int H) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)T * H) return;
     const char* unused_base;
     int nslots;
     pick_slots(sl, unused_base, nslots);
-    const int t = (int)(idx / H);
-    const int h = (int)(idx - (size_t)t * H);
-    float acc = 0.0f;
-    for (int k = 0; k < K; ++k) {
-        const int sl = slot_ids[t * K + k];
-        const float v = (sl >= 0 && sl < nslots) ? y[((size_t)t * K + k) * H + h] : 0.0f;
-        acc = fmaf(topk_w[(size_t)t * K + k], v, acc);
+    const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (h >= H) return;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int k = k0 + q;
+                const int s = k < K ? slot_ids[t * K + k] : -1;
+                v[q] = (s >= 0 && s < nslots) ? *reinterpret_cast<const float4*>(y + ((size_t)t * K + k) * H + h)
+                                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int k = k0 + q;
+                if (k >= K) break;
+                const float w = topk_w[(size_t)t * K + k];
+                a0 = fmaf(w, v[q].x, a0);
+                a1 = fmaf(w, v[q].y, a1);
+                a2 = fmaf(w, v[q].z, a2);
+                a3 = fmaf(w, v[q].w, a3);
+            }
+        }
+        const size_t o = (size_t)t * H + h;
+        if (resid) {
+            a0 += load_act<AT>(resid, o);
+            a1 += load_act<AT>(resid, o + 1);
+            a2 += load_act<AT>(resid, o + 2);
+            a3 += load_act<AT>(resid, o + 3);
+        }
+        if (AT == A_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = make_float4(a0, a1, a2, a3);
+        } else {
+            uint2 u;
+            u.x = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+            u.y = (uint32_t)f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = u;
+        }
     }
-    if (resid) acc += load_act<AT>(resid, idx);
-    if (AT == A_F32)
-        static_cast<float*>(out)[idx] = acc;
-    else
-        static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1311,15 +1382,16 @@ namespace {
 
 // Row blocks per wave of the grouped GEMMs, from the average pairs per expert
 // (the weights of a slot are read once per tile; small groups keep one block).
-// Measured on OLMoE shapes (64 and 256 pairs per expert): 4 blocks run w13 1.6x
-// faster than 1 (occupancy 1, but four MFMAs per weight load); 2 sit in between.
+// Measured on OLMoE-shaped prefill (skewed routing, 64 and 256 pairs per expert on
+// average): 4 blocks match 1 at 64 and run the layer 1.4x faster at 256; 2 blocks
+// were slower than either for w2, so they are not chosen.
 #ifndef MOE_GROUPED_MT
 #define MOE_GROUPED_MT 0
 #endif
 int grouped_mt(int n_pairs, int n_experts) {
     if (MOE_GROUPED_MT > 0) return MOE_GROUPED_MT;
     const int per = n_pairs / (n_pairs < n_experts ? n_pairs : n_experts);
-    return per >= 40 ? 4 : per >= 20 ? 2 : 1;
+    return per >= 40 ? 4 : 1;
 }
 
 template <int AT, int MT>
@@ -1348,8 +1420,7 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
         hipLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H,
                            g.I, g.off_w2, a.y);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t nt = (size_t)a.T * g.H;
-    const dim3 gc((unsigned)((nt + 255) / 256));
+    const dim3 gc((unsigned)((g.H / 4 + 255) / 256), (unsigned)(a.T < 65535 ? a.T : 65535));
     if (ev && ev->w2_stop)
         hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.sl, a.y, a.topk_w,
                               a.slot_ids, a.resid, a.out, a.T, g.K, g.H);
@@ -1363,7 +1434,7 @@ template <int AT>
 hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     switch (grouped_mt(a.T * g.K, g.E)) {
         case 4: return run_grouped_mt<AT, 4>(g, a, ev, s);
-        case 2: return run_grouped_mt<AT, 2>(g, a, ev, s);
+        case 2: return run_grouped_mt<AT, 2>(g, a, ev, s);   // only when forced at build time
         default: return run_grouped_mt<AT, 1>(g, a, ev, s);
     }
 }
