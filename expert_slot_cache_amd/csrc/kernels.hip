@@ -352,10 +352,39 @@ struct XChunk<W_BF16, XT_BF16> {
     }
 };
 
+// Activation chunks of an INT4 GEMV already repacked (XChunk<W_INT4> below) and stored
+// in LDS by the workgroup, 80 bytes per 32 elements: the 16 words, then the sum.
+// Element e0 of the packed vectors is chunk (e0 - e_base) / 32.
+constexpr int kPackedChunkBytes = 80;
+struct PackedX {
+    const char* base;
+    size_t e_base;
+};
+
 template <>
 struct XChunk<W_INT4, XT_I4> {
     uint32_t p[16];
     float sx;
+    template <int AT>
+    __device__ __forceinline__ void load(const PackedX& m, size_t e0) {
+        const char* d = m.base + ((e0 - m.e_base) >> 5) * kPackedChunkBytes;
+        const uint4* q = reinterpret_cast<const uint4*>(d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = q[i];
+            p[4 * i + 0] = v.x;
+            p[4 * i + 1] = v.y;
+            p[4 * i + 2] = v.z;
+            p[4 * i + 3] = v.w;
+        }
+        sx = *reinterpret_cast<const float*>(d + 64);
+    }
+    __device__ __forceinline__ void store_packed(char* d) const {
+        uint4* q = reinterpret_cast<uint4*>(d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = make_uint4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+        *reinterpret_cast<float*>(d + 64) = sx;
+    }
     template <int AT, class M>
     __device__ __forceinline__ void load(const M& m, size_t e0) {
         float s = 0.0f;
@@ -443,7 +472,7 @@ template <int WT, int AT, int CPL, int RP, int WPR>
 __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const int32_t* __restrict__ slot_ids,
                                          const void* __restrict__ x, int H, int I, int gs, size_t off_w,
                                          size_t off_s, void* __restrict__ act, int t, int pair, int rblk,
-                                         float (*red)[2][RP]) {
+                                         float (*red)[2][RP], char* xs) {
     using X = XChunk<WT, XSel<WT, AT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
@@ -471,45 +500,15 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
 
     float pg[RP], pu[RP];
-    if (ok) {
+    if constexpr (WT == W_INT4) {
+        // The token's activation vector is repacked once per workgroup into LDS (xs)
+        // while the weight loads are in flight; a lane then reads its chunks from there
+        // instead of repacking each chunk it uses (the repacking was most of the
+        // kernel's vector instructions).
         const SlotReader rd(ebase, stride);
         uint4 wg[RP][CPL], wu[RP][CPL];
-#pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            const int i = min(i0 + p, I - 1);
-            const size_t g = off_w + (size_t)i * row_bytes;
-            const size_t u = off_w + (size_t)(I + i) * row_bytes;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = (part * CPL + j) * G + gl;
-                wg[p][j] = rd.load16(g + (size_t)c * 16);
-                wu[p][j] = rd.load16(u + (size_t)c * 16);
-            }
-        }
         float sg[RP][CPL], su[RP][CPL];
-        if (WT == W_INT4) {
-            const int spr = H / 128;
-#pragma unroll
-            for (int p = 0; p < RP; ++p) {
-                const int i = min(i0 + p, I - 1);
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    const int c = (part * CPL + j) * G + gl;
-                    sg[p][j] = rd.scale(off_s + ((size_t)i * spr + (c >> 2)) * 2);
-                    su[p][j] = rd.scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
-                }
-            }
-        }
-        X xv[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-            xv[j].template load<AT>(PlainMem(x), (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
-        // every load of the lane is in flight before the first use: the scheduler
-        // would otherwise hold some back to save registers (two round trips)
-        __builtin_amdgcn_sched_barrier(0);
-        if (ps.to) {
-            // a miss read from the store: the lane writes what it read to the slot
-            const SlotWriter wr(ps.to, stride);
+        if (ok) {
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
                 const int i = min(i0 + p, I - 1);
@@ -518,8 +517,8 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = (part * CPL + j) * G + gl;
-                    wr.store16(g + (size_t)c * 16, wg[p][j]);
-                    wr.store16(u + (size_t)c * 16, wu[p][j]);
+                    wg[p][j] = rd.load16(g + (size_t)c * 16);
+                    wu[p][j] = rd.load16(u + (size_t)c * 16);
                 }
             }
             if (WT == W_INT4) {
@@ -530,46 +529,192 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
 #pragma unroll
                     for (int j = 0; j < CPL; ++j) {
                         const int c = (part * CPL + j) * G + gl;
-                        if ((c & 3) == 0) {
-                            wr.store_scale(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
-                            wr.store_scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
-                        }
+                        sg[p][j] = rd.scale(off_s + ((size_t)i * spr + (c >> 2)) * 2);
+                        su[p][j] = rd.scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
                     }
                 }
             }
         }
+        for (int c = threadIdx.x; c < H / 32; c += blockDim.x) {
+            X xc;
+            xc.template load<AT>(PlainMem(x), (size_t)t * H + (size_t)c * 32);
+            xc.store_packed(xs + c * kPackedChunkBytes);
+        }
+        __syncthreads();
+        if (ok) {
+            X xv[CPL];
 #pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            float a = 0.0f, b = 0.0f;
+            for (int j = 0; j < CPL; ++j)
+                xv[j].template load<AT>(PackedX{xs, (size_t)t * H},
+                                        (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+            // every load of the lane is in flight before the first use: the scheduler
+            // would otherwise hold some back to save registers (two round trips)
+            __builtin_amdgcn_sched_barrier(0);
+            if (ps.to) {
+                // a miss read from the store: the lane writes what it read to the slot
+                const SlotWriter wr(ps.to, stride);
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                float dg = cdot(wg[p][j], xv[j]);
-                float du = cdot(wu[p][j], xv[j]);
-                if (WT == W_INT4) {
-                    dg *= sg[p][j];
-                    du *= su[p][j];
+                for (int p = 0; p < RP; ++p) {
+                    const int i = min(i0 + p, I - 1);
+                    const size_t g = off_w + (size_t)i * row_bytes;
+                    const size_t u = off_w + (size_t)(I + i) * row_bytes;
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        const int c = (part * CPL + j) * G + gl;
+                        wr.store16(g + (size_t)c * 16, wg[p][j]);
+                        wr.store16(u + (size_t)c * 16, wu[p][j]);
+                    }
                 }
-                a += dg;
-                b += du;
+                if (WT == W_INT4) {
+                    const int spr = H / 128;
+#pragma unroll
+                    for (int p = 0; p < RP; ++p) {
+                        const int i = min(i0 + p, I - 1);
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) {
+                            const int c = (part * CPL + j) * G + gl;
+                            if ((c & 3) == 0) {
+                                wr.store_scale(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
+                                wr.store_scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
+                            }
+                        }
+                    }
+                }
             }
-            pg[p] = a;
-            pu[p] = b;
-        }
-        float gu[2 * RP];
 #pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            gu[2 * p] = pg[p];
-            gu[2 * p + 1] = pu[p];
-        }
-        group_sum_n<2 * RP>(gu, G);
+            for (int p = 0; p < RP; ++p) {
+                float a = 0.0f, b = 0.0f;
 #pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            pg[p] = gu[2 * p];
-            pu[p] = gu[2 * p + 1];
+                for (int j = 0; j < CPL; ++j) {
+                    float dg = cdot(wg[p][j], xv[j]);
+                    float du = cdot(wu[p][j], xv[j]);
+                    if (WT == W_INT4) {
+                        dg *= sg[p][j];
+                        du *= su[p][j];
+                    }
+                    a += dg;
+                    b += du;
+                }
+                pg[p] = a;
+                pu[p] = b;
+            }
+            float gu[2 * RP];
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                gu[2 * p] = pg[p];
+                gu[2 * p + 1] = pu[p];
+            }
+            group_sum_n<2 * RP>(gu, G);
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                pg[p] = gu[2 * p];
+                pu[p] = gu[2 * p + 1];
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
         }
     } else {
+        if (ok) {
+            const SlotReader rd(ebase, stride);
+            uint4 wg[RP][CPL], wu[RP][CPL];
 #pragma unroll
-        for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
+            for (int p = 0; p < RP; ++p) {
+                const int i = min(i0 + p, I - 1);
+                const size_t g = off_w + (size_t)i * row_bytes;
+                const size_t u = off_w + (size_t)(I + i) * row_bytes;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const int c = (part * CPL + j) * G + gl;
+                    wg[p][j] = rd.load16(g + (size_t)c * 16);
+                    wu[p][j] = rd.load16(u + (size_t)c * 16);
+                }
+            }
+            float sg[RP][CPL], su[RP][CPL];
+            if (WT == W_INT4) {
+                const int spr = H / 128;
+#pragma unroll
+                for (int p = 0; p < RP; ++p) {
+                    const int i = min(i0 + p, I - 1);
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        const int c = (part * CPL + j) * G + gl;
+                        sg[p][j] = rd.scale(off_s + ((size_t)i * spr + (c >> 2)) * 2);
+                        su[p][j] = rd.scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
+                    }
+                }
+            }
+            X xv[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+                xv[j].template load<AT>(PlainMem(x), (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+            // every load of the lane is in flight before the first use: the scheduler
+            // would otherwise hold some back to save registers (two round trips)
+            __builtin_amdgcn_sched_barrier(0);
+            if (ps.to) {
+                // a miss read from the store: the lane writes what it read to the slot
+                const SlotWriter wr(ps.to, stride);
+#pragma unroll
+                for (int p = 0; p < RP; ++p) {
+                    const int i = min(i0 + p, I - 1);
+                    const size_t g = off_w + (size_t)i * row_bytes;
+                    const size_t u = off_w + (size_t)(I + i) * row_bytes;
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        const int c = (part * CPL + j) * G + gl;
+                        wr.store16(g + (size_t)c * 16, wg[p][j]);
+                        wr.store16(u + (size_t)c * 16, wu[p][j]);
+                    }
+                }
+                if (WT == W_INT4) {
+                    const int spr = H / 128;
+#pragma unroll
+                    for (int p = 0; p < RP; ++p) {
+                        const int i = min(i0 + p, I - 1);
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) {
+                            const int c = (part * CPL + j) * G + gl;
+                            if ((c & 3) == 0) {
+                                wr.store_scale(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
+                                wr.store_scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                float a = 0.0f, b = 0.0f;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    float dg = cdot(wg[p][j], xv[j]);
+                    float du = cdot(wu[p][j], xv[j]);
+                    if (WT == W_INT4) {
+                        dg *= sg[p][j];
+                        du *= su[p][j];
+                    }
+                    a += dg;
+                    b += du;
+                }
+                pg[p] = a;
+                pu[p] = b;
+            }
+            float gu[2 * RP];
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                gu[2 * p] = pg[p];
+                gu[2 * p + 1] = pu[p];
+            }
+            group_sum_n<2 * RP>(gu, G);
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                pg[p] = gu[2 * p];
+                pu[p] = gu[2 * p + 1];
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
+        }
     }
     if (WPR > 1) {
         if (lane == 0)
@@ -603,8 +748,9 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
                                                   const void* __restrict__ x, int H, int I, int gs,
                                                   size_t off_w, size_t off_s, void* __restrict__ act) {
     __shared__ float red[4][2][RP];
+    extern __shared__ __attribute__((aligned(16))) char xs_packed[];   // INT4: the packed activations
     w13_rows<WT, AT, CPL, RP, WPR>(sl, stride, slot_ids, x, H, I, gs, off_w, off_s, act, blockIdx.z,
-                                   blockIdx.z * gridDim.y + blockIdx.y, blockIdx.x, red);
+                                   blockIdx.z * gridDim.y + blockIdx.y, blockIdx.x, red, xs_packed);
 }
 
 // ---- w2 + ordered top-k combine ------------------------------------------------
@@ -777,8 +923,24 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
         pick_slots(sl, wbase, nslots);
         W2Task<WT, CPL, RP> tk;
         w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, ps, t, K, H, I, gs, ln, wave, off_w, off_s);
-        w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
-                                    ys + (size_t)wave * ln.RB + ln.grp * RP);
+        if constexpr (WT == W_INT4) {
+            // the token's K act vectors, repacked once per workgroup while the weight
+            // loads are in flight (each lane would otherwise repack every chunk it uses)
+            using X = XChunk<W_INT4, XT_I4>;
+            char* xs = reinterpret_cast<char*>(ys) + ((K * WPR * ln.RB * 4 + 15) & ~15);
+            const size_t e0 = (size_t)t * K * I;
+            for (int c = threadIdx.x; c < K * (I >> 5); c += blockDim.x) {
+                X xc;
+                xc.template load<A_BF16>(PlainMem(act), e0 + (size_t)c * 32);
+                xc.store_packed(xs + c * kPackedChunkBytes);
+            }
+            __syncthreads();
+            w2_finish<WT, CPL, RP, WPR>(tk, PackedX{xs, e0}, H, I, gs, ln, stride, off_w, off_s,
+                                        ys + (size_t)wave * ln.RB + ln.grp * RP);
+        } else {
+            w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
+                                        ys + (size_t)wave * ln.RB + ln.grp * RP);
+        }
     } else {
         pick_slots(sl, wbase, nslots);
         for (int task = wave; task < K * WPR; task += nw) {
@@ -1260,12 +1422,13 @@ template <int WT, int AT, int CPL, int RP, int WPR>
 hipError_t launch_w13(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
     const int rows_per_block = (4 / WPR) * (64 / G) * RP;
     const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, g.K, a.T);
+    const size_t lds = WT == W_INT4 ? (size_t)(g.H / 32) * kPackedChunkBytes : 0;
     if (ev && ev->w13_start)
-        hipExtLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, ev->w13_start,
+        hipExtLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), (uint32_t)lds, s, ev->w13_start,
                               ev->w13_stop, 0, a.sl, g.slot_stride, a.slot_ids, a.x, g.H, g.I, log2_of(G), g.off_w13,
                               g.off_s13, a.act);
     else
-        hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), 0, s, a.sl, g.slot_stride,
+        hipLaunchKernelGGL((k_w13_gemv<WT, AT, CPL, RP, WPR>), grid, dim3(256), lds, s, a.sl, g.slot_stride,
                            a.slot_ids, a.x, g.H, g.I, log2_of(G), g.off_w13, g.off_s13, a.act);
     return hipGetLastError();
 }
@@ -1276,7 +1439,9 @@ hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEven
     const int RB = (64 / G) * RP;
     const int tasks = g.K * WPR;
     const int nw = tasks < NWMAX ? tasks : NWMAX;
-    const size_t lds = (size_t)tasks * RB * sizeof(float);
+    size_t lds = (size_t)tasks * RB * sizeof(float);
+    if (WT == W_INT4 && tasks <= NWMAX)   // the token's packed act vectors
+        lds = ((lds + 15) & ~(size_t)15) + (size_t)g.K * (g.I / 32) * kPackedChunkBytes;
     const dim3 grid((g.H + RB - 1) / RB, a.T);
     auto go = [&](auto kern) {
         if (ev && ev->w2_start)
