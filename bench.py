@@ -37,7 +37,7 @@ DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (b
 # WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
 # copy of known size; valid only for the kernel source these were taken on.
 PMC_TRAFFIC = {
-    ("olmoe_bf16_e64", "cf8a771d4a2b8417"): {"fetch_kib": 32816.0, "fetch_scale": 1.9998,
+    ("olmoe_bf16_e64", "99309ad20e78ad93"): {"fetch_kib": 32816.0, "fetch_scale": 1.9998,
                                              "write_kib": 32.1, "write_scale": 1.0},
 }
 

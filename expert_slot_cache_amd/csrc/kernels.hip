@@ -237,6 +237,11 @@ struct SlotReader {
     __device__ __forceinline__ float scale(size_t off) const {
         return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kCoherent));
     }
+    // the scale's bf16 bits, widened only where they are used (widening here would make
+    // the wave wait for this load, and every load issued before it, right away)
+    __device__ __forceinline__ uint16_t scale_bits(size_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kCoherent);
+    }
 };
 
 // Vector stores into a slot: the write-through of an expert that a kernel reads from
@@ -251,6 +256,9 @@ struct SlotWriter {
     }
     __device__ __forceinline__ void store_scale(size_t off, float v) const {
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(__float_as_uint(v) >> 16), r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ void store_scale_bits(size_t off, uint16_t b) const {
+        __builtin_amdgcn_raw_buffer_store_b16(b, r, (int)off, 0, 0);
     }
 };
 
@@ -385,12 +393,26 @@ struct XChunk<W_INT4, XT_I4> {
         for (int i = 0; i < 4; ++i) q[i] = make_uint4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
         *reinterpret_cast<float*>(d + 64) = sx;
     }
+    // the chunk's 32 bf16 activations as read (four 16-byte loads), before repacking
+    struct Raw {
+        uint4 u[4];
+    };
+    template <class M>
+    __device__ __forceinline__ static Raw fetch(const M& m, size_t e0) {
+        Raw r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.u[i] = m.ld16((e0 + 8 * i) * 2);
+        return r;
+    }
     template <int AT, class M>
     __device__ __forceinline__ void load(const M& m, size_t e0) {
+        pack(fetch(m, e0));
+    }
+    __device__ __forceinline__ void pack(const Raw& r) {
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {        // word i: elements 8i .. 8i+7
-            const uint4 u = m.ld16((e0 + 8 * i) * 2);
+            const uint4 u = r.u[i];
             p[4 * i + 0] = (u.x & 0xFFFFu) | (u.z << 16);          // (x0, x4)
             p[4 * i + 1] = (u.x >> 16) | (u.z & 0xFFFF0000u);      // (x1, x5)
             p[4 * i + 2] = (u.y & 0xFFFFu) | (u.w << 16);          // (x2, x6)
@@ -494,6 +516,15 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     const bool ok = slot >= 0 && slot < nslots && i0 < I;
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
+    // INT4: this thread's activation chunk is requested before anything that depends on
+    // the slot.  Loads complete in the order they are issued, so the repacking below
+    // waits for these loads only, not for the weights issued after them.
+    using XI4 = XChunk<W_INT4, XT_I4>;
+    [[maybe_unused]] XI4::Raw xr;
+    [[maybe_unused]] const int nxc = H / 32;
+    if constexpr (WT == W_INT4)
+        xr = XI4::fetch(PlainMem(x), (size_t)t * H + (size_t)min((int)threadIdx.x, nxc - 1) * 32);
+    __builtin_amdgcn_sched_barrier(0);
     // the expert's address in scalar registers before the branch, so that the
     // arguments it needs are loaded with the others (one round trip, not two)
     const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
@@ -501,14 +532,54 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
 
     float pg[RP], pu[RP];
     if constexpr (WT == W_INT4) {
-        // The token's activation vector is repacked once per workgroup into LDS (xs)
-        // while the weight loads are in flight; a lane then reads its chunks from there
-        // instead of repacking each chunk it uses (the repacking was most of the
-        // kernel's vector instructions).
-        const SlotReader rd(ebase, stride);
+        // Every lane issues all of its weight and scale loads with no branch between them
+        // and the activation loads: a lane group past the last row reads a clamped row and
+        // drops the result, and a pair without a valid slot gets a buffer of length zero,
+        // whose loads return zeros without touching memory.  The activation vector is then
+        // repacked once per workgroup into LDS (xs) while the weights are in flight, and
+        // each lane reads its chunks from there.
+        const bool sok = slot >= 0 && slot < nslots;
+        const SlotReader rd(sok ? ebase : wbase, sok ? stride : 0);
         uint4 wg[RP][CPL], wu[RP][CPL];
-        float sg[RP][CPL], su[RP][CPL];
-        if (ok) {
+        uint16_t sg[RP][CPL], su[RP][CPL];
+        const int spr = H / 128;
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int i = min(i0 + p, I - 1);
+            const size_t g = off_w + (size_t)i * row_bytes;
+            const size_t u = off_w + (size_t)(I + i) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = (part * CPL + j) * G + gl;
+                wg[p][j] = rd.load16(g + (size_t)c * 16);
+                wu[p][j] = rd.load16(u + (size_t)c * 16);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int i = min(i0 + p, I - 1);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = (part * CPL + j) * G + gl;
+                sg[p][j] = rd.scale_bits(off_s + ((size_t)i * spr + (c >> 2)) * 2);
+                su[p][j] = rd.scale_bits(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((int)threadIdx.x < nxc) {
+            XI4 xc;
+            xc.pack(xr);
+            xc.store_packed(xs + threadIdx.x * kPackedChunkBytes);
+        }
+        for (int c = threadIdx.x + blockDim.x; c < nxc; c += blockDim.x) {
+            XI4 xc;
+            xc.template load<AT>(PlainMem(x), (size_t)t * H + (size_t)c * 32);
+            xc.store_packed(xs + c * kPackedChunkBytes);
+        }
+        __syncthreads();
+        if (ps.to && ok) {
+            // a miss read from the store: the lane writes what it read to the slot
+            const SlotWriter wr(ps.to, stride);
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
                 const int i = min(i0 + p, I - 1);
@@ -517,102 +588,40 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = (part * CPL + j) * G + gl;
-                    wg[p][j] = rd.load16(g + (size_t)c * 16);
-                    wu[p][j] = rd.load16(u + (size_t)c * 16);
-                }
-            }
-            if (WT == W_INT4) {
-                const int spr = H / 128;
-#pragma unroll
-                for (int p = 0; p < RP; ++p) {
-                    const int i = min(i0 + p, I - 1);
-#pragma unroll
-                    for (int j = 0; j < CPL; ++j) {
-                        const int c = (part * CPL + j) * G + gl;
-                        sg[p][j] = rd.scale(off_s + ((size_t)i * spr + (c >> 2)) * 2);
-                        su[p][j] = rd.scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2);
+                    wr.store16(g + (size_t)c * 16, wg[p][j]);
+                    wr.store16(u + (size_t)c * 16, wu[p][j]);
+                    if ((c & 3) == 0) {
+                        wr.store_scale_bits(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
+                        wr.store_scale_bits(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
                     }
                 }
             }
         }
-        for (int c = threadIdx.x; c < H / 32; c += blockDim.x) {
-            X xc;
-            xc.template load<AT>(PlainMem(x), (size_t)t * H + (size_t)c * 32);
-            xc.store_packed(xs + c * kPackedChunkBytes);
+        // each packed chunk is read from LDS where it is used (holding all CPL of them
+        // would cost 17 registers each); every row still sums its chunks in j order
+#pragma unroll
+        for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            X xv;
+            xv.template load<AT>(PackedX{xs, (size_t)t * H}, (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+#pragma unroll
+            for (int p = 0; p < RP; ++p) {
+                pg[p] += cdot(wg[p][j], xv) * bf16_to_f32(sg[p][j]);
+                pu[p] += cdot(wu[p][j], xv) * bf16_to_f32(su[p][j]);
+            }
         }
-        __syncthreads();
-        if (ok) {
-            X xv[CPL];
+        float gu[2 * RP];
 #pragma unroll
-            for (int j = 0; j < CPL; ++j)
-                xv[j].template load<AT>(PackedX{xs, (size_t)t * H},
-                                        (size_t)t * H + (size_t)((part * CPL + j) * G + gl) * EPC);
-            // every load of the lane is in flight before the first use: the scheduler
-            // would otherwise hold some back to save registers (two round trips)
-            __builtin_amdgcn_sched_barrier(0);
-            if (ps.to) {
-                // a miss read from the store: the lane writes what it read to the slot
-                const SlotWriter wr(ps.to, stride);
+        for (int p = 0; p < RP; ++p) {
+            gu[2 * p] = pg[p];
+            gu[2 * p + 1] = pu[p];
+        }
+        group_sum_n<2 * RP>(gu, G);
 #pragma unroll
-                for (int p = 0; p < RP; ++p) {
-                    const int i = min(i0 + p, I - 1);
-                    const size_t g = off_w + (size_t)i * row_bytes;
-                    const size_t u = off_w + (size_t)(I + i) * row_bytes;
-#pragma unroll
-                    for (int j = 0; j < CPL; ++j) {
-                        const int c = (part * CPL + j) * G + gl;
-                        wr.store16(g + (size_t)c * 16, wg[p][j]);
-                        wr.store16(u + (size_t)c * 16, wu[p][j]);
-                    }
-                }
-                if (WT == W_INT4) {
-                    const int spr = H / 128;
-#pragma unroll
-                    for (int p = 0; p < RP; ++p) {
-                        const int i = min(i0 + p, I - 1);
-#pragma unroll
-                        for (int j = 0; j < CPL; ++j) {
-                            const int c = (part * CPL + j) * G + gl;
-                            if ((c & 3) == 0) {
-                                wr.store_scale(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
-                                wr.store_scale(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
-                            }
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < RP; ++p) {
-                float a = 0.0f, b = 0.0f;
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    float dg = cdot(wg[p][j], xv[j]);
-                    float du = cdot(wu[p][j], xv[j]);
-                    if (WT == W_INT4) {
-                        dg *= sg[p][j];
-                        du *= su[p][j];
-                    }
-                    a += dg;
-                    b += du;
-                }
-                pg[p] = a;
-                pu[p] = b;
-            }
-            float gu[2 * RP];
-#pragma unroll
-            for (int p = 0; p < RP; ++p) {
-                gu[2 * p] = pg[p];
-                gu[2 * p + 1] = pu[p];
-            }
-            group_sum_n<2 * RP>(gu, G);
-#pragma unroll
-            for (int p = 0; p < RP; ++p) {
-                pg[p] = gu[2 * p];
-                pu[p] = gu[2 * p + 1];
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
+        for (int p = 0; p < RP; ++p) {
+            pg[p] = gu[2 * p];
+            pu[p] = gu[2 * p + 1];
         }
     } else {
         if (ok) {
@@ -765,7 +774,7 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
 template <int WT, int CPL, int RP>
 struct W2Task {
     uint4 w[RP][CPL];
-    float sc[RP][CPL];   // int4 group scales (unused otherwise)
+    uint16_t sc[RP][CPL];   // int4 group scales, bf16 bits (unused otherwise)
     int pair;            // t * K + k
     int part;
     bool ok;             // the pair's slot id is valid
@@ -788,7 +797,10 @@ __device__ __forceinline__ W2Lane w2_lane(int gs, int RP, int rb0) {
 }
 
 // `slot` is slot_ids[t * K + task / WPR], loaded by the caller (so that it can be
-// read together with the path word, before any branch).
+// read together with the path word, before any branch).  INT4 tasks issue their loads
+// with no branch even for an invalid slot (a buffer of length zero, whose loads return
+// zeros without touching memory), so that a caller's activation loads issued earlier
+// can be waited for alone.
 template <int WT, int CPL, int RP, int WPR>
 __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wbase, int nslots, size_t stride,
                                          int slot, const PairSrc& ps, int t, int K, int H, int I, int gs,
@@ -801,10 +813,10 @@ __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wb
     tk.to = ps.to;
     const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
-    if (!tk.ok) return;
+    if (WT != W_INT4 && !tk.ok) return;
     const size_t row_bytes = (size_t)CPL * G * WPR * 16;
     const int spr = I / 128;
-    const SlotReader rd(ebase, stride);
+    const SlotReader rd(tk.ok ? ebase : wbase, tk.ok ? stride : 0);
 #pragma unroll
     for (int p = 0; p < RP; ++p) {
         const size_t row = off_w + (size_t)min(ln.r0 + p, H - 1) * row_bytes;
@@ -816,8 +828,8 @@ __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wb
         for (int p = 0; p < RP; ++p)
 #pragma unroll
             for (int j = 0; j < CPL; ++j)
-                tk.sc[p][j] = rd.scale(off_s + ((size_t)min(ln.r0 + p, H - 1) * spr +
-                                                (((tk.part * CPL + j) * G + ln.gl) >> 2)) * 2);
+                tk.sc[p][j] = rd.scale_bits(off_s + ((size_t)min(ln.r0 + p, H - 1) * spr +
+                                                     (((tk.part * CPL + j) * G + ln.gl) >> 2)) * 2);
     }
 }
 
@@ -836,10 +848,15 @@ __device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M
             for (int p = 0; p < RP; ++p) yk[p] = 0.0f;
         return;
     }
-    X av[CPL];
+    // activations read from global memory are all requested before the first use; packed
+    // ones (LDS) are read where they are used, which saves their registers
+    constexpr bool kLds = std::is_same<M, PackedX>::value;
+    X av[kLds ? 1 : CPL];
+    if constexpr (!kLds) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
-        av[j].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
+        for (int j = 0; j < CPL; ++j)
+            av[j].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (tk.to) {
         // a miss read from the store: the lane writes what it read to the slot
@@ -853,18 +870,23 @@ __device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M
             for (int j = 0; j < CPL; ++j) {
                 const int c = (tk.part * CPL + j) * G + ln.gl;
                 wr.store16(off_w + (size_t)r * row_bytes + (size_t)c * 16, tk.w[p][j]);
-                if (WT == W_INT4 && (c & 3) == 0) wr.store_scale(off_s + ((size_t)r * spr + (c >> 2)) * 2, tk.sc[p][j]);
+                if (WT == W_INT4 && (c & 3) == 0)
+                    wr.store_scale_bits(off_s + ((size_t)r * spr + (c >> 2)) * 2, tk.sc[p][j]);
             }
         }
     }
     float acc[RP];
 #pragma unroll
-    for (int p = 0; p < RP; ++p) {
-        acc[p] = 0.0f;
+    for (int p = 0; p < RP; ++p) acc[p] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            float d = cdot(tk.w[p][j], av[j]);
-            if (WT == W_INT4) d *= tk.sc[p][j];
+    for (int j = 0; j < CPL; ++j) {
+        if constexpr (kLds)
+            av[0].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
+        const X& a = av[kLds ? 0 : j];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            float d = cdot(tk.w[p][j], a);
+            if (WT == W_INT4) d *= bf16_to_f32(tk.sc[p][j]);
             acc[p] += d;
         }
     }
@@ -921,16 +943,28 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
         const int slot = slot_ids[t * K + wave / WPR];
         const PairSrc ps = pair_src(sl, t * K + wave / WPR);
         pick_slots(sl, wbase, nslots);
+        // INT4: the token's K act vectors are repacked once per workgroup (each lane
+        // would otherwise repack every chunk it uses).  A thread's first chunk is
+        // requested before the weights, so that the repacking waits for it alone.
+        using XI4 = XChunk<W_INT4, XT_I4>;
+        [[maybe_unused]] XI4::Raw xr;
+        [[maybe_unused]] const int nxc = K * (I >> 5);
+        [[maybe_unused]] const size_t e0 = (size_t)t * K * I;
+        if constexpr (WT == W_INT4)
+            xr = XI4::fetch(PlainMem(act), e0 + (size_t)min((int)threadIdx.x, nxc - 1) * 32);
+        __builtin_amdgcn_sched_barrier(0);
         W2Task<WT, CPL, RP> tk;
         w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, ps, t, K, H, I, gs, ln, wave, off_w, off_s);
         if constexpr (WT == W_INT4) {
-            // the token's K act vectors, repacked once per workgroup while the weight
-            // loads are in flight (each lane would otherwise repack every chunk it uses)
-            using X = XChunk<W_INT4, XT_I4>;
+            __builtin_amdgcn_sched_barrier(0);
             char* xs = reinterpret_cast<char*>(ys) + ((K * WPR * ln.RB * 4 + 15) & ~15);
-            const size_t e0 = (size_t)t * K * I;
-            for (int c = threadIdx.x; c < K * (I >> 5); c += blockDim.x) {
-                X xc;
+            if ((int)threadIdx.x < nxc) {
+                XI4 xc;
+                xc.pack(xr);
+                xc.store_packed(xs + threadIdx.x * kPackedChunkBytes);
+            }
+            for (int c = threadIdx.x + blockDim.x; c < nxc; c += blockDim.x) {
+                XI4 xc;
                 xc.template load<A_BF16>(PlainMem(act), e0 + (size_t)c * 32);
                 xc.store_packed(xs + c * kPackedChunkBytes);
             }
