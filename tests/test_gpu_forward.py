@@ -306,3 +306,43 @@ def test_grouped_full_batched_shape_sampled():
     ref = rig.reference(0, xs[0], trace[0, 0], ws[0], tokens=sample)
     check_close(got[sample], ref[sample], "bf16", "bf16", "batched shape")
     rig.close()
+
+
+@pytest.mark.parametrize("wtype,atype,T", [("f32", "f32", 1), ("bf16", "bf16", 1), ("int4", "bf16", 1),
+                                           ("bf16", "f32", 3), ("int4", "bf16", 3), ("bf16", "bf16", 24)])
+def test_slot_ids_outside_the_range_contribute_nothing(wtype, atype, T):
+    """A slot id outside the prepared range (-1, or past the pool) contributes nothing
+    and is never used as an address (the flash-2x32 page, section 3.4: an id of -1 must
+    not reach a kernel).  Since the k sum is fma(w_k, y_k, acc) in k order, the output
+    equals, bit for bit, the forward with those pairs' slots intact and gate weights 0,
+    and the oracle on the remaining pairs.  T = 24 takes the grouped GEMM path."""
+    K, N = 4, 8
+    wl = synth.Workload("badslot", 1, 16, K, 256, 128, N, T, 0, wtype, atype, 1.0, 0.0, 0, 23)
+    rig = Rig(wl, slots=N, fast=False, std=0.05)
+    rng = np.random.default_rng(5)
+    ids = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)   # fits the pool
+    xs, ws = _inputs(wl, 1, T)
+    x, w = xs[0], ws[0]
+    ids_d = torch.from_numpy(ids).to(DEV)
+    slot_d = torch.empty_like(ids_d)
+    path, _ = rig.pool.prepare(0, ids_d, T, slot_d)
+    assert path == binding.PATH_POOL
+    bad = np.zeros((T, K), bool)
+    bad[0, 1] = bad[T - 1, K - 1] = True
+    if T > 1:
+        bad[1, 0] = True
+    slots = slot_d.cpu().numpy()
+    slots_bad = slots.copy()
+    slots_bad[bad] = np.where(np.arange(bad.sum()) % 2 == 0, -1, N + 3)
+    w0 = w.copy()
+    w0[bad] = 0.0
+    dt = torch.float32 if atype == "f32" else torch.bfloat16
+    xd = to_dev_act(x, atype)
+    out_bad = torch.empty((T, wl.hidden), dtype=dt, device=DEV)
+    out_w0 = torch.empty_like(out_bad)
+    rig.pool.forward(0, xd, torch.from_numpy(slots_bad).to(DEV), torch.from_numpy(w).to(DEV), out_bad, T)
+    rig.pool.forward(0, xd, slot_d, torch.from_numpy(w0).to(DEV), out_w0, T)
+    got, want = from_dev_act(out_bad), from_dev_act(out_w0)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    check_close(got, rig.reference(0, x, ids, w0), atype, wtype, "outside slots skipped")
+    rig.close()
