@@ -58,20 +58,70 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     const bool lead = blockIdx.x == 0;
     unsigned long long* ctr = a.ctr;   // steps, hits, misses, fallbacks, bytes_h2d, staged
     int32_t* rec = a.rec;
+    // counter updates are additions nothing in the launch reads back: atomics without a
+    // return value, so that the lead thread does not wait for a read of the old values
+    auto bump = [](unsigned long long* c, unsigned long long v) {
+        __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    // the first 8 * kPolicyThreads ids (every workgroup reads them for the decision),
+    // and the one id this thread writes an output for first (index blockIdx.x *
+    // kPolicyThreads + tid, below), requested before the state so that the reads overlap
+    int e0[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = tid + q * kPolicyThreads;
+        e0[q] = i < a.n ? a.ids[i] : 0;
+    }
+    const int gid0 = blockIdx.x * kPolicyThreads + tid;
+    const int mine = gid0 < a.n ? a.ids[gid0] : 0;
+    auto id_at = [&](int i) { return i == gid0 ? mine : a.ids[i]; };
 
     // 0. the state the step starts from (loaded first: its latency overlaps the
     // distinct-id pass), and an empty presence bitmap
     if (!a.resident) {
-        for (int e = tid; e < E; e += kPolicyThreads) {
+        // a thread's loads for the first two rounds (E, N <= 512) are all issued before
+        // it writes any of them to LDS: one round trip, not one per array group
+        constexpr int R = 2;
+        int vm[R] = {}, vp[R] = {}, vn[R] = {}, vo[R] = {}, vf[R] = {};
+        int vmeta = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = tid + r * kPolicyThreads;
+            if (e < E) {
+                vm[r] = a.st.map[e];
+                vp[r] = a.st.prev[e];
+                vn[r] = a.st.next[e];
+            }
+            if (e < N) {
+                vo[r] = a.st.owner[e];
+                vf[r] = a.st.free[e];
+            }
+        }
+        if (tid < 3) vmeta = a.st.meta[tid];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = tid + r * kPolicyThreads;
+            if (e < E) {
+                map[e] = vm[r];
+                prv[e] = vp[r];
+                nxt[e] = vn[r];
+            }
+            if (e < N) {
+                own[e] = vo[r];
+                fre[e] = vf[r];
+            }
+        }
+        if (tid < 3) s_meta[tid] = vmeta;
+        for (int e = tid + R * kPolicyThreads; e < E; e += kPolicyThreads) {
             map[e] = a.st.map[e];
             prv[e] = a.st.prev[e];
             nxt[e] = a.st.next[e];
         }
-        for (int s = tid; s < N; s += kPolicyThreads) {
+        for (int s = tid + R * kPolicyThreads; s < N; s += kPolicyThreads) {
             own[s] = a.st.owner[s];
             fre[s] = a.st.free[s];
         }
-        if (tid < 3) s_meta[tid] = a.st.meta[tid];
     }
     for (int i = tid; i < nwords; i += kPolicyThreads) bits[i] = 0u;
     if (tid == 0) s_bad = 0;
@@ -93,7 +143,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int i = i0 + q * kPolicyThreads;
-                e[q] = i < a.n ? a.ids[i] : 0;
+                e[q] = i0 == tid ? e0[q] : (i < a.n ? a.ids[i] : 0);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -121,7 +171,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int i = i0 + q * kPolicyThreads;
-                e[q] = i < a.n ? a.ids[i] : 0;
+                e[q] = i0 == tid ? e0[q] : (i < a.n ? a.ids[i] : 0);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -163,7 +213,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         // (nothing to copy; the ids are spread over the launch's workgroups)
         const int gtid = blockIdx.x * kPolicyThreads + tid;
         const int gthreads = gridDim.x * kPolicyThreads;
-        for (int i = gtid; i < a.n; i += gthreads) a.out[i] = s_bad ? -1 : a.ids[i];
+        for (int i = gtid; i < a.n; i += gthreads) a.out[i] = s_bad ? -1 : id_at(i);
         if (lead && tid == 0) {
             *a.path = s_bad ? PATH_NONE : PATH_POOL;
             rec[0] = s_bad ? PATH_NONE : PATH_POOL;
@@ -173,8 +223,8 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
             if (s_bad) {
                 __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             } else {
-                ctr[0] += 1;
-                ctr[1] += (unsigned long long)D;
+                bump(ctr + 0, 1);
+                bump(ctr + 1, (unsigned long long)D);
             }
         }
         return;
@@ -217,7 +267,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         nlink = D;
         njobs = a.tab ? 0 : D;
         for (int i = gtid; i < a.n; i += gthreads) {
-            const int e = a.ids[i];
+            const int e = id_at(i);
             a.out[i] = rank[e];
             if (a.tab) a.tab[i] = PairSrc{store_at(e), nullptr};
         }
@@ -228,10 +278,10 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
                 rec[1] = D;
                 rec[2] = 0;
                 rec[3] = 0;
-                ctr[0] += 1;
-                ctr[3] += 1;
-                ctr[4] += (unsigned long long)D * a.eb;
-                ctr[5] += (unsigned long long)D;
+                bump(ctr + 0, 1);
+                bump(ctr + 3, 1);
+                bump(ctr + 4, (unsigned long long)D * a.eb);
+                bump(ctr + 5, (unsigned long long)D);
             }
         }
     } else {
@@ -293,10 +343,10 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
                 rec[1] = D;
                 rec[2] = misses;
                 rec[3] = 0;
-                ctr[0] += 1;
-                ctr[1] += (unsigned long long)hits;
-                ctr[2] += (unsigned long long)misses;
-                ctr[4] += (unsigned long long)misses * a.eb;
+                bump(ctr + 0, 1);
+                bump(ctr + 1, (unsigned long long)hits);
+                bump(ctr + 2, (unsigned long long)misses);
+                bump(ctr + 4, (unsigned long long)misses * a.eb);
             }
         }
         __syncthreads();
@@ -304,7 +354,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         njobs = a.tab ? 0 : nlink;
         // the remap, through the fresh table
         for (int i = gtid; i < a.n; i += gthreads) {
-            const int e = a.ids[i];
+            const int e = id_at(i);
             const int slot = map[e];
             a.out[i] = slot;
             if (a.tab)
