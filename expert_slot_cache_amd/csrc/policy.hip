@@ -185,7 +185,18 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     }
     __syncthreads();
     int base = 0;
-    for (int c0 = 0; c0 < E; c0 += kPolicyThreads) {
+    if (E <= 64) {
+        // the id set is one 64-bit mask: an expert's rank is the number of set bits below it
+        const uint64_t all = (uint64_t)bits[0] | (E > 32 ? (uint64_t)bits[1] << 32 : 0ull);
+        if (tid < E && ((all >> tid) & 1ull)) {
+            const int pos = __popcll(all & ((1ull << tid) - 1ull));
+            list[pos] = tid;
+            rank[tid] = pos;
+        }
+        base = __popcll(all);
+        __syncthreads();
+    }
+    for (int c0 = 0; E > 64 && c0 < E; c0 += kPolicyThreads) {
         const int e = c0 + tid;
         const bool present = e < E && ((bits[e >> 5] >> (e & 31)) & 1u);
         const uint64_t m = __ballot(present);
@@ -285,10 +296,104 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
             }
         }
     } else {
-        // 3. the LRU, in LDS, one id at a time.  Miss j's expert is written to list[j]
-        // (j <= the id being processed, so nothing unread is overwritten), and a
+        // 3. the LRU, one id at a time in ascending order.  Miss j's expert is written to
+        // list[j] (j <= the id being processed, so nothing unread is overwritten), and a
         // missed expert's rank entry becomes -1 (rank is not needed on this path).
-        if (tid == 0) {
+        if (E <= 64) {
+            // the lists in registers of wave 0: lane e holds expert e's map entry and
+            // neighbours, lane s slot s's owner and free-list entry; the wave walks the ids
+            // with scalar control flow, reading single lanes (readlane) and writing them
+            // (a select on the lane id); a chain of dependent LDS accesses costs ~0.3 us
+            // per id, these a few cycles each
+            if (wave == 0) {
+                int vmap = lane < E ? map[lane] : -1;
+                int vprv = lane < E ? prv[lane] : -1;
+                int vnxt = lane < E ? nxt[lane] : -1;
+                int vown = lane < N ? own[lane] : -1;
+                int vfre = lane < N ? fre[lane] : -1;
+                int head = __builtin_amdgcn_readfirstlane(s_meta[0]);
+                int tail = __builtin_amdgcn_readfirstlane(s_meta[1]);
+                int nfree = __builtin_amdgcn_readfirstlane(s_meta[2]);
+                const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[0]);
+                const uint32_t hi = E > 32 ? __builtin_amdgcn_readfirstlane(bits[1]) : 0u;
+                uint64_t todo = (uint64_t)lo | ((uint64_t)hi << 32);
+                int hits = 0, misses = 0;
+                auto get = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+                auto put = [lane](int& v, int l, int x) { v = lane == l ? x : v; };
+                auto unlink = [&](int e) {
+                    const int p = get(vprv, e), q = get(vnxt, e);
+                    if (p >= 0) put(vnxt, p, q); else head = q;
+                    if (q >= 0) put(vprv, q, p); else tail = p;
+                    put(vprv, e, -1);
+                    put(vnxt, e, -1);
+                };
+                auto push_mru = [&](int e) {
+                    put(vprv, e, tail);
+                    put(vnxt, e, -1);
+                    if (tail >= 0) put(vnxt, tail, e); else head = e;
+                    tail = e;
+                };
+                while (todo) {
+                    const int e = (int)__builtin_ctzll(todo);
+                    todo &= todo - 1ull;
+                    if (get(vmap, e) >= 0) {
+                        unlink(e);
+                        push_mru(e);
+                        ++hits;
+                        continue;
+                    }
+                    int slot, evicted;
+                    if (nfree > 0) {
+                        slot = get(vfre, --nfree);
+                        evicted = -1;
+                    } else {
+                        evicted = head;
+                        unlink(evicted);
+                        slot = get(vmap, evicted);
+                        put(vmap, evicted, -1);
+                    }
+                    put(vmap, e, slot);
+                    put(vown, slot, e);
+                    push_mru(e);
+                    if (lane == 0) {
+                        if (lead) {
+                            rec[4 + 3 * misses] = e;
+                            rec[5 + 3 * misses] = slot;
+                            rec[6 + 3 * misses] = evicted;
+                        }
+                        list[misses] = e;
+                        rank[e] = -1;
+                    }
+                    ++misses;
+                }
+                if (lane < E) {
+                    map[lane] = vmap;
+                    prv[lane] = vprv;
+                    nxt[lane] = vnxt;
+                }
+                if (lane < N) {
+                    own[lane] = vown;
+                    fre[lane] = vfre;
+                }
+                if (lane == 0) {
+                    s_meta[0] = head;
+                    s_meta[1] = tail;
+                    s_meta[2] = nfree;
+                    s_njobs = misses;
+                    if (lead) {
+                        *a.path = PATH_POOL;
+                        rec[0] = PATH_POOL;
+                        rec[1] = D;
+                        rec[2] = misses;
+                        rec[3] = 0;
+                        bump(ctr + 0, 1);
+                        bump(ctr + 1, (unsigned long long)hits);
+                        bump(ctr + 2, (unsigned long long)misses);
+                        bump(ctr + 4, (unsigned long long)misses * a.eb);
+                    }
+                }
+            }
+        } else if (tid == 0) {
             int head = s_meta[0], tail = s_meta[1], nfree = s_meta[2];
             int hits = 0, misses = 0;
             auto unlink = [&](int e) {
