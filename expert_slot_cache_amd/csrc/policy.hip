@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         // 3. the LRU, one id at a time in ascending order.  Miss j's expert is written to
         // list[j] (j <= the id being processed, so nothing unread is overwritten), and a
         // missed expert's rank entry becomes -1 (rank is not needed on this path).
-        if (E <= 64) {
+        if (E <= 64 && N <= 64) {
             // the lists in registers of wave 0: lane e holds expert e's map entry and
             // neighbours, lane s slot s's owner and free-list entry; the wave walks the ids
             // with scalar control flow, reading single lanes (readlane) and writing them

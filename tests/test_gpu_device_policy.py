@@ -31,6 +31,8 @@ def _check_state(rig, lrus):
 @pytest.mark.parametrize("name,slots,steps,layers,rule,tokens", [
     ("tiny_f32_e8", 4, 256, 1, "distinct", 1),
     ("tiny_f32_e8", 1, 64, 1, "distinct", 1),
+    ("tiny_f32_e8", 16, 64, 1, "distinct", 1),        # more slots than experts
+    ("tiny_f32_e8", 80, 64, 1, "distinct", 1),        # ... and more than one wave's lanes
     ("olmoe_bf16_e64", 16, 96, 2, "distinct", 1),
     ("fanout_int4_e512", 32, 48, 2, "distinct", 1),
     ("olmoe_bf16_e64", 16, 40, 1, "distinct", 4),     # 32 pairs, often > 16 distinct: fallbacks
