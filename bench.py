@@ -32,6 +32,7 @@ METRIC = "MoE decode tokens/s vs pool size; HBM GB/s on hits, link GB/s on misse
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (bf16)
+GRAPH_WARM = 3                   # untimed replays after a capture (--graph)
 
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
@@ -76,6 +77,10 @@ def parse():
     ap.add_argument("--read-through", type=int, default=0, choices=[0, 1],
                     help="device policy, one token per step: the forward's kernels read missed experts "
                          "from the pinned store and write them through to their slots (no copy first)")
+    ap.add_argument("--graph", action="store_true",
+                    help="device policy, one token per step: capture one decode token (every layer's "
+                         "step) in a HIP graph and time its replays; the kernel and link figures then "
+                         "come from event-timed eager warm-up steps (a capture cannot hold them)")
     ap.add_argument("--no-timing", action="store_true", help="no HIP events around kernels")
     ap.add_argument("--timing-every", type=int, default=7,
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
@@ -164,7 +169,18 @@ def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
 
 
 def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
-    """One pool, one timed run; returns the result dict and the expert size."""
+    """One pool, one timed run; returns the result dict and the expert size.  With
+    --graph the pool and everything around it run on a side stream, which a capture
+    needs."""
+    if not args.graph:
+        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
+    if args.policy != "device" or resident or wl.tokens != 1 or args.read_through:
+        raise SystemExit("--graph needs the device policy, a pooled stack and one token per step")
+    with torch.cuda.stream(torch.cuda.Stream()):
+        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
+
+
+def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
     dev = torch.device("cuda:0")
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
     t0 = time.perf_counter()
@@ -208,19 +224,68 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
                     binding._check(st)
                 x = out
 
+    g = None
+    if args.graph:
+        # one token's steps, captured on the static input buffers below; a replay reads
+        # the token's ids, gate weights and input copied there first
+        ids_s = torch.empty((L, T, K), dtype=torch.int32, device=dev)
+        w_s = torch.empty((L, T, K), dtype=torch.float32, device=dev)
+        x_s = torch.empty((T, H), dtype=adt, device=dev)
+
+        def record():
+            x = x_s.data_ptr()
+            for l in range(L):
+                out = buf_p[l & 1]
+                st = L_.moe_pool_step(h, l, ids_s.data_ptr() + l * ids_stride, T, slot_p + l * ids_stride,
+                                      x, w_s.data_ptr() + l * ids_stride, x, out, None, 0, None, None)
+                if st:
+                    binding._check(st)
+                x = out
+
+        def replay(s0, n):
+            for s in range(s0, s0 + n):
+                ids_s.copy_(ids_d[s])
+                w_s.copy_(ws_d[s])
+                x_s.copy_(xs_d[s])
+                g.replay()
+
     torch.cuda.synchronize()
-    run(0, args.warmup)
-    pool.sync()
+    if args.graph:
+        # warm-up eagerly; the kernel and link timings come from its second half
+        run(0, args.warmup // 2)
+        pool.sync()
+        pool.reset_timing()
+        run(args.warmup // 2, args.warmup - args.warmup // 2)
+        pool.sync()
+        tm = pool.timing()
+        pool.set_timing(0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+            record()
+        replay(args.warmup, GRAPH_WARM)          # the first replays, untimed
+        pool.sync()
+        s0 = args.warmup + GRAPH_WARM
+    else:
+        run(0, args.warmup)
+        pool.sync()
+        s0 = args.warmup
     st0 = pool.stats()
-    pool.reset_timing()
+    if not args.graph:
+        pool.reset_timing()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    run(args.warmup, args.steps)
+    if args.graph:
+        replay(s0, args.steps)
+    else:
+        run(s0, args.steps)
     pool.sync()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     st1 = pool.stats()
-    tm = pool.timing()
+    if not args.graph:
+        tm = pool.timing()
+    else:
+        g.reset()
     pool.close()
     del ids_d, slot_d, bufs
     d = {k: st1[k] - st0[k] for k in st1}
@@ -229,7 +294,7 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
     log(f"[bench] slots={slots}: {args.steps} steps in {elapsed:.3f} s: {value:.2f} tokens/s; {d}")
 
     # algorithmic work of one w13 / w2 launch, averaged over the timed layer-steps
-    timed = trace[args.warmup:args.warmup + args.steps]
+    timed = trace[s0:s0 + args.steps]
     flat = timed.reshape(-1, T * K)
     D_mean = float(np.mean([len(np.unique(r)) for r in flat]))
     wbytes = {"f32": 4.0, "bf16": 2.0, "int4": 0.5}[wl.wtype]
@@ -278,6 +343,8 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
             roof["hbm_gbps"] = round(ach, 1)
         if roof["bound"] == "hbm":
             roof["read_ceiling"] = read_ceiling(torch, dev, binding, int(w13_bytes), ach)
+        if args.graph:
+            roof["measured_in"] = "event-timed eager warm-up steps before the graph replays"
         res["roofline"] = roof
         res["hbm_gbps_hits"] = round((w13_bytes + w2_bytes) / ((w13_us + w2_us) * 1e-6) / 1e9, 1)
     torch.cuda.empty_cache()
@@ -309,7 +376,7 @@ def main():
         slots = wl.slots if wl.slots in points else points[0]
     wl = wl.with_(slots=slots)
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
-    S = args.warmup + args.steps
+    S = args.warmup + args.steps + (GRAPH_WARM if args.graph else 0)
     log(f"[bench] workload {wl.name}: L={L} E={E} K={K} H={H} I={I} slots={slots} T={T} "
         f"steps={S} rule={args.rule} resident={args.resident}")
 
@@ -342,7 +409,8 @@ def main():
                    "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
                    "resident": args.resident, "copy_streams": args.copy_streams,
                    "copy_engine": args.copy_engine, "policy": args.policy,
-                   "read_through": bool(args.read_through) and args.policy == "device" and not args.resident},
+                   "read_through": bool(args.read_through) and args.policy == "device" and not args.resident,
+                   "graph": bool(args.graph)},
     }
     for k, v in main_res.items():
         if k not in ("value", "ms_per_step", "slots", "roofline"):

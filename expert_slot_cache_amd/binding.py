@@ -96,6 +96,7 @@ _SIGS = {
     "moe_ptr_is_pinned_host": (_I32, [_P, _PI32]),
     "moe_pool_get_timing": (_I32, [_P, C.POINTER(Timing)]),
     "moe_pool_reset_timing": (_I32, [_P]),
+    "moe_pool_set_timing": (_I32, [_P, _I32]),
     "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
     "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _P, C.POINTER(C.c_double)]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
@@ -303,6 +304,10 @@ class MoePool:
 
     def reset_timing(self):
         _check(lib().moe_pool_reset_timing(self._h))
+
+    def set_timing(self, every: int):
+        """Event-timing period from now on (0 = off, e.g. before a graph capture)."""
+        _check(lib().moe_pool_set_timing(self._h, int(every)))
 
 
 def read_calibration(buf, bytes_per_launch: int, reps: int = 20, stream=None) -> float:

@@ -157,6 +157,7 @@ struct moe_pool {
     Layout lay;
     moe::Geom geom{};
     int32_t nslot_alloc = 0;
+    int32_t timing_alloc = 0;     // config.timing at create: > 0 if the timing events exist
     hipStream_t compute = nullptr;
     std::vector<hipStream_t> copy;
     std::vector<hipEvent_t> copy_done;
@@ -786,6 +787,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     moe_pool* p = new (std::nothrow) moe_pool();
     if (!p) FAIL(MOE_ENOMEM, "host allocation failed");
     p->cfg = c;
+    p->timing_alloc = c.timing;
     p->lay = lay;
     p->compute = static_cast<hipStream_t>(stream);
     p->geom.H = c.hidden;
@@ -1267,6 +1269,17 @@ moe_status_t moe_pool_get_timing(moe_pool_t* p, moe_pool_timing_t* out) {
     out->w2_ms = p->w2_ms;
     out->kernel_calls = p->kern_calls;
     out->sync_wait_ms = p->sync_ms;
+    return MOE_OK;
+}
+
+moe_status_t moe_pool_set_timing(moe_pool_t* p, int32_t every) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    if (every < 0) FAIL(MOE_EINVAL, "timing period %d < 0", every);
+    if (every > 0 && p->timing_alloc <= 0) FAIL(MOE_EINVAL, "the pool was created without timing events");
+    moe_status_t st = moe_pool_sync(p);
+    if (st) return st;
+    harvest_all(p);   // under the old period: nothing stays pending
+    p->cfg.timing = every;
     return MOE_OK;
 }
 

@@ -298,6 +298,12 @@ moe_status_t moe_ptr_is_pinned_host(const void* p, int32_t* is_pinned);
 /* Accumulated event timings (config.timing = 1); waits for queued work first. */
 moe_status_t moe_pool_get_timing(moe_pool_t* pool, moe_pool_timing_t* out);
 moe_status_t moe_pool_reset_timing(moe_pool_t* pool);
+/* The event-timing period from now on (config.timing's meaning).  0 stops the sampling,
+ * so that the pool's steps can be captured in a HIP graph (a capture cannot hold the
+ * timed launches); every >= 1 needs a pool created with timing >= 1, which owns the
+ * events.  Waits for queued work and keeps what was accumulated.
+ * Errors: EINVAL (every < 0, or >= 1 on a pool created without timing), EHIP. */
+moe_status_t moe_pool_set_timing(moe_pool_t* pool, int32_t every);
 
 /* ---- calibration (benchmarks) ----------------------------------------------- */
 /* What one kernel launch of `bytes` can read on this GPU: a plain streaming read
