@@ -56,6 +56,12 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     const int wave = tid >> 6;
     const int nwords = (E + 31) >> 5;
     const bool lead = blockIdx.x == 0;
+    // The arguments span four 64-byte lines of the scalar cache and the grid size (a
+    // hidden argument) a fifth: one field of each is read here, so that all lines are
+    // requested together instead of one miss at a time where each field is first used
+    // (the state pointers, for one, are needed right after the ids).
+    const int nblocks = (int)gridDim.x;
+    __asm__ volatile("" ::"s"(nblocks), "s"(a.st.map), "s"(a.st.meta), "s"(a.err), "s"(a.tab));
     unsigned long long* ctr = a.ctr;   // steps, hits, misses, fallbacks, bytes_h2d, staged
     int32_t* rec = a.rec;
     // counter updates are additions nothing in the launch reads back: atomics without a
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
         // every expert lives at slot = id: count the hits, the ids are the slots
         // (nothing to copy; the ids are spread over the launch's workgroups)
         const int gtid = blockIdx.x * kPolicyThreads + tid;
-        const int gthreads = gridDim.x * kPolicyThreads;
+        const int gthreads = nblocks * kPolicyThreads;
         for (int i = gtid; i < a.n; i += gthreads) a.out[i] = s_bad ? -1 : id_at(i);
         if (lead && tid == 0) {
             *a.path = s_bad ? PATH_NONE : PATH_POOL;
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     // every workgroup holds the decision, so the per-id outputs are spread over all
     // of them (each id is written by exactly one thread of the launch)
     const int gtid = blockIdx.x * kPolicyThreads + tid;
-    const int gthreads = gridDim.x * kPolicyThreads;
+    const int gthreads = nblocks * kPolicyThreads;
     if (s_bad) {
         // an id outside [0, E): nothing changes, the step produces no expert
         for (int i = gtid; i < a.n; i += gthreads) {
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     // once every other workgroup has its copy; the arrival word goes back to 0
     if (lead) {
         if (tid == 0) {
-            const int others = (int)gridDim.x - 1;
+            const int others = nblocks - 1;
             unsigned long long polls = 0;
             while (__hip_atomic_load(a.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < others) {
                 if (++polls > a.spin_limit) {
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
     // 5. the copies: 64 KiB work units over the launch, store -> slot / staging
     const size_t upj = (eb + kFillUnit - 1) / kFillUnit;
     const size_t units = upj * (size_t)njobs;
-    for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
+    for (size_t u = blockIdx.x; u < units; u += (size_t)nblocks) {
         const int j = (int)(u / upj);
         const int e = list[j];
         const size_t off = (u - (size_t)j * upj) * kFillUnit;
