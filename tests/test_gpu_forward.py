@@ -346,3 +346,25 @@ def test_slot_ids_outside_the_range_contribute_nothing(wtype, atype, T):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     check_close(got, rig.reference(0, x, ids, w0), atype, wtype, "outside slots skipped")
     rig.close()
+
+
+@pytest.mark.parametrize("wtype,atype", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("T", [1, 3])
+def test_gemv_ragged_row_blocks(wtype, atype, T):
+    """H = 80, I = 48: the w13 GEMV's row block (128 rows for bf16 weights, 64 for fp32)
+    is larger than I, and for bf16 weights the w2 kernel's last workgroup holds 16 of its
+    32 rows; the rows past the end are computed from clamped reads and dropped.  Oracle
+    within tolerance and pooled = all-resident bit for bit, through evictions."""
+    wl = synth.Workload("ragged", 1, 12, 3, 80, 48, 6, T, 0, wtype, atype, 1.0, 0.0, 0, 19)
+    rng = np.random.default_rng(29)
+    seq = [np.stack([rng.permutation(12)[:3] for _ in range(T)]) for _ in range(6)]
+    trace = np.stack(seq)[:, None].astype(np.int32)
+    xs, ws = _inputs(wl, len(seq), T)
+    pooled = Rig(wl, slots=6, fast=False, std=0.05)
+    resident = Rig(wl, slots=6, resident=True, experts=pooled.experts)
+    out_p = _run(pooled, trace, xs, ws)
+    out_r = _run(resident, trace, xs, ws)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    assert pooled.pool.stats()["misses"] > 0
+    pooled.close()
+    resident.close()
