@@ -368,3 +368,25 @@ def test_gemv_ragged_row_blocks(wtype, atype, T):
     assert pooled.pool.stats()["misses"] > 0
     pooled.close()
     resident.close()
+
+
+@pytest.mark.parametrize("wtype,K,T", [("bf16", 20, 1), ("bf16", 64, 1), ("int4", 20, 1), ("f32", 24, 3),
+                                       ("bf16", 20, 12)])
+def test_large_top_k(wtype, K, T):
+    """top_k above 16 gives the w2 kernel more (expert, part) tasks than waves, so it
+    takes its looping form; at T = 12 (bf16) the grouped path's combine sums the k terms
+    over several chunks of 8, the last one partial; 64 is the largest top_k accepted.
+    Oracle within tolerance and pooled = all-resident bit for bit."""
+    atype = "f32" if wtype == "f32" else "bf16"
+    wl = synth.Workload("bigk", 1, 64, K, 256, 128, 64, T, 0, wtype, atype, 1.0, 0.0, 0, 31)
+    rng = np.random.default_rng(37)
+    seq = [np.stack([rng.permutation(64)[:K] for _ in range(T)]) for _ in range(3)]
+    trace = np.stack(seq)[:, None].astype(np.int32)
+    xs, ws = _inputs(wl, len(seq), T)
+    pooled = Rig(wl, slots=64, fast=False, std=0.05)
+    resident = Rig(wl, slots=64, resident=True, experts=pooled.experts)
+    out_p = _run(pooled, trace, xs, ws)
+    out_r = _run(resident, trace, xs, ws)
+    _assert_bitwise(out_p, out_r, "pooled vs resident")
+    pooled.close()
+    resident.close()
