@@ -38,9 +38,16 @@ def _check_state(rig, lrus):
     ("olmoe_bf16_e64", 16, 40, 1, "distinct", 4),     # 32 pairs, often > 16 distinct: fallbacks
     ("olmoe_bf16_e64", 24, 40, 1, "static", 3),       # 24 pairs: pooled; 4 tokens would fall back
     ("olmoe_bf16_e64", 0, 8, 1, "distinct", 1),       # no pool: every step stages
+    # 2048 experts, the device policy's limit (its state lives in LDS): state loads and
+    # write-back past the first 512 experts, more than 256 slots, the LDS walk
+    pytest.param(synth.Workload("dev2048", 1, 2048, 8, 64, 32, 300, 1, 64, "f32", "f32", 1.1, 0.0, 0, 47),
+                 300, 64, 1, "distinct", 1, id="e2048-n300"),
+    pytest.param(synth.Workload("dev2048t", 1, 2048, 8, 64, 32, 100, 8, 24, "f32", "f32", 1.1, 0.0, 0, 48),
+                 100, 24, 1, "distinct", 8, id="e2048-n100-t8"),
 ])
 def test_device_policy_matches_oracle(name, slots, steps, layers, rule, tokens):
-    wl = synth.WORKLOADS[name].with_(layers=layers, tokens=tokens)
+    base = synth.WORKLOADS[name] if isinstance(name, str) else name
+    wl = base.with_(layers=layers, tokens=tokens)
     trace = synth.make_trace(wl, steps=steps)
     eb = synth.expert_bytes(wl.wtype, wl.hidden, wl.inter)
     zero = np.zeros(eb, np.uint8)          # the policy never reads expert bytes
