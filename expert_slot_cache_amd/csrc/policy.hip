@@ -339,6 +339,39 @@ __global__ __launch_bounds__(kPolicyThreads) void k_policy(PolicyArgs a) {
                     if (tail >= 0) put(vnxt, tail, e); else head = e;
                     tail = e;
                 };
+                // A step whose ids all hit (most decode steps): its experts leave the list
+                // and rejoin at the tail in ascending order, the others keep their order --
+                // what the walk below ends with, computed by all lanes at once.  Each lane
+                // finds its nearest neighbours outside the step by pointer doubling (a list
+                // of at most 64 needs 6 rounds; the bound keeps a damaged state from looping).
+                const bool mine = lane < E && ((todo >> lane) & 1ull);
+                if (todo && !__ballot(mine && vmap < 0)) {
+                    const uint64_t S = todo;
+                    auto in_step = [S](int x) { return x >= 0 && ((S >> x) & 1ull) != 0; };
+                    int jp = vprv, jn = vnxt;
+                    for (int r = 0; r < 7 && __ballot(in_step(jp) || in_step(jn)); ++r) {
+                        const int pp = __shfl(jp, jp < 0 ? lane : jp, 64);
+                        const int nn = __shfl(jn, jn < 0 ? lane : jn, 64);
+                        if (in_step(jp)) jp = pp;
+                        if (in_step(jn)) jn = nn;
+                    }
+                    const int s_min = (int)__builtin_ctzll(S), s_max = 63 - (int)__builtin_clzll(S);
+                    const int r_tail = in_step(tail) ? get(jp, tail) : tail;   // last one staying
+                    const int r_head = in_step(head) ? get(jn, head) : head;   // first one staying
+                    if (mine) {
+                        const uint64_t below = S & ((1ull << lane) - 1ull);
+                        const uint64_t above = lane < 63 ? S >> (lane + 1) : 0ull;
+                        vprv = lane == s_min ? r_tail : 63 - (int)__builtin_clzll(below);
+                        vnxt = above ? lane + 1 + (int)__builtin_ctzll(above) : -1;
+                    } else if (vmap >= 0) {
+                        vprv = jp;
+                        vnxt = jn >= 0 ? jn : s_min;
+                    }
+                    head = r_head >= 0 ? r_head : s_min;
+                    tail = s_max;
+                    hits = __popcll(S);
+                    todo = 0ull;
+                }
                 while (todo) {
                     const int e = (int)__builtin_ctzll(todo);
                     todo &= todo - 1ull;
