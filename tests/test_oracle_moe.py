@@ -171,3 +171,69 @@ def test_tolerance_metric():
     assert moe.max_rel_err(ref + np.array([0, 0.04, 0]), ref) == pytest.approx(0.01)
     assert moe.tolerance("f32", "f32") == 1e-5
     assert moe.tolerance("bf16", "int4") == 2e-2
+
+
+# ---------------------------------------------------------------------------
+# expert_matrices, bf16 and INT4 branches, wired region by region: H != I and
+# H != 2I, so a transposed or reshaped W2 and a swapped region cannot pass.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,I", [(24, 16), (40, 8), (8, 24)])
+def test_bf16_expert_matrices_equal_torch_rounding(H, I):
+    """Each matrix equals torch's own bf16 rounding of the fp32 matrix it was
+    packed from, element by element (torch's conversion is independent of the
+    generator's bit twiddling)."""
+    rng = np.random.default_rng(H * 100 + I)
+    W13 = rng.standard_normal((2 * I, H)).astype(np.float32)
+    W2 = (rng.standard_normal((H, I)) * 7.0).astype(np.float32)   # another scale: a swap shows
+    buf = synth.pack_expert("bf16", H, I, W13, W2)
+    A13, A2 = moe.expert_matrices(buf, "bf16", H, I)
+    r13 = torch.from_numpy(W13).to(torch.bfloat16).double().numpy()
+    r2 = torch.from_numpy(W2).to(torch.bfloat16).double().numpy()
+    assert A13.shape == (2 * I, H) and A2.shape == (H, I)
+    np.testing.assert_array_equal(A13, r13)
+    np.testing.assert_array_equal(A2, r2)
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (128, 384), (384, 256)])
+def test_int4_expert_matrices_within_half_a_step_of_their_own_group(H, I):
+    """|W_hat - W| <= s/2 element by element, where s is the scale torch computes
+    for that element's own row and 128-group (bf16 of max|w|/7; values chosen
+    inside [-7s, 7s] so that no code clips).  W13 and W2 are drawn at scales 1000
+    apart, so s13 and s2 differ and a swapped scale region fails."""
+    rng = np.random.default_rng(H + 7 * I)
+    W13 = rng.standard_normal((2 * I, H)).astype(np.float32)
+    W2 = (rng.standard_normal((H, I)) * 1e-3).astype(np.float32)
+    buf = synth.pack_expert("int4", H, I, W13, W2)
+    A13, A2 = moe.expert_matrices(buf, "int4", H, I)
+    assert A13.shape == (2 * I, H) and A2.shape == (H, I)
+    for A, W in ((A13, W13), (A2, W2)):
+        rows, cols = W.shape
+        g = torch.from_numpy(W).reshape(rows, cols // 128, 128).abs().amax(dim=2)
+        s = (g / 7.0).to(torch.bfloat16).double().numpy()         # [rows, groups]
+        s_el = np.repeat(s, 128, axis=1)
+        err = np.abs(A - W.astype(np.float64))
+        # exact halves can round either way in the quantiser: allow s/2 plus rounding
+        assert (err <= s_el * (0.5 + 1e-6) + 2.0 ** -30).all()
+        # and the decoded values sit on the grid (q - 8) * s of their own group
+        q = A / s_el
+        np.testing.assert_allclose(q, np.rint(q), atol=1e-9)
+        assert (np.rint(q) >= -8).all() and (np.rint(q) <= 7).all()
+
+
+def test_int4_swapped_scale_regions_would_fail():
+    """Guard for the test above: decoding with the scale regions exchanged (done
+    here by hand on the raw bytes) is far outside the half-step bound."""
+    H, I = 256, 128
+    rng = np.random.default_rng(5)
+    W13 = rng.standard_normal((2 * I, H)).astype(np.float32)
+    W2 = (rng.standard_normal((H, I)) * 1e-3).astype(np.float32)
+    buf = synth.pack_expert("int4", H, I, W13, W2)
+    lay = moe.layout("int4", H, I)
+    o13, n13 = lay["s13"]
+    o2, n2 = lay["s2"]
+    n = min(n13, n2)      # exchange the leading scales of the two regions
+    bad = buf.copy()
+    bad[o13:o13 + n] = buf[o2:o2 + n]
+    bad[o2:o2 + n] = buf[o13:o13 + n]
+    B13, _ = moe.expert_matrices(bad, "int4", H, I)
+    assert np.abs(B13 - W13).max() > 0.5
