@@ -29,6 +29,8 @@ RULES = {"distinct": RULE_DISTINCT, "static": RULE_STATIC}
 COPY_ENGINES = {"dma": COPY_DMA, "kernel": COPY_KERNEL}
 POLICY_HOST, POLICY_DEVICE = 0, 1
 POLICIES = {"host": POLICY_HOST, "device": POLICY_DEVICE}
+EVICT_LRU, EVICT_FIFO, EVICT_LFU, EVICT_SLRU = 0, 1, 2, 3
+EVICTS = {"lru": EVICT_LRU, "fifo": EVICT_FIFO, "lfu": EVICT_LFU, "slru": EVICT_SLRU}
 
 
 class MoeError(RuntimeError):
@@ -52,7 +54,7 @@ class Config(C.Structure):
                 ("resident", C.c_int32), ("max_tokens", C.c_int32), ("n_copy_streams", C.c_int32),
                 ("copy_chunk_bytes", C.c_size_t), ("hbm_budget_bytes", C.c_size_t),
                 ("timing", C.c_int32), ("copy_engine", C.c_int32), ("policy", C.c_int32),
-                ("read_through", C.c_int32)]
+                ("read_through", C.c_int32), ("evict", C.c_int32)]
 
 
 class Miss(C.Structure):
@@ -167,12 +169,12 @@ class MoePool:
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
                  copy_engine: str = "kernel", policy: str = "host", read_through: bool = False,
-                 stream=None):
+                 evict: str = "lru", stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
                      copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine],
-                     POLICIES[policy], int(bool(read_through)))
+                     POLICIES[policy], int(bool(read_through)), EVICTS[evict])
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -184,6 +186,7 @@ class MoePool:
         self.hidden, self.inter, self.slots = hidden, inter, slots
         self.wtype, self.atype, self.resident = wtype, atype, resident
         self.policy = policy
+        self.evict = evict
         self.read_through = bool(read_through)
         self.max_tokens = max_tokens
         self.expert_nbytes = expert_bytes(wtype, hidden, inter)

@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "kernels.hpp"
+#include "policy_dev.hpp"
 
 namespace moe {
 
@@ -262,12 +263,14 @@ struct SlotWriter {
     }
 };
 
-// The pair's source override (null pointers when the forward reads slots only).
-__device__ __forceinline__ PairSrc pair_src(const Slots& sl, int pair) {
-    PairSrc ps{nullptr, nullptr};
-    if (sl.src) ps = sl.src[pair];
-    return ps;
-}
+// Where one (token, expert) pair reads its expert: a slot or staging entry, or (a
+// read-through step) the expert in the device-mapped pinned store, which a missed
+// expert's lanes also write through to its slot (`to`).
+struct PairIn {
+    const char* ebase;
+    char* to;
+    bool valid;     // the pair has an expert (else it contributes zeros)
+};
 
 // Activation-sized reads of a buffer, by byte offset (data written by an earlier
 // kernel).
@@ -491,18 +494,12 @@ __device__ __forceinline__ void store_act(void* __restrict__ p, size_t i, float 
 // G = 1 << gs lanes share a row.  The slot id and the path word are read first, side by
 // side: they are the only loads the weight addresses depend on.
 template <int WT, int AT, int CPL, int RP, int WPR>
-__device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const int32_t* __restrict__ slot_ids,
-                                         const void* __restrict__ x, int H, int I, int gs, size_t off_w,
-                                         size_t off_s, void* __restrict__ act, int t, int pair, int rblk,
-                                         float (*red)[2][RP], char* xs) {
+__device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const void* __restrict__ x, int H, int I,
+                                         int gs, size_t off_w, size_t off_s, void* __restrict__ act, int t, int pair,
+                                         int rblk, float (*red)[2][RP], char* xs, bool xr_ready = false) {
     using X = XChunk<WT, XSel<WT, AT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
-    const int slot = slot_ids[pair];
-    const PairSrc ps = pair_src(sl, pair);
-    const char* wbase;
-    int nslots;
-    pick_slots(sl, wbase, nslots);
     const int G = 1 << gs;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -512,12 +509,12 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     const int part = wave % WPR;
     const int i0 = ((rblk * (4 / WPR) + wave / WPR) * groups + grp) * RP;
     // lane groups past the last row skip their loads; no early return, which would
-    // let the compiler sink the slot and path loads below it
-    const bool ok = slot >= 0 && slot < nslots && i0 < I;
+    // let the compiler sink the pair's loads below it
+    const bool ok = pin.valid && i0 < I;
     const int nc = CPL * G * WPR;
     const size_t row_bytes = (size_t)nc * 16;
     // INT4: this thread's activation chunk is requested before anything that depends on
-    // the slot.  Loads complete in the order they are issued, so the repacking below
+    // the expert.  Loads complete in the order they are issued, so the repacking below
     // waits for these loads only, not for the weights issued after them.
     using XI4 = XChunk<W_INT4, XT_I4>;
     [[maybe_unused]] XI4::Raw xr;
@@ -527,7 +524,7 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
     __builtin_amdgcn_sched_barrier(0);
     // the expert's address in scalar registers before the branch, so that the
     // arguments it needs are loaded with the others (one round trip, not two)
-    const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
+    const char* ebase = pin.ebase;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
 
     float pg[RP], pu[RP];
@@ -538,8 +535,7 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
         // whose loads return zeros without touching memory.  The activation vector is then
         // repacked once per workgroup into LDS (xs) while the weights are in flight, and
         // each lane reads its chunks from there.
-        const bool sok = slot >= 0 && slot < nslots;
-        const SlotReader rd(sok ? ebase : wbase, sok ? stride : 0);
+        const SlotReader rd(ebase, pin.valid ? stride : 0);
         uint4 wg[RP][CPL], wu[RP][CPL];
         uint16_t sg[RP][CPL], su[RP][CPL];
         const int spr = H / 128;
@@ -577,9 +573,9 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
             xc.store_packed(xs + c * kPackedChunkBytes);
         }
         __syncthreads();
-        if (ps.to && ok) {
+        if (pin.to && ok) {
             // a miss read from the store: the lane writes what it read to the slot
-            const SlotWriter wr(ps.to, stride);
+            const SlotWriter wr(pin.to, stride);
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
                 const int i = min(i0 + p, I - 1);
@@ -660,9 +656,9 @@ __device__ __forceinline__ void w13_rows(const Slots& sl, size_t stride, const i
             // every load of the lane is in flight before the first use: the scheduler
             // would otherwise hold some back to save registers (two round trips)
             __builtin_amdgcn_sched_barrier(0);
-            if (ps.to) {
+            if (pin.to) {
                 // a miss read from the store: the lane writes what it read to the slot
-                const SlotWriter wr(ps.to, stride);
+                const SlotWriter wr(pin.to, stride);
 #pragma unroll
                 for (int p = 0; p < RP; ++p) {
                     const int i = min(i0 + p, I - 1);
@@ -758,8 +754,132 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
                                                   size_t off_w, size_t off_s, void* __restrict__ act) {
     __shared__ float red[4][2][RP];
     extern __shared__ __attribute__((aligned(16))) char xs_packed[];   // INT4: the packed activations
-    w13_rows<WT, AT, CPL, RP, WPR>(sl, stride, slot_ids, x, H, I, gs, off_w, off_s, act, blockIdx.z,
-                                   blockIdx.z * gridDim.y + blockIdx.y, blockIdx.x, red, xs_packed);
+    // the slot id and the path word, side by side before any branch: they are the only
+    // loads the weight addresses depend on
+    const int pair = blockIdx.z * gridDim.y + blockIdx.y;
+    const int slot = slot_ids[pair];
+    const char* wbase;
+    int nslots;
+    pick_slots(sl, wbase, nslots);
+    const bool valid = slot >= 0 && slot < nslots;
+    const PairIn pin{valid ? wbase + (size_t)slot * stride : wbase, nullptr, valid};
+    w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, blockIdx.z, pair, blockIdx.x, red,
+                                   xs_packed);
+}
+
+// ---- the fused one-token decode step: decision + w13 + tail copies ----------------------
+// Workgroup roles by index: 0 = the lead (the decision, the state after the step, the
+// counters, the step's slot ids and path word); 1 .. n_copy = copy workers (the part
+// of each missed or staged expert from its w2 region on: store -> slot or staging);
+// the rest = the w13 GEMV blocks (row block, k).  Every workgroup first reads the
+// step's ids and their entries in the current map: when each id is valid and
+// resident (and the static rule does not fire) every id hits, the map stays as it is
+// and the GEMV blocks start at once from it; otherwise every workgroup runs the
+// decision on its own LDS copy of the state.  A missed expert's w13 rows are read
+// from the pinned store and written through to its slot by the GEMV blocks that use
+// them; a staged expert's are read from the store.  No workgroup waits for another.
+template <int WT, int AT, int CPL, int RP, int WPR>
+__global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, const void* __restrict__ x, int H,
+                                                  int I, int gs, size_t off_w, size_t off_s, size_t tail_off,
+                                                  void* __restrict__ act, int n_copy, int nrb, int xs_off) {
+    extern __shared__ __attribute__((aligned(16))) char dyn[];
+    __shared__ float red[4][2][RP];
+    const int b = blockIdx.x;
+    const int K = pa.n;                    // one token: n == top_k
+    const int tid = threadIdx.x;
+    const int E = pa.E, N = pa.N;
+    const int par = pa.ds.ctl[0] & 1;
+    char* cur_base = pa.ds.copy[par];
+    const bool lead = b == 0;
+    const int g = b - 1 - n_copy;              // GEMV block index (when >= 0)
+    const int k = g >= 0 ? g / nrb : 0;
+    const int rblk = g - k * nrb;
+    // The step's ids and their entries in the current map, through the scalar cache
+    // (uniform addresses; the current copy is only read during this launch): eight ids
+    // per round, every load of a round issued before the first is used.
+    typedef const __attribute__((address_space(4))) int32_t cint4;
+    cint4* ids4 = (cint4*)pa.ids;
+    cint4* map4 = (cint4*)(cur_base + slot_state_layout(E, N).map);
+    int bad = 0, myslot = -1;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int idv[8], mv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) idv[q] = ids4[min(k0 + q, K - 1)];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const bool ok = (unsigned)idv[q] < (unsigned)E;
+            bad |= !ok;
+            mv[q] = pa.resident ? idv[q] : map4[ok ? idv[q] : 0];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            bad |= mv[q] < 0;
+            myslot = k0 + q == k ? mv[q] : myslot;
+        }
+    }
+    const bool fast = !bad && (pa.resident || pa.rule == 0 || K <= N);
+    const PolLds L = pol_lds(reinterpret_cast<int32_t*>(dyn), E, N);
+    Decision d{};
+    if (lead || !fast) d = pol_decide(pa, slot_view(cur_base, E, N), L);
+    // (the w2 launch that follows makes the lead's copy current: every read of the
+    // current copy is in this launch)
+    if (lead) {
+        pol_publish(pa, slot_view(pa.ds.copy[par ^ 1], E, N), L, d);
+        if (tid < K) {
+            const int id = pa.ids[tid];
+            int v = -1;
+            if (d.path == PATH_POOL) v = pa.resident ? id : L.map[id];
+            else if (d.path == PATH_STAGE) v = L.rank[id];
+            pa.out[tid] = v;
+        }
+        return;
+    }
+    if (b <= n_copy) {
+        if (fast || pa.resident || d.path == PATH_NONE) return;
+        const bool pool = d.path == PATH_POOL;
+        const int njobs = pool ? d.nmiss : d.D;
+        const size_t eb = pa.eb;
+        constexpr size_t kUnit = (size_t)64 << 10;
+        const size_t upj = (eb - tail_off + kUnit - 1) / kUnit;
+        const size_t units = upj * (size_t)njobs;
+        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+        for (size_t u = (size_t)(b - 1); u < units; u += (size_t)n_copy) {
+            const int j = (int)(u / upj);
+            const int e = L.list[j];
+            const size_t off = tail_off + (u - (size_t)j * upj) * kUnit;
+            const size_t nvec = (eb - off < kUnit ? eb - off : kUnit) / 16;
+            const u32x4c* __restrict__ s4 = reinterpret_cast<const u32x4c*>(pol_store_at(pa, e) + off);
+            u32x4c* __restrict__ d4 =
+                reinterpret_cast<u32x4c*>((pool ? pa.slots + (size_t)L.map[e] * eb : pa.staging + (size_t)j * eb) + off);
+            for (size_t i0 = tid; i0 < nvec; i0 += 4 * 256) {
+                u32x4c v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const size_t i = i0 + (size_t)q * 256;
+                    if (i < nvec) v[q] = s4[i];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const size_t i = i0 + (size_t)q * 256;
+                    if (i < nvec) __builtin_nontemporal_store(v[q], d4 + i);
+                }
+            }
+        }
+        return;
+    }
+    const int e = ids4[k];
+    PairIn pin{pa.slots, nullptr, false};
+    if (fast) {
+        pin = PairIn{pa.slots + (size_t)myslot * stride, nullptr, true};
+    } else if (d.path == PATH_POOL) {
+        const int slot = __builtin_amdgcn_readfirstlane(pa.resident ? e : L.map[e]);
+        const bool miss = !pa.resident && __builtin_amdgcn_readfirstlane(L.rank[e]) < 0;
+        pin = miss ? PairIn{pol_store_at(pa, e), pa.slots + (size_t)slot * stride, true}
+                   : PairIn{pa.slots + (size_t)slot * stride, nullptr, true};
+    } else if (d.path == PATH_STAGE) {
+        pin = PairIn{pol_store_at(pa, e), nullptr, true};
+    }
+    w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, 0, k, rblk, red, dyn + xs_off);
 }
 
 // ---- w2 + ordered top-k combine ------------------------------------------------
@@ -778,7 +898,6 @@ struct W2Task {
     int pair;            // t * K + k
     int part;
     bool ok;             // the pair's slot id is valid
-    char* to;            // write-through slot of an expert read from the store, or null
 };
 
 // Lane geometry of a w2 workgroup.
@@ -803,15 +922,14 @@ __device__ __forceinline__ W2Lane w2_lane(int gs, int RP, int rb0) {
 // can be waited for alone.
 template <int WT, int CPL, int RP, int WPR>
 __device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wbase, int nslots, size_t stride,
-                                         int slot, const PairSrc& ps, int t, int K, int H, int I, int gs,
+                                         int slot, int t, int K, int H, int I, int gs,
                                          const W2Lane& ln, int task, size_t off_w, size_t off_s) {
     const int G = 1 << gs;
     const int k = task / WPR;
     tk.part = task - k * WPR;
     tk.pair = t * K + k;
     tk.ok = slot >= 0 && slot < nslots;
-    tk.to = ps.to;
-    const char* ebase = ps.from ? ps.from : wbase + (size_t)slot * stride;
+    const char* ebase = wbase + (size_t)slot * stride;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
     if (WT != W_INT4 && !tk.ok) return;
     const size_t row_bytes = (size_t)CPL * G * WPR * 16;
@@ -858,23 +976,6 @@ __device__ __forceinline__ void w2_finish(const W2Task<WT, CPL, RP>& tk, const M
             av[j].template load<ACT>(m, (size_t)tk.pair * I + (size_t)((tk.part * CPL + j) * G + ln.gl) * EPC);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (tk.to) {
-        // a miss read from the store: the lane writes what it read to the slot
-        const SlotWriter wr(tk.to, stride);
-        const size_t row_bytes = (size_t)CPL * G * WPR * 16;
-        const int spr = I / 128;
-#pragma unroll
-        for (int p = 0; p < RP; ++p) {
-            const int r = min(ln.r0 + p, H - 1);
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = (tk.part * CPL + j) * G + ln.gl;
-                wr.store16(off_w + (size_t)r * row_bytes + (size_t)c * 16, tk.w[p][j]);
-                if (WT == W_INT4 && (c & 3) == 0)
-                    wr.store_scale_bits(off_s + ((size_t)r * spr + (c >> 2)) * 2, tk.sc[p][j]);
-            }
-        }
-    }
     float acc[RP];
 #pragma unroll
     for (int p = 0; p < RP; ++p) acc[p] = 0.0f;
@@ -929,8 +1030,11 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
                                                            const float* __restrict__ topk_w,
                                                            const void* __restrict__ act,
                                                            const void* __restrict__ resid, void* __restrict__ out,
-                                                           int K, int H, int I, int gs, size_t off_w, size_t off_s) {
+                                                           int K, int H, int I, int gs, size_t off_w, size_t off_s,
+                                                           int32_t* __restrict__ flip) {
     extern __shared__ float ys[];               // [K][WPR][RB]
+    // after a fused step: the decision's state copy becomes current (nothing here reads it)
+    if (flip && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *flip ^= 1;
     const int nw = blockDim.x >> 6;
     const int wave = wave_id();
     const int t = blockIdx.y;
@@ -941,7 +1045,6 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
     if (ONE) {
         // the wave's slot and the path word, side by side, before any branch
         const int slot = slot_ids[t * K + wave / WPR];
-        const PairSrc ps = pair_src(sl, t * K + wave / WPR);
         pick_slots(sl, wbase, nslots);
         // INT4: the token's K act vectors are repacked once per workgroup (each lane
         // would otherwise repack every chunk it uses).  A thread's first chunk is
@@ -954,7 +1057,7 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
             xr = XI4::fetch(PlainMem(act), e0 + (size_t)min((int)threadIdx.x, nxc - 1) * 32);
         __builtin_amdgcn_sched_barrier(0);
         W2Task<WT, CPL, RP> tk;
-        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, ps, t, K, H, I, gs, ln, wave, off_w, off_s);
+        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, t, K, H, I, gs, ln, wave, off_w, off_s);
         if constexpr (WT == W_INT4) {
             __builtin_amdgcn_sched_barrier(0);
             char* xs = reinterpret_cast<char*>(ys) + ((K * WPR * ln.RB * 4 + 15) & ~15);
@@ -979,8 +1082,8 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
         pick_slots(sl, wbase, nslots);
         for (int task = wave; task < K * WPR; task += nw) {
             W2Task<WT, CPL, RP> tk;
-            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR],
-                                       pair_src(sl, t * K + task / WPR), t, K, H, I, gs, ln, task, off_w, off_s);
+            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR], t, K, H, I, gs, ln,
+                                       task, off_w, off_s);
             w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
                                         ys + (size_t)task * ln.RB + ln.grp * RP);
         }
@@ -1481,10 +1584,10 @@ hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEven
         if (ev && ev->w2_start)
             hipExtLaunchKernelGGL(kern, grid, dim3(64 * nw), (uint32_t)lds, s, ev->w2_start, ev->w2_stop, 0, a.sl,
                                   g.slot_stride, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I,
-                                  log2_of(G), g.off_w2, g.off_s2);
+                                  log2_of(G), g.off_w2, g.off_s2, a.flip_par);
         else
             hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, s, a.sl, g.slot_stride, a.slot_ids, a.topk_w, a.act,
-                               a.resid, a.out, g.K, g.H, g.I, log2_of(G), g.off_w2, g.off_s2);
+                               a.resid, a.out, g.K, g.H, g.I, log2_of(G), g.off_w2, g.off_s2, a.flip_par);
     };
     if (tasks <= NWMAX)
         go(k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX, true>);
@@ -1548,6 +1651,51 @@ hipError_t run_decode(const Geom& g, const ForwardArgs& a, const StageEvents* ev
     hipError_t e = run_w13<WT, AT>(g, a, ev, s);
     if (e != hipSuccess) return e;
     return run_w2<WT, AT>(g, a, ev, s);
+}
+
+template <int WT, int AT, int CPL, int RP, int WPR>
+hipError_t launch_step_w13(const Geom& g, const PolicyArgs& pa, const ForwardArgs& a, int G, int n_copy,
+                           const StageEvents* ev, hipStream_t s) {
+    const int rows_per_block = (4 / WPR) * (64 / G) * RP;
+    const int nrb = (g.I + rows_per_block - 1) / rows_per_block;
+    const size_t pol = (policy_lds_bytes(g.E, pa.N) + 15) / 16 * 16;
+    const size_t lds = pol + (WT == W_INT4 ? (size_t)(g.H / 32) * kPackedChunkBytes : 0);
+    const size_t tail = (size_t)2 * g.I * g.H * (WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1)) / (WT == W_INT4 ? 2 : 1);
+    const dim3 grid(1 + n_copy + nrb * g.K);
+    if (ev && ev->w13_start)
+        hipExtLaunchKernelGGL((k_step_w13<WT, AT, CPL, RP, WPR>), grid, dim3(256), (uint32_t)lds, s, ev->w13_start,
+                              ev->w13_stop, 0, pa, g.slot_stride, a.x, g.H, g.I, log2_of(G), g.off_w13, g.off_s13, tail,
+                              a.act, n_copy, nrb, (int)pol);
+    else
+        hipLaunchKernelGGL((k_step_w13<WT, AT, CPL, RP, WPR>), grid, dim3(256), lds, s, pa, g.slot_stride, a.x, g.H,
+                           g.I, log2_of(G), g.off_w13, g.off_s13, tail, a.act, n_copy, nrb, (int)pol);
+    return hipGetLastError();
+}
+
+template <int WT, int AT>
+hipError_t run_step(const Geom& g, const PolicyArgs& pa, const ForwardArgs& a, int n_copy, const StageEvents* ev,
+                    hipStream_t s) {
+    const int nc = chunks_of(WT, g.H);
+    const int G = group_lanes(nc);
+    const int wpr = waves_per_row(nc, G, MOE_W13_WPR);
+    const int cpl = nc / (G * wpr);
+    hipError_t e = hipErrorInvalidValue;
+    auto pick = [&]() -> hipError_t {
+        if (G != 64) {
+            MOE_CPL_SWITCH(cpl, (launch_step_w13<WT, AT, C, 1, 1>(g, pa, a, G, n_copy, ev, s)))
+        }
+        if (wpr == 4) {
+            MOE_CPL_SWITCH(cpl, (launch_step_w13<WT, AT, C, MOE_W13_RP64, 4>(g, pa, a, G, n_copy, ev, s)))
+        }
+        if (wpr == 2) {
+            MOE_CPL_SWITCH(cpl, (launch_step_w13<WT, AT, C, MOE_W13_RP64, 2>(g, pa, a, G, n_copy, ev, s)))
+        }
+        MOE_CPL_SWITCH(cpl, (launch_step_w13<WT, AT, C, MOE_W13_RP64, 1>(g, pa, a, G, n_copy, ev, s)))
+    };
+    if ((e = pick()) != hipSuccess) return e;
+    ForwardArgs a2 = a;
+    a2.flip_par = pa.ds.ctl;
+    return run_w2<WT, AT>(g, a2, ev, s);
 }
 
 bool split_ok(int nc, int want) {
@@ -1639,6 +1787,21 @@ hipError_t run_grouped(const Geom& g, const ForwardArgs& a, const StageEvents* e
 }
 
 }  // namespace
+
+hipError_t launch_step_decode(const Geom& g, const PolicyArgs& pol, const ForwardArgs& fw, int n_copy,
+                              const StageEvents* ev, hipStream_t s) {
+    if (fw.T != 1 || pol.n != g.K || fw.slot_ids != pol.out || n_copy < 1 || pol.eb % 16 ||
+        pol.evict < EVICT_LRU || pol.evict > EVICT_SLRU || (!pol.resident && pol.per_piece < 1))
+        return hipErrorInvalidValue;
+    switch (g.wtype * 2 + g.atype) {
+        case W_F32 * 2 + A_F32: return run_step<W_F32, A_F32>(g, pol, fw, n_copy, ev, s);
+        case W_F32 * 2 + A_BF16: return run_step<W_F32, A_BF16>(g, pol, fw, n_copy, ev, s);
+        case W_BF16 * 2 + A_F32: return run_step<W_BF16, A_F32>(g, pol, fw, n_copy, ev, s);
+        case W_BF16 * 2 + A_BF16: return run_step<W_BF16, A_BF16>(g, pol, fw, n_copy, ev, s);
+        case W_INT4 * 2 + A_BF16: return run_step<W_INT4, A_BF16>(g, pol, fw, n_copy, ev, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_forward(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t stream) {
     if (a.T <= 0) return hipSuccess;

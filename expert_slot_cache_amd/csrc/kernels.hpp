@@ -49,22 +49,14 @@ struct StageEvents {
 };
 
 // The two places a layer's experts can be read from; *path (written by the
-// step's remap) picks one: PATH_POOL -> pool, PATH_STAGE -> stage, PATH_NONE -> none.
-// Where a (token, expert) pair's expert is read from when it is not its slot: the
-// expert in the device-mapped pinned store (`from`), and the slot it is written
-// through to as it is read (`to`, or null).
-struct PairSrc {
-    const char* from;
-    char* to;
-};
-
+// step's decision or remap) picks one: PATH_POOL -> pool, PATH_STAGE -> stage,
+// PATH_NONE -> none.
 struct Slots {
     const char* pool;
     const char* stage;
     int npool;              // valid slot ids in the pool: [0, npool)
     int nstage;             // valid staging ranks: [0, nstage)
     const int32_t* path;    // device word
-    const PairSrc* src;     // null, or per pair: a non-null `from` replaces the slot (decode GEMVs)
 };
 
 struct ForwardArgs {
@@ -81,6 +73,7 @@ struct ForwardArgs {
     int32_t* grp;           // grouped-path index buffer (grouped_index_bytes)
     int nslots_alloc;       // slot count the grp buffer was sized for
     int max_pairs;          // max_tokens * K the scratch was sized for
+    int32_t* flip_par;      // decode w2 launch of a fused step: the state-copy word it flips (else null)
 };
 
 // The slot-indexed fused MoE for one layer.
@@ -112,27 +105,49 @@ struct FillBatch {
 hipError_t launch_fill(const FillBatch& b, hipStream_t s);
 
 // ---- the slot manager on the GPU -----------------------------------------------------
-// One layer's LRU state (HBM, int32): map[E] (slot or -1), owner[N] (expert or -1),
-// free[N] (stack of free slots; meta[2] entries valid), prev/next[E] (the LRU list
-// over expert ids, -1 terminated), meta = {head, tail, nfree}.
-struct LruState {
-    int32_t* map;
-    int32_t* owner;
-    int32_t* free;
-    int32_t* prev;
-    int32_t* next;
-    int32_t* meta;
-};
+// Eviction policies (the victim among the resident experts the step has not yet
+// processed is the one with the smallest key):
+//   LRU : key = tick of the last touch
+//   FIFO: key = tick of the insertion
+//   LFU : (use = touches since insertion, key = tick of the last touch)
+//   SLRU: (prot = protected segment, key = tick of taking its place in the segment);
+//         the probationary segment (prot 0) gives the victim while it has a candidate
+enum { EVICT_LRU = 0, EVICT_FIFO = 1, EVICT_LFU = 2, EVICT_SLRU = 3 };
 
-// The state plus ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d, staged},
-// rec = the last step {path, D, n_miss, bad, then (expert, slot, evicted) per miss}
-// and arrive = the step's count of workgroups holding their copy of the state (0
-// between steps).
+// One copy of a layer's slot-manager state, all slot-indexed except map:
+// map[E] (slot or -1), owner[N] (expert or -1), free[N] (a stack, meta[0] entries
+// valid, popped from the top), key[N], use[N] (u32), prot[N], meta = {nfree, tick,
+// nprot, 0}.  Each layer holds two copies: a launch reads copy ctl[0] and its
+// lead workgroup writes the state after the step into the other copy.
+struct SlotStateLayout {
+    size_t map, owner, free, key, use, prot, meta, total;
+};
+__host__ __device__ inline size_t slot_state_align(size_t n) { return (n + 255) / 256 * 256; }
+__host__ __device__ inline SlotStateLayout slot_state_layout(int E, int N) {
+    SlotStateLayout L{};
+    size_t o = 0;
+    L.map = o;   o = slot_state_align(o + (size_t)E * 4);
+    L.owner = o; o = slot_state_align(o + (size_t)N * 4);
+    L.free = o;  o = slot_state_align(o + (size_t)N * 4);
+    L.key = o;   o = slot_state_align(o + (size_t)N * 4);
+    L.use = o;   o = slot_state_align(o + (size_t)N * 4);
+    L.prot = o;  o = slot_state_align(o + (size_t)N * 4);
+    L.meta = o;  o = slot_state_align(o + 16 * 4);
+    L.total = o;
+    return L;
+}
+
+// A layer's device-side slot manager: the two state copies, the control words
+// ctl = {par: the current copy, readers: workgroups of the running launch that have
+// read it (0 between launches)}, counters ctr = u64 {steps, hits, misses,
+// fallbacks, bytes_h2d, staged} and the last step's record rec = {path, D, n_miss,
+// bad, then (expert, slot, evicted) per miss}.  The launch's last reader flips par,
+// so no workgroup ever waits for another.
 struct DevState {
-    LruState s;
+    char* copy[2];
+    int32_t* ctl;
     unsigned long long* ctr;
     int32_t* rec;
-    int32_t* arrive;
 };
 
 struct PolicyArgs {
@@ -140,29 +155,33 @@ struct PolicyArgs {
     int n;                   // n_tokens * top_k (>= 1)
     int E, N;
     int rule;                // 0: fallback iff D > N; 1: iff n > N (and D > 0)
+    int evict;               // EVICT_*
     int resident;            // 1: every expert at slot = id (count hits only)
     unsigned long long eb;   // bytes per expert (bytes_h2d counter; a multiple of 16)
-    LruState st;             // the layer's state, updated in place
-    unsigned long long* ctr;
-    int32_t* rec;
-    int32_t* arrive;         // 0 at launch; left 0
+    DevState ds;
     int32_t* out;            // [n] slot ids (or staging ranks)
     int32_t* path;           // the layer's path word
-    uint32_t* err;           // host-mapped: 1 = an id outside [0, E); 2 = the write-back's
-                             // wait for the other workgroups timed out
-    unsigned long long spin_limit;  // bound on that wait (polls)
+    uint32_t* err;           // host-mapped: 1 = an id outside [0, E)
     // the copies (unused when resident)
     const char* const* pieces;  // device array: device-mapped base of each store piece
     int per_piece;           // experts per piece
     char* slots;             // the layer's slot pool
     char* staging;           // the staging area
     int32_t* timed_jobs;     // host-mapped, or null: experts the step moves over the link
-    PairSrc* tab;            // null: copy the step's experts; else [n]: the forward reads them
-                             // through (misses are written to their slots on the way)
 };
+// Dynamic LDS of the decision for E experts and N slots.
 size_t policy_lds_bytes(int E, int N);
 // grid: workgroups of the launch (the per-id outputs and the copies spread over them).
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
+
+// The one-token decode step in two launches (read-through misses): the first runs the
+// decision in every workgroup that needs it, the w13 GEMV + SwiGLU (a missed expert's
+// rows read from the pinned store and written through to its slot, a staged one's
+// read from the store), and copies the rest of each missed or staged expert (from its
+// w2 region on) into the slot or staging entry; the second is the w2 GEMV + combine.
+// fw.slot_ids must be pol.out; n_copy: workgroups that copy.
+hipError_t launch_step_decode(const Geom& g, const PolicyArgs& pol, const ForwardArgs& fw, int n_copy,
+                              const StageEvents* ev, hipStream_t s);
 
 // One launch of the streaming-read calibration kernel over [p, p + bytes) (bytes a
 // multiple of 16), timed by the event pair; sink: 1 KiB of device scratch.

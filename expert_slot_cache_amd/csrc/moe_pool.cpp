@@ -112,6 +112,9 @@ constexpr size_t kStorePiece = (size_t)1 << 30;
 // Workgroups of one device-policy step: each runs the decision, then the copies
 // (64 KiB units) spread over all of them.
 constexpr int kPolicyGrid = 128;
+// Copy workers of a fused one-token step (the part of each missed expert past its w13
+// rows, 64 KiB units).
+constexpr int kStepCopyWorkers = 64;
 
 struct LayerState {
     moe::SlotLRU lru;
@@ -142,7 +145,6 @@ struct LayerState {
     // addresses (device array), and the fill timing of this layer
     char* dev_block = nullptr;
     moe::DevState ds{};
-    bool rt_prepared = false;    // the current prepare left a pair table (read-through forward)
     bool rt_sample = false;      // the pending w13/w2 timing sample is a read-through step
     const char** pieces_dev = nullptr;
     bool last_empty = false;     // the last step had no tokens (not seen by the GPU)
@@ -173,10 +175,6 @@ struct moe_pool {
     int32_t* rank_dev = nullptr;  // HBM [E]
     int32_t* ident_dev = nullptr; // HBM [E] identity table (resident mode)
     int32_t* paths_dev = nullptr; // HBM [n_layers]
-    // polls a device step's write-back waits at most for the step's other workgroups
-    // to hold their copy of the state (each poll is a load and a short sleep; the
-    // wait normally ends within a few microseconds)
-    unsigned long long spin_limit = 1ull << 22;
     void* act = nullptr;          // HBM [max_tokens * K][I] SwiGLU output
     float* y = nullptr;           // HBM [max_tokens * K][H] per-pair w2 output
     int32_t* grp = nullptr;       // HBM grouped-path index buffer
@@ -189,7 +187,6 @@ struct moe_pool {
     int32_t* timed_jobs_dev = nullptr;
     int32_t* rt_jobs_host = nullptr;    // pinned coherent [n_layers]: experts read through by the
     int32_t* rt_jobs_dev = nullptr;     //   last timed read-through step
-    moe::PairSrc* tab_dev = nullptr;    // [top_k]: the read-through pair table (one-token steps)
     int32_t last_prepared = -1;         // the layer of the latest prepare (device policy)
     std::vector<char> used_copy;
     int copy_rr = 0;
@@ -242,7 +239,6 @@ void destroy_pool(moe_pool* p) {
     if (p->errs_host) (void)hipHostFree(p->errs_host);
     if (p->timed_jobs_host) (void)hipHostFree(p->timed_jobs_host);
     if (p->rt_jobs_host) (void)hipHostFree(p->rt_jobs_host);
-    if (p->tab_dev) (void)hipFree(p->tab_dev);
     delete p;
 }
 
@@ -568,14 +564,11 @@ void finish_prepare(moe_pool* p, LayerState& L, int32_t n_tokens, int32_t the_pa
 }
 
 moe::Slots layer_slots(const moe_pool* p, const LayerState& L) {
-    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev,
-                      L.rt_prepared ? p->tab_dev : nullptr};
+    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev};
 }
 
-// timed: -1 = sample by the timing period, else as given (already counted).
-moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
-                                  const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev,
-                                  int timed_as = -1) {
+moe::ForwardArgs forward_args(const moe_pool* p, const LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
+                              const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev) {
     moe::ForwardArgs a{};
     a.sl = layer_slots(p, L);
     a.slot_ids = slot_ids_dev;
@@ -589,10 +582,15 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
     a.grp = p->grp;
     a.nslots_alloc = std::max(1, p->grp_slots);
     a.max_pairs = p->cfg.max_tokens * p->cfg.top_k;
+    return a;
+}
+
+moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
+                                  const float* topk_w_dev, const void* resid_dev, int32_t n_tokens, void* out_dev) {
+    const moe::ForwardArgs a = forward_args(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
     moe::StageEvents ev;
-    const bool timed = timed_as >= 0 ? timed_as > 0
-                                     : p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
-                                           !L.w13_t.pending && !L.w2_t.pending;
+    const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 && !L.w13_t.pending &&
+                       !L.w2_t.pending;
     if (timed) {
         ev.w13_start = L.w13_t.a;
         ev.w13_stop = L.w13_t.b;
@@ -608,47 +606,40 @@ moe_status_t launch_layer_forward(moe_pool* p, LayerState& L, const void* x_dev,
 }
 
 // ---- MOE_POLICY_DEVICE ------------------------------------------------------------
-// Byte layout of one layer's device state block (see moe::DevState).
+// Byte layout of one layer's device state block: the two state copies
+// (moe::slot_state_layout), the control words {par, readers}, the counters and the
+// last step's record.
 struct DevLayout {
-    size_t map, owner, free, prev, next, meta, ctr, rec, arrive, total;
+    size_t copy0, copy1, ctl, ctr, rec, total;
 };
 
 DevLayout dev_layout(int32_t E, int32_t N) {
     DevLayout d{};
-    size_t o = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = o;
-        o = round_up(o + bytes);
-        return at;
-    };
-    d.map = take((size_t)E * 4);
-    d.owner = take((size_t)N * 4);
-    d.free = take((size_t)N * 4);
-    d.prev = take((size_t)E * 4);
-    d.next = take((size_t)E * 4);
-    d.meta = take(16 * 4);
-    d.ctr = take(8 * 8);
-    d.rec = take((size_t)(4 + 3 * N) * 4);
-    d.arrive = take(4);
-    d.total = o;
+    const size_t one = moe::slot_state_layout(E, N).total;
+    d.copy0 = 0;
+    d.copy1 = one;
+    d.ctl = 2 * one;
+    d.ctr = d.ctl + kAlign;
+    d.rec = d.ctr + kAlign;
+    d.total = round_up(d.rec + (size_t)(4 + 3 * N) * 4);
     return d;
 }
 
-// The cold state image: map -1, owners -1, free slots 0..N-1 (popped from the end),
-// empty LRU list, counters and the arrival word zero.
+// The cold state image: in both copies map -1, owners -1, free slots 0..N-1 (popped
+// from the end), keys and uses 0, nothing protected, meta {nfree = N, tick 0,
+// nprot 0}; par 0, no readers, counters and record zero.
 std::vector<char> dev_cold_image(const moe_pool* p) {
     const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
     const DevLayout d = dev_layout(E, N);
+    const moe::SlotStateLayout o = moe::slot_state_layout(E, N);
     std::vector<char> img(d.total, 0);
-    auto w = [&](size_t off) { return reinterpret_cast<int32_t*>(img.data() + off); };
-    std::fill(w(d.map), w(d.map) + E, -1);
-    std::fill(w(d.owner), w(d.owner) + N, -1);
-    for (int32_t s2 = 0; s2 < N; ++s2) w(d.free)[s2] = s2;
-    std::fill(w(d.prev), w(d.prev) + E, -1);
-    std::fill(w(d.next), w(d.next) + E, -1);
-    w(d.meta)[0] = -1;
-    w(d.meta)[1] = -1;
-    w(d.meta)[2] = N;
+    for (size_t base : {d.copy0, d.copy1}) {
+        auto w = [&](size_t off) { return reinterpret_cast<int32_t*>(img.data() + base + off); };
+        std::fill(w(o.map), w(o.map) + E, -1);
+        std::fill(w(o.owner), w(o.owner) + N, -1);
+        for (int32_t s2 = 0; s2 < N; ++s2) w(o.free)[s2] = s2;
+        w(o.meta)[0] = N;
+    }
     return img;
 }
 
@@ -656,7 +647,6 @@ moe_status_t dev_init_layers(moe_pool* p) {
     const std::vector<char> img = dev_cold_image(p);
     for (auto& L : p->layers) {
         HIPCHK(hipMemcpy(L.dev_block, img.data(), img.size(), hipMemcpyHostToDevice));
-        L.rt_prepared = false;
         L.rt_sample = false;
         L.has_last = false;
         L.last_empty = false;
@@ -669,38 +659,28 @@ moe_status_t dev_init_layers(moe_pool* p) {
 // An id outside [0,E) found by a layer's earlier device step.
 moe_status_t check_dev_err(moe_pool* p, int32_t layer) {
     volatile uint32_t* e = p->errs_host + layer;
-    const uint32_t v = *e;
-    if (v) {
+    if (*e) {
         *e = 0;
-        if (v == 2)
-            FAIL(MOE_EHIP, "layer %d: a device step's write-back gave up waiting for its workgroups (the GPU did"
-                           " not run them); the layer's state may be inconsistent: reset the pool", layer);
         FAIL(MOE_ERANGE, "layer %d: an earlier step had an expert id outside [0,%d); it changed nothing and its"
                          " output is undefined", layer, p->cfg.n_experts);
     }
     return MOE_OK;
 }
 
-// Queue the slot manager and the copy kernel for one step (n_tokens >= 1).
-// rt: leave the pair table for a read-through forward (one-token steps); rt_timed:
-// that forward is timed, so the launch records how many experts it reads through.
-moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
-                         int32_t* slot_ids_dev, bool rt = false, bool rt_timed = false) {
-    const int n = n_tokens * p->cfg.top_k;
+// The decision's arguments for one step of layer `layer` (n_tokens >= 1).
+moe::PolicyArgs policy_args(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
+                            int32_t* slot_ids_dev) {
     const bool resident = p->cfg.resident != 0;
     moe::PolicyArgs a{};
     a.ids = ids_dev;
-    a.n = n;
+    a.n = n_tokens * p->cfg.top_k;
     a.E = p->cfg.n_experts;
     a.N = resident ? 0 : p->cfg.n_slots;
     a.rule = p->cfg.rule;
+    a.evict = p->cfg.evict;
     a.resident = p->cfg.resident;
     a.eb = p->lay.total;
-    a.st = L.ds.s;
-    a.ctr = L.ds.ctr;
-    a.rec = L.ds.rec;
-    a.arrive = L.ds.arrive;
-    a.spin_limit = p->spin_limit;
+    a.ds = L.ds;
     a.out = slot_ids_dev;
     a.path = L.path_dev;
     a.err = p->errs_dev + layer;
@@ -708,17 +688,22 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
     a.per_piece = L.per_piece;
     a.slots = L.slots;
     a.staging = p->staging;
+    return a;
+}
+
+// Queue the slot manager with its copies for one step (n_tokens >= 1).
+moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
+                         int32_t* slot_ids_dev) {
+    const bool resident = p->cfg.resident != 0;
+    moe::PolicyArgs a = policy_args(p, L, layer, ids_dev, n_tokens, slot_ids_dev);
     // the copy span of a timed step is the launch's (its decision takes a few us)
-    const bool timed = !resident && !rt && p->cfg.timing > 0 &&
+    const bool timed = !resident && p->cfg.timing > 0 &&
                        (p->n_copy_batches++ % (uint64_t)p->cfg.timing) == 0 && !L.fill_t.pending;
-    a.timed_jobs = timed ? p->timed_jobs_dev + layer : (rt && rt_timed ? p->rt_jobs_dev + layer : nullptr);
-    a.tab = rt ? p->tab_dev : nullptr;
+    a.timed_jobs = timed ? p->timed_jobs_dev + layer : nullptr;
     // resident: no copies, so only as many workgroups as the ids need (256 per)
-    const int grid = resident ? std::max(1, std::min(kPolicyGrid, n / 256)) : kPolicyGrid;
-    HIPCHK(moe::launch_policy(a, grid, timed ? L.fill_t.a : nullptr,
-                              timed ? L.fill_t.b : nullptr, p->compute));
+    const int grid = resident ? std::max(1, std::min(kPolicyGrid, a.n / 256)) : kPolicyGrid;
+    HIPCHK(moe::launch_policy(a, grid, timed ? L.fill_t.a : nullptr, timed ? L.fill_t.b : nullptr, p->compute));
     if (timed) L.fill_t.pending = true;
-    L.rt_prepared = rt;
     L.prepared = true;
     L.prep_tokens = n_tokens;
     L.prep_path = -1;            // known on the GPU only
@@ -775,8 +760,15 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.policy != MOE_POLICY_HOST && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "policy %d invalid", c.policy);
     if (c.read_through != 0 && c.read_through != 1) FAIL(MOE_EINVAL, "read_through %d invalid", c.read_through);
     if (c.read_through && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "read_through needs the device policy");
+    if (c.evict < MOE_EVICT_LRU || c.evict > MOE_EVICT_SLRU) FAIL(MOE_EINVAL, "evict %d invalid", c.evict);
+    if (c.evict != MOE_EVICT_LRU && c.policy != MOE_POLICY_DEVICE)
+        FAIL(MOE_EINVAL, "the host slot manager implements LRU only; evict %d needs the device policy", c.evict);
     if (c.policy == MOE_POLICY_DEVICE && c.n_experts > 2048)
         FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS: n_experts %d > 2048", c.n_experts);
+    if (c.policy == MOE_POLICY_DEVICE &&
+        moe::policy_lds_bytes(c.n_experts, c.resident ? 0 : c.n_slots) + (size_t)(c.hidden / 32) * 80 + 16 > 65536)
+        FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS (64 KiB per workgroup): %d experts and %d"
+                         " slots do not fit", c.n_experts, c.n_slots);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
     Layout lay;
     if (!make_layout(c.wtype, c.hidden, c.inter, &lay)) FAIL(MOE_EINVAL, "unsupported shape/format (wtype %d, H %d, I %d)", c.wtype, c.hidden, c.inter);
@@ -900,11 +892,11 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
         const DevLayout d = dev_layout(E, c.resident ? 0 : c.n_slots);
         for (auto& L : p->layers) {
             CREATE_HIP(hipMalloc((void**)&L.dev_block, d.total));
-            auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(L.dev_block + off); };
-            L.ds.s = moe::LruState{at(d.map), at(d.owner), at(d.free), at(d.prev), at(d.next), at(d.meta)};
+            L.ds.copy[0] = L.dev_block + d.copy0;
+            L.ds.copy[1] = L.dev_block + d.copy1;
+            L.ds.ctl = reinterpret_cast<int32_t*>(L.dev_block + d.ctl);
             L.ds.ctr = reinterpret_cast<unsigned long long*>(L.dev_block + d.ctr);
-            L.ds.rec = at(d.rec);
-            L.ds.arrive = at(d.arrive);
+            L.ds.rec = reinterpret_cast<int32_t*>(L.dev_block + d.rec);
             if (!L.store_dev.empty()) {
                 CREATE_HIP(hipMalloc((void**)&L.pieces_dev, sizeof(char*) * L.store_dev.size()));
                 CREATE_HIP(hipMemcpy(L.pieces_dev, L.store_dev.data(), sizeof(char*) * L.store_dev.size(),
@@ -922,12 +914,11 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
                                  hipHostMallocCoherent | hipHostMallocMapped));
         std::memset(p->timed_jobs_host, 0, sizeof(int32_t) * c.n_layers);
         CREATE_HIP(hipHostGetDevicePointer((void**)&p->timed_jobs_dev, p->timed_jobs_host, 0));
-        if (c.read_through && !c.resident) {
+        if (c.read_through) {
             CREATE_HIP(hipHostMalloc((void**)&p->rt_jobs_host, sizeof(int32_t) * c.n_layers,
                                      hipHostMallocCoherent | hipHostMallocMapped));
             std::memset(p->rt_jobs_host, 0, sizeof(int32_t) * c.n_layers);
             CREATE_HIP(hipHostGetDevicePointer((void**)&p->rt_jobs_dev, p->rt_jobs_host, 0));
-            CREATE_HIP(hipMalloc((void**)&p->tab_dev, sizeof(moe::PairSrc) * c.top_k));
         }
         const moe_status_t ist = dev_init_layers(p);
         if (ist) {
@@ -1003,7 +994,6 @@ moe_status_t moe_pool_prepare(moe_pool_t* p, int32_t layer, const int32_t* topk_
             L.prepared = true;
             L.prep_tokens = 0;
             L.prep_path = MOE_PATH_POOL;
-            L.rt_prepared = false;
             L.has_last = true;
             L.last_empty = true;
             L.empty_steps++;
@@ -1066,12 +1056,12 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev, const void* resid_dev,
                            void* out_dev, moe_miss_t* miss_host, int32_t miss_cap, int32_t* n_miss, int32_t* path) {
     if (n_tokens > 0 && (!x_dev || !topk_w_dev || !out_dev)) FAIL(MOE_EINVAL, "null buffer");
-    if (p && p->tab_dev && n_tokens == 1) {
-        // Read-through (device policy, one token): the decision leaves a pair table
-        // and copies nothing; the forward's kernels read each missed or staged expert
-        // from the store and write a missed one through to its slot.  Everything the
-        // forward needs is checked before the decision is queued, so a queued
-        // decision always has its forward (a miss's slot is filled by the forward).
+    if (p && p->cfg.policy == MOE_POLICY_DEVICE && p->cfg.read_through && n_tokens == 1) {
+        // The fused one-token step (device policy): the decision runs inside the w13
+        // launch, a missed expert's w13 rows are read from the store and written through
+        // to its slot by the GEMV blocks while copy workers of the same launch move the
+        // rest of it, and the hit experts' GEMVs run alongside.  Everything the forward
+        // needs is checked before anything is queued.
         moe_status_t st = check_layer(p, layer);
         if (st) return st;
         if (!topk_ids_dev || !slot_ids_dev) FAIL(MOE_EINVAL, "null ids");
@@ -1083,16 +1073,27 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
         if (path) *path = -1;
         const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
                            !L.w13_t.pending && !L.w2_t.pending;
-        st = dev_prepare(p, L, layer, topk_ids_dev, 1, slot_ids_dev, true, timed);
-        if (st) return st;
+        moe::PolicyArgs pa = policy_args(p, L, layer, topk_ids_dev, 1, slot_ids_dev);
+        pa.timed_jobs = timed && p->rt_jobs_dev ? p->rt_jobs_dev + layer : nullptr;
+        moe::ForwardArgs a = forward_args(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, 1, out_dev);
+        moe::StageEvents ev;
+        if (timed) {
+            ev.w13_start = L.w13_t.a;
+            ev.w13_stop = L.w13_t.b;
+            ev.w2_start = L.w2_t.a;
+            ev.w2_stop = L.w2_t.b;
+        }
+        HIPCHK(moe::launch_step_decode(p->geom, pa, a, kStepCopyWorkers, timed ? &ev : nullptr, p->compute));
+        if (timed) {
+            L.w13_t.pending = true;
+            L.w2_t.pending = true;
+            L.rt_sample = true;
+        }
         p->last_prepared = layer;
-        st = launch_layer_forward(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, 1, out_dev, timed ? 1 : 0);
-        // the step's pair table belongs to this forward alone (staged experts were
-        // never written to staging): another forward needs another prepare
+        // the step is complete: a forward needs a prepare of its own
         L.prepared = false;
-        L.rt_prepared = false;
-        if (st) return st;
-        if (timed) L.rt_sample = true;
+        L.has_last = true;
+        L.last_empty = false;
         if (p->cfg.timing) harvest_all(p);
         return MOE_OK;
     }
@@ -1185,17 +1186,35 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
     if (p->cfg.policy == MOE_POLICY_DEVICE) {
         const LayerState& L = p->layers[layer];
         const int32_t E = p->cfg.n_experts, N = p->cfg.resident ? 0 : p->cfg.n_slots;
-        std::vector<int32_t> map(E), owner(N), next(E), meta(16);
-        const moe::LruState& cur = L.ds.s;
-        if ((st = dev_read(p, map.data(), cur.map, E))) return st;
-        if (N && (st = dev_read(p, owner.data(), cur.owner, N))) return st;
-        if ((st = dev_read(p, next.data(), cur.next, E))) return st;
-        if ((st = dev_read(p, meta.data(), cur.meta, 16))) return st;
+        int32_t ctl[2] = {0, 0};
+        if ((st = dev_read(p, ctl, L.ds.ctl, 2))) return st;
+        const moe::SlotStateLayout o = moe::slot_state_layout(E, N);
+        const char* cur = L.ds.copy[ctl[0] & 1];
+        std::vector<int32_t> map(E), owner(N), prot(N);
+        std::vector<uint32_t> key(N), use(N);
+        if ((st = dev_read(p, map.data(), cur + o.map, E))) return st;
+        if (N && (st = dev_read(p, owner.data(), cur + o.owner, N))) return st;
+        if (N && (st = dev_read(p, key.data(), cur + o.key, N))) return st;
+        if (N && (st = dev_read(p, use.data(), cur + o.use, N))) return st;
+        if (N && (st = dev_read(p, prot.data(), cur + o.prot, N))) return st;
         if (map_E) std::copy(map.begin(), map.end(), map_E);
         if (owner_N) std::copy(owner.begin(), owner.end(), owner_N);
         if (lru_N) {
+            // the eviction order: resident slots by the policy's key (SLRU: the
+            // probationary segment first)
+            std::vector<int32_t> res;
+            for (int32_t q = 0; q < N; ++q)
+                if (owner[q] >= 0) res.push_back(q);
+            const int32_t ev = p->cfg.evict;
+            auto k = [&](int32_t q) {
+                uint64_t v = key[q];
+                if (ev == MOE_EVICT_LFU) v |= (uint64_t)use[q] << 32;
+                if (ev == MOE_EVICT_SLRU) v |= (uint64_t)(prot[q] != 0) << 32;
+                return v;
+            };
+            std::sort(res.begin(), res.end(), [&](int32_t a, int32_t b) { return k(a) < k(b); });
             int32_t i = 0;
-            for (int32_t e = meta[0]; e >= 0 && i < N; e = next[e]) lru_N[i++] = e;
+            for (int32_t q : res) lru_N[i++] = owner[q];
             for (; i < N; ++i) lru_N[i] = -1;
         }
         return MOE_OK;

@@ -1,0 +1,488 @@
+// The slot manager's decision as device code, shared by the launches that need it
+// (the prepare launch, which also copies the step's experts, and the fused decode
+// step, whose workgroups each know their own expert from it).
+//
+// The rule is the one of vLLM PR "Run MoE models exceeding VRAM via expert CPU
+// offloading with GPU cache" (section "How it works"; the eviction policies its
+// review thread lists): the step's distinct ids ascending, one at a time; a hit
+// records the use, a miss takes the last free slot (free slots start as 0..N-1) or
+// the slot of the victim -- the resident expert, not yet processed by this step,
+// with the smallest key under the layer's policy.  The route rule is the llama.cpp
+// "Persistent expert slot pool" prefill rule: a step that exceeds the slots takes the
+// selective-copy path and leaves the state untouched.
+//
+// Every workgroup that runs the decision reads the layer's current state copy into
+// LDS and runs the same steps on it, so every such workgroup reaches the same
+// result without waiting for another.  The policy walk runs in one wave: the ids in
+// order, each touching one slot (LDS), a victim found by a wave-wide minimum over
+// the slots.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kPolThreads = 256;
+constexpr int kPolWaves = kPolThreads / 64;
+
+// The decision's LDS arrays (int32 words): map, rank, list [E]; presence bits
+// [E/32 + 1]; owner, free, key, use, prot, touched, evicted-by-miss [N]; misc [16].
+struct PolLds {
+    int32_t *map, *rank, *list, *owner, *fre, *prot, *tch, *mev, *misc;
+    uint32_t *key, *use, *bits;
+};
+
+// misc words
+enum { PM_NFREE = 0, PM_TICK = 1, PM_NPROT = 2, PM_D = 3, PM_PATH = 4, PM_NMISS = 5, PM_HITS = 6, PM_BAD = 7,
+       PM_WAVES = 8 /* 4 words: per-wave counts of the compaction */ };
+
+__host__ __device__ inline size_t pol_lds_words(int E, int N) {
+    return (size_t)3 * E + (size_t)(E / 32 + 1) + (size_t)7 * N + 16;
+}
+
+__device__ inline PolLds pol_lds(int32_t* w, int E, int N) {
+    PolLds L;
+    L.map = w;  w += E;
+    L.rank = w; w += E;
+    L.list = w; w += E;
+    L.bits = reinterpret_cast<uint32_t*>(w); w += E / 32 + 1;
+    L.owner = w; w += N;
+    L.fre = w;  w += N;
+    L.key = reinterpret_cast<uint32_t*>(w); w += N;
+    L.use = reinterpret_cast<uint32_t*>(w); w += N;
+    L.prot = w; w += N;
+    L.tch = w;  w += N;
+    L.mev = w;  w += N;
+    L.misc = w;
+    return L;
+}
+
+// Pointers into one state copy.
+struct SlotView {
+    int32_t* map;
+    int32_t* owner;
+    int32_t* fre;
+    uint32_t* key;
+    uint32_t* use;
+    int32_t* prot;
+    int32_t* meta;
+};
+
+__device__ inline SlotView slot_view(char* base, int E, int N) {
+    const SlotStateLayout o = slot_state_layout(E, N);
+    SlotView v;
+    v.map = reinterpret_cast<int32_t*>(base + o.map);
+    v.owner = reinterpret_cast<int32_t*>(base + o.owner);
+    v.fre = reinterpret_cast<int32_t*>(base + o.free);
+    v.key = reinterpret_cast<uint32_t*>(base + o.key);
+    v.use = reinterpret_cast<uint32_t*>(base + o.use);
+    v.prot = reinterpret_cast<int32_t*>(base + o.prot);
+    v.meta = reinterpret_cast<int32_t*>(base + o.meta);
+    return v;
+}
+
+// The wave-wide minimum of a 64-bit value (every lane gets it).
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+// One wave (all 64 lanes, uniform control flow): the slot with the smallest key
+// among the candidates.  prot_only: the protected slots (SLRU demotion); else the
+// resident slots the step has not touched, ordered by the policy's key.  Keys are
+// distinct (each is a tick drawn once), so the minimum is unique; with no candidate
+// (which a pooled step cannot reach) slot 0 is returned so that no access leaves
+// the arrays.
+__device__ __forceinline__ int pol_argmin(const PolLds& L, int N, int evict, bool prot_only) {
+    const int lane = threadIdx.x & 63;
+    uint64_t best = ~0ull;
+    int bs = -1;
+    for (int s = lane; s < N; s += 64) {
+        bool c;
+        uint64_t k = L.key[s];
+        if (prot_only) {
+            c = L.prot[s] != 0;
+        } else {
+            c = L.owner[s] >= 0 && L.tch[s] == 0;
+            if (evict == EVICT_LFU) k |= (uint64_t)L.use[s] << 32;
+            if (evict == EVICT_SLRU) k |= (uint64_t)(L.prot[s] != 0) << 32;
+        }
+        if (c && k < best) {
+            best = k;
+            bs = s;
+        }
+    }
+    const uint64_t m = wave_min_u64(best);
+    const uint64_t who = __ballot(bs >= 0 && best == m);
+    if (!who) return 0;
+    return __shfl(bs, (int)__builtin_ctzll(who), 64);
+}
+
+struct Decision {
+    int path;    // PATH_POOL, PATH_STAGE, PATH_NONE (an id outside [0, E))
+    int D;       // distinct ids
+    int nmiss;   // misses (pool path)
+    int hits;
+};
+
+// The decision of one step, by all kPolThreads threads of the workgroup.  Leaves in
+// LDS: the state after the step (map, owner, free, key, use, prot, misc
+// nfree/tick/nprot), list[0, nmiss) = the missed experts in order with mev[j] = the
+// expert each evicted (-1: a free slot), rank[e] = position of e among the distinct
+// ids (-1 for a missed expert on the pool path); on the staging path list[0, D) =
+// the distinct ids (the staging order).
+__device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, const PolLds& L) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int E = a.E, N = a.N;
+    const int nwords = (E + 31) >> 5;
+
+    // the first 8 * kPolThreads ids, requested before the state so that the reads overlap
+    int e0[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = tid + q * kPolThreads;
+        e0[q] = i < a.n ? a.ids[i] : 0;
+    }
+
+    // 0. the state the step starts from; a thread's loads of the first two rounds
+    // (E, N <= 512) are all issued before it writes any of them to LDS
+    if (!a.resident) {
+        constexpr int R = 2;
+        int vm[R] = {}, vo[R] = {}, vf[R] = {}, vp[R] = {};
+        uint32_t vk[R] = {}, vu[R] = {};
+        int vmeta = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = tid + r * kPolThreads;
+            if (e < E) vm[r] = cur.map[e];
+            if (e < N) {
+                vo[r] = cur.owner[e];
+                vf[r] = cur.fre[e];
+                vk[r] = cur.key[e];
+                vu[r] = cur.use[e];
+                vp[r] = cur.prot[e];
+            }
+        }
+        if (tid < 3) vmeta = cur.meta[tid];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = tid + r * kPolThreads;
+            if (e < E) L.map[e] = vm[r];
+            if (e < N) {
+                L.owner[e] = vo[r];
+                L.fre[e] = vf[r];
+                L.key[e] = vk[r];
+                L.use[e] = vu[r];
+                L.prot[e] = vp[r];
+            }
+        }
+        if (tid < 3) L.misc[tid] = vmeta;
+        for (int e = tid + R * kPolThreads; e < E; e += kPolThreads) L.map[e] = cur.map[e];
+        for (int s = tid + R * kPolThreads; s < N; s += kPolThreads) {
+            L.owner[s] = cur.owner[s];
+            L.fre[s] = cur.fre[s];
+            L.key[s] = cur.key[s];
+            L.use[s] = cur.use[s];
+            L.prot[s] = cur.prot[s];
+        }
+    }
+    for (int i = tid; i < nwords; i += kPolThreads) L.bits[i] = 0u;
+    if (tid == 0) L.misc[PM_BAD] = 0;
+    __syncthreads();
+
+    // 1. distinct ids: presence bitmap, then ordered compaction (ballot + mbcnt).  With
+    // at most 64 experts the marks go into a 64-bit mask per lane, OR-ed across the
+    // wave, and one lane sets the two bitmap words.
+    if (E <= 64) {
+        uint64_t m = 0;
+        bool bad = false;
+        for (int i0 = tid; i0 < a.n; i0 += 8 * kPolThreads) {
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * kPolThreads;
+                e[q] = i0 == tid ? e0[q] : (i < a.n ? a.ids[i] : 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (i0 + q * kPolThreads >= a.n) break;
+                if ((unsigned)e[q] < (unsigned)E)
+                    m |= 1ull << e[q];
+                else
+                    bad = true;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+            m |= (uint64_t)(uint32_t)__shfl_xor((int)lo, off, 64) |
+                 ((uint64_t)(uint32_t)__shfl_xor((int)hi, off, 64) << 32);
+        }
+        if (bad) L.misc[PM_BAD] = 1;
+        if (lane == 0) {
+            if ((uint32_t)m) atomicOr(&L.bits[0], (uint32_t)m);
+            if (E > 32 && (uint32_t)(m >> 32)) atomicOr(&L.bits[1], (uint32_t)(m >> 32));
+        }
+    } else {
+        for (int i0 = tid; i0 < a.n; i0 += 8 * kPolThreads) {
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = i0 + q * kPolThreads;
+                e[q] = i0 == tid ? e0[q] : (i < a.n ? a.ids[i] : 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (i0 + q * kPolThreads >= a.n) break;
+                if ((unsigned)e[q] < (unsigned)E)
+                    atomicOr(&L.bits[e[q] >> 5], 1u << (e[q] & 31));
+                else
+                    L.misc[PM_BAD] = 1;
+            }
+        }
+    }
+    __syncthreads();
+    int base = 0;
+    if (E <= 64) {
+        // the id set is one 64-bit mask: an expert's rank is the number of set bits below it
+        const uint64_t all = (uint64_t)L.bits[0] | (E > 32 ? (uint64_t)L.bits[1] << 32 : 0ull);
+        if (tid < E && ((all >> tid) & 1ull)) {
+            const int pos = __popcll(all & ((1ull << tid) - 1ull));
+            L.list[pos] = tid;
+            L.rank[tid] = pos;
+        }
+        base = __popcll(all);
+    } else {
+        for (int c0 = 0; c0 < E; c0 += kPolThreads) {
+            const int e = c0 + tid;
+            const bool present = e < E && ((L.bits[e >> 5] >> (e & 31)) & 1u);
+            const uint64_t m = __ballot(present);
+            const uint32_t below =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (lane == 0) L.misc[PM_WAVES + wave] = __popcll(m);
+            __syncthreads();
+            int off = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < kPolWaves; ++w) {
+                const int cnt = L.misc[PM_WAVES + w];
+                off += (w < wave) ? cnt : 0;
+                total += cnt;
+            }
+            if (present) {
+                const int pos = base + off + (int)below;
+                L.list[pos] = e;
+                L.rank[e] = pos;
+            }
+            base += total;
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+    Decision d{};
+    d.D = base;
+    if (L.misc[PM_BAD]) {
+        d.path = PATH_NONE;
+        return d;
+    }
+    if (a.resident) {
+        d.path = PATH_POOL;
+        d.hits = d.D;
+        return d;
+    }
+    if (a.rule == 1 ? (a.n > N && d.D > 0) : (d.D > N)) {
+        d.path = PATH_STAGE;
+        return d;
+    }
+
+    d.path = PATH_POOL;
+    // 2a. a step whose ids all hit (most decode steps) under LRU, FIFO or LFU: id i of
+    // the ascending list takes tick + i as its key, so every id is updated at once
+    // (the order of the walk below fixes nothing else; SLRU promotions do, and walk)
+    if (tid == 0) L.misc[PM_PATH] = 0;
+    __syncthreads();
+    for (int i = tid; i < d.D; i += kPolThreads)
+        if (L.map[L.list[i]] < 0) L.misc[PM_PATH] = 1;
+    __syncthreads();
+    if (L.misc[PM_PATH] == 0 && a.evict != EVICT_SLRU) {
+        const uint32_t tick = (uint32_t)L.misc[PM_TICK];
+        for (int i = tid; i < d.D; i += kPolThreads) {
+            const int s = L.map[L.list[i]];
+            if (a.evict != EVICT_FIFO) L.key[s] = tick + (uint32_t)i;
+            if (a.evict == EVICT_LFU) L.use[s] = L.use[s] + 1u;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            L.misc[PM_TICK] = (int32_t)(tick + (uint32_t)d.D);
+            L.misc[PM_NMISS] = 0;
+            L.misc[PM_HITS] = d.D;
+        }
+        __syncthreads();
+        d.nmiss = 0;
+        d.hits = d.D;
+        return d;
+    }
+
+    // 2b. the policy, one distinct id at a time in ascending order, in wave 0.  Miss j's
+    // expert goes to list[j] (j <= the id being processed, so nothing unread is
+    // overwritten).
+    if (wave == 0) {
+        const int evict = a.evict;
+        const int cap = (4 * N) / 5;              // SLRU: protected segment capacity
+        int nfree = L.misc[PM_NFREE];
+        int nprot = L.misc[PM_NPROT];
+        uint32_t tick = (uint32_t)L.misc[PM_TICK];
+        for (int s = lane; s < N; s += 64) L.tch[s] = 0;
+        int hits = 0, nm = 0;
+        for (int i = 0; i < d.D; ++i) {
+            const int e = L.list[i];
+            int s = L.map[e];
+            if (s >= 0) {
+                ++hits;
+                const uint32_t t = tick++;
+                const int was_prot = L.prot[s];
+                if (lane == 0) {
+                    if (evict != EVICT_FIFO) L.key[s] = t;
+                    if (evict == EVICT_LFU) L.use[s] = L.use[s] + 1u;
+                    if (evict == EVICT_SLRU && !was_prot) L.prot[s] = 1;
+                    L.tch[s] = 1;
+                }
+                if (evict == EVICT_SLRU && !was_prot && ++nprot > cap) {
+                    // the protected segment is over its share: its oldest place is demoted
+                    const int dm = pol_argmin(L, N, evict, true);
+                    if (lane == 0) {
+                        L.prot[dm] = 0;
+                        L.key[dm] = tick;
+                    }
+                    ++tick;
+                    --nprot;
+                }
+            } else {
+                int ev = -1;
+                if (nfree > 0) {
+                    s = L.fre[--nfree];
+                } else {
+                    s = pol_argmin(L, N, evict, false);
+                    ev = L.owner[s];
+                    if (evict == EVICT_SLRU && L.prot[s]) --nprot;
+                    if (lane == 0 && ev >= 0) L.map[ev] = -1;
+                }
+                const uint32_t t = tick++;
+                if (lane == 0) {
+                    L.map[e] = s;
+                    L.owner[s] = e;
+                    L.key[s] = t;
+                    L.use[s] = 1u;
+                    L.prot[s] = 0;
+                    L.tch[s] = 1;
+                    L.list[nm] = e;
+                    L.mev[nm] = ev;
+                    L.rank[e] = -1;
+                }
+                ++nm;
+            }
+        }
+        if (lane == 0) {
+            L.misc[PM_NFREE] = nfree;
+            L.misc[PM_TICK] = (int32_t)tick;
+            L.misc[PM_NPROT] = nprot;
+            L.misc[PM_NMISS] = nm;
+            L.misc[PM_HITS] = hits;
+        }
+    }
+    __syncthreads();
+    d.nmiss = L.misc[PM_NMISS];
+    d.hits = L.misc[PM_HITS];
+    return d;
+}
+
+// Counters without a read-back (the lead's thread 0 does not wait for old values).
+__device__ __forceinline__ void pol_bump(unsigned long long* c, unsigned long long v) {
+    __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The lead workgroup's write-out of a decision: the state after the step into the
+// other copy, the counters, the step record and the layer's path word.
+__device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, const PolLds& L, const Decision& d) {
+    const int tid = threadIdx.x;
+    const int E = a.E, N = a.N;
+    for (int e = tid; !a.resident && e < E; e += kPolThreads) nxt.map[e] = L.map[e];
+    for (int s = tid; !a.resident && s < N; s += kPolThreads) {
+        nxt.owner[s] = L.owner[s];
+        nxt.fre[s] = L.fre[s];
+        nxt.key[s] = L.key[s];
+        nxt.use[s] = L.use[s];
+        nxt.prot[s] = L.prot[s];
+    }
+    if (tid < 3 && !a.resident) nxt.meta[tid] = L.misc[tid];
+    for (int j = tid; d.path == PATH_POOL && j < d.nmiss; j += kPolThreads) {
+        const int e = L.list[j];
+        a.ds.rec[4 + 3 * j] = e;
+        a.ds.rec[5 + 3 * j] = L.map[e];
+        a.ds.rec[6 + 3 * j] = L.mev[j];
+    }
+    if (tid == 0) {
+        *a.path = d.path;
+        a.ds.rec[0] = d.path;
+        a.ds.rec[1] = d.D;
+        a.ds.rec[2] = d.path == PATH_POOL ? d.nmiss : 0;
+        a.ds.rec[3] = d.path == PATH_NONE ? 1 : 0;
+        unsigned long long* ctr = a.ds.ctr;
+        if (d.path == PATH_NONE) {
+            __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        } else if (d.path == PATH_STAGE) {
+            pol_bump(ctr + 0, 1);
+            pol_bump(ctr + 3, 1);
+            pol_bump(ctr + 4, (unsigned long long)d.D * a.eb);
+            pol_bump(ctr + 5, (unsigned long long)d.D);
+        } else {
+            pol_bump(ctr + 0, 1);
+            pol_bump(ctr + 1, (unsigned long long)d.hits);
+            if (d.nmiss) {
+                pol_bump(ctr + 2, (unsigned long long)d.nmiss);
+                pol_bump(ctr + 4, (unsigned long long)d.nmiss * a.eb);
+            }
+        }
+        if (a.timed_jobs) {
+            const int nlink = d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0);
+            __hip_atomic_store(a.timed_jobs, nlink, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
+// A workgroup of a prepare launch has read everything it reads of the current state
+// copy: it counts itself in (one thread, after the workgroup's reads have returned);
+// pol_last_reader, called at the end of the workgroup with the returned count, lets
+// the last one of the launch make the other copy current.  Nothing of the launch
+// reads the current copy after that, and the lead's writes to the other copy are
+// complete when the launch is.  (The count is read back only at the end, so its
+// round trip overlaps the workgroup's work.)
+__device__ __forceinline__ int pol_reader_arrive(int32_t* ctl) {
+    return __hip_atomic_fetch_add(&ctl[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void pol_last_reader(int32_t* ctl, int old, int nblocks) {
+    if (old == nblocks - 1) {
+        __hip_atomic_store(&ctl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int par = __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl[0], par ^ 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The device-mapped store address of expert e.
+__device__ __forceinline__ const char* pol_store_at(const PolicyArgs& a, int e) {
+    return a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * a.eb;
+}
+
+}  // namespace moe

@@ -76,9 +76,19 @@ typedef int32_t moe_status_t;
 #define MOE_POLICY_HOST   0  /* on the host: prepare reads the step's distinct ids back
                                 (one sync per layer) and returns the path and misses */
 #define MOE_POLICY_DEVICE 1  /* on the GPU: prepare and step only queue work (a kernel runs
-                                the same LRU on device-resident state, a copy kernel pulls
+                                the same slot manager on device-resident state and pulls
                                 the misses); the path and misses of a step are read later
                                 with moe_pool_last_step */
+/* eviction policy: which resident expert a miss replaces ([vLLM-cache] review thread:
+   the four policies it lists).  The victim is always a resident expert the step has
+   not yet processed; among those: */
+#define MOE_EVICT_LRU  0  /* the least recently used (default; the policy the PR ships) */
+#define MOE_EVICT_FIFO 1  /* the earliest inserted */
+#define MOE_EVICT_LFU  2  /* the fewest uses since insertion, then the least recently used */
+#define MOE_EVICT_SLRU 3  /* segmented LRU: a miss enters a probationary segment, a hit there
+                             promotes to a protected segment of (4 N) / 5 experts (its
+                             oldest is demoted back when it overflows); victims come from
+                             the probationary segment first */
 /* path a step took */
 #define MOE_PATH_POOL     0
 #define MOE_PATH_FALLBACK 1
@@ -115,14 +125,17 @@ typedef struct {
     int32_t policy;         /* MOE_POLICY_HOST (0) or MOE_POLICY_DEVICE (1, n_experts <=
                                2048, copies by the copy kernel on the compute stream).
                                Both give the same slot ids, misses, counters and bits. */
-    int32_t read_through;   /* 1 (device policy, not resident): a one-token moe_pool_step
-                               copies nothing before its forward; the forward's kernels
-                               read each missed or staged expert from the pinned store and
-                               write a missed one through to its slot as they read it, so
-                               the step's compute overlaps its transfers.  Slot bytes,
-                               counters and outputs are those of the copying step.  0: the
-                               step's experts are copied first (prepare + forward always
-                               copy). */
+    int32_t read_through;   /* 1 (device policy): a one-token moe_pool_step is two launches.
+                               The first runs the decision in its own workgroups and the
+                               w13 GEMV: a missed expert's w13 rows are read from the
+                               pinned store and written through to its slot by the GEMV
+                               blocks, while copy workers of the same launch move the
+                               rest of it (a staged expert likewise goes to staging), so
+                               the hit experts' compute and the miss transfers overlap.
+                               The second is the w2 GEMV + combine.  Slot bytes, counters
+                               and outputs are those of the copying step.  0: the step's
+                               experts are copied first (prepare + forward always copy). */
+    int32_t evict;          /* MOE_EVICT_* (non-LRU policies need MOE_POLICY_DEVICE) */
 } moe_pool_config_t;
 
 typedef struct {
@@ -151,6 +164,8 @@ typedef struct {
 } moe_pool_timing_t;
 
 /* ---- errors -------------------------------------------------------------- */
+/* A fixed message for a status code (overflow is not one of them: it is the
+ * fallback path, [llama-pool] "Why not the other approaches on the table"). */
 const char* moe_strerror(moe_status_t s);
 /* Message for the calling thread's most recent failing call (static storage). */
 const char* moe_last_error(void);
@@ -171,10 +186,13 @@ size_t moe_expert_bytes(int32_t wtype, int32_t hidden, int32_t inter);
  * hbm_budget_bytes, when set, caps the HBM part ([llama-pool] Design item 4).
  * Errors: EINVAL (bad config), ENOMEM, EHIP. */
 moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_pool_t** out);
+/* Frees everything moe_pool_create allocated, after the pool's queued work; NULL is
+ * accepted.  The caller's buffers are not touched. */
 void moe_pool_destroy(moe_pool_t* pool);
 
 /* Copies one expert's bytes from `host_src` (moe_expert_bytes bytes) into the
- * pinned store ([vLLM-cache] "CPUBackingStore -- pinned DRAM, all local experts").
+ * pinned store ([vLLM-cache] "Architecture": the pinned host backing store that
+ * holds every expert of the layer).
  * In resident mode the bytes go straight to HBM slot `expert` instead.  If the expert
  * is currently resident in a slot, that slot is not refreshed: load experts before
  * the first prepare.  Byte layout (regions in order, each on a 256-byte boundary):
@@ -188,8 +206,10 @@ void moe_pool_destroy(moe_pool_t* pool);
 moe_status_t moe_pool_load_expert(moe_pool_t* pool, int32_t layer, int32_t expert,
                                   const void* host_src, size_t nbytes);
 
-/* Returns the pool to cold: every map entry -1, all slots free, LRU empty,
- * counters zero (resident mode: counters only).  Slot bytes are not cleared. */
+/* Returns the pool to cold ([vLLM-cache] "How it works": the cache state the first
+ * prepare starts from): every map entry -1, all slots free, eviction order empty,
+ * counters zero (resident mode: counters only).  Slot bytes are not cleared.
+ * Errors: EINVAL, EHIP. */
 moe_status_t moe_pool_reset(moe_pool_t* pool);
 
 /* ---- the step --------------------------------------------------------------- */
@@ -216,9 +236,12 @@ moe_status_t moe_pool_reset(moe_pool_t* pool);
  * highest index down; a non-resident expert maps to -1.
  * Errors: EINVAL, ERANGE (an id outside [0,E): nothing changes), EHIP.
  *
- * Under MOE_POLICY_DEVICE prepare only queues two kernels on the compute stream (the
- * slot manager, then the copy kernel) and returns: *n_miss and *path are set to -1
- * and miss_host is not written (moe_pool_last_step reads them later).  An id outside
+ * Under MOE_POLICY_DEVICE prepare is asynchronous: it queues one launch on the compute
+ * stream (the decision, the remap and the copies; [llama-pool] "Limitations" names the
+ * per-layer readback as the cost this removes) and returns at once.  The step's path
+ * and miss list -- the same values the host policy returns here -- are a record the
+ * launch leaves in device memory: *n_miss and *path are set to -1, miss_host is not
+ * written, and moe_pool_last_step returns the record after waiting for the step.  An id outside
  * [0,E) is found on the GPU: that step changes nothing and writes -1 slot ids;
  * moe_pool_last_step and moe_pool_sync report it as ERANGE, and so does any later
  * prepare/step on the layer that runs after the GPU has flagged it.  A forward must
@@ -270,21 +293,30 @@ moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_
 moe_status_t moe_pool_last_step(moe_pool_t* pool, int32_t layer, int32_t* path, moe_miss_t* miss_host,
                                 int32_t miss_cap, int32_t* n_miss);
 
-/* Waits until all of the pool's copies and kernels issued so far are complete.
+/* Waits until all of the pool's copies and kernels issued so far are complete
+ * ([prefetch]: the compute stream joins the copy stream before results are used).
  * Under MOE_POLICY_DEVICE it then reports (and clears) an out-of-range id found by
- * a queued step (ERANGE). */
+ * a queued step (ERANGE).  Errors: EINVAL, EHIP, ERANGE. */
 moe_status_t moe_pool_sync(moe_pool_t* pool);
 
 /* ---- introspection (tests, benchmarks) ------------------------------------ */
-/* layer = -1 sums over layers. */
+/* The hit / miss counters of [vLLM-cache] "How it works" (hits and misses counted per
+ * distinct expert of a step) and the fallback count of [llama-pool] "Design" item 2.
+ * layer = -1 sums over layers.  Under MOE_POLICY_DEVICE it waits for queued work.
+ * Errors: EINVAL, EHIP. */
 moe_status_t moe_pool_get_stats(const moe_pool_t* pool, int32_t layer, moe_pool_stats_t* out);
-/* map_E: int32[E] expert -> slot or -1; owner_N: int32[N] slot -> expert or -1;
- * lru_N: int32[N] resident experts least recently used first, -1 padded.
- * Any pointer may be NULL. */
+/* The slot manager's state ([vLLM-cache] review thread: the persistent expert -> slot
+ * mapping and the cache's eviction order).  map_E: int32[E] expert -> slot or -1;
+ * owner_N: int32[N] slot -> expert or -1; lru_N: int32[N] resident experts in the
+ * order the layer's policy would evict them (LRU: least recently used first), -1
+ * padded.  Any pointer may be NULL.  Under MOE_POLICY_DEVICE it waits for queued
+ * work.  Errors: EINVAL, EHIP. */
 moe_status_t moe_pool_get_state(const moe_pool_t* pool, int32_t layer, int32_t* map_E,
                                 int32_t* owner_N, int32_t* lru_N);
-/* Synchronously copies n bytes (<= one expert) of HBM slot `slot` of `layer`
- * (slot < 0: staging entry -slot-1) into host_dst, after the pool's queued work. */
+/* Test hook for the slot-contents check of [vLLM-cache] "Test results" (a slot holds
+ * its expert's bytes after eviction and reload): synchronously copies n bytes
+ * (<= one expert) of HBM slot `slot` of `layer` (slot < 0: staging entry -slot-1)
+ * into host_dst, after the pool's queued work.  Errors: EINVAL, EHIP. */
 moe_status_t moe_pool_read_slot(moe_pool_t* pool, int32_t layer, int32_t slot,
                                 void* host_dst, size_t n);
 /* Device address of slot `slot` of `layer` (constant for the pool's lifetime). */
