@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 DECODE_MAX_TOKENS = 8            # larger ubatches take the grouped MFMA path (bf16)
 GRAPH_WARM = 3                   # untimed replays after a capture (--graph)
+PF_AFTER_LAYER, PF_AFTER_QUEUED, PF_AFTER_PREVIOUS = 0, 1, 2   # moe_pool_prefetch start points
 
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
@@ -81,6 +82,13 @@ def parse():
                     help="device policy, one token per step: capture one decode token (every layer's "
                          "step) in a HIP graph and time its replays; the kernel and link figures then "
                          "come from event-timed eager warm-up steps (a capture cannot hold them)")
+    ap.add_argument("--prefetch-accuracy", type=float, default=None,
+                    help="cross-layer prefetch with a stand-in predictor that is right for this fraction of "
+                         "(step, layer) id rows (default: no prefetch)")
+    ap.add_argument("--prefetch-distance", type=int, default=1,
+                    help="layers ahead that a layer's predicted experts are prefetched")
+    ap.add_argument("--prefetch-slots", type=int, default=None,
+                    help="prefetch entries per layer (default: 2 x top_k, at most 64)")
     ap.add_argument("--no-timing", action="store_true", help="no HIP events around kernels")
     ap.add_argument("--timing-every", type=int, default=7,
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
@@ -174,7 +182,7 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
     needs."""
     if not args.graph:
         return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
-    if args.policy != "device" or resident or wl.tokens != 1 or args.read_through:
+    if args.policy != "device" or resident or wl.tokens != 1:
         raise SystemExit("--graph needs the device policy, a pooled stack and one token per step")
     with torch.cuda.stream(torch.cuda.Stream()):
         return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
@@ -183,13 +191,16 @@ def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
 def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
     dev = torch.device("cuda:0")
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
+    prefetch = args.prefetch_accuracy is not None and slots > 0 and not resident
+    pf_slots = (args.prefetch_slots or min(64, 2 * K)) if prefetch else 0
     t0 = time.perf_counter()
     pool = binding.MoePool(layers=L, experts=E, top_k=K, hidden=H, inter=I, slots=slots,
                            wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
                            max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20, copy_engine=args.copy_engine,
                            policy=args.policy, read_through=bool(args.read_through) and args.policy == "device"
-                           and not resident, timing=0 if args.no_timing else args.timing_every)
+                           and not resident, timing=0 if args.no_timing else args.timing_every,
+                           prefetch_slots=pf_slots)
     eb = pool.expert_nbytes
     if resident:
         buf = np.empty(eb, np.uint8)
@@ -213,10 +224,27 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
     L_ = binding.lib()
     h = pool._h
 
+    if prefetch:
+        pred_d = torch.from_numpy(synth.predictions(wl, trace, args.prefetch_accuracy)).to(dev)
+        pred_p = pred_d.data_ptr()
+        dist = max(1, args.prefetch_distance)
+
     def run(s0, n):
         for s in range(s0, s0 + n):
             x = x_p + s * x_stride
+            if prefetch:
+                # the first layers' predictions are issued at the start of the token; each
+                # copy may start once its layer's last step is done
+                for l in range(min(dist, L)):
+                    st = L_.moe_pool_prefetch(h, l, pred_p + (s * L + l) * ids_stride, T, PF_AFTER_LAYER)
+                    if st:
+                        binding._check(st)
             for l in range(L):
+                if prefetch and l + dist < L:
+                    st = L_.moe_pool_prefetch(h, l + dist, pred_p + (s * L + l + dist) * ids_stride, T,
+                                              PF_AFTER_LAYER)
+                    if st:
+                        binding._check(st)
                 out = buf_p[l & 1]
                 st = L_.moe_pool_step(h, l, ids_p + (s * L + l) * ids_stride, T, slot_p + l * ids_stride,
                                       x, w_p + (s * L + l) * ids_stride, x, out, None, 0, None, None)
@@ -232,9 +260,25 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
         w_s = torch.empty((L, T, K), dtype=torch.float32, device=dev)
         x_s = torch.empty((T, H), dtype=adt, device=dev)
 
+        if prefetch:
+            pred_s = torch.empty((L, T, K), dtype=torch.int32, device=dev)
+
         def record():
             x = x_s.data_ptr()
+            if prefetch:
+                # the capture forks the copy stream once, at its start; a replay runs after
+                # the previous one has finished, so every later copy follows the previous one
+                for l in range(min(dist, L)):
+                    st = L_.moe_pool_prefetch(h, l, pred_s.data_ptr() + l * ids_stride, T,
+                                              PF_AFTER_QUEUED if l == 0 else PF_AFTER_PREVIOUS)
+                    if st:
+                        binding._check(st)
             for l in range(L):
+                if prefetch and l + dist < L:
+                    st = L_.moe_pool_prefetch(h, l + dist, pred_s.data_ptr() + (l + dist) * ids_stride, T,
+                                              PF_AFTER_PREVIOUS)
+                    if st:
+                        binding._check(st)
                 out = buf_p[l & 1]
                 st = L_.moe_pool_step(h, l, ids_s.data_ptr() + l * ids_stride, T, slot_p + l * ids_stride,
                                       x, w_s.data_ptr() + l * ids_stride, x, out, None, 0, None, None)
@@ -247,6 +291,8 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
                 ids_s.copy_(ids_d[s])
                 w_s.copy_(ws_d[s])
                 x_s.copy_(xs_d[s])
+                if prefetch:
+                    pred_s.copy_(pred_d[s])
                 g.replay()
 
     torch.cuda.synchronize()
@@ -311,6 +357,12 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
            "fallback_steps": d["fallbacks"], "staged_experts": d["staged"],
            "h2d_gb": round(d["bytes_h2d"] / 1e9, 3),
            "readback_wait_ms_per_step": round(tm["sync_wait_ms"] / args.steps, 4)}
+    if prefetch:
+        res["prefetch"] = {"predictor_accuracy": args.prefetch_accuracy, "distance": max(1, args.prefetch_distance),
+                           "slots": pf_slots, "served_from_prefetch_per_token": round(d["prefetched"] / tokens, 4),
+                           "prefetch_gb": round(d["prefetch_bytes"] / 1e9, 3),
+                           "predictor": "stand-in: the trace's own ids of the (step, layer) with this "
+                                        "probability, else an independent trace's"}
     if tm["copy_ms"] > 0:
         res["link_gbps_misses"] = round(tm["copy_bytes"] / (tm["copy_ms"] * 1e-3) / 1e9, 2)
         res["miss_batch_bytes"] = int(tm["copy_bytes"] // max(1, tm["copy_calls"]))
@@ -410,7 +462,7 @@ def main():
                    "resident": args.resident, "copy_streams": args.copy_streams,
                    "copy_engine": args.copy_engine, "policy": args.policy,
                    "read_through": bool(args.read_through) and args.policy == "device" and not args.resident,
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "prefetch_accuracy": args.prefetch_accuracy},
     }
     for k, v in main_res.items():
         if k not in ("value", "ms_per_step", "slots", "roofline"):

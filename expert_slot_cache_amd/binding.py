@@ -31,6 +31,7 @@ POLICY_HOST, POLICY_DEVICE = 0, 1
 POLICIES = {"host": POLICY_HOST, "device": POLICY_DEVICE}
 EVICT_LRU, EVICT_FIFO, EVICT_LFU, EVICT_SLRU = 0, 1, 2, 3
 EVICTS = {"lru": EVICT_LRU, "fifo": EVICT_FIFO, "lfu": EVICT_LFU, "slru": EVICT_SLRU}
+PREFETCH_AFTER = {"layer": 0, "queued": 1, "previous": 2}
 
 
 class MoeError(RuntimeError):
@@ -54,7 +55,7 @@ class Config(C.Structure):
                 ("resident", C.c_int32), ("max_tokens", C.c_int32), ("n_copy_streams", C.c_int32),
                 ("copy_chunk_bytes", C.c_size_t), ("hbm_budget_bytes", C.c_size_t),
                 ("timing", C.c_int32), ("copy_engine", C.c_int32), ("policy", C.c_int32),
-                ("read_through", C.c_int32), ("evict", C.c_int32)]
+                ("read_through", C.c_int32), ("evict", C.c_int32), ("prefetch_slots", C.c_int32)]
 
 
 class Miss(C.Structure):
@@ -63,7 +64,8 @@ class Miss(C.Structure):
 
 class Stats(C.Structure):
     _fields_ = [("steps", C.c_uint64), ("hits", C.c_uint64), ("misses", C.c_uint64),
-                ("fallbacks", C.c_uint64), ("bytes_h2d", C.c_uint64), ("staged", C.c_uint64)]
+                ("fallbacks", C.c_uint64), ("bytes_h2d", C.c_uint64), ("staged", C.c_uint64),
+                ("prefetched", C.c_uint64), ("prefetch_bytes", C.c_uint64)]
 
 
 class Timing(C.Structure):
@@ -89,6 +91,7 @@ _SIGS = {
     "moe_pool_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, C.POINTER(Miss), _I32, _PI32,
                              _PI32]),
     "moe_pool_sync": (_I32, [_P]),
+    "moe_pool_prefetch": (_I32, [_P, _I32, _P, _I32, _I32]),
     "moe_pool_last_step": (_I32, [_P, _I32, _PI32, C.POINTER(Miss), _I32, _PI32]),
     "moe_pool_get_stats": (_I32, [_P, _I32, C.POINTER(Stats)]),
     "moe_pool_get_state": (_I32, [_P, _I32, _P, _P, _P]),
@@ -169,12 +172,12 @@ class MoePool:
                  resident: bool = False, max_tokens: int = 1, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, hbm_budget_bytes: int = 0, timing: int = 0,
                  copy_engine: str = "kernel", policy: str = "host", read_through: bool = False,
-                 evict: str = "lru", stream=None):
+                 evict: str = "lru", prefetch_slots: int = 0, stream=None):
         self._h = None
         cfg = Config(layers, experts, top_k, hidden, inter, slots, WTYPES[wtype], ATYPES[atype],
                      RULES[rule], int(bool(resident)), max_tokens, copy_streams,
                      copy_chunk_bytes, hbm_budget_bytes, int(timing), COPY_ENGINES[copy_engine],
-                     POLICIES[policy], int(bool(read_through)), EVICTS[evict])
+                     POLICIES[policy], int(bool(read_through)), EVICTS[evict], int(prefetch_slots))
         if stream is None:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -250,6 +253,14 @@ class MoePool:
 
     def sync(self):
         _check(lib().moe_pool_sync(self._h))
+
+    def prefetch(self, layer: int, predicted_ids, n_tokens: int, after: str = "queued"):
+        """Hint: the next step of `layer` will use these ids (int32 [n_tokens, top_k] on
+        the device); predicted experts the layer does not hold are copied into its
+        prefetch buffer on a copy stream, starting after everything queued on the compute
+        stream ("queued"), after the layer's last step ("layer") or after the previous
+        prefetch ("previous")."""
+        _check(lib().moe_pool_prefetch(self._h, layer, _ptr(predicted_ids), n_tokens, PREFETCH_AFTER[after]))
 
     def last_step(self, layer: int):
         """(path, misses) of the layer's last prepare/step (waits for it under the

@@ -848,7 +848,7 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
             const int e = L.list[j];
             const size_t off = tail_off + (u - (size_t)j * upj) * kUnit;
             const size_t nvec = (eb - off < kUnit ? eb - off : kUnit) / 16;
-            const u32x4c* __restrict__ s4 = reinterpret_cast<const u32x4c*>(pol_store_at(pa, e) + off);
+            const u32x4c* __restrict__ s4 = reinterpret_cast<const u32x4c*>(pol_src(pa, e) + off);
             u32x4c* __restrict__ d4 =
                 reinterpret_cast<u32x4c*>((pool ? pa.slots + (size_t)L.map[e] * eb : pa.staging + (size_t)j * eb) + off);
             for (size_t i0 = tid; i0 < nvec; i0 += 4 * 256) {
@@ -874,10 +874,10 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
     } else if (d.path == PATH_POOL) {
         const int slot = __builtin_amdgcn_readfirstlane(pa.resident ? e : L.map[e]);
         const bool miss = !pa.resident && __builtin_amdgcn_readfirstlane(L.rank[e]) < 0;
-        pin = miss ? PairIn{pol_store_at(pa, e), pa.slots + (size_t)slot * stride, true}
+        pin = miss ? PairIn{pol_src(pa, e), pa.slots + (size_t)slot * stride, true}
                    : PairIn{pa.slots + (size_t)slot * stride, nullptr, true};
     } else if (d.path == PATH_STAGE) {
-        pin = PairIn{pol_store_at(pa, e), nullptr, true};
+        pin = PairIn{pol_src(pa, e), nullptr, true};
     }
     w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, 0, k, rblk, red, dyn + xs_off);
 }

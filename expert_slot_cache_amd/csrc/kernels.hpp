@@ -168,11 +168,36 @@ struct PolicyArgs {
     char* slots;             // the layer's slot pool
     char* staging;           // the staging area
     int32_t* timed_jobs;     // host-mapped, or null: experts the step moves over the link
+    // the layer's prefetch buffer (pf_n = 0: none): pf_n entries of eb bytes at pf_buf,
+    // entry j holding an exact copy of expert pf_tag[j] (-1: nothing); a missed or staged
+    // expert found there is read from it instead of over the host link
+    const int32_t* pf_tag;
+    char* pf_buf;
+    int pf_n;
 };
 // Dynamic LDS of the decision for E experts and N slots.
 size_t policy_lds_bytes(int E, int N);
 // grid: workgroups of the launch (the per-id outputs and the copies spread over them).
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
+
+// Prefetch of predicted experts for a layer's next step ([vLLM-cache] planned async
+// H2D with cross-layer prediction; [prefetch]: copies on a copy stream, joined by an
+// event before the layer runs), one launch: the predicted ids' distinct experts that
+// the layer's current state copy does not hold, ascending, at most pf_n, are copied
+// into entries 0, 1, ... and tagged.
+struct PrefetchArgs {
+    const int32_t* ids;      // [n] predicted top-k ids (1 <= n <= 256)
+    int n;
+    int E, N;
+    DevState ds;             // the layer's slot-manager state (map of the current copy)
+    int32_t* tag;            // [pf_n]
+    char* buf;               // pf_n entries of eb bytes
+    int pf_n;                // 1..64
+    const char* const* pieces;
+    int per_piece;
+    unsigned long long eb;
+};
+hipError_t launch_prefetch(const PrefetchArgs& a, int copy_grid, hipStream_t s);
 
 // The one-token decode step in two launches (read-through misses): the first runs the
 // decision in every workgroup that needs it, the w13 GEMV + SwiGLU (a missed expert's

@@ -115,6 +115,8 @@ constexpr int kPolicyGrid = 128;
 // Copy workers of a fused one-token step (the part of each missed expert past its w13
 // rows, 64 KiB units).
 constexpr int kStepCopyWorkers = 64;
+// Workgroups of a prefetch's copy launch.
+constexpr int kPrefetchGrid = 64;
 
 struct LayerState {
     moe::SlotLRU lru;
@@ -146,6 +148,14 @@ struct LayerState {
     char* dev_block = nullptr;
     moe::DevState ds{};
     bool rt_sample = false;      // the pending w13/w2 timing sample is a read-through step
+    // prefetch buffer (prefetch_slots entries), its tags and job list (device), and the
+    // event the next step of the layer waits for
+    char* pf_buf = nullptr;
+    int32_t* pf_tag = nullptr;
+    hipEvent_t pf_done = nullptr;
+    bool pf_pending = false;
+    hipEvent_t step_done = nullptr;   // after the layer's last prepare or step
+    bool stepped = false;
     const char** pieces_dev = nullptr;
     bool last_empty = false;     // the last step had no tokens (not seen by the GPU)
     uint64_t empty_steps = 0;    // steps with no tokens (counted on the host)
@@ -163,6 +173,7 @@ struct moe_pool {
     hipStream_t compute = nullptr;
     std::vector<hipStream_t> copy;
     std::vector<hipEvent_t> copy_done;
+    hipEvent_t pf_issue = nullptr;  // compute-stream point a prefetch starts after
     std::vector<LayerState> layers;
     char* staging = nullptr;
     int32_t staging_cap = 0;
@@ -215,6 +226,10 @@ void destroy_pool(moe_pool* p) {
         if (L.upd_host) (void)hipHostFree(L.upd_host);
         if (L.dev_block) (void)hipFree(L.dev_block);
         if (L.pieces_dev) (void)hipFree(L.pieces_dev);
+        if (L.pf_buf) (void)hipFree(L.pf_buf);
+        if (L.pf_tag) (void)hipFree(L.pf_tag);
+        if (L.pf_done) (void)hipEventDestroy(L.pf_done);
+        if (L.step_done) (void)hipEventDestroy(L.step_done);
         if (L.fill_t.a) (void)hipEventDestroy(L.fill_t.a);
         if (L.fill_t.b) (void)hipEventDestroy(L.fill_t.b);
         for (auto& t : L.copy_t) {
@@ -228,6 +243,7 @@ void destroy_pool(moe_pool* p) {
     }
     for (auto s : p->copy) (void)hipStreamDestroy(s);
     for (auto e : p->copy_done) (void)hipEventDestroy(e);
+    if (p->pf_issue) (void)hipEventDestroy(p->pf_issue);
     if (p->staging) (void)hipFree(p->staging);
     if (p->rb_host) (void)hipHostFree(p->rb_host);
     if (p->rank_dev) (void)hipFree(p->rank_dev);
@@ -688,13 +704,37 @@ moe::PolicyArgs policy_args(moe_pool* p, LayerState& L, int32_t layer, const int
     a.per_piece = L.per_piece;
     a.slots = L.slots;
     a.staging = p->staging;
+    a.pf_tag = L.pf_tag;
+    a.pf_buf = L.pf_buf;
+    a.pf_n = L.pf_buf ? p->cfg.prefetch_slots : 0;
     return a;
+}
+
+// A step of the layer starts after the layer's last prefetch (the join of the copy
+// stream into the compute stream).
+moe_status_t join_prefetch(moe_pool* p, LayerState& L) {
+    if (!L.pf_pending) return MOE_OK;
+    HIPCHK(hipStreamWaitEvent(p->compute, L.pf_done, 0));
+    L.pf_pending = false;
+    return MOE_OK;
+}
+
+// Every prefetch tag of the layer back to "nothing held".
+moe_status_t clear_prefetch(moe_pool* p, LayerState& L) {
+    if (!L.pf_tag) return MOE_OK;
+    L.stepped = false;
+    const std::vector<int32_t> none(p->cfg.prefetch_slots, -1);
+    HIPCHK(hipMemcpy(L.pf_tag, none.data(), none.size() * 4, hipMemcpyHostToDevice));
+    L.pf_pending = false;
+    return MOE_OK;
 }
 
 // Queue the slot manager with its copies for one step (n_tokens >= 1).
 moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_t* ids_dev, int32_t n_tokens,
                          int32_t* slot_ids_dev) {
     const bool resident = p->cfg.resident != 0;
+    moe_status_t st = join_prefetch(p, L);
+    if (st) return st;
     moe::PolicyArgs a = policy_args(p, L, layer, ids_dev, n_tokens, slot_ids_dev);
     // the copy span of a timed step is the launch's (its decision takes a few us)
     const bool timed = !resident && p->cfg.timing > 0 &&
@@ -704,6 +744,10 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
     const int grid = resident ? std::max(1, std::min(kPolicyGrid, a.n / 256)) : kPolicyGrid;
     HIPCHK(moe::launch_policy(a, grid, timed ? L.fill_t.a : nullptr, timed ? L.fill_t.b : nullptr, p->compute));
     if (timed) L.fill_t.pending = true;
+    if (L.step_done) {
+        HIPCHK(hipEventRecord(L.step_done, p->compute));
+        L.stepped = true;
+    }
     L.prepared = true;
     L.prep_tokens = n_tokens;
     L.prep_path = -1;            // known on the GPU only
@@ -714,6 +758,7 @@ moe_status_t dev_prepare(moe_pool* p, LayerState& L, int32_t layer, const int32_
 
 template <class T>
 moe_status_t dev_read(const moe_pool* p, T* dst, const void* src, size_t n) {
+    for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));   // a prefetch counts its bytes
     HIPCHK(hipStreamSynchronize(p->compute));
     HIPCHK(hipMemcpy(dst, src, n * sizeof(T), hipMemcpyDeviceToHost));
     return MOE_OK;
@@ -761,6 +806,9 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.read_through != 0 && c.read_through != 1) FAIL(MOE_EINVAL, "read_through %d invalid", c.read_through);
     if (c.read_through && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "read_through needs the device policy");
     if (c.evict < MOE_EVICT_LRU || c.evict > MOE_EVICT_SLRU) FAIL(MOE_EINVAL, "evict %d invalid", c.evict);
+    if (c.prefetch_slots < 0 || c.prefetch_slots > 64) FAIL(MOE_EINVAL, "prefetch_slots %d outside [0,64]", c.prefetch_slots);
+    if (c.prefetch_slots && (c.policy != MOE_POLICY_DEVICE || c.resident))
+        FAIL(MOE_EINVAL, "prefetch needs the device policy and a pool (not the all-resident mode)");
     if (c.evict != MOE_EVICT_LRU && c.policy != MOE_POLICY_DEVICE)
         FAIL(MOE_EINVAL, "the host slot manager implements LRU only; evict %d needs the device policy", c.evict);
     if (c.policy == MOE_POLICY_DEVICE && c.n_experts > 2048)
@@ -803,8 +851,8 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     const size_t y_bytes = (size_t)c.max_tokens * c.top_k * c.hidden * sizeof(float);
     p->grp_slots = std::max(p->nslot_alloc, p->staging_cap);
     const size_t grp_bytes = moe::grouped_index_bytes(c.max_tokens, c.top_k, std::max(1, p->grp_slots));
-    const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4) + (size_t)p->staging_cap * eb + act_bytes +
-                       y_bytes + grp_bytes + (size_t)E * 8;
+    const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4 + (size_t)c.prefetch_slots * eb) +
+                       (size_t)p->staging_cap * eb + act_bytes + y_bytes + grp_bytes + (size_t)E * 8;
     if (c.hbm_budget_bytes && hbm > c.hbm_budget_bytes) {
         delete p;
         FAIL(MOE_ENOMEM, "pool needs %zu HBM bytes, budget is %zu", hbm, c.hbm_budget_bytes);
@@ -906,7 +954,19 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
                 CREATE_HIP(hipEventCreateWithFlags(&L.fill_t.a, tflag));
                 CREATE_HIP(hipEventCreateWithFlags(&L.fill_t.b, tflag));
             }
+            if (c.prefetch_slots) {
+                CREATE_HIP(hipMalloc((void**)&L.pf_buf, (size_t)c.prefetch_slots * eb));
+                CREATE_HIP(hipMalloc((void**)&L.pf_tag, (size_t)c.prefetch_slots * 4));
+                CREATE_HIP(hipEventCreateWithFlags(&L.pf_done, hipEventDisableTiming));
+                CREATE_HIP(hipEventCreateWithFlags(&L.step_done, hipEventDisableTiming));
+                const moe_status_t cst = clear_prefetch(p, L);
+                if (cst) {
+                    destroy_pool(p);
+                    return cst;
+                }
+            }
         }
+        if (c.prefetch_slots) CREATE_HIP(hipEventCreateWithFlags(&p->pf_issue, hipEventDisableTiming));
         CREATE_HIP(hipHostMalloc((void**)&p->errs_host, sizeof(uint32_t) * c.n_layers,
                                  hipHostMallocCoherent | hipHostMallocMapped));
         CREATE_HIP(hipHostGetDevicePointer((void**)&p->errs_dev, p->errs_host, 0));
@@ -950,6 +1010,12 @@ moe_status_t moe_pool_load_expert(moe_pool_t* p, int32_t layer, int32_t expert, 
         HIPCHK(hipMemcpy(L.slots + (size_t)expert * p->lay.total, host_src, nbytes, hipMemcpyHostToDevice));
     else
         std::memcpy(L.expert(expert, p->lay.total), host_src, nbytes);
+    // a prefetched copy of the old bytes must not be used
+    if (L.pf_tag) {
+        HIPCHK(hipStreamSynchronize(p->compute));
+        const moe_status_t st2 = clear_prefetch(p, L);
+        if (st2) return st2;
+    }
     return MOE_OK;
 }
 
@@ -967,6 +1033,10 @@ moe_status_t moe_pool_reset(moe_pool_t* p) {
     }
     p->staging_owner = -1;
     p->last_prepared = -1;
+    for (auto& L : p->layers) {
+        const moe_status_t cst = clear_prefetch(p, L);
+        if (cst) return cst;
+    }
     if (p->cfg.policy == MOE_POLICY_DEVICE) return dev_init_layers(p);
     return MOE_OK;
 }
@@ -1073,6 +1143,8 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
         if (path) *path = -1;
         const bool timed = p->cfg.timing > 0 && (p->n_forwards++ % (uint64_t)p->cfg.timing) == 0 &&
                            !L.w13_t.pending && !L.w2_t.pending;
+        st = join_prefetch(p, L);
+        if (st) return st;
         moe::PolicyArgs pa = policy_args(p, L, layer, topk_ids_dev, 1, slot_ids_dev);
         pa.timed_jobs = timed && p->rt_jobs_dev ? p->rt_jobs_dev + layer : nullptr;
         moe::ForwardArgs a = forward_args(p, L, x_dev, slot_ids_dev, topk_w_dev, resid_dev, 1, out_dev);
@@ -1084,6 +1156,10 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
             ev.w2_stop = L.w2_t.b;
         }
         HIPCHK(moe::launch_step_decode(p->geom, pa, a, kStepCopyWorkers, timed ? &ev : nullptr, p->compute));
+        if (L.step_done) {
+            HIPCHK(hipEventRecord(L.step_done, p->compute));
+            L.stepped = true;
+        }
         if (timed) {
             L.w13_t.pending = true;
             L.w2_t.pending = true;
@@ -1101,6 +1177,42 @@ moe_status_t moe_pool_step(moe_pool_t* p, int32_t layer, const int32_t* topk_ids
                                        path);
     if (st) return st;
     return moe_pool_forward(p, layer, x_dev, slot_ids_dev, topk_w_dev, resid_dev, n_tokens, out_dev);
+}
+
+moe_status_t moe_pool_prefetch(moe_pool_t* p, int32_t layer, const int32_t* predicted_ids_dev, int32_t n_tokens,
+                               int32_t after) {
+    moe_status_t st = check_layer(p, layer);
+    if (st) return st;
+    LayerState& L = p->layers[layer];
+    if (!L.pf_buf) FAIL(MOE_EINVAL, "the pool has no prefetch buffer (prefetch_slots = 0)");
+    const int64_t n = (int64_t)n_tokens * p->cfg.top_k;
+    if (n_tokens < 1 || n > 256) FAIL(MOE_EINVAL, "prefetch of %d tokens x top_k %d: need 1..256 ids", n_tokens, p->cfg.top_k);
+    if (!predicted_ids_dev) FAIL(MOE_EINVAL, "null ids");
+    if (after < MOE_PREFETCH_AFTER_LAYER || after > MOE_PREFETCH_AFTER_PREVIOUS) FAIL(MOE_EINVAL, "after %d invalid", after);
+    moe::PrefetchArgs a{};
+    a.ids = predicted_ids_dev;
+    a.n = (int)n;
+    a.E = p->cfg.n_experts;
+    a.N = p->cfg.n_slots;
+    a.ds = L.ds;
+    a.tag = L.pf_tag;
+    a.buf = L.pf_buf;
+    a.pf_n = p->cfg.prefetch_slots;
+    a.pieces = L.pieces_dev;
+    a.per_piece = L.per_piece;
+    a.eb = p->lay.total;
+    hipStream_t cs = p->copy[0];
+    // when it may start (see moe_pool.h); the layer's next step joins it
+    if (after == MOE_PREFETCH_AFTER_QUEUED) {
+        HIPCHK(hipEventRecord(p->pf_issue, p->compute));
+        HIPCHK(hipStreamWaitEvent(cs, p->pf_issue, 0));
+    } else if (after == MOE_PREFETCH_AFTER_LAYER && L.stepped) {
+        HIPCHK(hipStreamWaitEvent(cs, L.step_done, 0));
+    }
+    HIPCHK(moe::launch_prefetch(a, kPrefetchGrid, cs));
+    HIPCHK(hipEventRecord(L.pf_done, cs));
+    L.pf_pending = true;
+    return MOE_OK;
 }
 
 moe_status_t moe_pool_last_step(moe_pool_t* p, int32_t layer, int32_t* path, moe_miss_t* miss_host,
@@ -1167,6 +1279,8 @@ moe_status_t moe_pool_get_stats(const moe_pool_t* p, int32_t layer, moe_pool_sta
             out->fallbacks += c[3];
             out->bytes_h2d += c[4];
             out->staged += c[5];
+            out->prefetched += c[6];
+            out->prefetch_bytes += c[7];
             continue;
         }
         out->steps += L.lru.steps();

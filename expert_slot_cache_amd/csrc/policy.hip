@@ -38,7 +38,7 @@ __device__ __forceinline__ void copy_step(const PolicyArgs& a, const PolLds& L, 
         const int e = L.list[j];
         const size_t off = (u - (size_t)j * upj) * kFillUnit;
         const size_t nvec = (eb - off < kFillUnit ? eb - off : kFillUnit) / 16;
-        const char* src = pol_store_at(a, e) + off;
+        const char* src = pol_src(a, e) + off;
         char* dst = (pool ? a.slots + (size_t)L.map[e] * eb : a.staging + (size_t)j * eb) + off;
         const u32x4v* __restrict__ s4 = reinterpret_cast<const u32x4v*>(src);
         u32x4v* __restrict__ d4 = reinterpret_cast<u32x4v*>(dst);
@@ -84,6 +84,89 @@ __global__ __launch_bounds__(kPolThreads) void k_policy(PolicyArgs a) {
     }
     if (!a.resident && d.path != PATH_NONE) copy_step(a, L, d);
     if (tid == 0) pol_last_reader(a.ds.ctl, arrived, nblocks);
+}
+
+// ---- prefetch ------------------------------------------------------------------------
+// One launch: every workgroup finds the same plan -- the predicted experts that the
+// layer's current state copy does not hold, ascending, at most pf_n, to entries 0, 1,
+// ... -- and copies its share of them (64 KiB units); workgroup 0 writes the entries'
+// tags (entries past the plan keep theirs: their bytes are untouched).  Nothing in the
+// launch reads the tags, and a step reads them only after the launch is complete.
+__global__ __launch_bounds__(kPolThreads) void k_prefetch(PrefetchArgs a) {
+    __shared__ uint32_t bits[kMaxExperts / 32];
+    __shared__ int32_t list[64];
+    __shared__ int32_t cnt[kPolWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int E = a.E;
+    const int nwords = (E + 31) >> 5;
+    const int par = a.ds.ctl[0] & 1;
+    const int32_t* map = reinterpret_cast<const int32_t*>(a.ds.copy[par] + slot_state_layout(E, a.N).map);
+    for (int i = tid; i < nwords; i += kPolThreads) bits[i] = 0u;
+    __syncthreads();
+    if (tid < a.n) {
+        const int e = a.ids[tid];
+        if ((unsigned)e < (unsigned)E && map[e] < 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    int base = 0;
+    for (int c0 = 0; c0 < E && base < a.pf_n; c0 += kPolThreads) {
+        const int e = c0 + tid;
+        const bool present = e < E && ((bits[e >> 5] >> (e & 31)) & 1u);
+        const uint64_t m = __ballot(present);
+        const uint32_t below =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (lane == 0) cnt[wave] = __popcll(m);
+        __syncthreads();
+        int off = 0, total = 0;
+        for (int w = 0; w < kPolWaves; ++w) {
+            off += w < wave ? cnt[w] : 0;
+            total += cnt[w];
+        }
+        const int pos = base + off + (int)below;
+        if (present && pos < a.pf_n) list[pos] = e;
+        base += total;
+        __syncthreads();
+    }
+    const int njobs = base < a.pf_n ? base : a.pf_n;
+    if (blockIdx.x == 0) {
+        if (tid < njobs) a.tag[tid] = list[tid];
+        if (tid == 0 && njobs) pol_bump(a.ds.ctr + 7, (unsigned long long)njobs * a.eb);
+    }
+    const size_t eb = a.eb;
+    const size_t upj = (eb + kFillUnit - 1) / kFillUnit;
+    const size_t units = upj * (size_t)njobs;
+    for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int j = (int)(u / upj);
+        const int e = list[j];
+        const size_t off = (u - (size_t)j * upj) * kFillUnit;
+        const size_t nvec = (eb - off < kFillUnit ? eb - off : kFillUnit) / 16;
+        const u32x4v* __restrict__ s4 =
+            reinterpret_cast<const u32x4v*>(a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * eb + off);
+        u32x4v* __restrict__ d4 = reinterpret_cast<u32x4v*>(a.buf + (size_t)j * eb + off);
+        for (size_t i0 = tid; i0 < nvec; i0 += 4 * kPolThreads) {
+            u32x4v v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const size_t i = i0 + (size_t)q * kPolThreads;
+                if (i < nvec) v[q] = s4[i];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const size_t i = i0 + (size_t)q * kPolThreads;
+                if (i < nvec) __builtin_nontemporal_store(v[q], d4 + i);
+            }
+        }
+    }
+}
+
+hipError_t launch_prefetch(const PrefetchArgs& a, int copy_grid, hipStream_t s) {
+    if (a.n < 1 || a.n > kPolThreads || a.pf_n < 1 || a.pf_n > 64 || a.E > kMaxExperts || a.eb % 16 ||
+        a.per_piece < 1 || copy_grid < 1)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_prefetch, dim3(copy_grid), dim3(kPolThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 size_t policy_lds_bytes(int E, int N) { return pol_lds_words(E, N) * sizeof(int32_t); }

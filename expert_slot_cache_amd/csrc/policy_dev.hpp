@@ -407,6 +407,28 @@ __device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, 
     return d;
 }
 
+// The device-mapped store address of expert e.
+__device__ __forceinline__ const char* pol_store_at(const PolicyArgs& a, int e) {
+    return a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * a.eb;
+}
+
+// The prefetch entry holding expert e, or -1.  All lanes of a wave call it with the
+// same e.
+__device__ __forceinline__ int pol_pf_entry(const PolicyArgs& a, int e) {
+    if (a.pf_n <= 0) return -1;
+    const int lane = threadIdx.x & 63;
+    const int t = lane < a.pf_n ? a.pf_tag[lane] : -1;
+    const uint64_t m = __ballot(t == e);
+    return m ? (int)__builtin_ctzll(m) : -1;
+}
+
+// Where a missed or staged expert's bytes are read from: its prefetch entry (HBM) if
+// it has one, else the pinned store over the host link.  Wave-uniform e.
+__device__ __forceinline__ const char* pol_src(const PolicyArgs& a, int e) {
+    const int j = pol_pf_entry(a, e);
+    return j >= 0 ? a.pf_buf + (size_t)j * a.eb : pol_store_at(a, e);
+}
+
 // Counters without a read-back (the lead's thread 0 does not wait for old values).
 __device__ __forceinline__ void pol_bump(unsigned long long* c, unsigned long long v) {
     __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -426,6 +448,12 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
         nxt.prot[s] = L.prot[s];
     }
     if (tid < 3 && !a.resident) nxt.meta[tid] = L.misc[tid];
+    // experts of the step read from the prefetch buffer (wave 0, one expert at a time)
+    int npf = 0;
+    if (a.pf_n > 0 && tid < 64) {
+        const int nj = d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0);
+        for (int j = 0; j < nj; ++j) npf += pol_pf_entry(a, L.list[j]) >= 0 ? 1 : 0;
+    }
     for (int j = tid; d.path == PATH_POOL && j < d.nmiss; j += kPolThreads) {
         const int e = L.list[j];
         a.ds.rec[4 + 3 * j] = e;
@@ -444,18 +472,19 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
         } else if (d.path == PATH_STAGE) {
             pol_bump(ctr + 0, 1);
             pol_bump(ctr + 3, 1);
-            pol_bump(ctr + 4, (unsigned long long)d.D * a.eb);
+            pol_bump(ctr + 4, (unsigned long long)(d.D - npf) * a.eb);
             pol_bump(ctr + 5, (unsigned long long)d.D);
         } else {
             pol_bump(ctr + 0, 1);
             pol_bump(ctr + 1, (unsigned long long)d.hits);
             if (d.nmiss) {
                 pol_bump(ctr + 2, (unsigned long long)d.nmiss);
-                pol_bump(ctr + 4, (unsigned long long)d.nmiss * a.eb);
+                pol_bump(ctr + 4, (unsigned long long)(d.nmiss - npf) * a.eb);
             }
         }
+        if (npf) pol_bump(ctr + 6, (unsigned long long)npf);
         if (a.timed_jobs) {
-            const int nlink = d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0);
+            const int nlink = (d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0)) - npf;
             __hip_atomic_store(a.timed_jobs, nlink, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
@@ -478,11 +507,6 @@ __device__ __forceinline__ void pol_last_reader(int32_t* ctl, int old, int nbloc
         const int par = __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&ctl[0], par ^ 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-}
-
-// The device-mapped store address of expert e.
-__device__ __forceinline__ const char* pol_store_at(const PolicyArgs& a, int e) {
-    return a.pieces[e / a.per_piece] + (size_t)(e % a.per_piece) * a.eb;
 }
 
 }  // namespace moe

@@ -375,6 +375,16 @@ def make_trace(wl: Workload, steps: int | None = None, tokens: int | None = None
     return ids
 
 
+def predictions(wl: Workload, trace: np.ndarray, accuracy: float, seed: int = 0) -> np.ndarray:
+    """Stand-in for a cross-layer router prediction: for each (step, layer) the trace's
+    own ids with probability `accuracy`, else the ids of an independent trace with the
+    same statistics (same shape; seeded)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed * 7919 + 17 + seed))
+    other = make_trace(wl, steps=trace.shape[0], tokens=trace.shape[2], rng=rng)
+    keep = rng.random(trace.shape[:2]) < accuracy
+    return np.where(keep[:, :, None, None], trace, other).astype(np.int32)
+
+
 def bottom_decile_share(ids_layer: np.ndarray, n_experts: int) -> float:
     """Share of selections that fall on the least selected 10 % of experts."""
     c = np.sort(np.bincount(ids_layer.ravel(), minlength=n_experts))

@@ -136,6 +136,8 @@ typedef struct {
                                and outputs are those of the copying step.  0: the step's
                                experts are copied first (prepare + forward always copy). */
     int32_t evict;          /* MOE_EVICT_* (non-LRU policies need MOE_POLICY_DEVICE) */
+    int32_t prefetch_slots; /* 0 = none; 1..64 (device policy, not resident): HBM entries per
+                               layer that moe_pool_prefetch fills with predicted experts */
 } moe_pool_config_t;
 
 typedef struct {
@@ -149,8 +151,11 @@ typedef struct {
     uint64_t hits;       /* distinct experts found resident, per step */
     uint64_t misses;     /* distinct experts copied into a slot, per step */
     uint64_t fallbacks;  /* steps that bypassed the pool */
-    uint64_t bytes_h2d;  /* bytes copied host -> HBM (misses and staging) */
+    uint64_t bytes_h2d;  /* bytes steps copied host -> HBM (misses and staging not served
+                            from a prefetch buffer) */
     uint64_t staged;     /* experts copied into staging by fallback steps */
+    uint64_t prefetched; /* missed or staged experts a step took from its prefetch buffer */
+    uint64_t prefetch_bytes; /* bytes moved host -> HBM by moe_pool_prefetch */
 } moe_pool_stats_t;
 
 typedef struct {
@@ -284,6 +289,34 @@ moe_status_t moe_pool_step(moe_pool_t* pool, int32_t layer, const int32_t* topk_
                            int32_t* slot_ids_dev, const void* x_dev, const float* topk_w_dev,
                            const void* resid_dev, void* out_dev, moe_miss_t* miss_host, int32_t miss_cap,
                            int32_t* n_miss, int32_t* path);
+
+/* Cross-layer prefetch ([vLLM-cache] "Planned follow-ups": async H2D with cross-layer
+ * prediction; [prefetch] "how the prefetch enters forward": after one layer runs, a
+ * later layer's weights are copied on a copy stream, and that layer waits for them
+ * through an event before it runs).  A hint that the next step of `layer` will use
+ * the experts in predicted_ids_dev (int32 [n_tokens][top_k], device, 1 <= n_tokens *
+ * top_k <= 256): on a copy stream, starting as `after` says (AFTER_LAYER: the ids
+ * must already be in place; AFTER_QUEUED: the ids may come from work queued on the
+ * compute stream; AFTER_PREVIOUS: the caller guarantees that the layer's last step
+ * is done when the copy stream gets there), the predicted experts the layer does not
+ * hold (ascending, at most prefetch_slots of them) are copied from the pinned store
+ * into the layer's prefetch buffer entries 0, 1, ....  The layer's next prepare or step waits for
+ * that copy (an event joins the streams; no kernel waits) and takes a missed or staged
+ * expert found in the buffer from HBM instead of over the host link.  The cache is
+ * unchanged by a prefetch: slot ids, misses, evictions, counters other than
+ * prefetched / prefetch_bytes / bytes_h2d, and outputs are those of the same steps
+ * without it.  Invalid ids are ignored.  predicted_ids_dev is read on the copy
+ * stream: keep it unchanged until the layer's next prepare or step has been queued
+ * (later work on the compute stream is ordered after the prefetch from then on).
+ * Errors: EINVAL (no prefetch buffer, bad sizes), EHIP. */
+#define MOE_PREFETCH_AFTER_LAYER    0  /* once the layer's last prepare or step is done */
+#define MOE_PREFETCH_AFTER_QUEUED   1  /* once everything queued on the compute stream is done */
+#define MOE_PREFETCH_AFTER_PREVIOUS 2  /* after the pool's previous prefetch only (for a
+                                          captured graph, whose replays run one after another:
+                                          the first prefetch of the capture waits for the
+                                          queued work, the rest follow it) */
+moe_status_t moe_pool_prefetch(moe_pool_t* pool, int32_t layer, const int32_t* predicted_ids_dev,
+                               int32_t n_tokens, int32_t after);
 
 /* The path and misses of the layer's last prepare (or step), as that call would have
  * returned them under MOE_POLICY_HOST; under MOE_POLICY_DEVICE the call first waits

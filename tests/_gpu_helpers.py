@@ -31,7 +31,7 @@ class Rig:
                  fast: bool = True, experts=None, std: float = 0.02, copy_streams: int = 1,
                  copy_chunk_bytes: int = 0, one_call: bool = False, timing: int = 0,
                  copy_engine: str = "kernel", policy: str = "host", read_through: bool = False,
-                 evict: str = "lru"):
+                 evict: str = "lru", prefetch_slots: int = 0):
         self.wl = wl
         self.one_call = one_call   # one moe_pool_step call per layer instead of prepare + forward
         self.L = wl.layers if layers is None else layers
@@ -47,7 +47,7 @@ class Rig:
                                     max_tokens=max_tokens or wl.tokens, copy_streams=copy_streams,
                                     copy_chunk_bytes=copy_chunk_bytes, timing=timing,
                                     copy_engine=copy_engine, policy=policy, read_through=read_through,
-                                    evict=evict)
+                                    evict=evict, prefetch_slots=prefetch_slots)
         for l in range(self.L):
             for e in range(self.E):
                 self.pool.load_expert(l, e, experts[l][e])
