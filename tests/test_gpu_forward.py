@@ -103,7 +103,7 @@ def test_fanout_int4_and_resident_identity(one_call, engine):
 
 
 @pytest.mark.parametrize("wtype,atype", [("f32", "f32"), ("bf16", "bf16"), ("int4", "bf16"),
-                                         ("bf16", "f32")])
+                                         ("bf16", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("T", [1, 3])
 @ONE_CALL
 def test_backend_matrix(wtype, atype, T, one_call):
