@@ -104,6 +104,7 @@ _SIGS = {
     "moe_pool_set_timing": (_I32, [_P, _I32]),
     "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
     "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _P, C.POINTER(C.c_double)]),
+    "moe_forward_slots": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
     "moe_lru_destroy": (None, [_P]),
     "moe_lru_step": (_I32, [_P, _P, _I32, _I32, _P, C.POINTER(Miss), _I32, _PI32, _PI32]),
@@ -143,6 +144,18 @@ def _check(status: int):
     if status == ESTATE:
         raise StateError(status, msg)
     raise MoeError(status, msg)
+
+
+def forward_slots(*, wtype: str, atype: str, hidden: int, inter: int, top_k: int, slots, n_slots: int,
+                  slot_ids, x, topk_w, out, n_tokens: int, resid=None, stream=None):
+    """moe_forward_slots: the fused MoE over caller-held slots, scratch in the library's
+    static device array (no allocation)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(lib().moe_forward_slots(WTYPES[wtype], ATYPES[atype], hidden, inter, top_k, _ptr(slots), n_slots,
+                                   _ptr(slot_ids), _ptr(x), _ptr(topk_w), _ptr(resid), n_tokens, _ptr(out),
+                                   C.c_void_p(stream)))
 
 
 def expert_bytes(wtype: str, hidden: int, inter: int) -> int:

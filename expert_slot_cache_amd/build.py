@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_pool.so")
 
-SOURCES = ["kernels.hip", "fill.hip", "policy.hip", "calibrate.hip", "moe_pool.cpp"]
+SOURCES = ["kernels.hip", "fill.hip", "policy.hip", "calibrate.hip", "moe_pool.cpp", "noalloc.cpp"]
 ARCH = "gfx950"
 
 # Every HIP compile disables packed fp32 instructions (v_pk_*_f32).

@@ -32,6 +32,7 @@
 
 #include "moe_pool.h"
 #include "kernels.hpp"
+#include "layout.hpp"
 #include "slot_lru.hpp"
 
 namespace {
@@ -44,6 +45,16 @@ void set_err(const char* fmt, ...) {
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
 }
+
+}  // namespace
+
+namespace moe {
+// The calling thread's last error message (moe_last_error), for the library's other
+// translation units.
+void set_last_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+}  // namespace moe
+
+namespace {
 
 #define FAIL(code, ...)        \
     do {                       \
@@ -63,43 +74,8 @@ void set_err(const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
-struct Layout {
-    size_t off_w13 = 0, off_w2 = 0, off_s13 = 0, off_s2 = 0, total = 0;
-};
-
-bool make_layout(int32_t wtype, int32_t H, int32_t I, Layout* L) {
-    if (H <= 0 || I <= 0) return false;
-    size_t w13, w2, s13 = 0, s2 = 0;
-    if (wtype == MOE_W_F32) {
-        if (H % 4 || I % 4) return false;
-        w13 = (size_t)2 * I * H * 4;
-        w2 = (size_t)H * I * 4;
-    } else if (wtype == MOE_W_BF16) {
-        if (H % 8 || I % 8) return false;
-        w13 = (size_t)2 * I * H * 2;
-        w2 = (size_t)H * I * 2;
-    } else if (wtype == MOE_W_INT4_G128) {
-        if (H % 128 || I % 128) return false;
-        w13 = (size_t)I * H;           // 2I rows x H/2 bytes
-        w2 = (size_t)H * I / 2;
-        s13 = (size_t)2 * I * (H / 128) * 2;
-        s2 = (size_t)H * (I / 128) * 2;
-    } else {
-        return false;
-    }
-    L->off_w13 = 0;
-    L->off_w2 = round_up(w13);
-    size_t end = round_up(L->off_w2 + w2);
-    if (wtype == MOE_W_INT4_G128) {
-        L->off_s13 = end;
-        L->off_s2 = round_up(L->off_s13 + s13);
-        end = round_up(L->off_s2 + s2);
-    } else {
-        L->off_s13 = L->off_s2 = 0;
-    }
-    L->total = end;
-    return true;
-}
+using moe::Layout;
+using moe::make_layout;
 
 struct Timing {
     hipEvent_t a = nullptr, b = nullptr;   // start, stop

@@ -389,6 +389,26 @@ moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t 
  * events.  *avg_us = mean duration.  Errors: EINVAL, ENOMEM, EHIP. */
 moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, void* stream, double* avg_us);
 
+/* ---- a forward that allocates nothing ---------------------------------------- */
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same fused MoE as
+ * moe_pool_forward (the same kernels, so the same bits for the same slot bytes and
+ * slot ids), over n_slots experts the caller holds contiguously at slots_dev (expert
+ * s at slots_dev + s * moe_expert_bytes(wtype, hidden, inter), the byte layout of
+ * moe_pool_load_expert), without a pool.  slot_ids_dev, x_dev, topk_w_dev, resid_dev
+ * (optional), out_dev and n_tokens as in moe_pool_forward; a slot id outside
+ * [0, n_slots) contributes nothing.  Its scratch lives in a device array of 64 MiB
+ * per GPU that the library holds until the process ends; a call needing more
+ * (decode: n_tokens * top_k * inter * 2 bytes; more than 8 tokens with bf16 weights:
+ * also n_tokens * top_k * hidden * 4 and the index lists) is refused with EINVAL.
+ * Calls on one GPU share that array: calls that overlap on one GPU race.  The call
+ * makes no allocation (its first call on a device looks up the array's address).
+ * Errors: EINVAL, EHIP. */
+moe_status_t moe_forward_slots(int32_t wtype, int32_t atype, int32_t hidden, int32_t inter, int32_t top_k,
+                               const void* slots_dev, int32_t n_slots, const int32_t* slot_ids_dev,
+                               const void* x_dev, const float* topk_w_dev, const void* resid_dev,
+                               int32_t n_tokens, void* out_dev, void* stream);
+
 /* ---- the slot manager alone (host only, no GPU) ----------------------------- */
 /* The same per-layer LRU state machine prepare() runs, driven from host ids, for
  * pool-size planning and for checking the bookkeeping without a GPU.  Semantics
