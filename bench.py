@@ -1,17 +1,19 @@
-"""Benchmark: MoE decode tokens/s of a pooled expert stack on one MI355X.
+"""Benchmark: MoE decode tokens/s vs pool size of a pooled expert stack on one MI355X.
 
 A step is one ubatch (default: one batch-1 decode token) through every layer of
-the stack: per layer, prepare (distinct ids, LRU, miss copies, table update,
-remap) and forward (w13 + SwiGLU, w2 + top-k combine, residual added), issued as
+the stack: per layer the slot manager (distinct ids, eviction policy, miss copies,
+remap) and the forward (w13 + SwiGLU, w2 + top-k combine, residual added), issued as
 one moe_pool_step call.  Inputs (routing trace, activations, gate weights) are
 resident in HBM before the timed region; the experts live in the library's pinned
 host store and stream into the slot pools on misses.
 
-Prints one JSON line.  Default workload: OLMoE-1B-7B shapes in bf16, 16 layers x
-64 experts, top-8, hidden 2048, intermediate 1024, 16 slots per layer.
---sweep 0,16,32 repeats the run per slot count (fresh pool and store each) and
-reports every point in the line's "sweep" field; "value" is the workload's own
-slot count (or the first point).
+Prints one JSON line.  `value` is the headline workload (default: OLMoE-1B-7B shapes
+in bf16, 16 layers x 64 experts, top-8, hidden 2048, intermediate 1024, 16 slots per
+layer).  `sweep` is the pool-size curve of the large fan-out workload (48 layers x 512
+INT4-g128 experts, top-10) at 0/16/32/48/64 slots per layer, on one filled store.
+`link_calibration` is the host-link sweep (both copy engines, 2-256 MiB, 1-4
+streams) whose best rate is `link_peak_gbps`; `roofline` is the dominant kernel's;
+`cpu_baseline` is the oracle on the host cores (a bounded sample).
 """
 from __future__ import annotations
 
@@ -62,7 +64,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="olmoe_bf16_e64", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--slots", type=int, default=None, help="slots per layer (default: workload's)")
-    ap.add_argument("--sweep", default="", help="comma-separated slot counts")
+    ap.add_argument("--sweep", default="0,16,32,48,64",
+                    help="comma-separated slot counts of the pool-size sweep ('' = none)")
+    ap.add_argument("--sweep-workload", default="fanout_int4_e512", choices=sorted(synth.WORKLOADS),
+                    help="workload of the pool-size sweep (one filled store serves every point)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None, help="tokens per ubatch (default: workload's)")
     ap.add_argument("--rule", default="distinct", choices=["distinct", "static"])
@@ -75,9 +80,10 @@ def parse():
     ap.add_argument("--policy", default="device", choices=["host", "device"],
                     help="slot manager: LRU on the host (reads back the distinct ids) or in one GPU "
                          "workgroup (no host round trip on the decode path)")
-    ap.add_argument("--read-through", type=int, default=0, choices=[0, 1],
-                    help="device policy, one token per step: the forward's kernels read missed experts "
-                         "from the pinned store and write them through to their slots (no copy first)")
+    ap.add_argument("--read-through", type=int, default=-1, choices=[-1, 0, 1],
+                    help="device policy, one token per step: the fused step (decision inside the w13 "
+                         "launch, missed experts read through from the pinned store); -1 = the faster "
+                         "form for the weight format (fused for bf16 / fp32, copying for INT4)")
     ap.add_argument("--graph", action="store_true",
                     help="device policy, one token per step: capture one decode token (every layer's "
                          "step) in a HIP graph and time its replays; the kernel and link figures then "
@@ -94,6 +100,9 @@ def parse():
                     help="time every Nth forward / copy batch with HIP events (coprime with layers)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget for the oracle's CPU baseline (0 = skip)")
+    ap.add_argument("--link-sweep", default="2,8,32,128,256",
+                    help="transfer sizes (MiB) of the host-link calibration sweep, each with both copy "
+                         "engines over 1, 2 and 4 streams")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB 4 times (for scaling the HBM "
                          "traffic counters) and exit")
@@ -129,17 +138,24 @@ def read_ceiling(torch, dev, binding, nbytes: int, achieved_gbps: float) -> dict
             "method": "plain streaming read of the same bytes in one launch, event-timed, 8 rotating regions"}
 
 
-def link_peak_gbps(binding, nbytes: int) -> dict:
-    """Pinned host -> HBM rate for one transfer of `nbytes` (the mean bytes of one
-    timed miss batch of the run, so that the ceiling and the measured rate move the
-    same amount per event pair) with each copy engine (the library's calibration
-    call, event-timed); the peak is the better of the two."""
-    r = {}
-    for engine in ("dma", "kernel"):
-        us = binding.link_calibration(nbytes, engine=engine, reps=8)
-        r[engine] = round(nbytes / (us * 1e-6) / 1e9, 2)
-    r["peak"] = max(r["dma"], r["kernel"])
-    return r
+def link_sweep(binding, sizes_mib, eb: int) -> dict:
+    """Pinned host -> HBM rate of one transfer per size (MiB, plus one expert), with
+    both copy engines (the library's calibration call: hipMemcpyAsync, or the copy
+    kernel reading the device-mapped store), split over 1, 2 and 4 streams, each
+    event-timed; the peak is the best of all."""
+    sizes = sorted({int(m) << 20 for m in sizes_mib} | {(eb + 15) // 16 * 16})
+    table = []
+    for nbytes in sizes:
+        for engine in ("dma", "kernel"):
+            for streams in (1, 2, 4):
+                us = binding.link_calibration(nbytes, engine=engine, reps=4, streams=streams)
+                table.append({"bytes": nbytes, "engine": engine, "streams": streams,
+                              "gbps": round(nbytes / (us * 1e-6) / 1e9, 2)})
+    best = max(table, key=lambda r: r["gbps"])
+    at_expert = max((r for r in table if r["bytes"] == sizes[0] or r["bytes"] == (eb + 15) // 16 * 16),
+                    key=lambda r: r["gbps"])
+    return {"peak": best["gbps"], "peak_at": {k: best[k] for k in ("bytes", "engine", "streams")},
+            "best_at_one_expert": at_expert, "table": table}
 
 
 def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
@@ -176,31 +192,25 @@ def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
                       f"{dt:.1f} s"}
 
 
-def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
-    """One pool, one timed run; returns the result dict and the expert size.  With
-    --graph the pool and everything around it run on a side stream, which a capture
-    needs."""
-    if not args.graph:
-        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
-    if args.policy != "device" or resident or wl.tokens != 1:
-        raise SystemExit("--graph needs the device policy, a pooled stack and one token per step")
-    with torch.cuda.stream(torch.cuda.Stream()):
-        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident)
+def read_through_for(args, wl) -> bool:
+    """The fused one-token step (read-through misses) or the copying step."""
+    if args.policy != "device" or wl.tokens != 1:
+        return False
+    if args.read_through >= 0:
+        return bool(args.read_through)
+    return wl.wtype != "int4"
 
 
-def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident):
-    dev = torch.device("cuda:0")
+def make_pool(args, binding, wl, slots, gen, resident, prefetch_slots=0):
+    """A pool for the workload with its store (or, resident, its slots) filled."""
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
-    prefetch = args.prefetch_accuracy is not None and slots > 0 and not resident
-    pf_slots = (args.prefetch_slots or min(64, 2 * K)) if prefetch else 0
     t0 = time.perf_counter()
     pool = binding.MoePool(layers=L, experts=E, top_k=K, hidden=H, inter=I, slots=slots,
                            wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
                            max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20, copy_engine=args.copy_engine,
-                           policy=args.policy, read_through=bool(args.read_through) and args.policy == "device"
-                           and not resident, timing=0 if args.no_timing else args.timing_every,
-                           prefetch_slots=pf_slots)
+                           policy=args.policy, read_through=read_through_for(args, wl),
+                           timing=0 if args.no_timing else args.timing_every, prefetch_slots=prefetch_slots)
     eb = pool.expert_nbytes
     if resident:
         buf = np.empty(eb, np.uint8)
@@ -211,8 +221,35 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
         for l in range(L):
             for e in range(E):
                 gen.expert(l, e, pool.store_view(l, e))
-    log(f"[bench] slots={slots}: store filled, {L * E * eb / 2**30:.2f} GiB pinned, "
+    log(f"[bench] {wl.name}: store filled, {L * E * eb / 2**30:.2f} GiB pinned, "
         f"{time.perf_counter() - t0:.1f} s")
+    return pool
+
+
+def run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident, pool=None):
+    """One timed run at `slots` slots per layer, on `pool` (set to that many slots and
+    cold) or on a pool of its own; returns the result dict and the expert size.  With
+    --graph the pool and everything around it run on a side stream, which a capture
+    needs."""
+    if not args.graph:
+        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident, pool)
+    if args.policy != "device" or resident or wl.tokens != 1:
+        raise SystemExit("--graph needs the device policy, a pooled stack and one token per step")
+    with torch.cuda.stream(torch.cuda.Stream()):
+        return _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident, pool)
+
+
+def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident, shared=None):
+    dev = torch.device("cuda:0")
+    L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
+    prefetch = args.prefetch_accuracy is not None and slots > 0 and not resident and shared is None
+    pf_slots = (args.prefetch_slots or min(64, 2 * K)) if prefetch else 0
+    if shared is not None:
+        pool = shared
+        pool.set_slots(slots)
+        pool.reset_timing()
+    else:
+        pool = make_pool(args, binding, wl, slots, gen, resident, pf_slots)
     adt = torch.float32 if wl.atype == "f32" else torch.bfloat16
     slot_d = torch.empty((L, T, K), dtype=torch.int32, device=dev)
     bufs = [torch.empty((T, H), dtype=adt, device=dev) for _ in range(2)]
@@ -332,7 +369,9 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
         tm = pool.timing()
     else:
         g.reset()
-    pool.close()
+    eb = pool.expert_nbytes
+    if shared is None:
+        pool.close()
     del ids_d, slot_d, bufs
     d = {k: st1[k] - st0[k] for k in st1}
     tokens = args.steps * T
@@ -372,7 +411,9 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
         w2_us = tm["w2_ms"] / n * 1e3
         ach = w13_bytes / (w13_us * 1e-6) / 1e9
         tflops = w13_flops / (w13_us * 1e-6) / 1e12
-        name = "k_grouped_w13 (grouped MFMA w13 + SwiGLU)" if grouped else "k_w13_gemv (w13 + SwiGLU)"
+        fused = read_through_for(args, wl) and not resident
+        name = ("k_grouped_w13 (grouped MFMA w13 + SwiGLU)" if grouped else
+                "k_step_w13 (decision + w13 + SwiGLU, fused step)" if fused else "k_w13_gemv (w13 + SwiGLU)")
         intensity = w13_flops / w13_bytes
         mfma_bound = grouped and intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
         if mfma_bound:
@@ -424,32 +465,51 @@ def main():
         wl = wl.with_(tokens=args.tokens)
     points = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
     slots = wl.slots if args.slots is None else args.slots
-    if points and args.slots is None:
-        slots = wl.slots if wl.slots in points else points[0]
     wl = wl.with_(slots=slots)
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
     S = args.warmup + args.steps + (GRAPH_WARM if args.graph else 0)
     log(f"[bench] workload {wl.name}: L={L} E={E} K={K} H={H} I={I} slots={slots} T={T} "
         f"steps={S} rule={args.rule} resident={args.resident}")
 
-    trace = synth.make_trace(wl, steps=S)
-    _, _, rx, rg = synth.streams(wl)
-    xs = synth.draw_activations(rx, (S, T, H), wl.atype)
-    ws = synth.draw_gate_weights(rg, (S, L, T, K))
-    gen = synth.WindowedExperts(wl)
-    if wl.atype == "f32":
-        xs_d = torch.from_numpy(xs).to(dev)
-    else:
-        xs_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
-    ws_d = torch.from_numpy(ws).to(dev)
+    def inputs(w):
+        tr = synth.make_trace(w, steps=S)
+        _, _, rx, rg = synth.streams(w)
+        xs = synth.draw_activations(rx, (S, w.tokens, w.hidden), w.atype)
+        ws = synth.draw_gate_weights(rg, (S, w.layers, w.tokens, w.top_k))
+        if w.atype == "f32":
+            xd = torch.from_numpy(xs).to(dev)
+        else:
+            xd = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        return tr, xs, ws, xd, torch.from_numpy(ws).to(dev)
 
-    results = {}
-    eb = 0
-    for n in (points or [slots]):
-        results[n], eb = run_point(args, torch, binding, wl, n, trace, xs_d, ws_d, gen, args.resident)
-    main_res = results[slots]
-    batch_bytes = main_res.get("miss_batch_bytes", eb)
-    link = link_peak_gbps(binding, max(eb, (batch_bytes + 4095) // 4096 * 4096))
+    # the headline: the workload at its own slot count
+    trace, xs, ws, xs_d, ws_d = inputs(wl)
+    gen = synth.WindowedExperts(wl)
+    main_res, eb = run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, args.resident)
+    del xs_d, ws_d
+    torch.cuda.empty_cache()
+
+    # the pool-size sweep: one pool with the largest slot count, its store filled once,
+    # set to each point's slot count (cold) in turn
+    sweep = None
+    if points:
+        swl = synth.WORKLOADS[args.sweep_workload]
+        swl = swl.with_(slots=max(points))
+        log(f"[bench] sweep {swl.name}: slots {points}")
+        s_trace, _, _, s_xd, s_wd = inputs(swl)
+        s_gen = synth.WindowedExperts(swl)
+        s_pool = make_pool(args, binding, swl, max(points), s_gen, False)
+        sweep = {"workload": swl.name, "layers": swl.layers, "experts": swl.experts, "top_k": swl.top_k,
+                 "hidden": swl.hidden, "inter": swl.inter, "weights": swl.wtype, "activations": swl.atype,
+                 "expert_bytes": s_pool.expert_nbytes, "read_through": read_through_for(args, swl), "points": []}
+        for n in points:
+            r, _ = run_point(args, torch, binding, swl, n, s_trace, s_xd, s_wd, s_gen, False, pool=s_pool)
+            sweep["points"].append(r)
+        s_pool.close()
+        del s_xd, s_wd
+        torch.cuda.empty_cache()
+
+    link = link_sweep(binding, [v for v in args.link_sweep.split(",") if v.strip()], eb)
     peak_link = link["peak"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "tokens/s", "n_gpus": 1,
@@ -461,20 +521,22 @@ def main():
                    "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
                    "resident": args.resident, "copy_streams": args.copy_streams,
                    "copy_engine": args.copy_engine, "policy": args.policy,
-                   "read_through": bool(args.read_through) and args.policy == "device" and not args.resident,
+                   "read_through": read_through_for(args, wl) and not args.resident,
                    "graph": bool(args.graph), "prefetch_accuracy": args.prefetch_accuracy},
     }
     for k, v in main_res.items():
         if k not in ("value", "ms_per_step", "slots", "roofline"):
             line[k] = v
     line["link_peak_gbps"] = round(peak_link, 2)
-    line["link_calibration_gbps"] = {"dma": link["dma"], "kernel": link["kernel"],
-                                     "bytes": max(eb, (batch_bytes + 4095) // 4096 * 4096)}
+    line["link_calibration"] = link
     if "link_gbps_misses" in main_res:
         line["link_frac"] = round(main_res["link_gbps_misses"] / peak_link, 4)
     line["roofline"] = main_res.get("roofline")
-    if points:
-        line["sweep"] = [results[n] for n in points]
+    if sweep is not None:
+        for r in sweep["points"]:
+            if "link_gbps_misses" in r:
+                r["link_frac"] = round(r["link_gbps_misses"] / peak_link, 4)
+        line["sweep"] = sweep
     if args.cpu_seconds > 0:
         n_cpu = min(S, 64)
         line["cpu_baseline"] = cpu_baseline(wl, lambda l, e: gen.expert(l, e), trace[:n_cpu],

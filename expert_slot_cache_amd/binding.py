@@ -103,7 +103,8 @@ _SIGS = {
     "moe_pool_reset_timing": (_I32, [_P]),
     "moe_pool_set_timing": (_I32, [_P, _I32]),
     "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
-    "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _P, C.POINTER(C.c_double)]),
+    "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _I32, _P, C.POINTER(C.c_double)]),
+    "moe_pool_set_slots": (_I32, [_P, _I32]),
     "moe_forward_slots": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
     "moe_lru_destroy": (None, [_P]),
@@ -234,6 +235,11 @@ class MoePool:
     def reset(self):
         _check(lib().moe_pool_reset(self._h))
 
+    def set_slots(self, n_slots: int):
+        """Slots per layer from now on (<= the count at create); the pool goes cold."""
+        _check(lib().moe_pool_set_slots(self._h, n_slots))
+        self.slots = n_slots
+
     # -- the step ------------------------------------------------------------------
     def prepare(self, layer: int, topk_ids, n_tokens: int, slot_ids):
         """topk_ids/slot_ids: int32 [n_tokens, top_k] on the device (tensor or address).
@@ -349,14 +355,15 @@ def read_calibration(buf, bytes_per_launch: int, reps: int = 20, stream=None) ->
     return us.value
 
 
-def link_calibration(nbytes: int, engine: str = "kernel", reps: int = 8, stream=None) -> float:
+def link_calibration(nbytes: int, engine: str = "kernel", reps: int = 8, streams: int = 1, stream=None) -> float:
     """Mean event-timed duration (us) of one pinned host -> HBM copy of nbytes with
-    the given engine ("kernel" or "dma")."""
+    the given engine ("kernel" or "dma"), split over `streams` streams."""
     if stream is None:
         import torch
         stream = torch.cuda.current_stream().cuda_stream
     us = C.c_double(0)
-    _check(lib().moe_link_calibration(nbytes, reps, COPY_ENGINES[engine], C.c_void_p(stream), C.byref(us)))
+    _check(lib().moe_link_calibration(nbytes, reps, COPY_ENGINES[engine], streams, C.c_void_p(stream),
+                                      C.byref(us)))
     return us.value
 
 

@@ -1000,7 +1000,7 @@ moe_status_t moe_pool_reset(moe_pool_t* p) {
     HIPCHK(hipStreamSynchronize(p->compute));
     for (auto s : p->copy) HIPCHK(hipStreamSynchronize(s));
     for (auto& L : p->layers) {
-        L.lru.reset();
+        L.lru.init(p->cfg.n_experts, p->cfg.resident ? 0 : p->cfg.n_slots, p->cfg.rule);
         HIPCHK(hipMemset(L.map_dev, 0xFF, (size_t)p->cfg.n_experts * 4));
         L.prepared = false;
         L.bytes_h2d = 0;
@@ -1437,14 +1437,18 @@ moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t 
     return MOE_OK;
 }
 
-moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, void* stream, double* avg_us) {
-    if (!avg_us || reps < 1 || bytes < 16 || bytes % 16 || (engine != MOE_COPY_KERNEL && engine != MOE_COPY_DMA))
+moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, int32_t n_streams, void* stream,
+                                  double* avg_us) {
+    if (!avg_us || reps < 1 || bytes < 16 || bytes % 16 || (engine != MOE_COPY_KERNEL && engine != MOE_COPY_DMA) ||
+        n_streams < 1 || n_streams > 8)
         FAIL(MOE_EINVAL, "bad calibration arguments");
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* host = nullptr;
     char* host_dev = nullptr;
     char* dev = nullptr;
     hipEvent_t a = nullptr, b = nullptr;
+    std::vector<hipStream_t> side(n_streams, nullptr);   // side[0] stays `stream`
+    std::vector<hipEvent_t> done(n_streams, nullptr);
     moe_status_t st = MOE_OK;
     double total = 0;
     auto fail = [&](hipError_t err, const char* what) {
@@ -1460,24 +1464,49 @@ moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, vo
     if (!st && (e = hipMalloc((void**)&dev, bytes)) != hipSuccess) fail(e, "hipMalloc");
     if (!st && (e = hipEventCreate(&a)) != hipSuccess) fail(e, "hipEventCreate");
     if (!st && (e = hipEventCreate(&b)) != hipSuccess) fail(e, "hipEventCreate");
+    side[0] = s;
+    for (int i = 1; !st && i < n_streams; ++i)
+        if ((e = hipStreamCreateWithFlags(&side[i], hipStreamNonBlocking)) != hipSuccess) fail(e, "hipStreamCreate");
+    for (int i = 0; !st && i < n_streams; ++i)
+        if ((e = hipEventCreateWithFlags(&done[i], hipEventDisableTiming)) != hipSuccess) fail(e, "hipEventCreate");
+    // the transfer split into n_streams parts of 16-byte multiples, one per stream
+    const size_t part = (bytes / 16 + n_streams - 1) / n_streams * 16;
     for (int32_t i = -1; !st && i < reps; ++i) {
         if ((e = hipEventRecord(a, s)) != hipSuccess) { fail(e, "hipEventRecord"); break; }
-        if (engine == MOE_COPY_KERNEL) {
-            moe::FillBatch fb{};
-            fb.n = 1;
-            fb.bytes = bytes;
-            fb.job[0] = moe::FillJob{host_dev, dev};
-            e = moe::launch_fill(fb, s);
-        } else {
-            e = hipMemcpyAsync(dev, host, bytes, hipMemcpyHostToDevice, s);
+        for (int k = 0; !st && k < n_streams; ++k) {
+            const size_t off = (size_t)k * part;
+            if (off >= bytes) break;
+            const size_t n = std::min(part, bytes - off);
+            if (k > 0 && (e = hipStreamWaitEvent(side[k], a, 0)) != hipSuccess) { fail(e, "hipStreamWaitEvent"); break; }
+            if (engine == MOE_COPY_KERNEL) {
+                moe::FillBatch fb{};
+                fb.n = 1;
+                fb.bytes = n;
+                fb.job[0] = moe::FillJob{host_dev + off, dev + off};
+                e = moe::launch_fill(fb, side[k]);
+            } else {
+                e = hipMemcpyAsync(dev + off, host + off, n, hipMemcpyHostToDevice, side[k]);
+            }
+            if (e != hipSuccess) { fail(e, "copy"); break; }
+            if (k > 0) {
+                if ((e = hipEventRecord(done[k], side[k])) != hipSuccess) { fail(e, "hipEventRecord"); break; }
+                if ((e = hipStreamWaitEvent(s, done[k], 0)) != hipSuccess) { fail(e, "hipStreamWaitEvent"); break; }
+            }
         }
-        if (e != hipSuccess) { fail(e, "copy"); break; }
+        if (st) break;
         if ((e = hipEventRecord(b, s)) != hipSuccess) { fail(e, "hipEventRecord"); break; }
         if ((e = hipEventSynchronize(b)) != hipSuccess) { fail(e, "hipEventSynchronize"); break; }
         float ms = 0;
         if ((e = hipEventElapsedTime(&ms, a, b)) != hipSuccess) { fail(e, "hipEventElapsedTime"); break; }
         if (i >= 0) total += ms * 1e3;
     }
+    for (int i = 1; i < n_streams; ++i)
+        if (side[i]) {
+            (void)hipStreamSynchronize(side[i]);
+            (void)hipStreamDestroy(side[i]);
+        }
+    for (auto ev : done)
+        if (ev) (void)hipEventDestroy(ev);
     if (a) (void)hipEventDestroy(a);
     if (b) (void)hipEventDestroy(b);
     if (dev) (void)hipFree(dev);
@@ -1485,6 +1514,34 @@ moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, vo
     if (st) return st;
     *avg_us = total / reps;
     return MOE_OK;
+}
+
+moe_status_t moe_pool_set_slots(moe_pool_t* p, int32_t n_slots) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    if (p->cfg.resident) FAIL(MOE_EINVAL, "the all-resident mode has no slot pool");
+    if (n_slots < 0 || n_slots > p->nslot_alloc)
+        FAIL(MOE_EINVAL, "n_slots %d outside [0,%d] (the slots allocated at create)", n_slots, p->nslot_alloc);
+    if (p->cfg.policy == MOE_POLICY_DEVICE &&
+        moe::policy_lds_bytes(p->cfg.n_experts, n_slots) + (size_t)(p->cfg.hidden / 32) * 80 + 16 > 65536)
+        FAIL(MOE_EINVAL, "%d slots do not fit the device slot manager's LDS", n_slots);
+    moe_status_t st = moe_pool_sync(p);
+    if (st) return st;
+    if (p->cfg.policy == MOE_POLICY_DEVICE) {
+        const DevLayout d = dev_layout(p->cfg.n_experts, n_slots);
+        for (auto& L : p->layers) {
+            char* blk = nullptr;
+            HIPCHK(hipMalloc((void**)&blk, d.total));
+            HIPCHK(hipFree(L.dev_block));
+            L.dev_block = blk;
+            L.ds.copy[0] = blk + d.copy0;
+            L.ds.copy[1] = blk + d.copy1;
+            L.ds.ctl = reinterpret_cast<int32_t*>(blk + d.ctl);
+            L.ds.ctr = reinterpret_cast<unsigned long long*>(blk + d.ctr);
+            L.ds.rec = reinterpret_cast<int32_t*>(blk + d.rec);
+        }
+    }
+    p->cfg.n_slots = n_slots;
+    return moe_pool_reset(p);
 }
 
 // ---- host-only slot manager ---------------------------------------------------

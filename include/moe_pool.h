@@ -211,6 +211,13 @@ void moe_pool_destroy(moe_pool_t* pool);
 moe_status_t moe_pool_load_expert(moe_pool_t* pool, int32_t layer, int32_t expert,
                                   const void* host_src, size_t nbytes);
 
+/* The pool-size knob of [llama-pool] "Summary" (the -mec sweep): from now on each layer
+ * keeps at most n_slots experts, 0 <= n_slots <= the n_slots given at create (0: every
+ * step falls back), and the pool is returned to cold as by moe_pool_reset.  The store
+ * and the slot memory stay as they are, so one filled store serves every point of a
+ * sweep.  Errors: EINVAL (resident mode, n_slots out of range), EHIP. */
+moe_status_t moe_pool_set_slots(moe_pool_t* pool, int32_t n_slots);
+
 /* Returns the pool to cold ([vLLM-cache] "How it works": the cache state the first
  * prepare starts from): every map entry -1, all slots free, eviction order empty,
  * counters zero (resident mode: counters only).  Slot bytes are not cleared.
@@ -382,12 +389,14 @@ moe_status_t moe_pool_set_timing(moe_pool_t* pool, int32_t every);
 moe_status_t moe_read_calibration(const void* buf_dev, size_t buf_bytes, size_t bytes, int32_t reps,
                                   void* stream, double* avg_us);
 
-/* The host link's rate for whole-expert copies: `bytes` (a positive multiple of 16)
- * from pinned, device-mapped host memory to HBM (both allocated by the call and
- * freed before it returns), reps times after one untimed copy, with the given
- * engine (MOE_COPY_KERNEL or MOE_COPY_DMA) on `stream`, each copy timed with
- * events.  *avg_us = mean duration.  Errors: EINVAL, ENOMEM, EHIP. */
-moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, void* stream, double* avg_us);
+/* The host link's rate: `bytes` (a positive multiple of 16) from pinned, device-mapped
+ * host memory to HBM (both allocated by the call and freed before it returns), reps
+ * times after one untimed copy, with the given engine (MOE_COPY_KERNEL or MOE_COPY_DMA),
+ * split into n_streams (1..8) equal parts copied side by side on `stream` and
+ * n_streams - 1 streams of the call's own, each copy timed with events on `stream`
+ * around all parts.  *avg_us = mean duration.  Errors: EINVAL, ENOMEM, EHIP. */
+moe_status_t moe_link_calibration(size_t bytes, int32_t reps, int32_t engine, int32_t n_streams, void* stream,
+                                  double* avg_us);
 
 /* ---- a forward that allocates nothing ---------------------------------------- */
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight

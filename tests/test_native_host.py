@@ -123,9 +123,30 @@ def test_read_calibration_rejects_bad_arguments_without_a_gpu():
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 21, 4, None, C.byref(us)) == binding.EINVAL
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 100, 4, None, C.byref(us)) == binding.EINVAL
     assert L.moe_read_calibration(C.c_void_p(16), 1 << 20, 1 << 16, 0, None, C.byref(us)) == binding.EINVAL
-    assert L.moe_link_calibration(100, 4, binding.COPY_KERNEL, None, C.byref(us)) == binding.EINVAL
-    assert L.moe_link_calibration(1 << 20, 0, binding.COPY_DMA, None, C.byref(us)) == binding.EINVAL
-    assert L.moe_link_calibration(1 << 20, 4, 7, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(100, 4, binding.COPY_KERNEL, 1, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 0, binding.COPY_DMA, 1, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 4, 7, 1, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 4, binding.COPY_DMA, 0, None, C.byref(us)) == binding.EINVAL
+    assert L.moe_link_calibration(1 << 20, 4, binding.COPY_DMA, 9, None, C.byref(us)) == binding.EINVAL
+
+
+def test_create_rejects_bad_eviction_and_prefetch_settings():
+    """Config validation of the eviction policy and the prefetch buffer, before any
+    GPU call: a policy outside the four, a non-LRU policy with the host slot manager,
+    prefetch entries out of range, with the host slot manager or all-resident."""
+    import ctypes as C
+
+    def cfg(policy, evict, pf, resident=0):
+        return binding.Config(1, 8, 2, 64, 32, 4, binding.WTYPES["f32"], binding.ATYPES["f32"],
+                              binding.RULES["distinct"], resident, 1, 1, 0, 0, 0, binding.COPY_KERNEL, policy, 0,
+                              evict, pf)
+    for c in (cfg(binding.POLICY_DEVICE, 4, 0), cfg(binding.POLICY_DEVICE, -1, 0),
+              cfg(binding.POLICY_HOST, binding.EVICT_LFU, 0), cfg(binding.POLICY_DEVICE, 0, 65),
+              cfg(binding.POLICY_DEVICE, 0, -1), cfg(binding.POLICY_HOST, 0, 4),
+              cfg(binding.POLICY_DEVICE, 0, 4, resident=1)):
+        h = C.c_void_p()
+        assert binding.lib().moe_pool_create(C.byref(c), None, C.byref(h)) == binding.EINVAL
+        assert not h.value
 
 
 def test_create_rejects_read_through_without_the_device_policy():
