@@ -11,6 +11,9 @@ leg do.  It shares no code with the HIP library.
   and the review thread; llama.cpp discussion "Persistent expert slot pool for MoE
   CPU offload", section "Design" and the prefill rule under "Why not the other
   approaches").
+* ``oracle.decay`` -- placement by decayed use counts with periodic one-pair moves
+  and host reads instead of evictions ("Running 125B MoE on Two 32 GB Cards",
+  sections 4.3-4.4).
 * ``oracle.router`` -- softmax over the experts, top-k with ties to the lower id,
   gathered gate weights ("Running 125B MoE on Two 32 GB Cards", section 4.2).
 * ``oracle.moe`` -- the slot-indexed MoE layer in float64: dequantisation of the
