@@ -18,10 +18,12 @@ How that maps onto a layer's slot pool (the readings, listed in the design notes
   for that step only (it goes to staging and the pool is left as it is);
 * the step counter counts pooled steps; a step whose count is a multiple of 8 makes
   the decision first, from the counts of the steps before it: every count is
-  multiplied by 2**(-8/512) (float32), then among non-resident experts the largest
-  count (lowest id on ties) and among resident experts the smallest count (lowest
-  id on ties) are compared, and if the difference exceeds 2 the first takes the
-  second's slot (a move: copied in like a miss, recorded as (expert, slot, evicted));
+  multiplied by 2**(-8/512) (float32); then, if the pool is full (with a free slot a
+  host expert simply takes it when next selected), among non-resident experts the
+  largest count (lowest id on ties) and among resident experts the smallest count
+  (lowest id on ties) are compared, and if the difference exceeds 2 the first takes
+  the second's slot (a move: copied in like a miss, recorded as (expert, slot,
+  evicted));
 * then the step's distinct ids are processed in ascending order: resident -> hit,
   free slot -> inserted (a miss), else -> read from the host (staged, at the rank
   among the step's host-read experts, in ascending order);
@@ -72,6 +74,8 @@ class LayerDecay:
     def _decide(self):
         """Decay, then one move if the gap is large enough; returns the move or None."""
         self.count = (self.count * DECAY).astype(np.float32)
+        if self.free_slots:
+            return None
         host = [e for e in range(self.E) if self.map[e] < 0]
         gpu = [e for e in range(self.E) if self.map[e] >= 0]
         if not host or not gpu:

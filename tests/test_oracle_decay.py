@@ -59,7 +59,7 @@ class Plain:
             self.cnt = [np.float32(c * DECAY) for c in self.cnt]
             outside = [e for e in range(self.E) if e not in self.where]
             inside = [e for e in range(self.E) if e in self.where]
-            if outside and inside:
+            if outside and inside and not self.free:
                 best = outside[0]
                 for e in outside[1:]:
                     if self.cnt[e] > self.cnt[best]:
