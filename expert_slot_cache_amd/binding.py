@@ -29,8 +29,8 @@ RULES = {"distinct": RULE_DISTINCT, "static": RULE_STATIC}
 COPY_ENGINES = {"dma": COPY_DMA, "kernel": COPY_KERNEL}
 POLICY_HOST, POLICY_DEVICE = 0, 1
 POLICIES = {"host": POLICY_HOST, "device": POLICY_DEVICE}
-EVICT_LRU, EVICT_FIFO, EVICT_LFU, EVICT_SLRU = 0, 1, 2, 3
-EVICTS = {"lru": EVICT_LRU, "fifo": EVICT_FIFO, "lfu": EVICT_LFU, "slru": EVICT_SLRU}
+EVICT_LRU, EVICT_FIFO, EVICT_LFU, EVICT_SLRU, EVICT_DECAY = 0, 1, 2, 3, 4
+EVICTS = {"lru": EVICT_LRU, "fifo": EVICT_FIFO, "lfu": EVICT_LFU, "slru": EVICT_SLRU, "decay": EVICT_DECAY}
 PREFETCH_AFTER = {"layer": 0, "queued": 1, "previous": 2}
 
 
@@ -65,7 +65,7 @@ class Miss(C.Structure):
 class Stats(C.Structure):
     _fields_ = [("steps", C.c_uint64), ("hits", C.c_uint64), ("misses", C.c_uint64),
                 ("fallbacks", C.c_uint64), ("bytes_h2d", C.c_uint64), ("staged", C.c_uint64),
-                ("prefetched", C.c_uint64), ("prefetch_bytes", C.c_uint64)]
+                ("prefetched", C.c_uint64), ("prefetch_bytes", C.c_uint64), ("moves", C.c_uint64)]
 
 
 class Timing(C.Structure):

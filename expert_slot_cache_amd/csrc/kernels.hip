@@ -281,11 +281,26 @@ struct PlainMem {
     __device__ __forceinline__ uint2 ld8(size_t off) const { return *reinterpret_cast<const uint2*>(p + off); }
 };
 
-// The base and slot count of the step's path (see Slots).
-__device__ __forceinline__ void pick_slots(const Slots& sl, const char*& base, int& n) {
+// The slot ids of the step's path (see Slots): ids [0, na) at a, ids [na, na + nb) at
+// b (the staging entries a pooled step addresses past the pool).
+struct SlotSpan {
+    const char* a;
+    const char* b;
+    int na, nb;
+    __device__ __forceinline__ int n() const { return na + nb; }
+    __device__ __forceinline__ const char* at(int slot, size_t stride) const {
+        return slot < na ? a + (size_t)slot * stride : b + (size_t)(slot - na) * stride;
+    }
+};
+
+__device__ __forceinline__ SlotSpan pick_slots(const Slots& sl) {
     const int p = *sl.path;
-    base = p == PATH_STAGE ? sl.stage : sl.pool;
-    n = p == PATH_POOL ? sl.npool : (p == PATH_STAGE ? sl.nstage : 0);
+    SlotSpan r;
+    r.a = p == PATH_STAGE ? sl.stage : sl.pool;
+    r.na = p == PATH_POOL ? sl.npool : (p == PATH_STAGE ? sl.nstage : 0);
+    r.b = sl.stage;
+    r.nb = p == PATH_POOL ? sl.nmix : 0;
+    return r;
 }
 
 // The wave's index in its workgroup, as a value the compiler knows is uniform
@@ -758,11 +773,9 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
     // loads the weight addresses depend on
     const int pair = blockIdx.z * gridDim.y + blockIdx.y;
     const int slot = slot_ids[pair];
-    const char* wbase;
-    int nslots;
-    pick_slots(sl, wbase, nslots);
-    const bool valid = slot >= 0 && slot < nslots;
-    const PairIn pin{valid ? wbase + (size_t)slot * stride : wbase, nullptr, valid};
+    const SlotSpan sp = pick_slots(sl);
+    const bool valid = slot >= 0 && slot < sp.n();
+    const PairIn pin{valid ? sp.at(slot, stride) : sp.a, nullptr, valid};
     w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, blockIdx.z, pair, blockIdx.x, red,
                                    xs_packed);
 }
@@ -818,7 +831,7 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
         }
     }
     const bool fast = !bad && (pa.resident || pa.rule == 0 || K <= N);
-    const PolLds L = pol_lds(reinterpret_cast<int32_t*>(dyn), E, N);
+    const PolLds L = pol_lds(reinterpret_cast<int32_t*>(dyn), E, N, pa.evict);
     Decision d{};
     if (lead || !fast) d = pol_decide(pa, slot_view(cur_base, E, N), L);
     // (the w2 launch that follows makes the lead's copy current: every read of the
@@ -921,20 +934,20 @@ __device__ __forceinline__ W2Lane w2_lane(int gs, int RP, int rb0) {
 // zeros without touching memory), so that a caller's activation loads issued earlier
 // can be waited for alone.
 template <int WT, int CPL, int RP, int WPR>
-__device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const char* wbase, int nslots, size_t stride,
+__device__ __forceinline__ void w2_fetch(W2Task<WT, CPL, RP>& tk, const SlotSpan& sp, size_t stride,
                                          int slot, int t, int K, int H, int I, int gs,
                                          const W2Lane& ln, int task, size_t off_w, size_t off_s) {
     const int G = 1 << gs;
     const int k = task / WPR;
     tk.part = task - k * WPR;
     tk.pair = t * K + k;
-    tk.ok = slot >= 0 && slot < nslots;
-    const char* ebase = wbase + (size_t)slot * stride;
+    tk.ok = slot >= 0 && slot < sp.n();
+    const char* ebase = tk.ok ? sp.at(slot, stride) : sp.a;
     __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
     if (WT != W_INT4 && !tk.ok) return;
     const size_t row_bytes = (size_t)CPL * G * WPR * 16;
     const int spr = I / 128;
-    const SlotReader rd(tk.ok ? ebase : wbase, tk.ok ? stride : 0);
+    const SlotReader rd(ebase, tk.ok ? stride : 0);
 #pragma unroll
     for (int p = 0; p < RP; ++p) {
         const size_t row = off_w + (size_t)min(ln.r0 + p, H - 1) * row_bytes;
@@ -1040,12 +1053,10 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
     const int t = blockIdx.y;
     const W2Lane ln = w2_lane(gs, RP, blockIdx.x * (RP * (64 >> gs)));
     const int rb0 = blockIdx.x * ln.RB;
-    const char* wbase;
-    int nslots;
     if (ONE) {
         // the wave's slot and the path word, side by side, before any branch
         const int slot = slot_ids[t * K + wave / WPR];
-        pick_slots(sl, wbase, nslots);
+        const SlotSpan sp = pick_slots(sl);
         // INT4: the token's K act vectors are repacked once per workgroup (each lane
         // would otherwise repack every chunk it uses).  A thread's first chunk is
         // requested before the weights, so that the repacking waits for it alone.
@@ -1057,7 +1068,7 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
             xr = XI4::fetch(PlainMem(act), e0 + (size_t)min((int)threadIdx.x, nxc - 1) * 32);
         __builtin_amdgcn_sched_barrier(0);
         W2Task<WT, CPL, RP> tk;
-        w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot, t, K, H, I, gs, ln, wave, off_w, off_s);
+        w2_fetch<WT, CPL, RP, WPR>(tk, sp, stride, slot, t, K, H, I, gs, ln, wave, off_w, off_s);
         if constexpr (WT == W_INT4) {
             __builtin_amdgcn_sched_barrier(0);
             char* xs = reinterpret_cast<char*>(ys) + ((K * WPR * ln.RB * 4 + 15) & ~15);
@@ -1079,10 +1090,10 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
                                         ys + (size_t)wave * ln.RB + ln.grp * RP);
         }
     } else {
-        pick_slots(sl, wbase, nslots);
+        const SlotSpan sp = pick_slots(sl);
         for (int task = wave; task < K * WPR; task += nw) {
             W2Task<WT, CPL, RP> tk;
-            w2_fetch<WT, CPL, RP, WPR>(tk, wbase, nslots, stride, slot_ids[t * K + task / WPR], t, K, H, I, gs, ln,
+            w2_fetch<WT, CPL, RP, WPR>(tk, sp, stride, slot_ids[t * K + task / WPR], t, K, H, I, gs, ln,
                                        task, off_w, off_s);
             w2_finish<WT, CPL, RP, WPR>(tk, PlainMem(act), H, I, gs, ln, stride, off_w, off_s,
                                         ys + (size_t)task * ln.RB + ln.grp * RP);
@@ -1112,9 +1123,7 @@ constexpr int kGBN = 128;       // output columns per workgroup: 4 waves x 32
 __global__ __launch_bounds__(kGroupThreads) void k_group_build(Slots sl, const int32_t* __restrict__ slot_ids,
                                                                int n, int tile_stride, int tile_rows,
                                                                int32_t* __restrict__ grp) {
-    const char* unused_base;
-    int nslots;
-    pick_slots(sl, unused_base, nslots);
+    const int nslots = pick_slots(sl).n();
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts];
     __shared__ int32_t toff[kMaxExperts];
@@ -1271,9 +1280,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w13(Slots sl, size_t stride,
     __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
-    const char* wbase;
-    int nslots;
-    pick_slots(sl, wbase, nslots);
+    const SlotSpan sp = pick_slots(sl);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
@@ -1291,7 +1298,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w13(Slots sl, size_t stride,
     const size_t sx = srow ? (size_t)(perm[row0 + min(sr, rows - 1)] / K) * H + sh * 32 : 0;
     const int n = min(j0 + l32, I - 1);
     const size_t rb = (size_t)H * 2;
-    const char* ex = wbase + (size_t)slot * stride + off_w;
+    const char* ex = sp.at(slot, stride) + off_w;
     const char* gr = ex + (size_t)n * rb + hl * 64;
     const char* ur = ex + (size_t)(I + n) * rb + hl * 64;
     f32x16_t cg[MT], cu[MT];
@@ -1370,9 +1377,7 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
     const int tile = blockIdx.x;
     if (tile >= grp[0]) return;
-    const char* wbase;
-    int nslots;
-    pick_slots(sl, wbase, nslots);
+    const SlotSpan spn = pick_slots(sl);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
     const int rows = grp[16 + 2 * tile_stride + tile];
@@ -1388,7 +1393,7 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     const bool srow = sr < nb * kGBM;
     const uint16_t* sp = act_sorted + (size_t)(row0 + min(sr, rows - 1)) * I + sh * 32;
     const int n = min(h0 + l32, H - 1);
-    const char* br = wbase + (size_t)slot * stride + off_w + (size_t)n * I * 2 + hl * 64;
+    const char* br = spn.at(slot, stride) + off_w + (size_t)n * I * 2 + hl * 64;
     f32x16_t c[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) c[m] = f32x16_t{};
@@ -1457,9 +1462,7 @@ __global__ __launch_bounds__(256) void k_combine(Slots sl, const float* __restri
                                                  const int32_t* __restrict__ slot_ids,
                                                  const void* __restrict__ resid, void* __restrict__ out, int T,
                                                  int K, int H) {
-    const char* unused_base;
-    int nslots;
-    pick_slots(sl, unused_base, nslots);
+    const int nslots = pick_slots(sl).n();
     const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (h >= H) return;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
@@ -1658,7 +1661,7 @@ hipError_t launch_step_w13(const Geom& g, const PolicyArgs& pa, const ForwardArg
                            const StageEvents* ev, hipStream_t s) {
     const int rows_per_block = (4 / WPR) * (64 / G) * RP;
     const int nrb = (g.I + rows_per_block - 1) / rows_per_block;
-    const size_t pol = (policy_lds_bytes(g.E, pa.N) + 15) / 16 * 16;
+    const size_t pol = (policy_lds_bytes(g.E, pa.N, pa.evict) + 15) / 16 * 16;
     const size_t lds = pol + (WT == W_INT4 ? (size_t)(g.H / 32) * kPackedChunkBytes : 0);
     const size_t tail = (size_t)2 * g.I * g.H * (WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1)) / (WT == W_INT4 ? 2 : 1);
     const dim3 grid(1 + n_copy + nrb * g.K);
@@ -1745,7 +1748,7 @@ template <int AT, int MT>
 hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     const int n = a.T * g.K;
     const int stride_t = grouped_tile_stride(a.max_pairs, a.nslots_alloc);
-    const int nsl = a.sl.npool > a.sl.nstage ? a.sl.npool : a.sl.nstage;
+    const int nsl = a.sl.npool + a.sl.nmix > a.sl.nstage ? a.sl.npool + a.sl.nmix : a.sl.nstage;
     const int tiles = n / (kGBM * MT) + (nsl < n ? nsl : n) + 1;   // bound on this call's tiles
     hipLaunchKernelGGL(k_group_build, dim3(1), dim3(kGroupThreads), 0, s, a.sl, a.slot_ids, n, stride_t, kGBM * MT,
                        a.grp);

@@ -51,11 +51,15 @@ struct StageEvents {
 // The two places a layer's experts can be read from; *path (written by the
 // step's decision or remap) picks one: PATH_POOL -> pool, PATH_STAGE -> stage,
 // PATH_NONE -> none.
+// On the pool path, slot ids npool .. npool + nmix - 1 name staging entries 0 ..
+// nmix - 1 (experts a step reads from the host without placing them: the placement by
+// decayed use counts); nmix is 0 under the other policies.
 struct Slots {
     const char* pool;
     const char* stage;
     int npool;              // valid slot ids in the pool: [0, npool)
     int nstage;             // valid staging ranks: [0, nstage)
+    int nmix;               // staging entries the pool path also addresses
     const int32_t* path;    // device word
 };
 
@@ -112,15 +116,24 @@ hipError_t launch_fill(const FillBatch& b, hipStream_t s);
 //   LFU : (use = touches since insertion, key = tick of the last touch)
 //   SLRU: (prot = protected segment, key = tick of taking its place in the segment);
 //         the probationary segment (prot 0) gives the victim while it has a candidate
-enum { EVICT_LRU = 0, EVICT_FIFO = 1, EVICT_LFU = 2, EVICT_SLRU = 3 };
+// DECAY is placement by decayed use counts instead ("Running 125B MoE on Two 32 GB
+// Cards", sections 4.3-4.4): a miss on a full pool is read from the host for the
+// step (staging entry r, slot id N + r) and evicts nothing; every 8th pooled step
+// first multiplies every count by 2^(-1/64) and, with the pool full, moves the most
+// used host expert into the slot of the least used resident one when its count is
+// larger by more than 2; each pooled step then adds its (token, k) selections.
+enum { EVICT_LRU = 0, EVICT_FIFO = 1, EVICT_LFU = 2, EVICT_SLRU = 3, EVICT_DECAY = 4 };
+constexpr int kDecayEvery = 8;          // pooled steps between decisions
+constexpr float kDecayThreshold = 2.0f; // the count gap a move needs
 
 // One copy of a layer's slot-manager state, all slot-indexed except map:
 // map[E] (slot or -1), owner[N] (expert or -1), free[N] (a stack, meta[0] entries
-// valid, popped from the top), key[N], use[N] (u32), prot[N], meta = {nfree, tick,
-// nprot, 0}.  Each layer holds two copies: a launch reads copy ctl[0] and its
-// lead workgroup writes the state after the step into the other copy.
+// valid, popped from the top), key[N], use[N] (u32), prot[N], cnt[E] (f32 decayed use
+// counts), meta = {nfree, tick, nprot, pooled steps}.  Each layer holds two copies: a
+// launch reads copy ctl[0] and its lead workgroup writes the state after the step
+// into the other copy.
 struct SlotStateLayout {
-    size_t map, owner, free, key, use, prot, meta, total;
+    size_t map, owner, free, key, use, prot, cnt, meta, total;
 };
 __host__ __device__ inline size_t slot_state_align(size_t n) { return (n + 255) / 256 * 256; }
 __host__ __device__ inline SlotStateLayout slot_state_layout(int E, int N) {
@@ -132,6 +145,7 @@ __host__ __device__ inline SlotStateLayout slot_state_layout(int E, int N) {
     L.key = o;   o = slot_state_align(o + (size_t)N * 4);
     L.use = o;   o = slot_state_align(o + (size_t)N * 4);
     L.prot = o;  o = slot_state_align(o + (size_t)N * 4);
+    L.cnt = o;   o = slot_state_align(o + (size_t)E * 4);
     L.meta = o;  o = slot_state_align(o + 16 * 4);
     L.total = o;
     return L;
@@ -140,7 +154,8 @@ __host__ __device__ inline SlotStateLayout slot_state_layout(int E, int N) {
 // A layer's device-side slot manager: the two state copies, the control words
 // ctl = {par: the current copy, readers: workgroups of the running launch that have
 // read it (0 between launches)}, counters ctr = u64 {steps, hits, misses,
-// fallbacks, bytes_h2d, staged} and the last step's record rec = {path, D, n_miss,
+// fallbacks, bytes_h2d, staged, prefetched, prefetch bytes, moves} and the last
+// step's record rec = {path, D, n_miss,
 // bad, then (expert, slot, evicted) per miss}.  The launch's last reader flips par,
 // so no workgroup ever waits for another.
 struct DevState {
@@ -175,8 +190,8 @@ struct PolicyArgs {
     char* pf_buf;
     int pf_n;
 };
-// Dynamic LDS of the decision for E experts and N slots.
-size_t policy_lds_bytes(int E, int N);
+// Dynamic LDS of the decision for E experts and N slots under policy evict.
+size_t policy_lds_bytes(int E, int N, int evict);
 // grid: workgroups of the launch (the per-id outputs and the copies spread over them).
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s);
 

@@ -555,8 +555,19 @@ void finish_prepare(moe_pool* p, LayerState& L, int32_t n_tokens, int32_t the_pa
     L.last_misses = p->misses;
 }
 
+// Staging entries a pooled step addresses past the pool (slot ids N + r): the
+// experts that placement by decayed counts reads from the host for one step (at most
+// the step's distinct ids, so at most N and at most the staging capacity).
+int32_t mixed_entries(const moe_pool_config_t& c, int32_t staging_cap) {
+    return c.evict == MOE_EVICT_DECAY && !c.resident ? std::min(c.n_slots, staging_cap) : 0;
+}
+
 moe::Slots layer_slots(const moe_pool* p, const LayerState& L) {
-    return moe::Slots{L.slots, p->staging, p->nslot_alloc, p->staging_cap, L.path_dev};
+    const int32_t nmix = mixed_entries(p->cfg, p->staging_cap);
+    // with mixed ids the pool's valid ids end at the current n_slots (slot ids from N on
+    // are staging entries)
+    return moe::Slots{L.slots, p->staging, nmix ? p->cfg.n_slots : p->nslot_alloc, p->staging_cap, nmix,
+                      L.path_dev};
 }
 
 moe::ForwardArgs forward_args(const moe_pool* p, const LayerState& L, const void* x_dev, const int32_t* slot_ids_dev,
@@ -781,7 +792,13 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.policy != MOE_POLICY_HOST && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "policy %d invalid", c.policy);
     if (c.read_through != 0 && c.read_through != 1) FAIL(MOE_EINVAL, "read_through %d invalid", c.read_through);
     if (c.read_through && c.policy != MOE_POLICY_DEVICE) FAIL(MOE_EINVAL, "read_through needs the device policy");
-    if (c.evict < MOE_EVICT_LRU || c.evict > MOE_EVICT_SLRU) FAIL(MOE_EINVAL, "evict %d invalid", c.evict);
+    if (c.evict < MOE_EVICT_LRU || c.evict > MOE_EVICT_DECAY) FAIL(MOE_EINVAL, "evict %d invalid", c.evict);
+    if (c.evict == MOE_EVICT_DECAY && c.read_through)
+        FAIL(MOE_EINVAL, "placement by decayed counts changes the state on every pooled step; it runs with"
+                         " read_through 0 (copy, then compute)");
+    if (c.evict == MOE_EVICT_DECAY && (int64_t)c.n_slots * 2 > moe::kMaxExperts)
+        FAIL(MOE_EINVAL, "placement by decayed counts addresses n_slots slots plus as many staging entries: "
+                         "n_slots %d > %d", c.n_slots, moe::kMaxExperts / 2);
     if (c.prefetch_slots < 0 || c.prefetch_slots > 64) FAIL(MOE_EINVAL, "prefetch_slots %d outside [0,64]", c.prefetch_slots);
     if (c.prefetch_slots && (c.policy != MOE_POLICY_DEVICE || c.resident))
         FAIL(MOE_EINVAL, "prefetch needs the device policy and a pool (not the all-resident mode)");
@@ -790,7 +807,8 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     if (c.policy == MOE_POLICY_DEVICE && c.n_experts > 2048)
         FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS: n_experts %d > 2048", c.n_experts);
     if (c.policy == MOE_POLICY_DEVICE &&
-        moe::policy_lds_bytes(c.n_experts, c.resident ? 0 : c.n_slots) + (size_t)(c.hidden / 32) * 80 + 16 > 65536)
+        moe::policy_lds_bytes(c.n_experts, c.resident ? 0 : c.n_slots, c.evict) + (size_t)(c.hidden / 32) * 80 + 16 >
+            65536)
         FAIL(MOE_EINVAL, "the device policy keeps a layer's state in LDS (64 KiB per workgroup): %d experts and %d"
                          " slots do not fit", c.n_experts, c.n_slots);
     if ((size_t)c.max_tokens * c.top_k > (size_t)1 << 24) FAIL(MOE_EINVAL, "max_tokens * top_k too large");
@@ -825,7 +843,7 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     const size_t slot_bytes = (size_t)p->nslot_alloc * eb + kAlign;
     const size_t act_bytes = (size_t)c.max_tokens * c.top_k * moe::act_bytes_per_pair(c.wtype, c.inter);
     const size_t y_bytes = (size_t)c.max_tokens * c.top_k * c.hidden * sizeof(float);
-    p->grp_slots = std::max(p->nslot_alloc, p->staging_cap);
+    p->grp_slots = std::max(p->nslot_alloc + mixed_entries(c, p->staging_cap), p->staging_cap);
     const size_t grp_bytes = moe::grouped_index_bytes(c.max_tokens, c.top_k, std::max(1, p->grp_slots));
     const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4 + (size_t)c.prefetch_slots * eb) +
                        (size_t)p->staging_cap * eb + act_bytes + y_bytes + grp_bytes + (size_t)E * 8;
@@ -1246,8 +1264,8 @@ moe_status_t moe_pool_get_stats(const moe_pool_t* p, int32_t layer, moe_pool_sta
         if (layer >= 0 && l != layer) continue;
         const LayerState& L = p->layers[l];
         if (p->cfg.policy == MOE_POLICY_DEVICE) {
-            unsigned long long c[8];
-            const moe_status_t st = dev_read(p, c, L.ds.ctr, 8);
+            unsigned long long c[9];
+            const moe_status_t st = dev_read(p, c, L.ds.ctr, 9);
             if (st) return st;
             out->steps += c[0] + L.empty_steps;
             out->hits += c[1];
@@ -1257,6 +1275,7 @@ moe_status_t moe_pool_get_stats(const moe_pool_t* p, int32_t layer, moe_pool_sta
             out->staged += c[5];
             out->prefetched += c[6];
             out->prefetch_bytes += c[7];
+            out->moves += c[8];
             continue;
         }
         out->steps += L.lru.steps();
@@ -1282,7 +1301,9 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
         const char* cur = L.ds.copy[ctl[0] & 1];
         std::vector<int32_t> map(E), owner(N), prot(N);
         std::vector<uint32_t> key(N), use(N);
+        std::vector<float> cnt(E);
         if ((st = dev_read(p, map.data(), cur + o.map, E))) return st;
+        if (p->cfg.evict == MOE_EVICT_DECAY && (st = dev_read(p, cnt.data(), cur + o.cnt, E))) return st;
         if (N && (st = dev_read(p, owner.data(), cur + o.owner, N))) return st;
         if (N && (st = dev_read(p, key.data(), cur + o.key, N))) return st;
         if (N && (st = dev_read(p, use.data(), cur + o.use, N))) return st;
@@ -1291,7 +1312,7 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
         if (owner_N) std::copy(owner.begin(), owner.end(), owner_N);
         if (lru_N) {
             // the eviction order: resident slots by the policy's key (SLRU: the
-            // probationary segment first)
+            // probationary segment first; DECAY: by use count, then expert id)
             std::vector<int32_t> res;
             for (int32_t q = 0; q < N; ++q)
                 if (owner[q] >= 0) res.push_back(q);
@@ -1300,6 +1321,11 @@ moe_status_t moe_pool_get_state(const moe_pool_t* p, int32_t layer, int32_t* map
                 uint64_t v = key[q];
                 if (ev == MOE_EVICT_LFU) v |= (uint64_t)use[q] << 32;
                 if (ev == MOE_EVICT_SLRU) v |= (uint64_t)(prot[q] != 0) << 32;
+                if (ev == MOE_EVICT_DECAY) {
+                    uint32_t cb;
+                    std::memcpy(&cb, &cnt[owner[q]], 4);   // non-negative: bits order like values
+                    v = ((uint64_t)cb << 32) | (uint32_t)owner[q];
+                }
                 return v;
             };
             std::sort(res.begin(), res.end(), [&](int32_t a, int32_t b) { return k(a) < k(b); });
@@ -1522,7 +1548,8 @@ moe_status_t moe_pool_set_slots(moe_pool_t* p, int32_t n_slots) {
     if (n_slots < 0 || n_slots > p->nslot_alloc)
         FAIL(MOE_EINVAL, "n_slots %d outside [0,%d] (the slots allocated at create)", n_slots, p->nslot_alloc);
     if (p->cfg.policy == MOE_POLICY_DEVICE &&
-        moe::policy_lds_bytes(p->cfg.n_experts, n_slots) + (size_t)(p->cfg.hidden / 32) * 80 + 16 > 65536)
+        moe::policy_lds_bytes(p->cfg.n_experts, n_slots, p->cfg.evict) + (size_t)(p->cfg.hidden / 32) * 80 + 16 >
+            65536)
         FAIL(MOE_EINVAL, "%d slots do not fit the device slot manager's LDS", n_slots);
     moe_status_t st = moe_pool_sync(p);
     if (st) return st;

@@ -124,7 +124,7 @@ moe_status_t moe_forward_slots(int32_t wtype, int32_t atype, int32_t hidden, int
     g.off_s13 = lay.off_s13;
     g.off_s2 = lay.off_s2;
     moe::ForwardArgs a{};
-    a.sl = moe::Slots{static_cast<const char*>(slots_dev), nullptr, n_slots, 0, path};
+    a.sl = moe::Slots{static_cast<const char*>(slots_dev), nullptr, n_slots, 0, 0, path};
     a.slot_ids = slot_ids_dev;
     a.x = x_dev;
     a.topk_w = topk_w_dev;

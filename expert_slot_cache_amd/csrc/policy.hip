@@ -24,12 +24,14 @@ constexpr size_t kFillUnit = (size_t)64 << 10;   // bytes of one copy work unit
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 // The step's copies: 64 KiB work units over the launch, store -> slot (misses, in
-// order) or staging (the distinct ids in rank order).
+// order), then -> staging (the distinct ids in rank order on the staging path, the
+// host-read experts on a pooled step under EVICT_DECAY).
 __device__ __forceinline__ void copy_step(const PolicyArgs& a, const PolLds& L, const Decision& d) {
     const int tid = threadIdx.x;
     const int nblocks = (int)gridDim.x;
     const bool pool = d.path == PATH_POOL;
-    const int njobs = pool ? d.nmiss : d.D;
+    const int njobs = pool ? d.nmiss + d.nhost : d.D;
+    const int nslot = pool ? d.nmiss : 0;     // jobs [0, nslot) go to slots, the rest to staging
     const size_t eb = a.eb;
     const size_t upj = (eb + kFillUnit - 1) / kFillUnit;
     const size_t units = upj * (size_t)njobs;
@@ -39,7 +41,7 @@ __device__ __forceinline__ void copy_step(const PolicyArgs& a, const PolLds& L, 
         const size_t off = (u - (size_t)j * upj) * kFillUnit;
         const size_t nvec = (eb - off < kFillUnit ? eb - off : kFillUnit) / 16;
         const char* src = pol_src(a, e) + off;
-        char* dst = (pool ? a.slots + (size_t)L.map[e] * eb : a.staging + (size_t)j * eb) + off;
+        char* dst = (j < nslot ? a.slots + (size_t)L.map[e] * eb : a.staging + (size_t)(j - nslot) * eb) + off;
         const u32x4v* __restrict__ s4 = reinterpret_cast<const u32x4v*>(src);
         u32x4v* __restrict__ d4 = reinterpret_cast<u32x4v*>(dst);
         for (size_t i0 = tid; i0 < nvec; i0 += 4 * kPolThreads) {
@@ -60,7 +62,7 @@ __device__ __forceinline__ void copy_step(const PolicyArgs& a, const PolLds& L, 
 
 __global__ __launch_bounds__(kPolThreads) void k_policy(PolicyArgs a) {
     extern __shared__ int32_t sm[];
-    const PolLds L = pol_lds(sm, a.E, a.N);
+    const PolLds L = pol_lds(sm, a.E, a.N, a.evict);
     const int tid = threadIdx.x;
     const bool lead = blockIdx.x == 0;
     const int nblocks = (int)gridDim.x;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kPolThreads) void k_policy(PolicyArgs a) {
     for (int i = gtid; i < a.n; i += gthreads) {
         const int e = a.ids[i];
         int v = -1;
-        if (d.path == PATH_POOL) v = a.resident ? e : L.map[e];
+        if (d.path == PATH_POOL) v = a.resident ? e : (L.map[e] >= 0 ? L.map[e] : L.rank[e]);
         else if (d.path == PATH_STAGE) v = L.rank[e];
         a.out[i] = v;
     }
@@ -169,13 +171,13 @@ hipError_t launch_prefetch(const PrefetchArgs& a, int copy_grid, hipStream_t s) 
     return hipGetLastError();
 }
 
-size_t policy_lds_bytes(int E, int N) { return pol_lds_words(E, N) * sizeof(int32_t); }
+size_t policy_lds_bytes(int E, int N, int evict) { return pol_lds_words(E, N, evict) * sizeof(int32_t); }
 
 hipError_t launch_policy(const PolicyArgs& a, int grid, hipEvent_t start, hipEvent_t stop, hipStream_t s) {
-    if (a.n < 1 || a.n > (1 << 24) || grid < 1 || a.eb % 16 || a.evict < EVICT_LRU || a.evict > EVICT_SLRU ||
+    if (a.n < 1 || a.n > (1 << 24) || grid < 1 || a.eb % 16 || a.evict < EVICT_LRU || a.evict > EVICT_DECAY ||
         (!a.resident && a.per_piece < 1))
         return hipErrorInvalidValue;
-    const size_t lds = policy_lds_bytes(a.E, a.N);
+    const size_t lds = policy_lds_bytes(a.E, a.N, a.evict);
     if (start)
         hipExtLaunchKernelGGL(k_policy, dim3(grid), dim3(kPolThreads), lds, s, start, stop, 0, a);
     else

@@ -29,23 +29,35 @@ namespace moe {
 constexpr int kPolThreads = 256;
 constexpr int kPolWaves = kPolThreads / 64;
 
-// The decision's LDS arrays (int32 words): map, rank, list [E]; presence bits
-// [E/32 + 1]; owner, free, key, use, prot, touched, evicted-by-miss [N]; misc [16].
+// The decision's LDS arrays (int32 words): misc [16]; map, rank, list [E]; presence
+// bits [E/32 + 1]; owner, free, key, use, prot, touched, evicted-by-miss [N]; and
+// under EVICT_DECAY a reduction area [16], cnt, occ [E] and the copy jobs [E + N + 2].
 struct PolLds {
     int32_t *map, *rank, *list, *owner, *fre, *prot, *tch, *mev, *misc;
     uint32_t *key, *use, *bits;
+    float* cnt;        // decayed use counts (DECAY)
+    int32_t* occ;      // the step's (token, k) selections per expert (DECAY)
+    int32_t* job;      // DECAY walk output: slot copies at [0, N + 1), host reads at [N + 1, ...)
+    uint64_t* red;     // DECAY: per-wave minima (8 words of 64 bits)
 };
 
 // misc words
-enum { PM_NFREE = 0, PM_TICK = 1, PM_NPROT = 2, PM_D = 3, PM_PATH = 4, PM_NMISS = 5, PM_HITS = 6, PM_BAD = 7,
-       PM_WAVES = 8 /* 4 words: per-wave counts of the compaction */ };
+enum { PM_NFREE = 0, PM_TICK = 1, PM_NPROT = 2, PM_POOLED = 3, PM_PATH = 4, PM_NMISS = 5, PM_HITS = 6, PM_BAD = 7,
+       PM_WAVES = 8 /* 4 words: per-wave counts of the compaction */, PM_NHOST = 12, PM_NMOVE = 13 };
 
-__host__ __device__ inline size_t pol_lds_words(int E, int N) {
-    return (size_t)3 * E + (size_t)(E / 32 + 1) + (size_t)7 * N + 16;
+__host__ __device__ inline size_t pol_lds_words(int E, int N, int evict) {
+    const size_t base = 16 + (size_t)3 * E + (size_t)(E / 32 + 1) + (size_t)7 * N;
+    return evict == EVICT_DECAY ? base + 16 + (size_t)3 * E + N + 2 : base;
 }
 
-__device__ inline PolLds pol_lds(int32_t* w, int E, int N) {
+__device__ inline PolLds pol_lds(int32_t* w, int E, int N, int evict) {
     PolLds L;
+    L.misc = w; w += 16;
+    L.red = nullptr;
+    if (evict == EVICT_DECAY) {
+        L.red = reinterpret_cast<uint64_t*>(w);   // 64 bytes into the (aligned) block
+        w += 16;
+    }
     L.map = w;  w += E;
     L.rank = w; w += E;
     L.list = w; w += E;
@@ -57,7 +69,13 @@ __device__ inline PolLds pol_lds(int32_t* w, int E, int N) {
     L.prot = w; w += N;
     L.tch = w;  w += N;
     L.mev = w;  w += N;
-    L.misc = w;
+    L.cnt = nullptr;
+    L.occ = L.job = nullptr;
+    if (evict == EVICT_DECAY) {
+        L.cnt = reinterpret_cast<float*>(w); w += E;
+        L.occ = w; w += E;
+        L.job = w;
+    }
     return L;
 }
 
@@ -69,6 +87,7 @@ struct SlotView {
     uint32_t* key;
     uint32_t* use;
     int32_t* prot;
+    float* cnt;
     int32_t* meta;
 };
 
@@ -81,6 +100,7 @@ __device__ inline SlotView slot_view(char* base, int E, int N) {
     v.key = reinterpret_cast<uint32_t*>(base + o.key);
     v.use = reinterpret_cast<uint32_t*>(base + o.use);
     v.prot = reinterpret_cast<int32_t*>(base + o.prot);
+    v.cnt = reinterpret_cast<float*>(base + o.cnt);
     v.meta = reinterpret_cast<int32_t*>(base + o.meta);
     return v;
 }
@@ -131,9 +151,118 @@ __device__ __forceinline__ int pol_argmin(const PolLds& L, int N, int evict, boo
 struct Decision {
     int path;    // PATH_POOL, PATH_STAGE, PATH_NONE (an id outside [0, E))
     int D;       // distinct ids
-    int nmiss;   // misses (pool path)
+    int nmiss;   // misses (pool path): experts copied into a slot
     int hits;
+    int nhost;   // DECAY, pool path: experts read from the host into staging for the step
+    int nmove;   // DECAY: 1 when the step's decision moved an expert (counted in nmiss)
 };
+
+// The decayed-count part of a pooled step (EVICT_DECAY), by all threads of the
+// workgroup, on the LDS state with list[0, D) = the step's distinct ids ascending and
+// occ = their selections.  Leaves the decision's fields in misc, and list[0, nmiss) =
+// the experts copied into slots (the move first) with mev = what each evicted,
+// list[nmiss, nmiss + nhost) = the host-read experts in staging order, rank[e] = N +
+// staging entry for a host-read expert.
+__device__ inline void pol_decay(const PolicyArgs& a, const PolLds& L, int D) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int E = a.E, N = a.N;
+    const int pooled = L.misc[PM_POOLED] + 1;
+    const bool decide = pooled % kDecayEvery == 0;
+    const float decay = 0x1.fa7c18p-1f;   // 2^(-1/64) rounded to float32 (half-life 512 steps)
+    if (decide)
+        for (int e = tid; e < E; e += kPolThreads) L.cnt[e] = __fmul_rn(L.cnt[e], decay);
+    __syncthreads();
+    int nmove = 0;
+    if (decide && L.misc[PM_NFREE] == 0) {
+        // the most used host expert (largest count, then lowest id) and the least used
+        // resident one (smallest count, then lowest id), as 64-bit minima: counts are
+        // non-negative, so their bit patterns order like their values
+        uint64_t bh = ~0ull, bg = ~0ull;
+        for (int e = tid; e < E; e += kPolThreads) {
+            const uint32_t c = __float_as_uint(L.cnt[e]);
+            const uint64_t kh = ((uint64_t)(~c) << 32) | (uint32_t)e;
+            const uint64_t kg = ((uint64_t)c << 32) | (uint32_t)e;
+            if (L.map[e] < 0) bh = kh < bh ? kh : bh;
+            else bg = kg < bg ? kg : bg;
+        }
+        bh = wave_min_u64(bh);
+        bg = wave_min_u64(bg);
+        if (lane == 0) {
+            L.red[wave] = bh;
+            L.red[kPolWaves + wave] = bg;
+        }
+        __syncthreads();
+        for (int w = 0; w < kPolWaves; ++w) {
+            bh = L.red[w] < bh ? L.red[w] : bh;
+            bg = L.red[kPolWaves + w] < bg ? L.red[kPolWaves + w] : bg;
+        }
+        if (bh != ~0ull && bg != ~0ull) {
+            const int h = (int)(uint32_t)bh, g = (int)(uint32_t)bg;
+            if (__fsub_rn(L.cnt[h], L.cnt[g]) > kDecayThreshold) {
+                nmove = 1;
+                __syncthreads();   // every thread has read map before it changes
+                if (tid == 0) {
+                    const int s = L.map[g];
+                    L.map[g] = -1;
+                    L.map[h] = s;
+                    L.owner[s] = h;
+                    L.job[0] = h;
+                    L.mev[0] = g;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // the distinct ids in order (wave 0, 64 at a time): resident -> hit; the j-th
+    // non-resident one takes free slot fre[nfree - 1 - j] while there is one, else it
+    // is read from the host into staging entry j - nfree
+    if (wave == 0) {
+        const int nfree = L.misc[PM_NFREE];
+        int j0 = 0, hits = 0;
+        for (int c0 = 0; c0 < D; c0 += 64) {
+            const int i = c0 + lane;
+            const int e = i < D ? L.list[i] : 0;
+            const bool in = i < D;
+            const bool res = in && L.map[e] >= 0;
+            const uint64_t m = __ballot(in && !res);
+            hits += __popcll(__ballot(res));
+            const int j = j0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (in && !res) {
+                if (j < nfree) {
+                    const int s = L.fre[nfree - 1 - j];
+                    L.map[e] = s;
+                    L.owner[s] = e;
+                    L.job[nmove + j] = e;
+                    L.mev[nmove + j] = -1;
+                    L.rank[e] = -1;
+                } else {
+                    L.job[N + 1 + (j - nfree)] = e;
+                    L.rank[e] = N + (j - nfree);
+                }
+            }
+            j0 += __popcll(m);
+        }
+        if (lane == 0) {
+            const int ins = j0 < nfree ? j0 : nfree;
+            L.misc[PM_NFREE] = nfree - ins;
+            L.misc[PM_NMISS] = nmove + ins;
+            L.misc[PM_NHOST] = j0 - ins;
+            L.misc[PM_HITS] = hits;
+            L.misc[PM_NMOVE] = nmove;
+            L.misc[PM_POOLED] = pooled;
+        }
+    }
+    __syncthreads();
+    // the step's selections join the counts (one float add per expert); the copy jobs
+    // go to list (its distinct ids are no longer needed)
+    for (int e = tid; e < E; e += kPolThreads) L.cnt[e] = __fadd_rn(L.cnt[e], (float)L.occ[e]);
+    const int nmiss = L.misc[PM_NMISS], nhost = L.misc[PM_NHOST];
+    for (int j = tid; j < nmiss + nhost; j += kPolThreads) L.list[j] = j < nmiss ? L.job[j] : L.job[N + 1 + j - nmiss];
+    __syncthreads();
+}
 
 // The decision of one step, by all kPolThreads threads of the workgroup.  Leaves in
 // LDS: the state after the step (map, owner, free, key, use, prot, misc
@@ -175,7 +304,7 @@ __device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, 
                 vp[r] = cur.prot[e];
             }
         }
-        if (tid < 3) vmeta = cur.meta[tid];
+        if (tid < 4) vmeta = cur.meta[tid];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int e = tid + r * kPolThreads;
@@ -188,7 +317,7 @@ __device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, 
                 L.prot[e] = vp[r];
             }
         }
-        if (tid < 3) L.misc[tid] = vmeta;
+        if (tid < 4) L.misc[tid] = vmeta;
         for (int e = tid + R * kPolThreads; e < E; e += kPolThreads) L.map[e] = cur.map[e];
         for (int s = tid + R * kPolThreads; s < N; s += kPolThreads) {
             L.owner[s] = cur.owner[s];
@@ -197,6 +326,11 @@ __device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, 
             L.use[s] = cur.use[s];
             L.prot[s] = cur.prot[s];
         }
+        if (a.evict == EVICT_DECAY)
+            for (int e = tid; e < E; e += kPolThreads) {
+                L.cnt[e] = cur.cnt[e];
+                L.occ[e] = 0;
+            }
     }
     for (int i = tid; i < nwords; i += kPolThreads) L.bits[i] = 0u;
     if (tid == 0) L.misc[PM_BAD] = 0;
@@ -307,6 +441,16 @@ __device__ inline Decision pol_decide(const PolicyArgs& a, const SlotView& cur, 
     }
 
     d.path = PATH_POOL;
+    if (a.evict == EVICT_DECAY) {
+        for (int i = tid; i < a.n; i += kPolThreads) atomicAdd(&L.occ[a.ids[i]], 1);
+        __syncthreads();
+        pol_decay(a, L, d.D);
+        d.nmiss = L.misc[PM_NMISS];
+        d.hits = L.misc[PM_HITS];
+        d.nhost = L.misc[PM_NHOST];
+        d.nmove = L.misc[PM_NMOVE];
+        return d;
+    }
     // 2a. a step whose ids all hit (most decode steps) under LRU, FIFO or LFU: id i of
     // the ascending list takes tick + i as its key, so every id is updated at once
     // (the order of the walk below fixes nothing else; SLRU promotions do, and walk)
@@ -447,11 +591,15 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
         nxt.use[s] = L.use[s];
         nxt.prot[s] = L.prot[s];
     }
-    if (tid < 3 && !a.resident) nxt.meta[tid] = L.misc[tid];
-    // experts of the step read from the prefetch buffer (wave 0, one expert at a time)
+    if (tid < 4 && !a.resident) nxt.meta[tid] = L.misc[tid];
+    if (a.evict == EVICT_DECAY && !a.resident)
+        for (int e = tid; e < E; e += kPolThreads) nxt.cnt[e] = L.cnt[e];
+    // experts the step moves (into slots, then staging), and those of them read from
+    // the prefetch buffer (wave 0, one expert at a time)
+    const int njobs = d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss + d.nhost : 0);
     int npf = 0;
     if (a.pf_n > 0 && tid < 64) {
-        const int nj = d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0);
+        const int nj = njobs;
         for (int j = 0; j < nj; ++j) npf += pol_pf_entry(a, L.list[j]) >= 0 ? 1 : 0;
     }
     for (int j = tid; d.path == PATH_POOL && j < d.nmiss; j += kPolThreads) {
@@ -477,16 +625,13 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
         } else {
             pol_bump(ctr + 0, 1);
             pol_bump(ctr + 1, (unsigned long long)d.hits);
-            if (d.nmiss) {
-                pol_bump(ctr + 2, (unsigned long long)d.nmiss);
-                pol_bump(ctr + 4, (unsigned long long)(d.nmiss - npf) * a.eb);
-            }
+            if (d.nmiss) pol_bump(ctr + 2, (unsigned long long)d.nmiss);
+            if (njobs) pol_bump(ctr + 4, (unsigned long long)(njobs - npf) * a.eb);
+            if (d.nhost) pol_bump(ctr + 5, (unsigned long long)d.nhost);
+            if (d.nmove) pol_bump(ctr + 8, (unsigned long long)d.nmove);
         }
         if (npf) pol_bump(ctr + 6, (unsigned long long)npf);
-        if (a.timed_jobs) {
-            const int nlink = (d.path == PATH_STAGE ? d.D : (d.path == PATH_POOL ? d.nmiss : 0)) - npf;
-            __hip_atomic_store(a.timed_jobs, nlink, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+        if (a.timed_jobs) __hip_atomic_store(a.timed_jobs, njobs - npf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 

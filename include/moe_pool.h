@@ -21,7 +21,8 @@
  *                1-4), "Why not the other approaches on the table" (prefill rule),
  *                "Validation" (stale map table).
  *  [flash-2x32]  "Running 125B MoE on Two 32 GB Cards": section 1 (INT4 g128 expert
- *                shape and bytes), section 3.4 (an id of -1 must never reach a kernel).
+ *                shape and bytes), section 3.4 (an id of -1 must never reach a kernel),
+ *                sections 4.3-4.4 (placement by decayed use counts).
  *  [prefetch]    article on vLLM PR #51710 (layer prefetch): copy stream joined back to
  *                the compute stream with events; large copies split into chunks.
  *
@@ -89,6 +90,17 @@ typedef int32_t moe_status_t;
                              promotes to a protected segment of (4 N) / 5 experts (its
                              oldest is demoted back when it overflows); victims come from
                              the probationary segment first */
+#define MOE_EVICT_DECAY 4 /* placement by decayed use counts ([flash-2x32] sections 4.3 and
+                             4.4, moving experts at run time): the pool fills from
+                             free slots; on a full pool a miss is read from the host into
+                             staging for that step only (its slot id is n_slots + the
+                             staging entry) and evicts nothing.  Every 8th pooled step first
+                             multiplies every expert's count by 2^(-1/64) (float32) and,
+                             with the pool full, moves the host expert of largest count
+                             into the slot of the resident expert of smallest count (lowest
+                             id on ties) when the gap exceeds 2 (a miss, and a move); each
+                             pooled step then adds its (token, k) selections to the counts.
+                             Needs read_through 0 and n_slots <= 2048. */
 /* path a step took */
 #define MOE_PATH_POOL     0
 #define MOE_PATH_FALLBACK 1
@@ -153,9 +165,12 @@ typedef struct {
     uint64_t fallbacks;  /* steps that bypassed the pool */
     uint64_t bytes_h2d;  /* bytes steps copied host -> HBM (misses and staging not served
                             from a prefetch buffer) */
-    uint64_t staged;     /* experts copied into staging by fallback steps */
+    uint64_t staged;     /* experts copied into staging by fallback steps (and by the
+                            host reads of pooled steps under MOE_EVICT_DECAY) */
     uint64_t prefetched; /* missed or staged experts a step took from its prefetch buffer */
     uint64_t prefetch_bytes; /* bytes moved host -> HBM by moe_pool_prefetch */
+    uint64_t moves;      /* MOE_EVICT_DECAY: experts its decisions moved into the pool
+                            (counted in misses); host reads count in staged */
 } moe_pool_stats_t;
 
 typedef struct {

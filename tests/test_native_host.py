@@ -132,16 +132,18 @@ def test_read_calibration_rejects_bad_arguments_without_a_gpu():
 
 def test_create_rejects_bad_eviction_and_prefetch_settings():
     """Config validation of the eviction policy and the prefetch buffer, before any
-    GPU call: a policy outside the four, a non-LRU policy with the host slot manager,
-    prefetch entries out of range, with the host slot manager or all-resident."""
+    GPU call: a policy outside the five, a non-LRU policy with the host slot manager,
+    decayed-count placement with read-through steps, prefetch entries out of range,
+    with the host slot manager or all-resident."""
     import ctypes as C
 
-    def cfg(policy, evict, pf, resident=0):
+    def cfg(policy, evict, pf, resident=0, rt=0):
         return binding.Config(1, 8, 2, 64, 32, 4, binding.WTYPES["f32"], binding.ATYPES["f32"],
-                              binding.RULES["distinct"], resident, 1, 1, 0, 0, 0, binding.COPY_KERNEL, policy, 0,
+                              binding.RULES["distinct"], resident, 1, 1, 0, 0, 0, binding.COPY_KERNEL, policy, rt,
                               evict, pf)
-    for c in (cfg(binding.POLICY_DEVICE, 4, 0), cfg(binding.POLICY_DEVICE, -1, 0),
-              cfg(binding.POLICY_HOST, binding.EVICT_LFU, 0), cfg(binding.POLICY_DEVICE, 0, 65),
+    for c in (cfg(binding.POLICY_DEVICE, 5, 0), cfg(binding.POLICY_DEVICE, -1, 0),
+              cfg(binding.POLICY_HOST, binding.EVICT_LFU, 0), cfg(binding.POLICY_HOST, binding.EVICT_DECAY, 0),
+              cfg(binding.POLICY_DEVICE, binding.EVICT_DECAY, 0, rt=1), cfg(binding.POLICY_DEVICE, 0, 65),
               cfg(binding.POLICY_DEVICE, 0, -1), cfg(binding.POLICY_HOST, 0, 4),
               cfg(binding.POLICY_DEVICE, 0, 4, resident=1)):
         h = C.c_void_p()
