@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--slots", type=int, default=None, help="slots per layer (default: workload's)")
     ap.add_argument("--sweep", default="0,16,32,48,64",
                     help="comma-separated slot counts of the pool-size sweep ('' = none)")
+    ap.add_argument("--sweep-evictions", default="lru,fifo,lfu,slru,decay",
+                    help="eviction policies of the pool-size sweep (the first gives its main points; "
+                         "each policy runs every point on the same filled store)")
+    ap.add_argument("--evict", default="lru", choices=["lru", "fifo", "lfu", "slru", "decay"],
+                    help="eviction policy of the headline run")
     ap.add_argument("--sweep-workload", default="fanout_int4_e512", choices=sorted(synth.WORKLOADS),
                     help="workload of the pool-size sweep (one filled store serves every point)")
     ap.add_argument("--layers", type=int, default=None)
@@ -194,23 +199,26 @@ def cpu_baseline(wl, experts_fn, trace, xs, ws, budget_s: float):
 
 def read_through_for(args, wl) -> bool:
     """The fused one-token step (read-through misses) or the copying step."""
-    if args.policy != "device" or wl.tokens != 1:
+    if args.policy != "device" or wl.tokens != 1 or args.evict == "decay":
         return False
     if args.read_through >= 0:
         return bool(args.read_through)
     return wl.wtype != "int4"
 
 
-def make_pool(args, binding, wl, slots, gen, resident, prefetch_slots=0):
+def make_pool(args, binding, wl, slots, gen, resident, prefetch_slots=0, read_through=None):
     """A pool for the workload with its store (or, resident, its slots) filled."""
+    if read_through is None:
+        read_through = read_through_for(args, wl)
     L, E, K, H, I, T = wl.layers, wl.experts, wl.top_k, wl.hidden, wl.inter, wl.tokens
     t0 = time.perf_counter()
     pool = binding.MoePool(layers=L, experts=E, top_k=K, hidden=H, inter=I, slots=slots,
                            wtype=wl.wtype, atype=wl.atype, rule=args.rule, resident=resident,
                            max_tokens=T, copy_streams=args.copy_streams,
                            copy_chunk_bytes=args.copy_chunk_mib << 20, copy_engine=args.copy_engine,
-                           policy=args.policy, read_through=read_through_for(args, wl),
-                           timing=0 if args.no_timing else args.timing_every, prefetch_slots=prefetch_slots)
+                           policy=args.policy, read_through=read_through,
+                           timing=0 if args.no_timing else args.timing_every, prefetch_slots=prefetch_slots,
+                           evict=args.evict)
     eb = pool.expert_nbytes
     if resident:
         buf = np.empty(eb, np.uint8)
@@ -391,7 +399,9 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
     w13_flops = 2.0 * 2 * I * H * T * K
     grouped = T > DECODE_MAX_TOKENS and wl.wtype == "bf16"
     res = {"slots": slots, "value": round(value, 3), "ms_per_step": round(elapsed / args.steps * 1e3, 4),
-           "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"]), 4),
+           # demanded experts served from the pool; staged ones (fallback steps, and the
+           # host reads of decayed-count placement) count against it
+           "hit_rate": round(d["hits"] / max(1, d["hits"] + d["misses"] + d["staged"]), 4),
            "misses_per_token": round(d["misses"] / tokens, 4),
            "fallback_steps": d["fallbacks"], "staged_experts": d["staged"],
            "h2d_gb": round(d["bytes_h2d"] / 1e9, 3),
@@ -411,7 +421,7 @@ def _run_point(args, torch, binding, wl, slots, trace, xs_d, ws_d, gen, resident
         w2_us = tm["w2_ms"] / n * 1e3
         ach = w13_bytes / (w13_us * 1e-6) / 1e9
         tflops = w13_flops / (w13_us * 1e-6) / 1e12
-        fused = read_through_for(args, wl) and not resident
+        fused = pool.read_through and not resident
         name = ("k_grouped_w13 (grouped MFMA w13 + SwiGLU)" if grouped else
                 "k_step_w13 (decision + w13 + SwiGLU, fused step)" if fused else "k_w13_gemv (w13 + SwiGLU)")
         intensity = w13_flops / w13_bytes
@@ -498,13 +508,25 @@ def main():
         log(f"[bench] sweep {swl.name}: slots {points}")
         s_trace, _, _, s_xd, s_wd = inputs(swl)
         s_gen = synth.WindowedExperts(swl)
-        s_pool = make_pool(args, binding, swl, max(points), s_gen, False)
+        # the copying step: every policy of the comparison runs on it
+        s_pool = make_pool(args, binding, swl, max(points), s_gen, False, read_through=False)
         sweep = {"workload": swl.name, "layers": swl.layers, "experts": swl.experts, "top_k": swl.top_k,
                  "hidden": swl.hidden, "inter": swl.inter, "weights": swl.wtype, "activations": swl.atype,
-                 "expert_bytes": s_pool.expert_nbytes, "read_through": read_through_for(args, swl), "points": []}
-        for n in points:
-            r, _ = run_point(args, torch, binding, swl, n, s_trace, s_xd, s_wd, s_gen, False, pool=s_pool)
-            sweep["points"].append(r)
+                 "expert_bytes": s_pool.expert_nbytes, "read_through": False, "points": []}
+        evicts = [v.strip() for v in args.sweep_evictions.split(",") if v.strip()] or [args.evict]
+        sweep["eviction"] = evicts[0]
+        sweep["by_eviction"] = {}
+        for ev in evicts:
+            s_pool.set_eviction(ev)
+            pts = []
+            for n in points:
+                r, _ = run_point(args, torch, binding, swl, n, s_trace, s_xd, s_wd, s_gen, False, pool=s_pool)
+                pts.append(r)
+            if ev == evicts[0]:
+                sweep["points"] = pts
+            sweep["by_eviction"][ev] = [
+                {k: r.get(k) for k in ("slots", "value", "hit_rate", "misses_per_token", "staged_experts",
+                                       "h2d_gb", "link_gbps_misses")} for r in pts]
         s_pool.close()
         del s_xd, s_wd
         torch.cuda.empty_cache()
@@ -520,7 +542,7 @@ def main():
                    "inter": I, "slots": slots, "tokens_per_step": T, "weights": wl.wtype,
                    "activations": wl.atype, "expert_bytes": eb, "rule": args.rule,
                    "resident": args.resident, "copy_streams": args.copy_streams,
-                   "copy_engine": args.copy_engine, "policy": args.policy,
+                   "copy_engine": args.copy_engine, "policy": args.policy, "evict": args.evict,
                    "read_through": read_through_for(args, wl) and not args.resident,
                    "graph": bool(args.graph), "prefetch_accuracy": args.prefetch_accuracy},
     }

@@ -105,6 +105,7 @@ _SIGS = {
     "moe_read_calibration": (_I32, [_P, C.c_size_t, C.c_size_t, _I32, _P, C.POINTER(C.c_double)]),
     "moe_link_calibration": (_I32, [C.c_size_t, _I32, _I32, _I32, _P, C.POINTER(C.c_double)]),
     "moe_pool_set_slots": (_I32, [_P, _I32]),
+    "moe_pool_set_eviction": (_I32, [_P, _I32]),
     "moe_forward_slots": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P]),
     "moe_lru_create": (_I32, [_I32, _I32, _I32, C.POINTER(_P)]),
     "moe_lru_destroy": (None, [_P]),
@@ -239,6 +240,12 @@ class MoePool:
         """Slots per layer from now on (<= the count at create); the pool goes cold."""
         _check(lib().moe_pool_set_slots(self._h, n_slots))
         self.slots = n_slots
+
+    def set_eviction(self, evict: str):
+        """Eviction policy from now on ("lru", "fifo", "lfu", "slru", "decay"); the pool
+        goes cold."""
+        _check(lib().moe_pool_set_eviction(self._h, EVICTS[evict]))
+        self.evict = evict
 
     # -- the step ------------------------------------------------------------------
     def prepare(self, layer: int, topk_ids, n_tokens: int, slot_ids):

@@ -843,7 +843,10 @@ moe_status_t moe_pool_create(const moe_pool_config_t* cfg, void* stream, moe_poo
     const size_t slot_bytes = (size_t)p->nslot_alloc * eb + kAlign;
     const size_t act_bytes = (size_t)c.max_tokens * c.top_k * moe::act_bytes_per_pair(c.wtype, c.inter);
     const size_t y_bytes = (size_t)c.max_tokens * c.top_k * c.hidden * sizeof(float);
-    p->grp_slots = std::max(p->nslot_alloc + mixed_entries(c, p->staging_cap), p->staging_cap);
+    // (room for the staging entries a decayed-count step addresses past the pool, so
+    // that the policy can be switched later)
+    p->grp_slots = std::max(p->nslot_alloc + (c.resident ? 0 : std::min(p->nslot_alloc, p->staging_cap)),
+                            p->staging_cap);
     const size_t grp_bytes = moe::grouped_index_bytes(c.max_tokens, c.top_k, std::max(1, p->grp_slots));
     const size_t hbm = (size_t)c.n_layers * (slot_bytes + (size_t)E * 4 + (size_t)c.prefetch_slots * eb) +
                        (size_t)p->staging_cap * eb + act_bytes + y_bytes + grp_bytes + (size_t)E * 8;
@@ -1568,6 +1571,26 @@ moe_status_t moe_pool_set_slots(moe_pool_t* p, int32_t n_slots) {
         }
     }
     p->cfg.n_slots = n_slots;
+    return moe_pool_reset(p);
+}
+
+moe_status_t moe_pool_set_eviction(moe_pool_t* p, int32_t evict) {
+    if (!p) FAIL(MOE_EINVAL, "null pool");
+    const moe_pool_config_t& c = p->cfg;
+    if (evict < MOE_EVICT_LRU || evict > MOE_EVICT_DECAY) FAIL(MOE_EINVAL, "evict %d invalid", evict);
+    if (evict != MOE_EVICT_LRU && c.policy != MOE_POLICY_DEVICE)
+        FAIL(MOE_EINVAL, "the host slot manager implements LRU only; evict %d needs the device policy", evict);
+    if (evict == MOE_EVICT_DECAY && c.read_through)
+        FAIL(MOE_EINVAL, "placement by decayed counts runs with read_through 0");
+    if (evict == MOE_EVICT_DECAY && (int64_t)p->nslot_alloc * 2 > moe::kMaxExperts)
+        FAIL(MOE_EINVAL, "placement by decayed counts: %d slots > %d", p->nslot_alloc, moe::kMaxExperts / 2);
+    if (c.policy == MOE_POLICY_DEVICE &&
+        moe::policy_lds_bytes(c.n_experts, c.resident ? 0 : c.n_slots, evict) + (size_t)(c.hidden / 32) * 80 + 16 >
+            65536)
+        FAIL(MOE_EINVAL, "the decision's state under evict %d does not fit its LDS", evict);
+    moe_status_t st = moe_pool_sync(p);
+    if (st) return st;
+    p->cfg.evict = evict;
     return moe_pool_reset(p);
 }
 

@@ -233,6 +233,14 @@ moe_status_t moe_pool_load_expert(moe_pool_t* pool, int32_t layer, int32_t exper
  * sweep.  Errors: EINVAL (resident mode, n_slots out of range), EHIP. */
 moe_status_t moe_pool_set_slots(moe_pool_t* pool, int32_t n_slots);
 
+/* The eviction policy knob ([vLLM-cache] review thread: the policies it lists; and
+ * [flash-2x32] sections 4.3-4.4): from now on the layers use MOE_EVICT_* `evict`, and
+ * the pool is returned to cold as by moe_pool_reset; the store and the slot memory
+ * stay as they are, so one filled store serves a comparison of the policies.
+ * Errors: EINVAL (evict out of range, a non-LRU policy with the host slot manager,
+ * MOE_EVICT_DECAY with read_through, the state not fitting the decision's LDS), EHIP. */
+moe_status_t moe_pool_set_eviction(moe_pool_t* pool, int32_t evict);
+
 /* Returns the pool to cold ([vLLM-cache] "How it works": the cache state the first
  * prepare starts from): every map entry -1, all slots free, eviction order empty,
  * counters zero (resident mode: counters only).  Slot bytes are not cleared.

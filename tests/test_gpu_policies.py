@@ -111,3 +111,32 @@ def test_host_policy_rejects_other_evictions():
     wl = synth.Workload("polhost", 1, 8, 2, 64, 32, 4, 1, 0, "f32", "f32", 1.0, 0.0, 0, 73)
     with pytest.raises(binding.MoeError):
         Rig(wl, slots=4, policy="host", evict="lfu")
+
+
+def test_set_eviction_switches_policy_from_cold():
+    """moe_pool_set_eviction returns the pool to cold under the new policy: the steps
+    after it match a fresh oracle of that policy, and the slot bytes their owners'."""
+    from oracle.decay import LayerDecay
+    wl = synth.Workload("polswitch", 1, 24, 4, 64, 32, 6, 1, 0, "f32", "f32", 0.7, 0.3, 12, 74)
+    trace = synth.make_trace(wl, steps=120)
+    rig = Rig(wl, slots=6, policy="device")
+    for evict, s0 in (("lfu", 0), ("decay", 40), ("slru", 80), ("lru", 0)):
+        rig.pool.set_eviction(evict)
+        ref = LayerDecay(24, 6) if evict == "decay" else LayerLRU(24, 6, "distinct", evict)
+        for s in range(s0, s0 + 40):
+            ids_d = torch.from_numpy(trace[s, 0]).to(DEV)
+            slot_d = torch.empty_like(ids_d)
+            rig.pool.prepare(0, ids_d, 1, slot_d)
+            r = ref.step(trace[s, 0])
+            assert rig.pool.last_step(0) == (r.path, r.misses), (evict, s)
+            assert (slot_d.cpu().numpy() == r.slot_ids).all(), (evict, s)
+        m, o, _ = rig.pool.state(0)
+        assert m.tolist() == ref.map and o.tolist() == ref.owner, evict
+        for s_, e in enumerate(o):
+            if e >= 0:
+                assert (rig.pool.read_slot(0, s_) == rig.experts[0][e]).all(), (evict, s_, e)
+    rig.close()
+    rt = Rig(wl, slots=6, policy="device", read_through=True)
+    with pytest.raises(binding.MoeError):
+        rt.pool.set_eviction("decay")
+    rt.close()
