@@ -235,6 +235,12 @@ struct SlotReader {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    // a per-lane offset plus a wave-uniform one (held in a scalar register): a lane keeps
+    // one offset per row instead of one per chunk
+    __device__ __forceinline__ uint4 load16(uint32_t voff, uint32_t soff) const {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCoherent);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
     __device__ __forceinline__ float scale(size_t off) const {
         return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kCoherent));
     }
@@ -254,6 +260,9 @@ struct SlotWriter {
         : r(__builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000)) {}
     __device__ __forceinline__ void store16(size_t off, uint4 v) const {
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ void store16(uint32_t voff, uint32_t soff, uint4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, (int)soff, 0);
     }
     __device__ __forceinline__ void store_scale(size_t off, float v) const {
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(__float_as_uint(v) >> 16), r, (int)off, 0, 0);
@@ -554,16 +563,17 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
         uint4 wg[RP][CPL], wu[RP][CPL];
         uint16_t sg[RP][CPL], su[RP][CPL];
         const int spr = H / 128;
+        uint32_t og[RP], ou[RP];   // per lane one offset per row; the chunk steps are wave-uniform
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
             const int i = min(i0 + p, I - 1);
-            const size_t g = off_w + (size_t)i * row_bytes;
-            const size_t u = off_w + (size_t)(I + i) * row_bytes;
+            og[p] = (uint32_t)(off_w + (size_t)i * row_bytes) + (uint32_t)gl * 16u;
+            ou[p] = (uint32_t)(off_w + (size_t)(I + i) * row_bytes) + (uint32_t)gl * 16u;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int c = (part * CPL + j) * G + gl;
-                wg[p][j] = rd.load16(g + (size_t)c * 16);
-                wu[p][j] = rd.load16(u + (size_t)c * 16);
+                const uint32_t so = (uint32_t)((part * CPL + j) * G) * 16u;
+                wg[p][j] = rd.load16(og[p], so);
+                wu[p][j] = rd.load16(ou[p], so);
             }
         }
 #pragma unroll
@@ -594,13 +604,12 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
                 const int i = min(i0 + p, I - 1);
-                const size_t g = off_w + (size_t)i * row_bytes;
-                const size_t u = off_w + (size_t)(I + i) * row_bytes;
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = (part * CPL + j) * G + gl;
-                    wr.store16(g + (size_t)c * 16, wg[p][j]);
-                    wr.store16(u + (size_t)c * 16, wu[p][j]);
+                    const uint32_t so = (uint32_t)((part * CPL + j) * G) * 16u;
+                    wr.store16(og[p], so, wg[p][j]);
+                    wr.store16(ou[p], so, wu[p][j]);
                     if ((c & 3) == 0) {
                         wr.store_scale_bits(off_s + ((size_t)i * spr + (c >> 2)) * 2, sg[p][j]);
                         wr.store_scale_bits(off_s + ((size_t)(I + i) * spr + (c >> 2)) * 2, su[p][j]);
@@ -638,16 +647,19 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
         if (ok) {
             const SlotReader rd(ebase, stride);
             uint4 wg[RP][CPL], wu[RP][CPL];
+            // per lane one offset per row (its gate and up rows, its first chunk); the
+            // chunk steps are wave-uniform
+            uint32_t og[RP], ou[RP];
 #pragma unroll
             for (int p = 0; p < RP; ++p) {
                 const int i = min(i0 + p, I - 1);
-                const size_t g = off_w + (size_t)i * row_bytes;
-                const size_t u = off_w + (size_t)(I + i) * row_bytes;
+                og[p] = (uint32_t)(off_w + (size_t)i * row_bytes) + (uint32_t)gl * 16u;
+                ou[p] = (uint32_t)(off_w + (size_t)(I + i) * row_bytes) + (uint32_t)gl * 16u;
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
-                    const int c = (part * CPL + j) * G + gl;
-                    wg[p][j] = rd.load16(g + (size_t)c * 16);
-                    wu[p][j] = rd.load16(u + (size_t)c * 16);
+                    const uint32_t so = (uint32_t)((part * CPL + j) * G) * 16u;
+                    wg[p][j] = rd.load16(og[p], so);
+                    wu[p][j] = rd.load16(ou[p], so);
                 }
             }
             float sg[RP][CPL], su[RP][CPL];
@@ -676,14 +688,11 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
                 const SlotWriter wr(pin.to, stride);
 #pragma unroll
                 for (int p = 0; p < RP; ++p) {
-                    const int i = min(i0 + p, I - 1);
-                    const size_t g = off_w + (size_t)i * row_bytes;
-                    const size_t u = off_w + (size_t)(I + i) * row_bytes;
 #pragma unroll
                     for (int j = 0; j < CPL; ++j) {
-                        const int c = (part * CPL + j) * G + gl;
-                        wr.store16(g + (size_t)c * 16, wg[p][j]);
-                        wr.store16(u + (size_t)c * 16, wu[p][j]);
+                        const uint32_t so = (uint32_t)((part * CPL + j) * G) * 16u;
+                        wr.store16(og[p], so, wg[p][j]);
+                        wr.store16(ou[p], so, wu[p][j]);
                     }
                 }
                 if (WT == W_INT4) {
