@@ -910,7 +910,7 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
 // sums) goes to LDS, then
 // out[t][r] = resid[t][r] + sum_{k = 0..K-1} w[t][k] * y_k[r]   (k in order).
 // A task is split into its weight fetch (which does not depend on act) and the
-// rest, so that the one-launch form can issue the fetch before its grid barrier.
+// rest, so that the weight loads are in flight while the workgroup repacks act.
 
 // Weight registers of one (expert, part) task of a lane: RP rows x CPL chunks.
 template <int WT, int CPL, int RP>
