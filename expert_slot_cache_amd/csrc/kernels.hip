@@ -840,13 +840,19 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
         }
     }
     const bool fast = !bad && (pa.resident || pa.rule == 0 || K <= N);
+    if (lead && fast && !pa.resident && pa.evict != EVICT_SLRU) {
+        // an all-hit step changes keys only: in place, and the copies keep their roles
+        pol_hit_in_place(pa, slot_view(cur_base, E, N), K);
+        return;
+    }
     const PolLds L = pol_lds(reinterpret_cast<int32_t*>(dyn), E, N, pa.evict);
     Decision d{};
     if (lead || !fast) d = pol_decide(pa, slot_view(cur_base, E, N), L);
-    // (the w2 launch that follows makes the lead's copy current: every read of the
-    // current copy is in this launch)
+    // (the w2 launch that follows makes the lead's copy current, ctl[2] = 1: every read
+    // of the current copy is in this launch)
     if (lead) {
         pol_publish(pa, slot_view(pa.ds.copy[par ^ 1], E, N), L, d);
+        if (tid == 0) pa.ds.ctl[2] = 1;
         if (tid < K) {
             const int id = pa.ids[tid];
             int v = -1;
@@ -1055,8 +1061,9 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
                                                            int K, int H, int I, int gs, size_t off_w, size_t off_s,
                                                            int32_t* __restrict__ flip) {
     extern __shared__ float ys[];               // [K][WPR][RB]
-    // after a fused step: the decision's state copy becomes current (nothing here reads it)
-    if (flip && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *flip ^= 1;
+    // after a fused step whose lead wrote the other state copy (ctl[2]): that copy becomes
+    // current (nothing here reads the state)
+    if (flip && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && flip[2]) flip[0] ^= 1;
     const int nw = blockDim.x >> 6;
     const int wave = wave_id();
     const int t = blockIdx.y;

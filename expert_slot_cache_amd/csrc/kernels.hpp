@@ -77,7 +77,7 @@ struct ForwardArgs {
     int32_t* grp;           // grouped-path index buffer (grouped_index_bytes)
     int nslots_alloc;       // slot count the grp buffer was sized for
     int max_pairs;          // max_tokens * K the scratch was sized for
-    int32_t* flip_par;      // decode w2 launch of a fused step: the state-copy word it flips (else null)
+    int32_t* flip_par;      // decode w2 launch of a fused step: the layer's ctl words (else null)
 };
 
 // The slot-indexed fused MoE for one layer.
@@ -153,11 +153,12 @@ __host__ __device__ inline SlotStateLayout slot_state_layout(int E, int N) {
 
 // A layer's device-side slot manager: the two state copies, the control words
 // ctl = {par: the current copy, readers: workgroups of the running launch that have
-// read it (0 between launches)}, counters ctr = u64 {steps, hits, misses,
-// fallbacks, bytes_h2d, staged, prefetched, prefetch bytes, moves} and the last
-// step's record rec = {path, D, n_miss,
-// bad, then (expert, slot, evicted) per miss}.  The launch's last reader flips par,
-// so no workgroup ever waits for another.
+// read it (0 between launches), wrote: the fused step's lead wrote the other copy},
+// counters ctr = u64 {steps, hits, misses, fallbacks, bytes_h2d, staged, prefetched,
+// prefetch bytes, moves} and the last step's record rec = {path, D, n_miss, bad, then
+// (expert, slot, evicted) per miss}.  A prepare launch's last reader flips par; after a
+// fused step the w2 launch flips it when `wrote` is set.  No workgroup ever waits for
+// another.
 struct DevState {
     char* copy[2];
     int32_t* ctl;

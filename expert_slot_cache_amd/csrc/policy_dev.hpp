@@ -635,6 +635,52 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
     }
 }
 
+// An all-hit one-token step under LRU, FIFO or LFU, by the lead workgroup of the fused
+// step (wave 0; every id valid and resident, K <= 64).  Such a step changes only the
+// keys (LFU: also the uses) of its slots and the tick, exactly as the all-hit path of
+// pol_decide does (distinct id i, ascending, gets key tick + i; tick += D), and nothing
+// else in the launch reads keys or uses on such a step, so the lead applies the changes
+// to the current state copy in place and marks that the copies keep their roles
+// (ctl[2] = 0: the w2 launch does not flip them).  Results, record and counters are
+// those of the decision.
+__device__ inline void pol_hit_in_place(const PolicyArgs& a, const SlotView& cur, int K) {
+    const int lane = threadIdx.x;
+    if (lane >= 64) return;
+    const int id = lane < K ? a.ids[lane] : 0x7fffffff;
+    const int s = lane < K ? cur.map[id] : -1;
+    const uint32_t tick = (uint32_t)cur.meta[1];
+    // the first occurrence of each id, then its rank among the distinct ids
+    bool first = lane < K;
+    for (int j = 0; j < K; ++j) {
+        const int idj = __shfl(id, j, 64);
+        first = first && !(j < lane && idj == id);
+    }
+    int rank = 0, D = 0;
+    for (int j = 0; j < K; ++j) {
+        const int fj = __shfl((int)first, j, 64);
+        const int idj = __shfl(id, j, 64);
+        D += fj;
+        rank += (fj && idj < id) ? 1 : 0;
+    }
+    if (first) {
+        if (a.evict != EVICT_FIFO) cur.key[s] = tick + (uint32_t)rank;
+        if (a.evict == EVICT_LFU) cur.use[s] = cur.use[s] + 1u;
+    }
+    if (lane < K) a.out[lane] = s;
+    if (lane == 0) {
+        cur.meta[1] = (int32_t)(tick + (uint32_t)D);
+        *a.path = PATH_POOL;
+        a.ds.rec[0] = PATH_POOL;
+        a.ds.rec[1] = D;
+        a.ds.rec[2] = 0;
+        a.ds.rec[3] = 0;
+        pol_bump(a.ds.ctr + 0, 1);
+        pol_bump(a.ds.ctr + 1, (unsigned long long)D);
+        if (a.timed_jobs) __hip_atomic_store(a.timed_jobs, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        a.ds.ctl[2] = 0;
+    }
+}
+
 // A workgroup of a prepare launch has read everything it reads of the current state
 // copy: it counts itself in (one thread, after the workgroup's reads have returned);
 // pol_last_reader, called at the end of the workgroup with the returned count, lets
