@@ -41,16 +41,24 @@ PF_AFTER_LAYER, PF_AFTER_QUEUED, PF_AFTER_PREVIOUS = 0, 1, 2   # moe_pool_prefet
 # WRITE_SIZE (KiB per dispatch), each scaled by the counter's reading for a plain
 # copy of known size; valid only for the kernel source these were taken on.
 PMC_TRAFFIC = {
-    ("olmoe_bf16_e64", "99309ad20e78ad93"): {"fetch_kib": 32816.0, "fetch_scale": 1.9998,
-                                             "write_kib": 32.1, "write_scale": 1.0},
+    # per dispatch, median over the run's dispatches (all-hit steps for the fused step);
+    # FETCH_SIZE scaled by the 256 MiB copy calibration (262144 / 131086.2 KiB)
+    ("olmoe_bf16_e64", "b6a1f5cd2517ce9e"): {"fetch_kib": 32891.5, "fetch_scale": 1.9998,
+                                             "write_kib": 32.3, "write_scale": 1.0},
+    ("fanout_int4_e512", "b6a1f5cd2517ce9e"): {"fetch_kib": 8336.5, "fetch_scale": 1.9998,
+                                               "write_kib": 12.5, "write_scale": 1.0},
 }
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 prefix of the sources of the timed decode kernels (the GEMVs and the fused
+    step, which includes the device decision)."""
     import hashlib
-    path = os.path.join(ROOT, "expert_slot_cache_amd", "csrc", "kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "policy_dev.hpp"):
+        with open(os.path.join(ROOT, "expert_slot_cache_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
