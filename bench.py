@@ -74,6 +74,11 @@ def parse():
     ap.add_argument("--slots", type=int, default=None, help="slots per layer (default: workload's)")
     ap.add_argument("--sweep", default="0,16,32,48,64",
                     help="comma-separated slot counts of the pool-size sweep ('' = none)")
+    ap.add_argument("--sweep-steps", type=int, default=100,
+                    help="timed steps of each sweep point (at least --steps)")
+    ap.add_argument("--sweep-warmup", type=int, default=64,
+                    help="untimed steps before each sweep point (at least --warmup): the pool's "
+                         "steady state, not its cold start")
     ap.add_argument("--sweep-evictions", default="lru,fifo,lfu,slru,decay",
                     help="eviction policies of the pool-size sweep (the first gives its main points; "
                          "each policy runs every point on the same filled store)")
@@ -489,7 +494,7 @@ def main():
     log(f"[bench] workload {wl.name}: L={L} E={E} K={K} H={H} I={I} slots={slots} T={T} "
         f"steps={S} rule={args.rule} resident={args.resident}")
 
-    def inputs(w):
+    def inputs(w, S=S):
         tr = synth.make_trace(w, steps=S)
         _, _, rx, rg = synth.streams(w)
         xs = synth.draw_activations(rx, (S, w.tokens, w.hidden), w.atype)
@@ -513,12 +518,16 @@ def main():
     if points:
         swl = synth.WORKLOADS[args.sweep_workload]
         swl = swl.with_(slots=max(points))
-        log(f"[bench] sweep {swl.name}: slots {points}")
-        s_trace, _, _, s_xd, s_wd = inputs(swl)
+        sargs = argparse.Namespace(**vars(args))
+        sargs.steps = max(args.steps, args.sweep_steps)
+        sargs.warmup = max(args.warmup, args.sweep_warmup)
+        log(f"[bench] sweep {swl.name}: slots {points}, {sargs.warmup} + {sargs.steps} steps per point")
+        s_trace, _, _, s_xd, s_wd = inputs(swl, sargs.warmup + sargs.steps + (GRAPH_WARM if args.graph else 0))
         s_gen = synth.WindowedExperts(swl)
         # the copying step: every policy of the comparison runs on it
         s_pool = make_pool(args, binding, swl, max(points), s_gen, False, read_through=False)
-        sweep = {"workload": swl.name, "layers": swl.layers, "experts": swl.experts, "top_k": swl.top_k,
+        sweep = {"workload": swl.name, "steps": sargs.steps, "warmup": sargs.warmup,
+                 "layers": swl.layers, "experts": swl.experts, "top_k": swl.top_k,
                  "hidden": swl.hidden, "inter": swl.inter, "weights": swl.wtype, "activations": swl.atype,
                  "expert_bytes": s_pool.expert_nbytes, "read_through": False, "points": []}
         evicts = [v.strip() for v in args.sweep_evictions.split(",") if v.strip()] or [args.evict]
@@ -528,7 +537,7 @@ def main():
             s_pool.set_eviction(ev)
             pts = []
             for n in points:
-                r, _ = run_point(args, torch, binding, swl, n, s_trace, s_xd, s_wd, s_gen, False, pool=s_pool)
+                r, _ = run_point(sargs, torch, binding, swl, n, s_trace, s_xd, s_wd, s_gen, False, pool=s_pool)
                 pts.append(r)
             if ev == evicts[0]:
                 sweep["points"] = pts

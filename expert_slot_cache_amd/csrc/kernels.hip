@@ -1292,10 +1292,15 @@ template <int AT, int MT>
 __global__ __launch_bounds__(256, 2) void k_grouped_w13(Slots sl, size_t stride,
                                                      const int32_t* __restrict__ grp, int tile_stride,
                                                      const void* __restrict__ x, int K, int H, int I,
-                                                     size_t off_w, uint16_t* __restrict__ act_sorted) {
+                                                     size_t off_w, uint16_t* __restrict__ act_sorted, int ncbp) {
     __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
-    const int tile = blockIdx.x;
-    if (tile >= grp[0]) return;
+    // column block fastest, with ncbp (a multiple of 8) blocks per tile: consecutive
+    // workgroups go to different XCDs round-robin, so a column block of every tile of a
+    // slot group lands on the same XCD close in time and the group's weights are read
+    // from HBM once and then from that XCD's L2
+    const int cbk = blockIdx.x % ncbp;
+    const int tile = blockIdx.x / ncbp;
+    if (tile >= grp[0] || cbk * kGBN >= I) return;
     const SlotSpan sp = pick_slots(sl);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
@@ -1305,7 +1310,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w13(Slots sl, size_t stride,
     const int lane = tid & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int j0 = blockIdx.y * kGBN + (tid >> 6) * 32;
+    const int j0 = cbk * kGBN + (tid >> 6) * 32;
     const bool cols = j0 < I;                    // the wave has columns (uniform per wave)
     const int nb = (rows + kGBM - 1) / kGBM;     // row blocks present (uniform)
     // staging: thread tid covers half `sh` of row `sr`
@@ -1389,10 +1394,11 @@ template <int MT>
 __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
                                                     const int32_t* __restrict__ grp, int tile_stride,
                                                     const uint16_t* __restrict__ act_sorted, int H, int I,
-                                                    size_t off_w, float* __restrict__ y) {
+                                                    size_t off_w, float* __restrict__ y, int ncbp) {
     __shared__ __attribute__((aligned(16))) char As[2][MT * kGBM * kARowBytes];
-    const int tile = blockIdx.x;
-    if (tile >= grp[0]) return;
+    const int cbk = blockIdx.x % ncbp;        // column block fastest (see k_grouped_w13)
+    const int tile = blockIdx.x / ncbp;
+    if (tile >= grp[0] || cbk * kGBN >= H) return;
     const SlotSpan spn = pick_slots(sl);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
@@ -1402,7 +1408,7 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     const int lane = tid & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int h0 = blockIdx.y * kGBN + (tid >> 6) * 32;
+    const int h0 = cbk * kGBN + (tid >> 6) * 32;
     const bool cols = h0 < H;
     const int nb = (rows + kGBM - 1) / kGBM;
     const int sr = tid >> 1, sh = tid & 1;
@@ -1771,20 +1777,21 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* act = static_cast<uint16_t*>(a.act);
-    const dim3 g13(tiles, (g.I + kGBN - 1) / kGBN), g2(tiles, (g.H + kGBN - 1) / kGBN);
+    const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8, ncb2 = ((g.H + kGBN - 1) / kGBN + 7) / 8 * 8;
+    const dim3 g13((unsigned)(tiles * ncb13)), g2((unsigned)(tiles * ncb2));
     if (ev && ev->w13_start)
         hipExtLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
-                              g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act);
+                              g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
     else
         hipLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, a.x,
-                           g.K, g.H, g.I, g.off_w13, act);
+                           g.K, g.H, g.I, g.off_w13, act, ncb13);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && ev->w2_start)
         hipExtLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
-                              a.grp, stride_t, act, g.H, g.I, g.off_w2, a.y);
+                              a.grp, stride_t, act, g.H, g.I, g.off_w2, a.y, ncb2);
     else
         hipLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H,
-                           g.I, g.off_w2, a.y);
+                           g.I, g.off_w2, a.y, ncb2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gc((unsigned)((g.H / 4 + 255) / 256), (unsigned)(a.T < 65535 ? a.T : 65535));
     if (ev && ev->w2_stop)
