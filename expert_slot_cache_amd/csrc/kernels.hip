@@ -1472,6 +1472,172 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
     }
 }
 
+// ---- grouped GEMMs for large slot groups: both operands through LDS -------------------
+// A workgroup computes a tile of 128 rows (4 MFMA blocks of 32) x 128 weight rows (w13:
+// 64 gate + the matching 64 up rows; w2: 128 output columns).  Each 64-element k span of
+// both operands (64 bytes of A and 64 of weights per thread) is loaded into registers
+// two spans ahead (two register sets), then written into one of two LDS buffers the
+// span before its MFMAs read it; two workgroups share a CU (64 KiB of LDS each), so one
+// computes while the other waits for memory.  (Three spans ahead needed more than the
+// 256 registers of two workgroups per CU and spilled; one workgroup per CU with three
+// spans ahead was 1.3x slower.)  A tile row is 128 bytes in
+// LDS with its 16-byte chunk c at position c ^ (row & 7), so the 32 rows one MFMA
+// operand reads hit distinct banks.  Waves: 2 x 2, each 2 row blocks x 2 weight blocks.
+// Per accumulator the k order (spans in order, then MFMA j = 0..3 with the lane-half
+// element split of the staged kernels) is the one of k_grouped_w13 / k_grouped_w2, so
+// every output row has the same bits whichever kernel computed it.
+namespace gg {
+constexpr int kTileBytes = 128 * 128;           // one operand of one span: 128 rows x 128 B
+constexpr int kBufBytes = 2 * kTileBytes;       // A then weights
+}  // namespace gg
+
+// The span's copies of one thread: rows q = 0..3 of its 1 KiB blocks, A then weights.
+struct GgRegs {
+    uint4 a[4], b[4];
+};
+
+template <bool W13>
+__global__ __launch_bounds__(256, 2) void k_gg(Slots sl, size_t stride, const int32_t* __restrict__ grp,
+                                               int tile_stride, const uint16_t* __restrict__ a_src, int K, int Kd,
+                                               int ncols, size_t off_w, void* __restrict__ out, int ncbp) {
+    __shared__ __attribute__((aligned(1024))) char lds[2][gg::kBufBytes];
+    const int cbk = blockIdx.x % ncbp;
+    const int tile = blockIdx.x / ncbp;
+    const int cspan = W13 ? 64 : 128;               // output columns per workgroup
+    if (tile >= grp[0] || cbk * cspan >= ncols) return;
+    const SlotSpan sp = pick_slots(sl);
+    const int slot = grp[16 + tile];
+    const int row0 = grp[16 + tile_stride + tile];
+    const int rows = grp[16 + 2 * tile_stride + tile];
+    const int32_t* perm = grp + 16 + 3 * tile_stride;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = wave_id();
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    const int wr = w >> 1, wc = w & 1;
+    const int c0 = cbk * cspan;
+    const char* wbase = sp.at(slot, stride) + off_w;
+    const size_t rowb = (size_t)Kd * 2;
+    // this thread copies chunk lane % 8 of tile rows w*32 + q*8 + lane/8 (q = 0..3) of
+    // both operands.  Weight rows are consecutive (the column blocks never pass the end:
+    // the shapes are multiples of 256), so are A rows for w2; w13 gathers its A rows.
+    // In LDS the chunk goes to position (lane % 8) ^ (lane / 8) of its row.
+    const int ck = lane & 7;
+    const int rb0 = w * 32 + (lane >> 3);
+    const int dst0 = rb0 * 128 + ((ck ^ (lane >> 3)) * 16);
+    const int wrow0 = W13 ? (rb0 < 64 ? c0 + rb0 : ncols + c0 + rb0 - 64) : c0 + rb0;
+    const char* bsrc = wbase + (size_t)wrow0 * rowb + ck * 16;
+    const char* abase = reinterpret_cast<const char*>(a_src) + ck * 16;
+    uint32_t aoff[4];                               // w13: byte offsets of the gathered rows
+    size_t arow0 = 0;
+    if (W13) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            aoff[q] = (uint32_t)((size_t)(perm[row0 + min(rb0 + q * 8, rows - 1)] / K) * rowb);
+    } else {
+        arow0 = (size_t)(row0 + rb0);
+    }
+    const int nsp = Kd / 64;                        // a multiple of 4
+    auto fetch = [&](GgRegs& g, int sn) {
+        const size_t kb = (size_t)sn * 128;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g.b[q] = load16(bsrc + (size_t)q * 8 * rowb + kb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // w2: rows past the tile's end read a row of the next tile (or the clamped
+            // last row): never stored
+            const size_t ar = W13 ? (size_t)aoff[q] : (size_t)min((int)arow0 + q * 8, row0 + rows - 1) * rowb;
+            g.a[q] = load16(abase + ar + kb);
+        }
+    };
+    auto put = [&](const GgRegs& g, char* buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<uint4*>(buf + dst0 + q * 1024) = g.a[q];
+            *reinterpret_cast<uint4*>(buf + gg::kTileBytes + dst0 + q * 1024) = g.b[q];
+        }
+    };
+    const int nb = (rows + kGBM - 1) / kGBM;        // row blocks present (uniform)
+    const bool m0 = 2 * wr < nb, m1 = 2 * wr + 1 < nb;
+    // weight blocks of the wave: W13 gate / up rows of its 32 columns, else two column blocks
+    const int n0 = W13 ? wc * 32 : wc * 64;
+    const int n1 = W13 ? 64 + wc * 32 : wc * 64 + 32;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+    auto compute = [&](const char* A) {
+        const char* B = A + gg::kTileBytes;
+        if (m0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int pos = ((4 * hl + j) ^ (l32 & 7)) * 16;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(A + (2 * wr * 32 + l32) * 128 + pos);
+                const uint4 b0 = *reinterpret_cast<const uint4*>(B + (n0 + l32) * 128 + pos);
+                const uint4 b1 = *reinterpret_cast<const uint4*>(B + (n1 + l32) * 128 + pos);
+                acc[0][0] = mfma_32x32x16(a0, b0, acc[0][0]);
+                acc[0][1] = mfma_32x32x16(a0, b1, acc[0][1]);
+                if (m1) {
+                    const uint4 a1 = *reinterpret_cast<const uint4*>(A + ((2 * wr + 1) * 32 + l32) * 128 + pos);
+                    acc[1][0] = mfma_32x32x16(a1, b0, acc[1][0]);
+                    acc[1][1] = mfma_32x32x16(a1, b1, acc[1][1]);
+                }
+            }
+        }
+    };
+    // span s: request span s + 2 (into the set span s came from), the MFMAs of span s
+    // (LDS buffer s % 2), then span s + 1 into the other buffer (last read by span s - 1,
+    // before the previous barrier).  The requests are never inside a branch, so the
+    // compiler's wait before a write to LDS counts exactly the loads issued after that
+    // span's: the last two spans run from a copy of the loop without the requests.
+    GgRegs rx, ry;
+    auto step = [&](int s, GgRegs& ahead, const GgRegs& next, bool fetch_ahead, bool put_next) {
+        if (fetch_ahead) fetch(ahead, s + 2);
+        compute(lds[s & 1]);
+        if (put_next) put(next, lds[(s + 1) & 1]);
+        __syncthreads();
+    };
+    fetch(rx, 0);
+    fetch(ry, 1);
+    put(rx, lds[0]);
+    __syncthreads();
+    int sn = 0;
+    for (; sn + 2 < nsp; sn += 2) {
+        step(sn, rx, ry, true, true);
+        step(sn + 1, ry, rx, true, true);
+    }
+    step(sn, rx, ry, false, true);
+    step(sn + 1, ry, rx, false, false);
+    // epilogue: accumulator element i of row block m is tile row m*32 + 8(i/4) + 4 hl + i%4
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int m = 2 * wr + mi;
+        if (m >= nb) break;
+        if (W13) {
+            const int col = c0 + wc * 32 + l32;
+            if (col < ncols)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    if (r < rows)
+                        static_cast<uint16_t*>(out)[(size_t)(row0 + r) * ncols + col] =
+                            f32_to_bf16_rne(silu(acc[mi][0][i]) * acc[mi][1][i]);
+                }
+        } else {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int col = c0 + wc * 64 + ni * 32 + l32;
+                if (col < ncols)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
+                        if (r < rows) static_cast<float*>(out)[(size_t)perm[row0 + r] * ncols + col] = acc[mi][ni][i];
+                    }
+            }
+        }
+    }
+}
+
 // ---- ordered top-k combine (grouped path) -------------------------------------------
 // out[t][h] = resid[t][h] + sum_{k = 0..K-1} w[t][k] * y[t*K + k][h]   (k in order;
 // pairs whose slot id is out of range contribute nothing).  grid.y walks the tokens
@@ -1766,6 +1932,18 @@ int grouped_mt(int n_pairs, int n_experts) {
     return per >= 40 ? 4 : 1;
 }
 
+template <int AT>
+hipError_t launch_grouped_combine(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
+    const dim3 gc((unsigned)((g.H / 4 + 255) / 256), (unsigned)(a.T < 65535 ? a.T : 65535));
+    if (ev && ev->w2_stop)
+        hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.sl, a.y, a.topk_w,
+                              a.slot_ids, a.resid, a.out, a.T, g.K, g.H);
+    else
+        hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.sl, a.y, a.topk_w, a.slot_ids, a.resid, a.out,
+                           a.T, g.K, g.H);
+    return hipGetLastError();
+}
+
 template <int AT, int MT>
 hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     const int n = a.T * g.K;
@@ -1777,6 +1955,39 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* act = static_cast<uint16_t*>(a.act);
+    if (MT == 4 && g.H % 256 == 0 && g.I % 256 == 0 && (size_t)a.T * g.H * 2 < ((size_t)1 << 32)) {
+        // tiles of 128 rows: both operands through LDS (k_gg); fp32 activations keep the
+        // staged w13 kernel, which converts them while staging
+        const int gcb13 = ((g.I + 63) / 64 + 7) / 8 * 8, gcb2 = ((g.H + 127) / 128 + 7) / 8 * 8;
+        const dim3 gg13((unsigned)(tiles * gcb13)), gg2((unsigned)(tiles * gcb2));
+        if (AT == A_BF16) {
+            if (ev && ev->w13_start)
+                hipExtLaunchKernelGGL((k_gg<true>), gg13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
+                                      g.slot_stride, a.grp, stride_t, static_cast<const uint16_t*>(a.x), g.K, g.H, g.I,
+                                      g.off_w13, (void*)act, gcb13);
+            else
+                hipLaunchKernelGGL((k_gg<true>), gg13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
+                                   static_cast<const uint16_t*>(a.x), g.K, g.H, g.I, g.off_w13, (void*)act, gcb13);
+        } else {
+            const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8;
+            const dim3 g13((unsigned)(tiles * ncb13));
+            if (ev && ev->w13_start)
+                hipExtLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0,
+                                      a.sl, g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
+            else
+                hipLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp,
+                                   stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (ev && ev->w2_start)
+            hipExtLaunchKernelGGL((k_gg<false>), gg2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
+                                  a.grp, stride_t, (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, gcb2);
+        else
+            hipLaunchKernelGGL((k_gg<false>), gg2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
+                               (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, gcb2);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return launch_grouped_combine<AT>(g, a, ev, s);
+    }
     const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8, ncb2 = ((g.H + kGBN - 1) / kGBN + 7) / 8 * 8;
     const dim3 g13((unsigned)(tiles * ncb13)), g2((unsigned)(tiles * ncb2));
     if (ev && ev->w13_start)
@@ -1793,14 +2004,7 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
         hipLaunchKernelGGL((k_grouped_w2<MT>), g2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t, act, g.H,
                            g.I, g.off_w2, a.y, ncb2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 gc((unsigned)((g.H / 4 + 255) / 256), (unsigned)(a.T < 65535 ? a.T : 65535));
-    if (ev && ev->w2_stop)
-        hipExtLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, nullptr, ev->w2_stop, 0, a.sl, a.y, a.topk_w,
-                              a.slot_ids, a.resid, a.out, a.T, g.K, g.H);
-    else
-        hipLaunchKernelGGL((k_combine<AT>), gc, dim3(256), 0, s, a.sl, a.y, a.topk_w, a.slot_ids, a.resid, a.out,
-                           a.T, g.K, g.H);
-    return hipGetLastError();
+    return launch_grouped_combine<AT>(g, a, ev, s);
 }
 
 template <int AT>

@@ -242,14 +242,17 @@ def test_step_equals_prepare_then_forward():
 
 @pytest.mark.parametrize("T", [9, 33, 64, 128, 256])
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
-def test_grouped_path_oracle_and_bitwise_across_paths(T, atype):
+@pytest.mark.parametrize("inter", [128, 256])
+def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
     """n_tokens above the decode limit run the slot-grouped MFMA GEMMs.  With skewed
     routing some slot groups span several tiles (T = 128 and 256 give ~21 and ~43
     pairs per expert: tiles of 64 and 128 rows, i.e. 2 and 4 row blocks per wave,
     with ragged last blocks).  All experts resident, a pool large enough for every
     step, and a pool small enough that every step falls back to staging must give the
-    same bits; all within tolerance of the oracle."""
-    wl = synth.Workload("grouped", 1, 24, 4, 256, 128, 24, T, 0, "bf16", atype, 1.3, 0.0, 0, 13)
+    same bits; all within tolerance of the oracle.  With intermediate 256 (hidden and
+    intermediate multiples of 256) the 128-row tiles run the GEMMs that stage both
+    operands through LDS."""
+    wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, T, 0, "bf16", atype, 1.3, 0.0, 0, 13)
     trace = synth.make_trace(wl, steps=4)
     xs, ws = _inputs(wl, 4, T)
     big = Rig(wl, slots=24, std=0.05)
@@ -271,11 +274,13 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype):
 
 
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
-def test_grouped_rows_do_not_depend_on_the_batch(atype):
+@pytest.mark.parametrize("inter", [128, 256])
+def test_grouped_rows_do_not_depend_on_the_batch(atype, inter):
     """A token's output depends only on its own inputs: computed in a 256-token step
-    (4 row blocks per wave, 128-row tiles) and again in a 12-token step (1 block per
-    wave) it has the same bits."""
-    wl = synth.Workload("grouped", 1, 24, 4, 256, 128, 24, 256, 0, "bf16", atype, 1.3, 0.0, 0, 14)
+    (128-row tiles; with intermediate 256 the kernels that stage both operands through
+    LDS) and again in a 12-token step (32-row tiles, the staged-activation kernels) it
+    has the same bits."""
+    wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, 256, 0, "bf16", atype, 1.3, 0.0, 0, 14)
     trace = synth.make_trace(wl, steps=1)
     xs, ws = _inputs(wl, 1, 256)
     rig = Rig(wl, slots=24, resident=True, std=0.05)
