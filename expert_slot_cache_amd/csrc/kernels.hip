@@ -1473,37 +1473,39 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
 }
 
 // ---- grouped GEMMs for large slot groups: both operands through LDS -------------------
-// A workgroup computes a tile of 128 rows (4 MFMA blocks of 32) x 128 weight rows (w13:
-// 64 gate + the matching 64 up rows; w2: 128 output columns).  Each 64-element k span of
-// both operands (64 bytes of A and 64 of weights per thread) is loaded into registers
-// two spans ahead (two register sets), then written into one of two LDS buffers the
-// span before its MFMAs read it; two workgroups share a CU (64 KiB of LDS each), so one
-// computes while the other waits for memory.  (Three spans ahead needed more than the
-// 256 registers of two workgroups per CU and spilled; one workgroup per CU with three
-// spans ahead was 1.3x slower.)  A tile row is 128 bytes in
-// LDS with its 16-byte chunk c at position c ^ (row & 7), so the 32 rows one MFMA
-// operand reads hit distinct banks.  Waves: 2 x 2, each 2 row blocks x 2 weight blocks.
+// A workgroup of 4 waves (2 x 2) computes a tile of 64*WR rows x 64*WC weight rows (w13:
+// the gate rows of 32*WC columns and the matching up rows; w2: 64*WC output columns);
+// each wave owns WR row blocks x WC weight blocks of 32 (WR*WC accumulators).  Each
+// 64-element k span of both operands is loaded into registers two spans ahead (two
+// register sets), then written into one of two LDS buffers the span before its MFMAs
+// read it.  A tile row is 128 bytes in LDS with its 16-byte chunk c at position
+// c ^ (row & 7), so the 32 rows one MFMA operand reads hit distinct banks.
+// The library uses WR = WC = 2: 128-row tiles, 64 KiB of LDS, two workgroups per CU (one
+// computes while the other waits for memory).  (Measured and not used: three spans ahead
+// needed more than the 256 registers of two workgroups per CU and spilled; one 128-row
+// workgroup per CU with three spans ahead was 1.3x slower; WR = WC = 4, 256-row tiles
+// with half an LDS operand read per MFMA but one workgroup per CU, 1.4x slower.)
 // Per accumulator the k order (spans in order, then MFMA j = 0..3 with the lane-half
 // element split of the staged kernels) is the one of k_grouped_w13 / k_grouped_w2, so
 // every output row has the same bits whichever kernel computed it.
-namespace gg {
-constexpr int kTileBytes = 128 * 128;           // one operand of one span: 128 rows x 128 B
-constexpr int kBufBytes = 2 * kTileBytes;       // A then weights
-}  // namespace gg
 
-// The span's copies of one thread: rows q = 0..3 of its 1 KiB blocks, A then weights.
+// The span's copies of one thread: NA chunks of A rows, NB of weight rows.
+template <int NA, int NB>
 struct GgRegs {
-    uint4 a[4], b[4];
+    uint4 a[NA], b[NB];
 };
 
-template <bool W13>
-__global__ __launch_bounds__(256, 2) void k_gg(Slots sl, size_t stride, const int32_t* __restrict__ grp,
-                                               int tile_stride, const uint16_t* __restrict__ a_src, int K, int Kd,
-                                               int ncols, size_t off_w, void* __restrict__ out, int ncbp) {
-    __shared__ __attribute__((aligned(1024))) char lds[2][gg::kBufBytes];
+template <bool W13, int WR, int WC>
+__global__ __launch_bounds__(256, (WR * WC > 4 ? 1 : 2)) void k_gg(Slots sl, size_t stride,
+        const int32_t* __restrict__ grp, int tile_stride, const uint16_t* __restrict__ a_src, int K, int Kd,
+        int ncols, size_t off_w, void* __restrict__ out, int ncbp) {
+    constexpr int RA = 64 * WR, RB = 64 * WC;        // tile rows of A and of the weights
+    constexpr int NA = RA / 32, NB = RB / 32;        // chunks per thread and span
+    constexpr int TA = RA * 128, TB = RB * 128;      // LDS bytes of one span
+    __shared__ __attribute__((aligned(1024))) char lds[2][TA + TB];
     const int cbk = blockIdx.x % ncbp;
     const int tile = blockIdx.x / ncbp;
-    const int cspan = W13 ? 64 : 128;               // output columns per workgroup
+    constexpr int cspan = W13 ? RB / 2 : RB;        // output columns per workgroup
     if (tile >= grp[0] || cbk * cspan >= ncols) return;
     const SlotSpan sp = pick_slots(sl);
     const int slot = grp[16 + tile];
@@ -1519,69 +1521,81 @@ __global__ __launch_bounds__(256, 2) void k_gg(Slots sl, size_t stride, const in
     const int c0 = cbk * cspan;
     const char* wbase = sp.at(slot, stride) + off_w;
     const size_t rowb = (size_t)Kd * 2;
-    // this thread copies chunk lane % 8 of tile rows w*32 + q*8 + lane/8 (q = 0..3) of
-    // both operands.  Weight rows are consecutive (the column blocks never pass the end:
-    // the shapes are multiples of 256), so are A rows for w2; w13 gathers its A rows.
-    // In LDS the chunk goes to position (lane % 8) ^ (lane / 8) of its row.
+    // this thread copies chunk lane % 8 of A rows w*RA/4 + q*8 + lane/8 (q < NA) and of
+    // weight rows w*RB/4 + q*8 + lane/8 (q < NB).  Weight rows are consecutive within a
+    // wave's share (the column blocks never pass the end: the shapes are multiples of
+    // 256, and a wave's share lies in one of the w13 gate / up halves), so are A rows for
+    // w2; w13 gathers its A rows.  In LDS the chunk goes to position (lane % 8) ^ (lane / 8)
+    // of its row.
     const int ck = lane & 7;
-    const int rb0 = w * 32 + (lane >> 3);
-    const int dst0 = rb0 * 128 + ((ck ^ (lane >> 3)) * 16);
-    const int wrow0 = W13 ? (rb0 < 64 ? c0 + rb0 : ncols + c0 + rb0 - 64) : c0 + rb0;
+    const int ra0 = w * (RA / 4) + (lane >> 3);
+    const int rb0 = w * (RB / 4) + (lane >> 3);
+    const int swz = (ck ^ (lane >> 3)) * 16;
+    const int wrow0 = W13 ? (rb0 < RB / 2 ? c0 + rb0 : ncols + c0 + rb0 - RB / 2) : c0 + rb0;
     const char* bsrc = wbase + (size_t)wrow0 * rowb + ck * 16;
     const char* abase = reinterpret_cast<const char*>(a_src) + ck * 16;
-    uint32_t aoff[4];                               // w13: byte offsets of the gathered rows
+    uint32_t aoff[W13 ? NA : 1];                    // w13: byte offsets of the gathered rows
     size_t arow0 = 0;
-    if (W13) {
+    if constexpr (W13) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            aoff[q] = (uint32_t)((size_t)(perm[row0 + min(rb0 + q * 8, rows - 1)] / K) * rowb);
+        for (int q = 0; q < NA; ++q)
+            aoff[q] = (uint32_t)((size_t)(perm[row0 + min(ra0 + q * 8, rows - 1)] / K) * rowb);
     } else {
-        arow0 = (size_t)(row0 + rb0);
+        arow0 = (size_t)(row0 + ra0);
     }
-    const int nsp = Kd / 64;                        // a multiple of 4
-    auto fetch = [&](GgRegs& g, int sn) {
+    const int nsp = Kd / 64;                        // even
+    using Regs = GgRegs<NA, NB>;
+    auto fetch = [&](Regs& g, int sn) {
         const size_t kb = (size_t)sn * 128;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) g.b[q] = load16(bsrc + (size_t)q * 8 * rowb + kb);
+        for (int q = 0; q < NB; ++q) g.b[q] = load16(bsrc + (size_t)q * 8 * rowb + kb);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // w2: rows past the tile's end read a row of the next tile (or the clamped
-            // last row): never stored
-            const size_t ar = W13 ? (size_t)aoff[q] : (size_t)min((int)arow0 + q * 8, row0 + rows - 1) * rowb;
+        for (int q = 0; q < NA; ++q) {
+            // w2: rows past the tile's end read the clamped last row: never stored
+            size_t ar;
+            if constexpr (W13) ar = (size_t)aoff[q];
+            else ar = (size_t)min((int)arow0 + q * 8, row0 + rows - 1) * rowb;
             g.a[q] = load16(abase + ar + kb);
         }
     };
-    auto put = [&](const GgRegs& g, char* buf) {
+    auto put = [&](const Regs& g, char* buf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<uint4*>(buf + dst0 + q * 1024) = g.a[q];
-            *reinterpret_cast<uint4*>(buf + gg::kTileBytes + dst0 + q * 1024) = g.b[q];
-        }
+        for (int q = 0; q < NA; ++q)
+            *reinterpret_cast<uint4*>(buf + (ra0 + q * 8) * 128 + swz) = g.a[q];
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+            *reinterpret_cast<uint4*>(buf + TA + (rb0 + q * 8) * 128 + swz) = g.b[q];
     };
     const int nb = (rows + kGBM - 1) / kGBM;        // row blocks present (uniform)
-    const bool m0 = 2 * wr < nb, m1 = 2 * wr + 1 < nb;
-    // weight blocks of the wave: W13 gate / up rows of its 32 columns, else two column blocks
-    const int n0 = W13 ? wc * 32 : wc * 64;
-    const int n1 = W13 ? 64 + wc * 32 : wc * 64 + 32;
-    f32x16_t acc[2][2];
+    const int mfirst = wr * WR;                      // the wave's first row block
+    // the wave's weight blocks: w13 gate blocks 0 .. WC/2-1 of its 32*WC/2 columns, then
+    // the matching up blocks; w2 WC consecutive column blocks
+    int nbk[WC];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+    for (int bi = 0; bi < WC; ++bi) {
+        if (W13) nbk[bi] = bi < WC / 2 ? wc * (WC / 2) * 32 + bi * 32 : RB / 2 + wc * (WC / 2) * 32 + (bi - WC / 2) * 32;
+        else nbk[bi] = wc * WC * 32 + bi * 32;
+    }
+    f32x16_t acc[WR][WC];
+#pragma unroll
+    for (int mi = 0; mi < WR; ++mi)
+#pragma unroll
+        for (int bi = 0; bi < WC; ++bi) acc[mi][bi] = f32x16_t{};
     auto compute = [&](const char* A) {
-        const char* B = A + gg::kTileBytes;
-        if (m0) {
+        const char* B = A + TA;
+        if (mfirst >= nb) return;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pos = ((4 * hl + j) ^ (l32 & 7)) * 16;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(A + (2 * wr * 32 + l32) * 128 + pos);
-                const uint4 b0 = *reinterpret_cast<const uint4*>(B + (n0 + l32) * 128 + pos);
-                const uint4 b1 = *reinterpret_cast<const uint4*>(B + (n1 + l32) * 128 + pos);
-                acc[0][0] = mfma_32x32x16(a0, b0, acc[0][0]);
-                acc[0][1] = mfma_32x32x16(a0, b1, acc[0][1]);
-                if (m1) {
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(A + ((2 * wr + 1) * 32 + l32) * 128 + pos);
-                    acc[1][0] = mfma_32x32x16(a1, b0, acc[1][0]);
-                    acc[1][1] = mfma_32x32x16(a1, b1, acc[1][1]);
-                }
+        for (int j = 0; j < 4; ++j) {
+            const int pos = ((4 * hl + j) ^ (l32 & 7)) * 16;
+            uint4 bf[WC];
+#pragma unroll
+            for (int bi = 0; bi < WC; ++bi) bf[bi] = *reinterpret_cast<const uint4*>(B + (nbk[bi] + l32) * 128 + pos);
+#pragma unroll
+            for (int mi = 0; mi < WR; ++mi) {
+                if (mfirst + mi >= nb) break;
+                const uint4 af = *reinterpret_cast<const uint4*>(A + ((mfirst + mi) * 32 + l32) * 128 + pos);
+#pragma unroll
+                for (int bi = 0; bi < WC; ++bi) acc[mi][bi] = mfma_32x32x16(af, bf[bi], acc[mi][bi]);
             }
         }
     };
@@ -1590,8 +1604,8 @@ __global__ __launch_bounds__(256, 2) void k_gg(Slots sl, size_t stride, const in
     // before the previous barrier).  The requests are never inside a branch, so the
     // compiler's wait before a write to LDS counts exactly the loads issued after that
     // span's: the last two spans run from a copy of the loop without the requests.
-    GgRegs rx, ry;
-    auto step = [&](int s, GgRegs& ahead, const GgRegs& next, bool fetch_ahead, bool put_next) {
+    Regs rx, ry;
+    auto step = [&](int s, Regs& ahead, const Regs& next, bool fetch_ahead, bool put_next) {
         if (fetch_ahead) fetch(ahead, s + 2);
         compute(lds[s & 1]);
         if (put_next) put(next, lds[(s + 1) & 1]);
@@ -1610,28 +1624,31 @@ __global__ __launch_bounds__(256, 2) void k_gg(Slots sl, size_t stride, const in
     step(sn + 1, ry, rx, false, false);
     // epilogue: accumulator element i of row block m is tile row m*32 + 8(i/4) + 4 hl + i%4
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int m = 2 * wr + mi;
+    for (int mi = 0; mi < WR; ++mi) {
+        const int m = mfirst + mi;
         if (m >= nb) break;
         if (W13) {
-            const int col = c0 + wc * 32 + l32;
-            if (col < ncols)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
-                    if (r < rows)
-                        static_cast<uint16_t*>(out)[(size_t)(row0 + r) * ncols + col] =
-                            f32_to_bf16_rne(silu(acc[mi][0][i]) * acc[mi][1][i]);
-                }
-        } else {
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int col = c0 + wc * 64 + ni * 32 + l32;
+            for (int p = 0; p < WC / 2; ++p) {
+                const int col = c0 + wc * (WC / 2) * 32 + p * 32 + l32;
                 if (col < ncols)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
-                        if (r < rows) static_cast<float*>(out)[(size_t)perm[row0 + r] * ncols + col] = acc[mi][ni][i];
+                        if (r < rows)
+                            static_cast<uint16_t*>(out)[(size_t)(row0 + r) * ncols + col] =
+                                f32_to_bf16_rne(silu(acc[mi][p][i]) * acc[mi][WC / 2 + p][i]);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int bi = 0; bi < WC; ++bi) {
+                const int col = c0 + wc * WC * 32 + bi * 32 + l32;
+                if (col < ncols)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int r = m * kGBM + 8 * (i >> 2) + 4 * hl + (i & 3);
+                        if (r < rows) static_cast<float*>(out)[(size_t)perm[row0 + r] * ncols + col] = acc[mi][bi][i];
                     }
             }
         }
@@ -1918,11 +1935,13 @@ bool grouped_shape(int wtype, int H, int I) { return wtype == W_BF16 && H % 64 =
 
 namespace {
 
-// Row blocks per wave of the grouped GEMMs, from the average pairs per expert
-// (the weights of a slot are read once per tile; small groups keep one block).
+// Rows per tile of the grouped GEMMs (MT blocks of 32), from the average pairs per
+// expert (the weights of a slot are read once per tile; small groups keep one block).
 // Measured on OLMoE-shaped prefill (skewed routing, 64 and 256 pairs per expert on
 // average): 4 blocks match 1 at 64 and run the layer 1.4x faster at 256; 2 blocks
-// were slower than either for w2, so they are not chosen.
+// were slower than either for w2, so they are not chosen.  (256-row tiles through the
+// LDS-staged kernels, one workgroup per CU, were 1.4x slower than 128-row tiles at 256
+// pairs per expert.)
 #ifndef MOE_GROUPED_MT
 #define MOE_GROUPED_MT 0
 #endif
@@ -1944,6 +1963,13 @@ hipError_t launch_grouped_combine(const Geom& g, const ForwardArgs& a, const Sta
     return hipGetLastError();
 }
 
+// Whether the LDS-staged grouped kernels (k_gg) take this shape: hidden and intermediate
+// multiples of 256 (whole column blocks, an even number of k spans) and byte offsets of
+// the activation rows within 32 bits.
+bool gg_shape(const Geom& g, const ForwardArgs& a) {
+    return g.H % 256 == 0 && g.I % 256 == 0 && (size_t)a.T * g.H * 2 < ((size_t)1 << 32);
+}
+
 template <int AT, int MT>
 hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents* ev, hipStream_t s) {
     const int n = a.T * g.K;
@@ -1955,35 +1981,37 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint16_t* act = static_cast<uint16_t*>(a.act);
-    if (MT == 4 && g.H % 256 == 0 && g.I % 256 == 0 && (size_t)a.T * g.H * 2 < ((size_t)1 << 32)) {
+    if (gg_shape(g, a) && MT == 4) {
         // tiles of 128 rows: both operands through LDS (k_gg); fp32 activations keep the
         // staged w13 kernel, which converts them while staging
-        const int gcb13 = ((g.I + 63) / 64 + 7) / 8 * 8, gcb2 = ((g.H + 127) / 128 + 7) / 8 * 8;
+        constexpr int W = 2;
+        const int gcb13 = ((g.I + 32 * W - 1) / (32 * W) + 7) / 8 * 8, gcb2 = ((g.H + 64 * W - 1) / (64 * W) + 7) / 8 * 8;
         const dim3 gg13((unsigned)(tiles * gcb13)), gg2((unsigned)(tiles * gcb2));
         if (AT == A_BF16) {
             if (ev && ev->w13_start)
-                hipExtLaunchKernelGGL((k_gg<true>), gg13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
+                hipExtLaunchKernelGGL((k_gg<true, W, W>), gg13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
                                       g.slot_stride, a.grp, stride_t, static_cast<const uint16_t*>(a.x), g.K, g.H, g.I,
                                       g.off_w13, (void*)act, gcb13);
             else
-                hipLaunchKernelGGL((k_gg<true>), gg13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
+                hipLaunchKernelGGL((k_gg<true, W, W>), gg13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
                                    static_cast<const uint16_t*>(a.x), g.K, g.H, g.I, g.off_w13, (void*)act, gcb13);
         } else {
             const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8;
             const dim3 g13((unsigned)(tiles * ncb13));
             if (ev && ev->w13_start)
-                hipExtLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0,
+                hipExtLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0,
                                       a.sl, g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
             else
-                hipLaunchKernelGGL((k_grouped_w13<AT, MT>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp,
+                hipLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp,
                                    stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (ev && ev->w2_start)
-            hipExtLaunchKernelGGL((k_gg<false>), gg2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl, g.slot_stride,
-                                  a.grp, stride_t, (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, gcb2);
+            hipExtLaunchKernelGGL((k_gg<false, W, W>), gg2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl,
+                                  g.slot_stride, a.grp, stride_t, (const uint16_t*)act, g.K, g.I, g.H, g.off_w2,
+                                  (void*)a.y, gcb2);
         else
-            hipLaunchKernelGGL((k_gg<false>), gg2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
+            hipLaunchKernelGGL((k_gg<false, W, W>), gg2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
                                (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, gcb2);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return launch_grouped_combine<AT>(g, a, ev, s);

@@ -240,7 +240,7 @@ def test_step_equals_prepare_then_forward():
     b.close()
 
 
-@pytest.mark.parametrize("T", [9, 33, 64, 128, 256])
+@pytest.mark.parametrize("T", [9, 33, 64, 128, 256, 1024])
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
 @pytest.mark.parametrize("inter", [128, 256])
 def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
@@ -251,7 +251,7 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
     step, and a pool small enough that every step falls back to staging must give the
     same bits; all within tolerance of the oracle.  With intermediate 256 (hidden and
     intermediate multiples of 256) the 128-row tiles run the GEMMs that stage both
-    operands through LDS."""
+    operands through LDS (T = 1024: ~170 pairs per expert, groups over several tiles)."""
     wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, T, 0, "bf16", atype, 1.3, 0.0, 0, 13)
     trace = synth.make_trace(wl, steps=4)
     xs, ws = _inputs(wl, 4, T)
@@ -274,15 +274,15 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
 
 
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
-@pytest.mark.parametrize("inter", [128, 256])
-def test_grouped_rows_do_not_depend_on_the_batch(atype, inter):
-    """A token's output depends only on its own inputs: computed in a 256-token step
-    (128-row tiles; with intermediate 256 the kernels that stage both operands through
-    LDS) and again in a 12-token step (32-row tiles, the staged-activation kernels) it
-    has the same bits."""
-    wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, 256, 0, "bf16", atype, 1.3, 0.0, 0, 14)
+@pytest.mark.parametrize("inter,tokens", [(128, 256), (256, 256), (256, 1024)])
+def test_grouped_rows_do_not_depend_on_the_batch(atype, inter, tokens):
+    """A token's output depends only on its own inputs: computed in a 256- or 1024-token
+    step (128-row tiles; with intermediate 256 the kernels that stage both operands
+    through LDS) and again in a 12-token step (32-row tiles, the staged-activation
+    kernels) it has the same bits."""
+    wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, tokens, 0, "bf16", atype, 1.3, 0.0, 0, 14)
     trace = synth.make_trace(wl, steps=1)
-    xs, ws = _inputs(wl, 1, 256)
+    xs, ws = _inputs(wl, 1, tokens)
     rig = Rig(wl, slots=24, resident=True, std=0.05)
     _, _, _, out_all = rig.step(0, trace[0, 0], to_dev_act(xs[0], atype), torch.from_numpy(ws[0]).to(DEV))
     got_all = from_dev_act(out_all)
