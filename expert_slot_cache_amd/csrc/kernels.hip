@@ -810,36 +810,59 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
     const int K = pa.n;                    // one token: n == top_k
     const int tid = threadIdx.x;
     const int E = pa.E, N = pa.N;
-    const int par = pa.ds.ctl[0] & 1;
-    char* cur_base = pa.ds.copy[par];
+    // the slot base with the first kernel-argument loads, not after the lookups below
+    __asm__ volatile("" ::"s"(pa.slots));
     const bool lead = b == 0;
     const int g = b - 1 - n_copy;              // GEMV block index (when >= 0)
-    const int k = g >= 0 ? g / nrb : 0;
+    const int k = max(g, 0) / nrb;             // (no branch before the loads below)
     const int rblk = g - k * nrb;
     // The step's ids and their entries in the current map, through the scalar cache
-    // (uniform addresses; the current copy is only read during this launch): eight ids
-    // per round, every load of a round issued before the first is used.
+    // (uniform addresses; neither the ids, the control word nor the current copy's map
+    // is written during this launch): the control word is read with the first eight
+    // ids and the copy picked from the kernel arguments, so that the chain before the
+    // weight loads is arguments -> ids -> map.  Eight ids per round, with no branch
+    // between the loads of a round.
     typedef const __attribute__((address_space(4))) int32_t cint4;
     cint4* ids4 = (cint4*)pa.ids;
-    cint4* map4 = (cint4*)(cur_base + slot_state_layout(E, N).map);
     int bad = 0, myslot = -1;
-    for (int k0 = 0; k0 < K; k0 += 8) {
-        int idv[8], mv[8];
+    auto load_ids = [&](int k0, int (&idv)[8]) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) idv[q] = ids4[min(k0 + q, K - 1)];
+    };
+    auto lookup = [&](cint4* map4, int k0, const int (&idv)[8]) {
+        int mv[8], nres = 0;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const bool ok = (unsigned)idv[q] < (unsigned)E;
             bad |= !ok;
-            mv[q] = pa.resident ? idv[q] : map4[ok ? idv[q] : 0];
+            mv[q] = map4[ok ? idv[q] : 0];      // (also in the all-resident mode: a select, not a branch)
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            bad |= mv[q] < 0;
-            myslot = k0 + q == k ? mv[q] : myslot;
+            const int m = pa.resident ? idv[q] : mv[q];
+            nres |= m;
+            myslot = k0 + q == k ? m : myslot;
         }
+        bad |= nres < 0;                         // some entry was -1 (not resident)
+    };
+    int id0[8];
+    load_ids(0, id0);
+    const int par = *(cint4*)pa.ds.ctl & 1;
+    char* cur_base = par ? pa.ds.copy[1] : pa.ds.copy[0];
+    cint4* map4 = (cint4*)(cur_base + slot_state_layout(E, N).map);
+    lookup(map4, 0, id0);
+    for (int k0 = 8; k0 < K; k0 += 8) {
+        int idn[8];
+        load_ids(k0, idn);
+        lookup(map4, k0, idn);
     }
     const bool fast = !bad && (pa.resident || pa.rule == 0 || K <= N);
+    if (g >= 0 && fast) {
+        // every id hits: the map stays as it is, and this block's expert is at myslot
+        const PairIn pin{pa.slots + (size_t)myslot * stride, nullptr, true};
+        w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, 0, k, rblk, red, dyn + xs_off);
+        return;
+    }
     if (lead && fast && !pa.resident && pa.evict != EVICT_SLRU) {
         // an all-hit step changes keys only: in place, and the copies keep their roles
         pol_hit_in_place(pa, slot_view(cur_base, E, N), K);
@@ -897,9 +920,7 @@ __global__ __launch_bounds__(256) void k_step_w13(PolicyArgs pa, size_t stride, 
     }
     const int e = ids4[k];
     PairIn pin{pa.slots, nullptr, false};
-    if (fast) {
-        pin = PairIn{pa.slots + (size_t)myslot * stride, nullptr, true};
-    } else if (d.path == PATH_POOL) {
+    if (d.path == PATH_POOL) {
         const int slot = __builtin_amdgcn_readfirstlane(pa.resident ? e : L.map[e]);
         const bool miss = !pa.resident && __builtin_amdgcn_readfirstlane(L.rank[e]) < 0;
         pin = miss ? PairIn{pol_src(pa, e), pa.slots + (size_t)slot * stride, true}

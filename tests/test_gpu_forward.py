@@ -240,7 +240,7 @@ def test_step_equals_prepare_then_forward():
     b.close()
 
 
-@pytest.mark.parametrize("T", [9, 33, 64, 128, 256, 1024])
+@pytest.mark.parametrize("T", [9, 33, 64, 128, 256, 1024, 2048])
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
 @pytest.mark.parametrize("inter", [128, 256])
 def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
@@ -251,7 +251,8 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
     step, and a pool small enough that every step falls back to staging must give the
     same bits; all within tolerance of the oracle.  With intermediate 256 (hidden and
     intermediate multiples of 256) the 128-row tiles run the GEMMs that stage both
-    operands through LDS (T = 1024: ~170 pairs per expert, groups over several tiles)."""
+    operands through LDS (T = 1024 and 2048: ~170 and ~340 pairs per expert, groups
+    over several tiles)."""
     wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, T, 0, "bf16", atype, 1.3, 0.0, 0, 13)
     trace = synth.make_trace(wl, steps=4)
     xs, ws = _inputs(wl, 4, T)
@@ -274,12 +275,12 @@ def test_grouped_path_oracle_and_bitwise_across_paths(T, atype, inter):
 
 
 @pytest.mark.parametrize("atype", ["bf16", "f32"])
-@pytest.mark.parametrize("inter,tokens", [(128, 256), (256, 256), (256, 1024)])
+@pytest.mark.parametrize("inter,tokens", [(128, 256), (256, 256), (256, 1024), (256, 2048)])
 def test_grouped_rows_do_not_depend_on_the_batch(atype, inter, tokens):
-    """A token's output depends only on its own inputs: computed in a 256- or 1024-token
-    step (128-row tiles; with intermediate 256 the kernels that stage both operands
-    through LDS) and again in a 12-token step (32-row tiles, the staged-activation
-    kernels) it has the same bits."""
+    """A token's output depends only on its own inputs: computed in a 256-, 1024- or
+    2048-token step (128-row tiles; with intermediate 256 the kernels that stage both
+    operands through LDS) and again in a 12-token step (32-row tiles, the
+    staged-activation kernels) it has the same bits."""
     wl = synth.Workload("grouped", 1, 24, 4, 256, inter, 24, tokens, 0, "bf16", atype, 1.3, 0.0, 0, 14)
     trace = synth.make_trace(wl, steps=1)
     xs, ws = _inputs(wl, 1, tokens)

@@ -116,3 +116,35 @@ def test_read_through_timing_splits_link_and_hbm_launches():
     gbps = tm["copy_bytes"] / (tm["copy_ms"] * 1e-3) / 1e9
     assert 5.0 < gbps < 80.0, gbps
     rig.close()
+
+
+@pytest.mark.parametrize("wl", [
+    synth.WORKLOADS["olmoe_bf16_e64"].with_(layers=2),
+    # top-10 (two rounds of ids), INT4 weights
+    synth.Workload("rtres10", 1, 40, 10, 256, 128, 40, 1, 0, "int4", "bf16", 0.8, 0.2, 0, 53),
+], ids=["olmoe", "int4-top10"])
+def test_read_through_all_resident_equals_copying_step(wl):
+    """In the all-resident mode every id hits at slot = id: the fused step's lookup
+    (which still reads the state's map, and drops it) gives the copying step's slot
+    ids, counters and output bits."""
+    steps = 6
+    trace = synth.make_trace(wl, steps=steps)
+    _, _, rx, rw = synth.streams(wl)
+    copy = Rig(wl, slots=wl.experts, one_call=True, policy="device", resident=True)
+    rt = Rig(wl, slots=wl.experts, one_call=True, policy="device", resident=True, read_through=True,
+             experts=copy.experts)
+    for s in range(steps):
+        x = synth.draw_activations(rx, (1, wl.hidden), wl.atype)
+        w = synth.draw_gate_weights(rw, (1, wl.top_k))
+        xd, wd = to_dev_act(x, wl.atype), torch.from_numpy(w).to(DEV)
+        for l in range(wl.layers):
+            _, _, sc, oc = copy.step(l, trace[s, l], xd, wd)
+            _, _, sr, orr = rt.step(l, trace[s, l], xd, wd)
+            assert (sr == trace[s, l]).all() and (sc == sr).all(), (s, l)
+            assert torch.equal(_bits(orr), _bits(oc)), (s, l)
+            if s == 0:
+                check_close(from_dev_act(orr), rt.reference(l, x, trace[s, l], w), wl.atype, wl.wtype,
+                            f"step {s} layer {l}")
+    assert rt.pool.stats() == copy.pool.stats()
+    copy.close()
+    rt.close()
