@@ -587,10 +587,15 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if ((int)threadIdx.x < nxc) {
+        {
+            // every thread repacks, and the chunk's sum (which reads all of it) is taken as
+            // used before the branch: the compiler would otherwise sink the activation loads
+            // into the branch, after the weights, and the repacking would wait for the
+            // weights too
             XI4 xc;
             xc.pack(xr);
-            xc.store_packed(xs + threadIdx.x * kPackedChunkBytes);
+            __asm__ volatile("" ::"v"(xc.sx));
+            if ((int)threadIdx.x < nxc) xc.store_packed(xs + threadIdx.x * kPackedChunkBytes);
         }
         for (int c = threadIdx.x + blockDim.x; c < nxc; c += blockDim.x) {
             XI4 xc;
