@@ -68,6 +68,23 @@ __global__ __launch_bounds__(kPolThreads) void k_policy(PolicyArgs a) {
     const int nblocks = (int)gridDim.x;
     const int par = a.ds.ctl[0] & 1;
     const SlotView cur = slot_view(a.ds.copy[par], a.E, a.N);
+    if (a.n <= 64 && !a.resident && a.evict != EVICT_SLRU && a.evict != EVICT_DECAY) {
+        // a decode step whose ids are all valid and resident (and the static rule quiet)
+        // changes keys only: the lead updates the current copy in place, the copies keep
+        // their roles, and no other workgroup has anything to do
+        __shared__ int allhit;
+        if (tid < 64) {
+            const int id = tid < a.n ? a.ids[tid] : 0;
+            const bool ok = tid >= a.n || ((unsigned)id < (unsigned)a.E && cur.map[id] >= 0);
+            const bool all = __all(ok);
+            if (tid == 0) allhit = all && (a.rule == 0 || a.n <= a.N);
+        }
+        __syncthreads();
+        if (allhit) {
+            if (lead) pol_hit_in_place(a, cur, a.n);
+            return;
+        }
+    }
     const Decision d = pol_decide(a, cur, L);
     // the workgroup's reads of the current copy returned before the decision's barriers
     int arrived = -1;

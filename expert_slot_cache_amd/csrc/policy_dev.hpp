@@ -687,9 +687,13 @@ __device__ inline void pol_hit_in_place(const PolicyArgs& a, const SlotView& cur
 // the last one of the launch make the other copy current.  Nothing of the launch
 // reads the current copy after that, and the lead's writes to the other copy are
 // complete when the launch is.  (The count is read back only at the end, so its
-// round trip overlaps the workgroup's work.)
+// round trip overlaps the workgroup's work.)  The count is relaxed: the reads it
+// stands for have returned (the wait below; their values fed the decision), which is
+// all it orders, and a release at agent scope would write back the XCD's L2 in every
+// workgroup.
 __device__ __forceinline__ int pol_reader_arrive(int32_t* ctl) {
-    return __hip_atomic_fetch_add(&ctl[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    return __hip_atomic_fetch_add(&ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void pol_last_reader(int32_t* ctl, int old, int nblocks) {
