@@ -635,14 +635,15 @@ __device__ inline void pol_publish(const PolicyArgs& a, const SlotView& nxt, con
     }
 }
 
-// An all-hit one-token step under LRU, FIFO or LFU, by the lead workgroup of the fused
-// step (wave 0; every id valid and resident, K <= 64).  Such a step changes only the
-// keys (LFU: also the uses) of its slots and the tick, exactly as the all-hit path of
-// pol_decide does (distinct id i, ascending, gets key tick + i; tick += D), and nothing
-// else in the launch reads keys or uses on such a step, so the lead applies the changes
-// to the current state copy in place and marks that the copies keep their roles
-// (ctl[2] = 0: the w2 launch does not flip them).  Results, record and counters are
-// those of the decision.
+// An all-hit step of at most 64 ids under LRU, FIFO or LFU, by the lead workgroup of
+// the fused step or of a prepare launch (wave 0; every id valid and resident; repeated
+// ids count once).  Such a step changes only the keys (LFU: also the uses) of its slots
+// and the tick, as the all-hit path of pol_decide does (distinct id i, ascending, gets
+// key tick + i; tick += D), and nothing else in the launch reads keys or uses on such a
+// step, so the lead applies the changes to the current state copy in place and marks
+// that the copies keep their roles (ctl[2] = 0: no flip after a fused step; a prepare
+// launch flips only after its readers have counted themselves in, which this one's do
+// not).  Results, record and counters are those of the decision.
 __device__ inline void pol_hit_in_place(const PolicyArgs& a, const SlotView& cur, int K) {
     const int lane = threadIdx.x;
     if (lane >= 64) return;
