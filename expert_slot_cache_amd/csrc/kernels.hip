@@ -1499,15 +1499,18 @@ __global__ __launch_bounds__(256) void k_grouped_w2(Slots sl, size_t stride,
 }
 
 // ---- grouped GEMMs for large slot groups: both operands through LDS -------------------
-// A workgroup of 4 waves (2 x 2) computes a tile of 64*WR rows x 64*WC weight rows (w13:
-// the gate rows of 32*WC columns and the matching up rows; w2: 64*WC output columns);
-// each wave owns WR row blocks x WC weight blocks of 32 (WR*WC accumulators).  Each
+// A workgroup of WGR x WGC waves computes a tile of 32*WR*WGR rows x 32*WC*WGC weight
+// rows (w13: the gate rows of half as many columns and the matching up rows; w2: as many
+// output columns); each wave owns WR row blocks x WC weight blocks of 32 (WR*WC
+// accumulators).  Each
 // 64-element k span of both operands is loaded into registers two spans ahead (two
 // register sets), then written into one of two LDS buffers the span before its MFMAs
 // read it.  A tile row is 128 bytes in LDS with its 16-byte chunk c at position
 // c ^ (row & 7), so the 32 rows one MFMA operand reads hit distinct banks.
-// The library uses WR = WC = 2: 128-row tiles, 64 KiB of LDS, two workgroups per CU (one
-// computes while the other waits for memory).  (Measured and not used: three spans ahead
+// The library uses WR = WC = 2 with 2 x 2 waves (128-row tiles of 128 weight rows, 64 KiB
+// of LDS, two workgroups per CU: one computes while the other waits for memory) or, for
+// large groups, 2 x 4 waves (128 x 256, 96 KiB, one workgroup of 8 waves per CU: each
+// activation row is read by half as many workgroups).  (Measured and not used: three spans ahead
 // needed more than the 256 registers of two workgroups per CU and spilled; one 128-row
 // workgroup per CU with three spans ahead was 1.3x slower; WR = WC = 4, 256-row tiles
 // with half an LDS operand read per MFMA but one workgroup per CU, 1.4x slower.)
@@ -1521,18 +1524,35 @@ struct GgRegs {
     uint4 a[NA], b[NB];
 };
 
-template <bool W13, int WR, int WC>
-__global__ __launch_bounds__(256, (WR * WC > 4 ? 1 : 2)) void k_gg(Slots sl, size_t stride,
+template <bool W13, int WR, int WC, int WGR, int WGC>
+__global__ __launch_bounds__(64 * WGR * WGC, (WGR * WGC > 4 ? 1 : 2)) void k_gg(Slots sl, size_t stride,
         const int32_t* __restrict__ grp, int tile_stride, const uint16_t* __restrict__ a_src, int K, int Kd,
         int ncols, size_t off_w, void* __restrict__ out, int ncbp) {
-    constexpr int RA = 64 * WR, RB = 64 * WC;        // tile rows of A and of the weights
-    constexpr int NA = RA / 32, NB = RB / 32;        // chunks per thread and span
+    constexpr int NW = WGR * WGC;                     // waves: WGR along rows x WGC along columns
+    constexpr int RA = 32 * WR * WGR, RB = 32 * WC * WGC;   // tile rows of A and of the weights
+    constexpr int NA = RA / (8 * NW), NB = RB / (8 * NW);   // chunks per thread and span
     constexpr int TA = RA * 128, TB = RB * 128;      // LDS bytes of one span
     __shared__ __attribute__((aligned(1024))) char lds[2][TA + TB];
-    const int cbk = blockIdx.x % ncbp;
-    const int tile = blockIdx.x / ncbp;
     constexpr int cspan = W13 ? RB / 2 : RB;        // output columns per workgroup
-    if (tile >= grp[0] || cbk * cspan >= ncols) return;
+    int cbk, tile;
+    if constexpr (NW == 4) {
+        cbk = blockIdx.x % ncbp;
+        tile = blockIdx.x / ncbp;
+        if (tile >= grp[0] || cbk * cspan >= ncols) return;
+    } else {
+        // ncbp = column blocks per tile.  The hardware hands workgroup b to XCD b % 8;
+        // each XCD takes one contiguous run of the (tile, column block) list, column block
+        // fastest, so the few column blocks of a tile (which read the same A rows) run
+        // side by side on one XCD
+        const int nwork = grp[0] * ncbp;
+        const int per = (nwork + 7) >> 3;
+        const int jx = (int)(blockIdx.x >> 3);
+        if (jx >= per) return;
+        const int wk = (int)(blockIdx.x & 7) * per + jx;
+        if (wk >= nwork) return;
+        tile = wk / ncbp;
+        cbk = wk - tile * ncbp;
+    }
     const SlotSpan sp = pick_slots(sl);
     const int slot = grp[16 + tile];
     const int row0 = grp[16 + tile_stride + tile];
@@ -1543,19 +1563,19 @@ __global__ __launch_bounds__(256, (WR * WC > 4 ? 1 : 2)) void k_gg(Slots sl, siz
     const int w = wave_id();
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int wr = w >> 1, wc = w & 1;
+    const int wr = w / WGC, wc = w % WGC;
     const int c0 = cbk * cspan;
     const char* wbase = sp.at(slot, stride) + off_w;
     const size_t rowb = (size_t)Kd * 2;
-    // this thread copies chunk lane % 8 of A rows w*RA/4 + q*8 + lane/8 (q < NA) and of
-    // weight rows w*RB/4 + q*8 + lane/8 (q < NB).  Weight rows are consecutive within a
+    // this thread copies chunk lane % 8 of A rows w*RA/NW + q*8 + lane/8 (q < NA) and of
+    // weight rows w*RB/NW + q*8 + lane/8 (q < NB).  Weight rows are consecutive within a
     // wave's share (the column blocks never pass the end: the shapes are multiples of
     // 256, and a wave's share lies in one of the w13 gate / up halves), so are A rows for
     // w2; w13 gathers its A rows.  In LDS the chunk goes to position (lane % 8) ^ (lane / 8)
     // of its row.
     const int ck = lane & 7;
-    const int ra0 = w * (RA / 4) + (lane >> 3);
-    const int rb0 = w * (RB / 4) + (lane >> 3);
+    const int ra0 = w * (RA / NW) + (lane >> 3);
+    const int rb0 = w * (RB / NW) + (lane >> 3);
     const int swz = (ck ^ (lane >> 3)) * 16;
     const int wrow0 = W13 ? (rb0 < RB / 2 ? c0 + rb0 : ncols + c0 + rb0 - RB / 2) : c0 + rb0;
     const char* bsrc = wbase + (size_t)wrow0 * rowb + ck * 16;
@@ -1971,6 +1991,9 @@ namespace {
 #ifndef MOE_GROUPED_MT
 #define MOE_GROUPED_MT 0
 #endif
+#ifndef MOE_GG_WIDE
+#define MOE_GG_WIDE 1
+#endif
 int grouped_mt(int n_pairs, int n_experts) {
     if (MOE_GROUPED_MT > 0) return MOE_GROUPED_MT;
     const int per = n_pairs / (n_pairs < n_experts ? n_pairs : n_experts);
@@ -2009,36 +2032,58 @@ hipError_t run_grouped_mt(const Geom& g, const ForwardArgs& a, const StageEvents
     uint16_t* act = static_cast<uint16_t*>(a.act);
     if (gg_shape(g, a) && MT == 4) {
         // tiles of 128 rows: both operands through LDS (k_gg); fp32 activations keep the
-        // staged w13 kernel, which converts them while staging
-        constexpr int W = 2;
-        const int gcb13 = ((g.I + 32 * W - 1) / (32 * W) + 7) / 8 * 8, gcb2 = ((g.H + 64 * W - 1) / (64 * W) + 7) / 8 * 8;
-        const dim3 gg13((unsigned)(tiles * gcb13)), gg2((unsigned)(tiles * gcb2));
-        if (AT == A_BF16) {
-            if (ev && ev->w13_start)
-                hipExtLaunchKernelGGL((k_gg<true, W, W>), gg13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0, a.sl,
-                                      g.slot_stride, a.grp, stride_t, static_cast<const uint16_t*>(a.x), g.K, g.H, g.I,
-                                      g.off_w13, (void*)act, gcb13);
-            else
-                hipLaunchKernelGGL((k_gg<true, W, W>), gg13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
-                                   static_cast<const uint16_t*>(a.x), g.K, g.H, g.I, g.off_w13, (void*)act, gcb13);
+        // staged w13 kernel, which converts them while staging.  With bf16 activations and
+        // 128 or more pairs per expert on average: 8 waves per workgroup over 256 weight
+        // rows (half the column blocks, one workgroup per CU); else 4 waves over 128.
+        // (Measured on OLMoE-shaped prefill, 64 slots: at 256 pairs per expert the wide
+        // form runs w2 in 181 us instead of 193, w13 alike; at 64 pairs it is 1-3 % slower.)
+        const int per = n / (n < g.E ? n : g.E);
+        const bool wide = MOE_GG_WIDE && AT == A_BF16 && per >= 128;
+        auto go = [&](auto kern, bool w13, int nthreads, unsigned nblocks, int cb) {
+            if (w13) {
+                if (ev && ev->w13_start)
+                    hipExtLaunchKernelGGL(kern, dim3(nblocks), dim3(nthreads), 0, s, ev->w13_start, ev->w13_stop, 0,
+                                          a.sl, g.slot_stride, a.grp, stride_t, static_cast<const uint16_t*>(a.x),
+                                          g.K, g.H, g.I, g.off_w13, (void*)act, cb);
+                else
+                    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(nthreads), 0, s, a.sl, g.slot_stride, a.grp,
+                                       stride_t, static_cast<const uint16_t*>(a.x), g.K, g.H, g.I, g.off_w13,
+                                       (void*)act, cb);
+            } else {
+                if (ev && ev->w2_start)
+                    hipExtLaunchKernelGGL(kern, dim3(nblocks), dim3(nthreads), 0, s, ev->w2_start, nullptr, 0, a.sl,
+                                          g.slot_stride, a.grp, stride_t, (const uint16_t*)act, g.K, g.I, g.H,
+                                          g.off_w2, (void*)a.y, cb);
+                else
+                    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(nthreads), 0, s, a.sl, g.slot_stride, a.grp,
+                                       stride_t, (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, cb);
+            }
+        };
+        if (wide) {
+            // column blocks per tile (exact); the grid covers the bound on (tile, block) pairs
+            const int cb13 = g.I / 128, cb2 = g.H / 256;
+            go(k_gg<true, 2, 2, 2, 4>, true, 512, (unsigned)((tiles * cb13 + 7) / 8 * 8), cb13);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            go(k_gg<false, 2, 2, 2, 4>, false, 512, (unsigned)((tiles * cb2 + 7) / 8 * 8), cb2);
         } else {
-            const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8;
-            const dim3 g13((unsigned)(tiles * ncb13));
-            if (ev && ev->w13_start)
-                hipExtLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop, 0,
-                                      a.sl, g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
-            else
-                hipLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp,
-                                   stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
+            constexpr int W = 2;
+            const int gcb13 = ((g.I + 32 * W - 1) / (32 * W) + 7) / 8 * 8, gcb2 = ((g.H + 64 * W - 1) / (64 * W) + 7) / 8 * 8;
+            if (AT == A_BF16) {
+                go(k_gg<true, W, W, 2, 2>, true, 256, (unsigned)(tiles * gcb13), gcb13);
+            } else {
+                const int ncb13 = ((g.I + kGBN - 1) / kGBN + 7) / 8 * 8;
+                const dim3 g13((unsigned)(tiles * ncb13));
+                if (ev && ev->w13_start)
+                    hipExtLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, ev->w13_start, ev->w13_stop,
+                                          0, a.sl, g.slot_stride, a.grp, stride_t, a.x, g.K, g.H, g.I, g.off_w13, act,
+                                          ncb13);
+                else
+                    hipLaunchKernelGGL((k_grouped_w13<AT, 4>), g13, dim3(256), 0, s, a.sl, g.slot_stride, a.grp,
+                                       stride_t, a.x, g.K, g.H, g.I, g.off_w13, act, ncb13);
+            }
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            go(k_gg<false, W, W, 2, 2>, false, 256, (unsigned)(tiles * gcb2), gcb2);
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (ev && ev->w2_start)
-            hipExtLaunchKernelGGL((k_gg<false, W, W>), gg2, dim3(256), 0, s, ev->w2_start, nullptr, 0, a.sl,
-                                  g.slot_stride, a.grp, stride_t, (const uint16_t*)act, g.K, g.I, g.H, g.off_w2,
-                                  (void*)a.y, gcb2);
-        else
-            hipLaunchKernelGGL((k_gg<false, W, W>), gg2, dim3(256), 0, s, a.sl, g.slot_stride, a.grp, stride_t,
-                               (const uint16_t*)act, g.K, g.I, g.H, g.off_w2, (void*)a.y, gcb2);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return launch_grouped_combine<AT>(g, a, ev, s);
     }
