@@ -140,3 +140,33 @@ def test_set_eviction_switches_policy_from_cold():
     with pytest.raises(binding.MoeError):
         rt.pool.set_eviction("decay")
     rt.close()
+
+
+@pytest.mark.parametrize("evict", POLICIES)
+@pytest.mark.parametrize("T,K,N,rule", [(8, 4, 12, "distinct"), (4, 4, 16, "static"), (16, 4, 14, "distinct")])
+def test_prepare_all_hit_steps_with_repeated_ids(T, K, N, rule, evict):
+    """Decode batches of several tokens (up to 64 ids, experts repeated across tokens) on a
+    small, hot expert set: most steps hit every id, and such a step's keys are updated in
+    place by the launch's lead.  Every step's path, misses and slot ids, and the state and
+    counters, match the oracle; steps with repeated ids that all hit do occur."""
+    E = 16
+    wl = synth.Workload(f"allhit-{T}", 1, E, K, 64, 32, N, T, 0, "f32", "f32", 1.4, 0.6, 0, 97 + T)
+    steps = 48
+    trace = synth.make_trace(wl, steps=steps)
+    zero = np.zeros(synth.expert_bytes("f32", 64, 32), np.uint8)
+    rig = Rig(wl, slots=N, rule=rule, policy="device", evict=evict, experts=[[zero] * E], max_tokens=T)
+    ref = LayerLRU(E, N, rule, evict)
+    repeated_all_hit = 0
+    for s in range(steps):
+        ids = trace[s, 0]
+        ids_d = torch.from_numpy(ids).to(DEV)
+        slot_d = torch.empty_like(ids_d)
+        rig.pool.prepare(0, ids_d, T, slot_d)
+        r = ref.step(ids)
+        assert rig.pool.last_step(0) == (r.path, r.misses), s
+        assert (slot_d.cpu().numpy() == r.slot_ids).all(), s
+        if r.path == 0 and not r.misses and len(np.unique(ids)) < ids.size:
+            repeated_all_hit += 1
+    _check_state(rig, [ref])
+    assert repeated_all_hit > 0
+    rig.close()
