@@ -794,6 +794,76 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
                                    xs_packed);
 }
 
+// INT4 w13 with a row's gate and up halves on two neighbouring lane groups (G <= 32
+// lanes each) instead of one: twice the waves for the same bytes, so more loads are in
+// flight per SIMD at batch 1.  Each group sums its row's chunks in chunk order and
+// butterflies over its G lanes exactly as w13_rows does for the gate and up sums, the
+// gate group takes the up sum from its neighbour (lane + G), and the result has the
+// same bits as w13_rows'.  grid.x: blocks of 4 * (32 / G) rows; grid.y: k; grid.z: tokens.
+template <int AT, int CPL>
+__global__ __launch_bounds__(256) void k_w13_i4s(Slots sl, size_t stride, const int32_t* __restrict__ slot_ids,
+                                                 const void* __restrict__ x, int H, int I, int gs, size_t off_w,
+                                                 size_t off_s, void* __restrict__ act) {
+    using X = XChunk<W_INT4, XSel<W_INT4, AT>::XT>;
+    using XI4 = XChunk<W_INT4, XT_I4>;
+    constexpr int EPC = WTraits<W_INT4>::EPC;
+    extern __shared__ __attribute__((aligned(16))) char xs[];   // the packed activations
+    const int t = blockIdx.z;
+    const int pair = blockIdx.z * gridDim.y + blockIdx.y;
+    const int slot = slot_ids[pair];
+    const SlotSpan sp = pick_slots(sl);
+    const bool valid = slot >= 0 && slot < sp.n();
+    const char* ebase = valid ? sp.at(slot, stride) : sp.a;
+    const int G = 1 << gs;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int gl = lane & (G - 1);
+    const int grp = lane >> gs;
+    const int half = grp & 1;                       // 0: the gate row, 1: the up row
+    const int i0 = ((int)blockIdx.x * 4 + wave) * (32 >> gs) + (grp >> 1);
+    const bool ok = valid && i0 < I;
+    const int nxc = H / 32;
+    // the activation chunk first (see w13_rows)
+    const XI4::Raw xr = XI4::fetch(PlainMem(x), (size_t)t * H + (size_t)min((int)threadIdx.x, nxc - 1) * 32);
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::"s"(ebase), "s"(stride), "s"(off_w));
+    const SlotReader rd(ebase, valid ? stride : 0);
+    const size_t row_bytes = (size_t)CPL * G * 16;
+    const int wrow = (half ? I : 0) + min(i0, I - 1);
+    const uint32_t ow = (uint32_t)(off_w + (size_t)wrow * row_bytes) + (uint32_t)gl * 16u;
+    const int spr = H / 128;
+    uint4 w[CPL];
+    uint16_t sc[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) w[j] = rd.load16(ow, (uint32_t)(j * G) * 16u);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) sc[j] = rd.scale_bits(off_s + ((size_t)wrow * spr + ((j * G + gl) >> 2)) * 2);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        XI4 xc;
+        xc.pack(xr);
+        __asm__ volatile("" ::"v"(xc.sx));
+        if ((int)threadIdx.x < nxc) xc.store_packed(xs + threadIdx.x * kPackedChunkBytes);
+    }
+    for (int c = threadIdx.x + blockDim.x; c < nxc; c += blockDim.x) {
+        XI4 xc;
+        xc.template load<AT>(PlainMem(x), (size_t)t * H + (size_t)c * 32);
+        xc.store_packed(xs + c * kPackedChunkBytes);
+    }
+    __syncthreads();
+    float v[1] = {0.0f};
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        X xv;
+        xv.template load<AT>(PackedX{xs, (size_t)t * H}, (size_t)t * H + (size_t)(j * G + gl) * EPC);
+        v[0] += cdot(w[j], xv) * bf16_to_f32(sc[j]);
+    }
+    group_sum_n<1>(v, G);
+    const float up = __shfl_xor(v[0], G, 64);
+    if (gl == 0 && half == 0 && i0 < I)
+        store_act<ActOf<W_INT4>::AT>(act, (size_t)pair * I + i0, ok ? silu(v[0]) * up : 0.0f);
+}
+
 // ---- the fused one-token decode step: decision + w13 + tail copies ----------------------
 // Workgroup roles by index: 0 = the lead (the decision, the state after the step, the
 // counters, the step's slot ids and path word); 1 .. n_copy = copy workers (the part
@@ -1766,6 +1836,9 @@ namespace {
 #ifndef MOE_W13_WPR
 #define MOE_W13_WPR 1
 #endif
+#ifndef MOE_W13_I4_SPLIT
+#define MOE_W13_I4_SPLIT 1
+#endif
 #ifndef MOE_W13_RP64
 #define MOE_W13_RP64 2
 #endif
@@ -1824,6 +1897,20 @@ hipError_t launch_w13(const Geom& g, const ForwardArgs& a, int G, const StageEve
     return hipGetLastError();
 }
 
+template <int AT, int CPL>
+hipError_t launch_w13_i4s(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
+    const int rows_per_block = 4 * (32 / G);
+    const dim3 grid((g.I + rows_per_block - 1) / rows_per_block, g.K, a.T);
+    const size_t lds = (size_t)(g.H / 32) * kPackedChunkBytes;
+    if (ev && ev->w13_start)
+        hipExtLaunchKernelGGL((k_w13_i4s<AT, CPL>), grid, dim3(256), (uint32_t)lds, s, ev->w13_start, ev->w13_stop, 0,
+                              a.sl, g.slot_stride, a.slot_ids, a.x, g.H, g.I, log2_of(G), g.off_w13, g.off_s13, a.act);
+    else
+        hipLaunchKernelGGL((k_w13_i4s<AT, CPL>), grid, dim3(256), lds, s, a.sl, g.slot_stride, a.slot_ids, a.x, g.H,
+                           g.I, log2_of(G), g.off_w13, g.off_s13, a.act);
+    return hipGetLastError();
+}
+
 template <int WT, int AT, int CPL, int RP, int WPR>
 hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEvents* ev, hipStream_t s) {
     constexpr int NWMAX = 16;
@@ -1870,6 +1957,9 @@ hipError_t run_w13(const Geom& g, const ForwardArgs& a, const StageEvents* ev, h
     const int G = group_lanes(nc);
     const int wpr = waves_per_row(nc, G, MOE_W13_WPR);
     const int cpl = nc / (G * wpr);
+    if (WT == W_INT4 && G != 64 && MOE_W13_I4_SPLIT) {
+        MOE_CPL_SWITCH(cpl, (launch_w13_i4s<AT, C>(g, a, G, ev, s)))
+    }
     if (G != 64) {
         MOE_CPL_SWITCH(cpl, (launch_w13<WT, AT, C, 1, 1>(g, a, G, ev, s)))
     }
