@@ -86,7 +86,7 @@ struct Timing {
 // Pinned allocations are made in pieces of at most this many bytes (whole experts).
 constexpr size_t kStorePiece = (size_t)1 << 30;
 // Workgroups of one device-policy step: each runs the decision, then the copies
-// (64 KiB units) spread over all of them.
+// (128 KiB units) spread over all of them.
 constexpr int kPolicyGrid = 128;
 // Copy workers of a fused one-token step (the part of each missed expert past its w13
 // rows, 64 KiB units).
