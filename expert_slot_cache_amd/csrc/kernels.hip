@@ -517,10 +517,14 @@ __device__ __forceinline__ void store_act(void* __restrict__ p, size_t i, float 
 // act[pair][i] = silu(W13[s][i] . x[t]) * (W13[s][I + i] . x[t])
 // G = 1 << gs lanes share a row.  The slot id and the path word are read first, side by
 // side: they are the only loads the weight addresses depend on.
-template <int WT, int AT, int CPL, int RP, int WPR>
+// MULTI (bf16 / fp32 weights, WPR == 1): `later` holds the pairs after `pair` that use
+// the same slot (pair q = token q / K, k = q % K); each is computed, in pair order, from
+// the weight registers of this one read, exactly as its own block would compute it.
+template <int WT, int AT, int CPL, int RP, int WPR, bool MULTI = false>
 __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const void* __restrict__ x, int H, int I,
                                          int gs, size_t off_w, size_t off_s, void* __restrict__ act, int t, int pair,
-                                         int rblk, float (*red)[2][RP], char* xs, bool xr_ready = false) {
+                                         int rblk, float (*red)[2][RP], char* xs, uint64_t later = 0, int K = 1) {
+    static_assert(!MULTI || (WT != W_INT4 && WPR == 1), "one read for several pairs: bf16 / fp32, one wave per row");
     using X = XChunk<WT, XSel<WT, AT>::XT>;
     constexpr int EPC = WTraits<WT>::EPC;
     constexpr int ACT = ActOf<WT>::AT;
@@ -745,6 +749,32 @@ __device__ __forceinline__ void w13_rows(const PairIn& pin, size_t stride, const
                 pg[p] = gu[2 * p];
                 pu[p] = gu[2 * p + 1];
             }
+            if constexpr (MULTI) {
+                for (uint64_t m = later; m; m &= m - 1) {
+                    const int q = __builtin_ctzll(m);
+                    const int tq = q / K;
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j)
+                        xv[j].template load<AT>(PlainMem(x), (size_t)tq * H + (size_t)((part * CPL + j) * G + gl) * EPC);
+                    float hq[2 * RP];
+#pragma unroll
+                    for (int p = 0; p < RP; ++p) {
+                        float a = 0.0f, b = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) {
+                            a += cdot(wg[p][j], xv[j]);
+                            b += cdot(wu[p][j], xv[j]);
+                        }
+                        hq[2 * p] = a;
+                        hq[2 * p + 1] = b;
+                    }
+                    group_sum_n<2 * RP>(hq, G);
+                    if (gl == 0)
+#pragma unroll
+                        for (int p = 0; p < RP; ++p)
+                            if (i0 + p < I) store_act<ACT>(act, (size_t)q * I + i0 + p, silu(hq[2 * p]) * hq[2 * p + 1]);
+                }
+            }
         } else {
 #pragma unroll
             for (int p = 0; p < RP; ++p) pg[p] = pu[p] = 0.0f;
@@ -790,6 +820,21 @@ __global__ __launch_bounds__(256) void k_w13_gemv(Slots sl, size_t stride, const
     const SlotSpan sp = pick_slots(sl);
     const bool valid = slot >= 0 && slot < sp.n();
     const PairIn pin{valid ? sp.at(slot, stride) : sp.a, nullptr, valid};
+    if constexpr (WT != W_INT4 && WPR == 1) {
+        // several tokens (at most 64 pairs): the block of the first pair on a slot computes
+        // every pair on it from one read of its rows; the other blocks on it have no work
+        const int TK = (int)(gridDim.y * gridDim.z);
+        if (gridDim.z > 1 && TK <= 64 && valid) {
+            const int lane = threadIdx.x & 63;
+            const int sq = slot_ids[min(lane, TK - 1)];
+            const uint64_t same = __ballot(lane < TK && sq == slot);
+            if (same & ((1ull << pair) - 1)) return;
+            const uint64_t later = pair == 63 ? 0 : same & (~0ull << (pair + 1));
+            w13_rows<WT, AT, CPL, RP, WPR, true>(pin, stride, x, H, I, gs, off_w, off_s, act, blockIdx.z, pair,
+                                                 blockIdx.x, red, xs_packed, later, (int)gridDim.y);
+            return;
+        }
+    }
     w13_rows<WT, AT, CPL, RP, WPR>(pin, stride, x, H, I, gs, off_w, off_s, act, blockIdx.z, pair, blockIdx.x, red,
                                    xs_packed);
 }

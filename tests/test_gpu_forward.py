@@ -130,6 +130,36 @@ def test_backend_matrix(wtype, atype, T, one_call):
     resident.close()
 
 
+@pytest.mark.parametrize("wtype,atype,H,I", [("bf16", "bf16", 256, 128), ("bf16", "bf16", 2048, 256),
+                                             ("f32", "f32", 256, 128), ("bf16", "f32", 512, 128),
+                                             ("int4", "bf16", 256, 128)])
+@pytest.mark.parametrize("T", [2, 5, 8])
+def test_decode_tokens_sharing_experts(wtype, atype, H, I, T):
+    """Decode ubatches whose tokens share experts (the w13 GEMV reads a shared expert's
+    rows once for all of its pairs): every token's row has the bits of the same token
+    run alone, pooled equals all-resident bit for bit, and the step is within tolerance
+    of the oracle."""
+    E, K = 12, 4
+    wl = synth.Workload("shared", 1, E, K, H, I, E, T, 0, wtype, atype, 1.0, 0.0, 0, 23)
+    rng = np.random.default_rng(29 + T)
+    rows = [rng.permutation(5)[:K] for _ in range(T - 1)] + [np.array([8, 9, 10, 11])]
+    ids = np.stack(rows).astype(np.int32)                      # most pairs on experts 0..4
+    xs, ws = _inputs(wl, 1, T)
+    res = Rig(wl, slots=E, resident=True, std=0.05, max_tokens=T)
+    pooled = Rig(wl, slots=E, experts=res.experts, max_tokens=T)
+    xd, wd = to_dev_act(xs[0], atype), torch.from_numpy(ws[0]).to(DEV)
+    got_r = from_dev_act(res.step(0, ids, xd, wd)[3])
+    got_p = from_dev_act(pooled.step(0, ids, xd, wd)[3])
+    assert np.array_equal(got_p.view(np.uint32), got_r.view(np.uint32)), "pooled vs resident"
+    check_close(got_r, res.reference(0, xs[0], ids, ws[0]), atype, wtype, f"T={T}")
+    for t in range(T):
+        one = from_dev_act(res.step(0, ids[t:t + 1], to_dev_act(xs[0][t:t + 1], atype),
+                                    torch.from_numpy(np.ascontiguousarray(ws[0][t:t + 1])).to(DEV))[3])
+        assert np.array_equal(one[0].view(np.uint32), got_r[t].view(np.uint32)), f"token {t} alone"
+    res.close()
+    pooled.close()
+
+
 @ONE_CALL
 def test_fallback_bitwise_equal_to_no_pool(one_call):
     """Bypass control: with a pool allocated, steps that overflow it take the
