@@ -67,7 +67,8 @@ typedef int32_t moe_status_t;
 #define MOE_A_BF16  1
 /* route rule: when a step bypasses the pool ([llama-pool] prefill rule) */
 #define MOE_RULE_DISTINCT 0  /* distinct experts of the step > n_slots (default) */
-#define MOE_RULE_STATIC   1  /* top_k * n_tokens > n_slots ("can touch more") */
+#define MOE_RULE_STATIC   1  /* top_k * n_tokens > n_slots (the ubatch could reach more
+                                experts than there are slots) */
 /* copy engine of the miss path (host store -> HBM) */
 #define MOE_COPY_KERNEL 0  /* a copy kernel on the copy streams, reading the pinned store
                               through its device mapping (default: on MI355X it moves a
@@ -200,8 +201,8 @@ size_t moe_expert_bytes(int32_t wtype, int32_t hidden, int32_t inter);
 /* Allocates the pinned store (n_layers * n_experts experts; contents undefined
  * until moe_pool_load_expert writes them), one HBM
  * pool per layer (n_slots experts plus a zeroed 256-byte tail, allocated once so
- * slot addresses never change: [vLLM-cache] "fixed-address (allocated once at
- * init)"; [llama-pool] Design item 1), a staging area of min(E, K*max_tokens)
+ * slot addresses never change: [vLLM-cache] Architecture, the slot pool allocated
+ * once at fixed addresses; [llama-pool] Design item 1), a staging area of min(E, K*max_tokens)
  * experts, the per-layer map tables (int32 [E], all -1) and scratch buffers.
  * hbm_budget_bytes, when set, caps the HBM part ([llama-pool] Design item 4).
  * Errors: EINVAL (bad config), ENOMEM, EHIP. */
