@@ -86,6 +86,12 @@ def parse():
                     help="eviction policy of the headline run")
     ap.add_argument("--sweep-workload", default="fanout_int4_e512", choices=sorted(synth.WORKLOADS),
                     help="workload of the pool-size sweep (one filled store serves every point)")
+    ap.add_argument("--multi-tokens", default="8",
+                    help="comma-separated tokens per step of extra decode points on the headline "
+                         "workload with every expert resident (the kernels at several tokens, no "
+                         "host link; '' = none)")
+    ap.add_argument("--multi-steps", type=int, default=100,
+                    help="timed steps of each multi-token point (untimed steps before it: 20)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None, help="tokens per ubatch (default: workload's)")
     ap.add_argument("--rule", default="distinct", choices=["distinct", "static"])
@@ -512,6 +518,24 @@ def main():
     del xs_d, ws_d
     torch.cuda.empty_cache()
 
+    # decode at several tokens per step, every expert resident: the GEMVs' rate on the
+    # distinct experts of a step (a shared expert's w13 rows are read once per step)
+    multi = []
+    for tm in [int(v) for v in args.multi_tokens.split(",") if v.strip()] if args.multi_tokens else []:
+        if tm < 2 or tm > DECODE_MAX_TOKENS or args.graph:
+            continue
+        mwl = wl.with_(tokens=tm)
+        margs = argparse.Namespace(**vars(args))
+        margs.steps, margs.warmup = args.multi_steps, 20
+        margs.prefetch_accuracy = None
+        log(f"[bench] multi-token point: {tm} tokens per step, all experts resident")
+        m_trace, _, _, m_xd, m_wd = inputs(mwl, margs.warmup + margs.steps)
+        r, _ = run_point(margs, torch, binding, mwl, E, m_trace, m_xd, m_wd, gen, True)
+        multi.append({"tokens_per_step": tm, "steps": margs.steps, "warmup": margs.warmup, "resident": True,
+                      **{k: r[k] for k in ("value", "ms_per_step", "roofline") if k in r}})
+        del m_xd, m_wd
+        torch.cuda.empty_cache()
+
     # the pool-size sweep: one pool with the largest slot count, its store filled once,
     # set to each point's slot count (cold) in turn
     sweep = None
@@ -571,6 +595,8 @@ def main():
     if "link_gbps_misses" in main_res:
         line["link_frac"] = round(main_res["link_gbps_misses"] / peak_link, 4)
     line["roofline"] = main_res.get("roofline")
+    if multi:
+        line["multi_token"] = multi
     if sweep is not None:
         for r in sweep["points"]:
             if "link_gbps_misses" in r:
