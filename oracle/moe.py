@@ -15,7 +15,7 @@ g128 experts in "Running 125B MoE on Two 32 GB Cards", section 1):
     out[t] = resid[t] + sum_k w_k * y_k   (resid = 0 when absent)
 
 Readings: rows [0, I) of w13 are the gate, rows [I, 2I) the up projection; no
-bias (the page-1 cache is disabled for MoE layers with bias); INT4-g128 weights
+bias (the vLLM PR's cache is off for MoE layers with bias, Limitations (PR 1)); INT4-g128 weights
 decode as (q - 8) * s with one bf16 scale per 128 inputs of a row and no zero
 point (the 2.417 MiB per expert of the 125B-MoE post fixes the byte count at
 codes plus bf16 scales only).

@@ -1,5 +1,5 @@
 """GPU tests of the slot manager on the GPU (policy "device"): the same LRU as the
-page-1 prepare() (vLLM PR "Run MoE models exceeding VRAM via expert CPU offloading
+prepare() of the vLLM PR "Run MoE models exceeding VRAM via expert CPU offloading
 with GPU cache", section "How it works" and the review thread's OrderedDict form)
 and the same route rule (llama.cpp "Persistent expert slot pool" prefill rule), run
 by a kernel on device-resident state.  Every step's path, miss list and slot ids,

@@ -1,6 +1,6 @@
 """GPU parity of the slot-indexed fused MoE against the float64 oracle, and
 bit-identity of the pooled layer with the all-resident layer (the pooled GPU path
-must match the all-resident GPU path exactly; the page-1 FullGPUProvider is the
+must match the all-resident GPU path exactly; the vLLM PR's FullGPUProvider is the
 all-resident path; the llama.cpp discussion's backend matrix compares pooled and
 host-copy paths bit for bit over dtype x ubatch {1, 3} x cold / full eviction /
 hit + reload / rebuild)."""
