@@ -1,6 +1,6 @@
 """GPU tests of prepare(): slot maps, miss lists, counters, LRU order and slot bytes,
 bit-exact against the oracle.  Re-creates the unit list of the vLLM PR "Run MoE
-models exceeding VRAM via expert CPU offloading with GPU cache", test results) and
+models exceeding VRAM via expert CPU offloading with GPU cache" (test results) and
 the llama.cpp discussion's checks (bypass control, stale map table)."""
 import time
 
