@@ -1,6 +1,6 @@
 """GPU tests of the slot manager on the GPU (policy "device"): the same LRU as the
 prepare() of the vLLM PR "Run MoE models exceeding VRAM via expert CPU offloading
-with GPU cache", section "How it works" and the review thread's OrderedDict form)
+with GPU cache" (section "How it works" and the review thread's OrderedDict form)
 and the same route rule (llama.cpp "Persistent expert slot pool" prefill rule), run
 by a kernel on device-resident state.  Every step's path, miss list and slot ids,
 and the final map / owners / LRU order / counters, are bit-exact against the
