@@ -1192,7 +1192,10 @@ __device__ __forceinline__ void w2_combine(const float* __restrict__ ys, int RB,
 
 // grid.x: blocks of RB output rows; grid.y: tokens.  ONE: the block has one wave
 // per (expert, part) task (K * WPR <= NWMAX), so a wave's slot is known before any
-// branch.
+// branch.  xcd_T > 1 (several tokens, row blocks a multiple of 8): a 1-D grid in which
+// the blocks of one row block for tokens 0..T-1 are 8 apart, so they run on the same
+// XCD one after another and an expert shared by several tokens is served from that
+// XCD's L2 after its first read (workgroups go to the 8 XCDs round robin).
 template <int WT, int AT, int CPL, int RP, int WPR, int NWMAX, bool ONE>
 __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stride,
                                                            const int32_t* __restrict__ slot_ids,
@@ -1200,16 +1203,21 @@ __global__ __launch_bounds__(NWMAX * 64) void k_w2_combine(Slots sl, size_t stri
                                                            const void* __restrict__ act,
                                                            const void* __restrict__ resid, void* __restrict__ out,
                                                            int K, int H, int I, int gs, size_t off_w, size_t off_s,
-                                                           int32_t* __restrict__ flip) {
+                                                           int32_t* __restrict__ flip, int xcd_T) {
     extern __shared__ float ys[];               // [K][WPR][RB]
+    int bx = blockIdx.x, t = blockIdx.y;
+    if (xcd_T > 1) {
+        const int j = (int)blockIdx.x >> 3;
+        t = j % xcd_T;
+        bx = (j / xcd_T) * 8 + ((int)blockIdx.x & 7);
+    }
     // after a fused step whose lead wrote the other state copy (ctl[2]): that copy becomes
     // current (nothing here reads the state)
-    if (flip && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && flip[2]) flip[0] ^= 1;
+    if (flip && bx == 0 && t == 0 && threadIdx.x == 0 && flip[2]) flip[0] ^= 1;
     const int nw = blockDim.x >> 6;
     const int wave = wave_id();
-    const int t = blockIdx.y;
-    const W2Lane ln = w2_lane(gs, RP, blockIdx.x * (RP * (64 >> gs)));
-    const int rb0 = blockIdx.x * ln.RB;
+    const W2Lane ln = w2_lane(gs, RP, bx * (RP * (64 >> gs)));
+    const int rb0 = bx * ln.RB;
     if (ONE) {
         // the wave's slot and the path word, side by side, before any branch
         const int slot = slot_ids[t * K + wave / WPR];
@@ -1965,15 +1973,17 @@ hipError_t launch_w2(const Geom& g, const ForwardArgs& a, int G, const StageEven
     size_t lds = (size_t)tasks * RB * sizeof(float);
     if (WT == W_INT4 && tasks <= NWMAX)   // the token's packed act vectors
         lds = ((lds + 15) & ~(size_t)15) + (size_t)g.K * (g.I / 32) * kPackedChunkBytes;
-    const dim3 grid((g.H + RB - 1) / RB, a.T);
+    const int nrb = (g.H + RB - 1) / RB;
+    const int xcd_T = a.T > 1 && nrb % 8 == 0 ? a.T : 0;
+    const dim3 grid = xcd_T ? dim3(nrb * a.T) : dim3(nrb, a.T);
     auto go = [&](auto kern) {
         if (ev && ev->w2_start)
             hipExtLaunchKernelGGL(kern, grid, dim3(64 * nw), (uint32_t)lds, s, ev->w2_start, ev->w2_stop, 0, a.sl,
                                   g.slot_stride, a.slot_ids, a.topk_w, a.act, a.resid, a.out, g.K, g.H, g.I,
-                                  log2_of(G), g.off_w2, g.off_s2, a.flip_par);
+                                  log2_of(G), g.off_w2, g.off_s2, a.flip_par, xcd_T);
         else
             hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, s, a.sl, g.slot_stride, a.slot_ids, a.topk_w, a.act,
-                               a.resid, a.out, g.K, g.H, g.I, log2_of(G), g.off_w2, g.off_s2, a.flip_par);
+                               a.resid, a.out, g.K, g.H, g.I, log2_of(G), g.off_w2, g.off_s2, a.flip_par, xcd_T);
     };
     if (tasks <= NWMAX)
         go(k_w2_combine<WT, AT, CPL, RP, WPR, NWMAX, true>);
