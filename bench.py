@@ -43,9 +43,9 @@ PF_AFTER_LAYER, PF_AFTER_QUEUED, PF_AFTER_PREVIOUS = 0, 1, 2   # moe_pool_prefet
 PMC_TRAFFIC = {
     # per dispatch, median over the run's dispatches (all-hit steps for the fused step);
     # FETCH_SIZE scaled by the 256 MiB copy calibration (262144 / 131086.1 KiB)
-    ("olmoe_bf16_e64", "303269196d14c46a"): {"fetch_kib": 32866.8, "fetch_scale": 1.9998,
-                                             "write_kib": 32.5, "write_scale": 1.0},
-    ("fanout_int4_e512", "303269196d14c46a"): {"fetch_kib": 8370.0, "fetch_scale": 1.9998,
+    ("olmoe_bf16_e64", "aad76ee1c1c849c7"): {"fetch_kib": 32860.3, "fetch_scale": 1.9998,
+                                             "write_kib": 64.7, "write_scale": 1.0},
+    ("fanout_int4_e512", "aad76ee1c1c849c7"): {"fetch_kib": 8369.9, "fetch_scale": 1.9998,
                                                "write_kib": 25.0, "write_scale": 1.0},
 }
 

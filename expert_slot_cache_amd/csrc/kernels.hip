@@ -1886,6 +1886,9 @@ namespace {
 
 // Launch shape when a whole wave shares a row (G == 64): waves per row (WPR) and
 // rows per lane group (RP); otherwise one wave part and one row (pair) per group.
+// Measured on the OLMoE shapes: w13 with one row per wave (the fused one-token step
+// 14.7 vs 15.2 us with two), w2 with four rows per wave (8.2-8.4 vs 8.3-8.6 us at one
+// token, 29.6 vs 33.2 us at eight; 9.1-9.7 / 43.0 us with one).
 #ifndef MOE_W13_WPR
 #define MOE_W13_WPR 1
 #endif
@@ -1893,13 +1896,13 @@ namespace {
 #define MOE_W13_I4_SPLIT 1
 #endif
 #ifndef MOE_W13_RP64
-#define MOE_W13_RP64 2
+#define MOE_W13_RP64 1
 #endif
 #ifndef MOE_W2_WPR
 #define MOE_W2_WPR 1
 #endif
 #ifndef MOE_W2_RP64
-#define MOE_W2_RP64 2
+#define MOE_W2_RP64 4
 #endif
 
 int log2_of(int g) {
